@@ -1,0 +1,427 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+No page prints a numeric output of any step, so each oracle function is pinned
+by closed forms, invariants, special cases, hand-worked int8 blocks
+(tests/golden/q8_blocks.txt) or float64 library routines, chosen so that a
+dropped term, a wrong sign or index, or a transposed operand fails a test.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from conftest import rel_l2
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_unit_rms(orc):
+    x = _rng(1).standard_normal(300) * 3.0
+    y = orc.rmsnorm(x, np.ones(300, np.float32), 0.0)
+    assert abs(math.sqrt(np.mean(y * y)) - 1.0) < 1e-15
+
+
+def test_rmsnorm_eps_closed_form(orc):
+    x = _rng(2).standard_normal(64) * 0.01
+    eps = 1e-5
+    ms = np.mean(x * x)
+    y = orc.rmsnorm(x, np.ones(64, np.float32), eps)
+    assert abs(math.sqrt(np.mean(y * y)) - math.sqrt(ms / (ms + eps))) < 1e-14
+
+
+def test_rmsnorm_scale_invariant_and_gain_elementwise(orc):
+    x = _rng(3).standard_normal(96)
+    g = (1 + 0.3 * _rng(4).standard_normal(96)).astype(np.float32)
+    y1 = orc.rmsnorm(x, np.ones(96, np.float32), 0.0)
+    assert np.allclose(orc.rmsnorm(7.5 * x, np.ones(96, np.float32), 0.0), y1, rtol=1e-14, atol=0)
+    assert np.allclose(orc.rmsnorm(x, g, 0.0), g.astype(np.float64) * y1, rtol=1e-14, atol=0)
+
+
+def test_rmsnorm_worked_example(orc):
+    # x = (3, 4): mean square 12.5, so y = x * sqrt(2) / 5
+    y = orc.rmsnorm(np.array([3.0, 4.0]), np.ones(2, np.float32), 0.0)
+    assert np.allclose(y, [3 * math.sqrt(2) / 5, 4 * math.sqrt(2) / 5], rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rope_position_zero_is_identity(orc):
+    u = _rng(5).standard_normal(128)
+    assert np.array_equal(orc.rope(u, 0), u)
+
+
+def test_rope_preserves_pair_norms(orc):
+    u = _rng(6).standard_normal(128)
+    r = orc.rope(u, 3071)
+    assert np.allclose(np.hypot(r[0::2], r[1::2]), np.hypot(u[0::2], u[1::2]), rtol=1e-14)
+
+
+def test_rope_closed_forms(orc):
+    # hd = 2: the only pair turns by pos * theta^0 = pos radians
+    assert np.allclose(orc.rope([1.0, 0.0], 1), [math.cos(1), math.sin(1)], atol=1e-15)
+    # hd = 4, theta = 10000: pair 1 turns by pos * 10000^(-1/2) = pos / 100
+    r = orc.rope([1.0, 0.0, 0.0, 1.0], 100, 10000.0)
+    assert np.allclose(r, [math.cos(100), math.sin(100), -math.sin(1), math.cos(1)], atol=1e-13)
+
+
+def test_rope_is_complex_rotation(orc):
+    hd, pos, theta = 48, 777, 10000.0
+    u = _rng(7).standard_normal(hd)
+    z = (u[0::2] + 1j * u[1::2]) * np.exp(1j * pos * theta ** (-np.arange(0, hd, 2) / hd))
+    r = orc.rope(u, pos, theta)
+    assert np.allclose(r[0::2], z.real, atol=1e-12) and np.allclose(r[1::2], z.imag, atol=1e-12)
+
+
+def test_rope_relative_position(orc):
+    q, k = _rng(8).standard_normal(64), _rng(9).standard_normal(64)
+    m, n = 900, 250
+    lhs = orc.rope(q, m) @ orc.rope(k, n)
+    rhs = orc.rope(q, m - n) @ k
+    assert abs(lhs - rhs) < 1e-11
+
+
+# ---------------------------------------------------------------- softmax / attention
+
+def test_softmax_sum_shift_and_closed_form(orc):
+    s = _rng(10).standard_normal(257) * 5
+    w = orc.softmax(s)
+    assert abs(w.sum() - 1.0) < 257 * 2.0 ** -52
+    assert np.allclose(orc.softmax(s + 123.0), w, rtol=1e-13, atol=0)
+    assert np.allclose(orc.softmax([0.0, math.log(3.0)]), [0.25, 0.75], rtol=1e-15)
+    assert np.allclose(orc.softmax(np.full(9, 2.5)), np.full(9, 1 / 9), rtol=1e-15)
+
+
+def test_attention_single_position_returns_v(orc):
+    hd = 128
+    K = _rng(11).standard_normal((1, hd)).astype(np.float32)
+    V = _rng(12).standard_normal((1, hd)).astype(np.float32)
+    q = _rng(13).standard_normal(hd)
+    assert np.array_equal(orc.attend(q, K, V), V[0].astype(np.float64))
+
+
+def test_attention_zero_query_is_mean(orc):
+    K = _rng(14).standard_normal((37, 16)).astype(np.float32)
+    V = _rng(15).standard_normal((37, 16)).astype(np.float32)
+    o = orc.attend(np.zeros(16), K, V)
+    assert np.allclose(o, V.astype(np.float64).mean(axis=0), rtol=1e-13, atol=1e-15)
+
+
+def test_attention_two_positions_closed_form(orc):
+    # q = (2 ln 3, 0, 0, 0), K rows e0 and 0: scores (ln 3, 0) after 1/sqrt(4)
+    q = np.array([2 * math.log(3.0), 0, 0, 0])
+    K = np.array([[1, 0, 0, 0], [0, 0, 0, 0]], np.float32)
+    V = np.array([[4, 0, 8, -4], [0, 4, -8, 12]], np.float32)
+    o = orc.attend(q, K, V)
+    assert np.allclose(o, 0.75 * V[0] + 0.25 * V[1], rtol=1e-14, atol=1e-14)
+
+
+def test_attention_position_permutation_and_bf16(orc):
+    K = _rng(16).standard_normal((50, 32)).astype(np.float32)
+    V = _rng(17).standard_normal((50, 32)).astype(np.float32)
+    q = _rng(18).standard_normal(32)
+    p = _rng(19).permutation(50)
+    assert np.allclose(orc.attend(q, K[p], V[p]), orc.attend(q, K, V), rtol=1e-13, atol=1e-15)
+    Kb, Vb = synth.f32_to_bf16_bits(K), synth.f32_to_bf16_bits(V)
+    wide = orc.attend(q, synth.bf16_bits_to_f32(Kb), synth.bf16_bits_to_f32(Vb))
+    assert np.array_equal(orc.attend(q, Kb, Vb, "bf16"), wide)
+
+
+# ---------------------------------------------------------------- projections / SwiGLU
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_matvec_matches_float64_matmul(orc, dtype):
+    Wf = _rng(20).standard_normal((70, 96)).astype(np.float32)
+    W = synth.f32_to_bf16_bits(Wf) if dtype == "bf16" else Wf
+    Wd = (synth.bf16_bits_to_f32(W) if dtype == "bf16" else W).astype(np.float64)
+    x = _rng(21).standard_normal(96)
+    assert rel_l2(orc.matvec(W, x, dtype), Wd @ x) < 1e-14
+    # a column block (row-split shard): columns 32..63
+    assert rel_l2(orc.matvec(W, x[:32], dtype, col0=32, K=32), Wd[:, 32:64] @ x[:32]) < 1e-14
+
+
+def test_silu(orc):
+    import torch
+    assert orc.silu(0.0) == 0.0
+    z = np.linspace(-30, 30, 121)
+    ref = torch.nn.functional.silu(torch.tensor(z, dtype=torch.float64)).numpy()
+    assert np.allclose([orc.silu(v) for v in z], ref, rtol=1e-14, atol=1e-300)
+    assert abs(orc.silu(40.0) - 40.0) < 1e-15 * 40
+
+
+# ---------------------------------------------------------------- int8 codec
+
+def _golden_blocks():
+    blocks, cur = [], None
+    with open(os.path.join(GOLDEN, "q8_blocks.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("block"):
+                cur = {"name": line.split()[1], "x": [], "codes": []}
+                blocks.append(cur)
+            elif line.startswith("scale"):
+                cur["scale"] = _num(line.split()[1])
+            else:
+                a, b = line.split("->")
+                cur["x"].append(_num(a.strip()))
+                cur["codes"].append(int(b))
+    return blocks
+
+
+def _num(s):
+    return float.fromhex(s) if "0x" in s else float(s)
+
+
+@pytest.mark.parametrize("blk", _golden_blocks(), ids=lambda b: b["name"])
+def test_q8_golden_blocks(orc, blk):
+    x = np.array(blk["x"], np.float32)
+    assert x.size == 32 and np.array_equal(x.astype(np.float64), np.array(blk["x"]))
+    codes, scales = orc.q8_quantize(x)
+    assert scales[0] == np.float32(blk["scale"])
+    assert codes.tolist() == blk["codes"]
+    # dequantisation is code * scale: exact here because scale is a power of two
+    assert np.array_equal(orc.q8_dequantize(codes, scales),
+                          np.array(blk["codes"], np.float64) * blk["scale"])
+
+
+def test_q8_bounds_and_extremes(orc):
+    r = _rng(22)
+    x = (r.standard_normal(32 * 500) * np.exp(r.uniform(-30, 30, 32 * 500))).astype(np.float32)
+    codes, scales = orc.q8_quantize(x)
+    assert codes.min() >= -127 and codes.max() <= 127
+    xb = x.reshape(-1, 32).astype(np.float64)
+    cb = codes.reshape(-1, 32)
+    arg = np.abs(xb).argmax(axis=1)
+    # the element of largest magnitude always maps to +-127 with its sign
+    assert np.array_equal(cb[np.arange(len(arg)), arg], np.sign(xb[np.arange(len(arg)), arg]) * 127)
+    y = orc.q8_dequantize(codes, scales).reshape(-1, 32).astype(np.float64)
+    s = scales.astype(np.float64)[:, None]
+    # |DQ(Q(x)) - x| <= scale/2 up to fp32 rounding of the quotient and product
+    assert np.all(np.abs(y - xb) <= s * (0.5 + 127 * 2.0 ** -22))
+
+
+def test_q8_multiples_of_scale_are_exact(orc):
+    k = _rng(23).integers(-127, 128, size=(40, 32))
+    k[:, 0] = 127
+    x = (k * 2.0 ** -9).astype(np.float32)
+    codes, scales = orc.q8_quantize(x)
+    assert np.array_equal(codes.reshape(40, 32), k)
+    assert np.array_equal(orc.q8_dequantize(codes, scales), x.reshape(-1))
+
+
+# ---------------------------------------------------------------- merge / wire
+
+def test_merge_integer_sums_exact(orc):
+    r = _rng(24)
+    res = r.integers(-1000, 1000, size=(3, 40)).astype(np.float64)
+    parts = r.integers(-1000, 1000, size=(5, 3, 40)).astype(np.float64)
+    out = orc.merge(res, parts)
+    assert np.array_equal(out, res + parts.sum(axis=0))
+
+
+def test_wire_passthrough_and_quantised(orc):
+    p = _rng(25).standard_normal((2, 64)) * 0.03
+    d, c, s = orc.wire(p, 0)
+    assert np.array_equal(d, p) and c is None
+    d, c, s = orc.wire(p, orc.Q_PARTIALS)
+    assert c.min() >= -127 and c.max() <= 127
+    # d sits on the block grid code * scale, and within half a step of fp32(p)
+    assert np.array_equal(d.astype(np.float32).reshape(-1),
+                          (c.reshape(-1).astype(np.float32) * np.repeat(s.reshape(-1), 32)))
+    assert np.all(np.abs(d - p).reshape(-1) <= np.repeat(s.reshape(-1), 32) * 0.5001 + 1e-9)
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _identity_block(D, batch=1, past=0, c=1.75, quant=0, w_dtype="f32"):
+    """One head with hd = D, F = D: Wq = Wk = 0, Wv = Wo = W3 = W2 = I, W1 = c*I."""
+    w = synth.small_llama(dim=D, n_heads=1, n_kv_heads=1, head_dim=D, ffn_hidden=D, tp=1,
+                          batch=batch, past=(past, past), quant=quant, w_dtype=w_dtype)
+    I = np.eye(D, dtype=np.float32)
+    Z = np.zeros((D, D), np.float32)
+    wts = {"wq": Z, "wk": Z, "wv": I, "wo": I, "w1": (c * I).astype(np.float32), "w3": I, "w2": I,
+           "g_att": (1 + 0.1 * _rng(26).standard_normal(D)).astype(np.float32),
+           "g_ffn": (1 + 0.1 * _rng(27).standard_normal(D)).astype(np.float32)}
+    if w_dtype == "bf16":
+        for k in ("wq", "wk", "wv", "wo", "w1", "w3", "w2"):
+            wts[k] = synth.f32_to_bf16_bits(wts[k])
+    return w, wts
+
+
+def test_layer_identity_weights_closed_form(orc):
+    """With no cached past the only attended position is the new token, so the
+    attention output is the stored v = xn; then h = x + xn and
+    out = h + silu(c * hn) * hn, hn = RMSNorm(h) (gains elementwise)."""
+    D, c = 32, 1.75
+    w, wts = _identity_block(D, c=c)
+    x = _rng(28).standard_normal((1, D)).astype(np.float32)
+    kc = np.full((1, 1, 1, D), np.nan, np.float32)
+    vc = kc.copy()
+    o = orc.llama_layer(w, wts, x, np.array([0], np.int32), kc, vc)
+    xd = x[0].astype(np.float64)
+    ms = np.mean(xd * xd)
+    xn = wts["g_att"].astype(np.float64) * xd / math.sqrt(ms + w.norm_eps)
+    v_stored = xn.astype(np.float32).astype(np.float64)
+    h = xd + v_stored
+    hn = wts["g_ffn"].astype(np.float64) * h / math.sqrt(np.mean(h * h) + w.norm_eps)
+    out = h + (c * hn) / (1 + np.exp(-c * hn)) * hn
+    assert rel_l2(o["h"][0], h) < 1e-14
+    assert rel_l2(o["out"][0], out) < 1e-14
+    assert np.array_equal(vc[0, 0, 0], xn.astype(np.float32))
+    assert np.array_equal(kc[0, 0, 0], np.zeros(D, np.float32))  # Wk = 0 -> rotated zero
+
+
+def test_layer_zero_query_averages_cache(orc):
+    """Wq = 0 gives equal scores, so the attention output is the mean of the
+    L + 1 stored values (past entries and the appended one)."""
+    D, L = 32, 6
+    w, wts = _identity_block(D, past=L)
+    x = _rng(29).standard_normal((1, D)).astype(np.float32)
+    kc = _rng(30).standard_normal((1, 1, L + 1, D)).astype(np.float32)
+    vc = _rng(31).standard_normal((1, 1, L + 1, D)).astype(np.float32)
+    o = orc.llama_layer(w, wts, x, np.array([L], np.int32), kc, vc)
+    assert rel_l2(o["att"][0, 0], vc[0, 0].astype(np.float64).mean(axis=0)) < 1e-14
+
+
+def test_layer_appends_rotated_k_at_position_len(orc):
+    """Wk = I: the slot at index lens[b] holds RoPE(xn, lens[b]) rounded to the
+    cache type; every other slot is bitwise unchanged."""
+    D, L = 16, 9
+    w, wts = _identity_block(D, past=L, w_dtype="bf16")
+    w = synth.small_llama(dim=D, n_heads=1, n_kv_heads=1, head_dim=D, ffn_hidden=D, tp=1,
+                          past=(L, L), w_dtype="bf16", kv_dtype="bf16")
+    wts["wk"] = synth.f32_to_bf16_bits(np.eye(D, dtype=np.float32))
+    x = _rng(32).standard_normal((1, D)).astype(np.float32)
+    kc = synth.f32_to_bf16_bits(_rng(33).standard_normal((1, 1, L + 3, D)).astype(np.float32))
+    vc = kc.copy()
+    w = synth.small_llama(dim=D, n_heads=1, n_kv_heads=1, head_dim=D, ffn_hidden=D, tp=1,
+                          past=(L, L + 2), w_dtype="bf16", kv_dtype="bf16")
+    k0 = kc.copy()
+    o = orc.llama_layer(w, wts, x, np.array([L], np.int32), kc, vc)
+    xd = x[0].astype(np.float64)
+    xn = wts["g_att"].astype(np.float64) * xd / math.sqrt(np.mean(xd * xd) + w.norm_eps)
+    z = (xn[0::2] + 1j * xn[1::2]) * np.exp(1j * L * w.rope_theta ** (-np.arange(0, D, 2) / D))
+    k = np.empty(D)
+    k[0::2], k[1::2] = z.real, z.imag
+    assert np.allclose(o["k"][0, 0], k, rtol=1e-12, atol=1e-14)
+    assert np.array_equal(kc[0, 0, L], synth.f32_to_bf16_bits(k.astype(np.float32)))
+    others = [t for t in range(L + 3) if t != L]
+    assert np.array_equal(kc[0, 0, others], k0[0, 0, others])
+
+
+def _layer(orc, w, d):
+    return orc.llama_layer(w, d, d["x"], d["lens"], d["kcache"].copy(), d["vcache"].copy())
+
+
+@pytest.mark.parametrize("shape", ["micro", "tiny"])
+def test_sharded_sum_equals_unsharded(orc, shape):
+    """[TP] row split: the partial sums of the shards add up to the unsharded
+    product, so without quantisation h and out do not depend on T."""
+    if shape == "micro":
+        base = synth.small_llama(dim=64, n_heads=4, n_kv_heads=4, head_dim=16, ffn_hidden=128,
+                                 tp=1, batch=2, past=(5, 9), seed=40)
+        tps = (1, 2, 4)
+    else:
+        import dataclasses
+        base = dataclasses.replace(synth.TINY, tp=1)
+        tps = (1, 2, 3, 6)
+    d = synth.llama_inputs(base)
+    ref = _layer(orc, base, d)
+    for T in tps[1:]:
+        import dataclasses
+        w = dataclasses.replace(base, tp=T)
+        o = _layer(orc, w, d)
+        assert rel_l2(o["p_att"].sum(axis=0), ref["p_att"][0]) < 1e-12
+        assert rel_l2(o["p_ffn"].sum(axis=0), ref["p_ffn"][0]) < 1e-12
+        assert rel_l2(o["h"] - d["x"], ref["h"] - d["x"]) < 1e-12
+        assert rel_l2(o["out"], ref["out"]) < 1e-13
+        # column split: the shards' q heads concatenate to the unsharded ones
+        assert rel_l2(np.concatenate(list(o["q"]), axis=1), ref["q"][0]) < 1e-13
+        assert rel_l2(np.concatenate(list(o["a"]), axis=1), ref["a"][0]) < 1e-13
+
+
+def test_gqa_equals_mha_with_repeated_kv(orc):
+    import dataclasses
+    g = synth.small_llama(dim=64, n_heads=8, n_kv_heads=2, head_dim=8, ffn_hidden=64, tp=2,
+                          batch=2, past=(3, 7), seed=41)
+    d = synth.llama_inputs(g)
+    m = dataclasses.replace(g, n_kv_heads=8)
+    G, hd = 4, 8
+    dm = dict(d)
+    dm["wk"] = np.repeat(d["wk"].reshape(2, hd, 64), G, axis=0).reshape(8 * hd, 64)
+    dm["wv"] = np.repeat(d["wv"].reshape(2, hd, 64), G, axis=0).reshape(8 * hd, 64)
+    dm["kcache"] = np.repeat(d["kcache"], G, axis=1)
+    dm["vcache"] = np.repeat(d["vcache"], G, axis=1)
+    og, om = _layer(orc, g, d), _layer(orc, m, dm)
+    assert rel_l2(og["att"], om["att"]) < 1e-14
+    assert rel_l2(og["out"], om["out"]) < 1e-14
+
+
+def test_batch_rows_independent(orc):
+    import dataclasses
+    w = synth.small_llama(dim=64, n_heads=4, n_kv_heads=2, head_dim=16, ffn_hidden=128, tp=2,
+                          batch=3, past=(2, 11), seed=42)
+    d = synth.llama_inputs(w)
+    full = _layer(orc, w, d)
+    w1 = dataclasses.replace(w, batch=1)
+    for b in range(3):
+        db = dict(d)
+        db["x"], db["lens"] = d["x"][b:b + 1], d["lens"][b:b + 1]
+        db["kcache"], db["vcache"] = d["kcache"][b:b + 1], d["vcache"][b:b + 1]
+        ob = _layer(orc, w1, db)
+        assert np.array_equal(ob["out"][0], full["out"][b])
+
+
+def test_quantised_inputs_lie_on_the_int8_grid(orc):
+    import dataclasses
+    w = dataclasses.replace(synth.TINY, quant=synth.Q_PARTIALS | synth.Q_INPUTS)
+    d = synth.llama_inputs(w)
+    o = _layer(orc, w, d)
+    def q8_round_trip(v):
+        return orc.q8_dequantize(*orc.q8_quantize(v.astype(np.float32))).astype(np.float64)
+    xn = q8_round_trip(orc.rmsnorm(d["x"][0], d["g_att"], w.norm_eps))
+    hn = q8_round_trip(orc.rmsnorm(o["h"][0], d["g_ffn"], w.norm_eps))
+    for s in range(w.tp):
+        assert np.array_equal(o["xn"][s, 0], xn) and np.array_equal(o["hn"][s, 0], hn)
+    # the merge used the dequantised partials
+    dd = [orc.wire(o["p_att"][s], orc.Q_PARTIALS)[0] for s in range(w.tp)]
+    assert np.array_equal(o["h"], orc.merge(d["x"].astype(np.float64), np.stack(dd)))
+
+
+# ---------------------------------------------------------------- 2D FFN block
+
+def test_ffn2d_closed_forms(orc):
+    E = F = 32
+    r = _rng(43)
+    X = synth.f32_to_bf16_bits(r.standard_normal((4, E)).astype(np.float32))
+    I = synth.f32_to_bf16_bits(np.eye(E, dtype=np.float32))
+    Z = synth.f32_to_bf16_bits(np.zeros((E, E), np.float32))
+    assert np.array_equal(orc.ffn2d(X, Z, I, I), np.zeros((4, E)))        # silu(0) = 0
+    c = 1.5
+    G = synth.f32_to_bf16_bits(c * np.eye(E, dtype=np.float32))
+    x = synth.bf16_bits_to_f32(X).astype(np.float64)
+    y = orc.ffn2d(X, G, I, I)
+    assert rel_l2(y, (c * x) / (1 + np.exp(-c * x)) * x) < 1e-14
+
+
+def test_ffn2d_matches_float64_matmul_and_row_subsets(orc):
+    import torch
+    r = _rng(44)
+    E, F, B = 64, 96, 5
+    X, Wg, Wi = (synth.f32_to_bf16_bits(r.standard_normal(s).astype(np.float32))
+                 for s in ((B, E), (F, E), (F, E)))
+    Wo = synth.f32_to_bf16_bits(r.standard_normal((E, F)).astype(np.float32))
+    t = lambda a: torch.tensor(synth.bf16_bits_to_f32(a), dtype=torch.float64)  # noqa: E731
+    ref = (torch.nn.functional.silu(t(X) @ t(Wg).T) * (t(X) @ t(Wi).T)) @ t(Wo).T
+    y = orc.ffn2d(X, Wg, Wi, Wo)
+    assert rel_l2(y, ref.numpy()) < 1e-13
+    assert np.array_equal(orc.ffn2d(X, Wg, Wi, Wo, row0=2, nrows=2), y[2:4])
