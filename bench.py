@@ -1,0 +1,246 @@
+"""Benchmark: decode layer-steps/s of one tensor-parallel shard on one MI355X.
+
+A step is one pass of the whole shard step for rank 0 of the workload:
+attention stage (RMSNorm, QKV, RoPE + KV append, GQA attention, W_O, int8
+wire when configured) -> merge of the T shard partials (rank 0's own plus
+the T-1 wires the other ranks produced, standing in for what would arrive
+over xGMI) -> FFN stage (RMSNorm, W1/W3 + SwiGLU, W2) -> merge. The output of
+a step is the next step's input. R layer copies (distinct weights, caches
+and workspaces in HBM, R x step bytes > 2 x the 256 MB Infinity Cache) are
+used in rotation so no step reads what the previous one left in the cache.
+
+Prints ONE JSON line (rank 0). Inputs are seeded synthetic tensors of the
+workload's shapes (no trained weights exist here), resident in HBM before the
+timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "decode layer-steps/s per TP shard + achieved HBM GB/s (% peak), 7B/70B shapes"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def llama_config(tp, w, rank):
+    dt = {synth.F32: tp.TP_F32, synth.BF16: tp.TP_BF16}
+    return tp.make_config(kind=tp.TP_LLAMA_BLOCK, dim=w.dim, n_heads=w.n_heads,
+                          n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn_hidden=w.ffn_hidden,
+                          tp_size=w.tp, tp_rank=rank, max_batch=w.batch, max_ctx=w.max_ctx,
+                          w_dtype=dt[w.w_dtype], kv_dtype=dt[w.kv_dtype], quant=w.quant,
+                          quant_block=32, rope_theta=w.rope_theta, norm_eps=w.norm_eps)
+
+
+def llama_bytes(w, lens):
+    """Algorithmic HBM bytes of rank 0's layer step: every packed weight of the
+    shard once, plus the cached K and V of the past positions of the shard's
+    kv heads (each kv head once, however many q heads share it)."""
+    e = 2 if w.w_dtype == synth.BF16 else 4
+    kve = 2 if w.kv_dtype == synth.BF16 else 4
+    T, D, hd = w.tp, w.dim, w.head_dim
+    Hq_s, Hkv_s, Fs = w.n_heads // T, w.n_kv_heads // T, w.ffn_hidden // T
+    weights = ((Hq_s + 2 * Hkv_s) * hd * D + D * Hq_s * hd + 2 * Fs * D + D * Fs) * e
+    kv = int(np.sum(lens)) * Hkv_s * hd * 2 * kve
+    w13 = 2 * Fs * D * e
+    return weights, kv, w13
+
+
+def run_llama(args, w):
+    import torch
+    import tensor_tp_shard_amd as tp
+    T, B = w.tp, w.batch
+    t_gen = time.time()
+    d = synth.llama_inputs(w)
+    log(f"generated inputs of {w.name} in {time.time() - t_gen:.1f}s")
+    W = {k: dev(d[k]) for k in ("wq", "wk", "wv", "wo", "w1", "w3", "w2", "g_att", "g_ffn")}
+    hs = w.n_kv_heads // T
+
+    def shard(rank):
+        sh = tp.Shard(llama_config(tp, w, rank), caches=False)
+        sh.load(W, k_cache=dev(d["kcache"][:, rank * hs:(rank + 1) * hs]).reshape(-1),
+                v_cache=dev(d["vcache"][:, rank * hs:(rank + 1) * hs]).reshape(-1))
+        return sh
+
+    x0 = dev(d["x"])
+    lens = dev(d["lens"])
+    # the other ranks' partials for this input (what rank 0 would receive)
+    others = [shard(r) for r in range(1, T)]
+    s0 = shard(0)
+    wa = [sh.new_wire() for sh in [s0] + others]
+    for sh, wr in zip([s0] + others, wa):
+        sh.step(tp.TP_STAGE_ATTN, x0, lens, B, wr)
+    h0 = torch.empty_like(x0)
+    s0.merge(tp.TP_STAGE_ATTN, wa, x0, h0, B)
+    wf = [sh.new_wire() for sh in [s0] + others]
+    for sh, wr in zip([s0] + others, wf):
+        sh.step(tp.TP_STAGE_FFN, h0, None, B, wr)
+    torch.cuda.synchronize()
+    other_att, other_ffn = wa[1:], wf[1:]
+    del others
+    # R copies of rank 0's layer
+    wbytes, kvbytes, w13bytes = llama_bytes(w, d["lens"])
+    step_bytes = wbytes + kvbytes
+    R = args.copies or max(2, int(np.ceil(3 * 256e6 / step_bytes)))
+    copies = [s0] + [shard(0) for _ in range(R - 1)]
+    del W
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    wires_a = [c.new_wire() for c in copies]
+    wires_f = [c.new_wire() for c in copies]
+    xs = [torch.empty_like(x0) for _ in range(R)]
+    hs_ = [torch.empty_like(x0) for _ in range(R)]
+    xs[0].copy_(x0)
+
+    def one_pass():
+        # layer copy r reads xs[r] and writes xs[r+1]; the pass ends where it began
+        for r, c in enumerate(copies):
+            xin, xout = xs[r], xs[(r + 1) % R]
+            c.step(tp.TP_STAGE_ATTN, xin, lens, B, wires_a[r])
+            c.merge(tp.TP_STAGE_ATTN, [wires_a[r]] + other_att, xin, hs_[r], B)
+            c.step(tp.TP_STAGE_FFN, hs_[r], None, B, wires_f[r])
+            c.merge(tp.TP_STAGE_FFN, [wires_f[r]] + other_ffn, hs_[r], xout, B)
+
+    passes = max(1, args.steps // R)
+    steps = passes * R
+    wpasses = max(1, args.warmup // R)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = None
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            one_pass()
+        if args.mode == "graph":
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                one_pass()
+        run = graph.replay if graph is not None else one_pass
+        for _ in range(wpasses):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(passes):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        assert torch.isfinite(xs[0]).all().item(), "non-finite layer output"
+        # dominant-kernel timing: library-recorded HIP events around each launch of the
+        # up-projection kernel, on the stream it is launched on, over the same number of steps
+        kid = tp.kernel_names().index("gemv_w13_swiglu")
+        for c in copies:
+            tp.kernel_timing_arm(c.handle, kid)
+        for _ in range(passes):
+            one_pass()
+        torch.cuda.synchronize()
+        tot, n = 0.0, 0
+        for c in copies:
+            t_, n_ = tp.kernel_timing_read(c.handle)
+            tot += t_
+            n += n_
+            tp.kernel_timing_arm(c.handle, -1)
+    ms_step = ms / steps
+    k_ms = tot / max(n, 1)
+    achieved = w13bytes / (k_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_step, 1),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": wpasses * R,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.w_dtype == synth.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "shard": f"rank 0 of TP={T}", "batch": B,
+                   "kv_positions": [int(d["lens"].min()), int(d["lens"].max())],
+                   "quant": w.quant, "layer_copies": R, "launch": args.mode,
+                   "step_bytes": int(step_bytes)},
+        "achieved_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"kernel": "gemv_w13_swiglu", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": int(w13bytes),
+                     "avg_launch_us": round(k_ms * 1e3, 3), "launches": n},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_llama(w, d, args.cpu_seconds)
+    return res
+
+
+def cpu_baseline_llama(w, d, seconds):
+    """The fp64 oracle, as it stands, doing rank 0's layer step on the host."""
+    import oracle
+    x = d["x"].astype(np.float64)
+    kc, vc = d["kcache"].copy(), d["vcache"].copy()
+    zeros = np.zeros((w.tp - 1, w.batch, w.dim))
+    n, t0 = 0, time.perf_counter()
+    while True:
+        a = oracle.attn_shard(w, d, 0, x, d["lens"], kc, vc)
+        da, _, _ = oracle.wire(a["p"], w.quant)
+        h = oracle.merge(x, np.concatenate([da[None], zeros]))
+        f = oracle.ffn_shard(w, d, 0, h)
+        df, _, _ = oracle.wire(f["p"], w.quant)
+        oracle.merge(h, np.concatenate([df[None], zeros]))
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(n / el, 3), "unit": "layer-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} rank-0 shard layer steps of {w.name} (attention stage, wire, merge, "
+                      f"FFN stage, wire, merge) by the single-threaded fp64 C oracle in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4000)
+    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--workload", default="llama2_7b_tp4_b1", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
+    ap.add_argument("--copies", type=int, default=0, help="layer copies in rotation (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the shard step runs every shard in turn on one device "
+              "and uses no collectives; --gpus above 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = synth.get(args.workload)
+    res = run_llama(args, w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+/*
+ * tpshard.h -- C ABI of the MI355X (gfx950) tensor-parallel shard library.
+ *
+ * The library runs, on one GPU, the decode-time forward step of one
+ * tensor-parallel (TP) shard of a Llama-style decoder block, and the dense
+ * FFN block a chip holds under 2D weight-stationary partitioning:
+ *
+ *   attention stage  RMSNorm -> [int8 round trip] -> column-split QKV ->
+ *                    RoPE + KV append -> grouped-query attention over the
+ *                    shard's cache -> row-split W_O -> partial sum
+ *                    -> [int8 block quantisation of the partial]
+ *   merge            residual + sum of the shards' (dequantised) partials
+ *   FFN stage        RMSNorm -> [int8 round trip] -> column-split W1/W3 +
+ *                    SwiGLU -> row-split W2 -> partial -> [int8]
+ *   merge            residual + sum of partials -> layer output
+ *
+ * Sources: distributed-llama issue "[Feature Suggest] Tensor Parallellism for
+ * Accelerating LLM" (buildLlama2Arch: the root/worker task list of one layer,
+ * llamaRmsAttNorm .. llamaMergeFfn2, with quantise / sync / dequantise /
+ * merge around the two partial-sum exchanges); aiterms.tw "Tensor
+ * Parallelism" (核心概念: column and row split; 運作原理: the FFN walk-through
+ * ending in an all-reduce of row-split partials); CS349E lecture 4
+ * 03_pope_partitioning.py (demo 1: PaLM-540B FFN under 2D weight-stationary
+ * partitioning; demo 3 observations: GQA head sharding without KV
+ * replication while TP <= number of KV groups).
+ *
+ * Conventions shared by every entry point:
+ *  - Every call returns an int32 status: TP_OK (0) or a negative TP_E* code.
+ *    tp_last_error() gives a thread-local message for the last failure.
+ *  - Device pointers are plain device addresses on the current HIP device;
+ *    the library NEVER allocates or frees device memory. The caller sizes
+ *    every device buffer from the byte counts init_shard returns.
+ *  - Compute calls only enqueue work on the given hipStream_t (passed as
+ *    void*; NULL = the null stream) and never synchronise. Argument errors
+ *    are detected on the host before anything is enqueued.
+ *  - Every device buffer must be 16-byte aligned (else TP_EALIGN).
+ *  - A handle is not thread-safe; distinct handles are independent.
+ *  - No C++ exception or abort crosses this boundary.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tp_shard tp_shard; /* opaque host-side handle; owns no device memory */
+
+enum { TP_F32 = 0, TP_BF16 = 1 };                         /* element types */
+enum { TP_LLAMA_BLOCK = 0, TP_FFN_2D = 1 };                /* tp_config.kind */
+enum { TP_STAGE_ATTN = 0, TP_STAGE_FFN = 1 };              /* decode_step / merge_partials stage */
+enum { TP_Q_NONE = 0, TP_Q_PARTIALS = 1, TP_Q_INPUTS = 2 }; /* tp_config.quant bit mask */
+
+enum {
+    TP_OK = 0,
+    TP_EINVAL = -1,   /* bad configuration, enum, size or null pointer */
+    TP_EALIGN = -2,   /* a device pointer is not 16-byte aligned */
+    TP_ESTATE = -3,   /* call out of order (e.g. decode_step before load_weights) */
+    TP_ENODEV = -4,   /* no HIP device, or the current device is not gfx950 */
+    TP_EHIP = -5,     /* a HIP runtime call or kernel launch failed */
+    TP_ENOTIMPL = -6  /* valid request the library does not implement */
+};
+
+/* Bits of the device error word (first 4 bytes of the workspace). */
+enum { TP_DERR_LEN = 1 }; /* some lens[b] was < 0 or >= max_ctx; that sequence was skipped */
+
+/*
+ * Shard configuration. Sizes are those of the FULL (unsharded) model; the
+ * library derives the shard's slice from tp_size / tp_rank:
+ *   q heads  [r*Hq/T, (r+1)*Hq/T), kv heads [r*Hkv/T, (r+1)*Hkv/T),
+ *   FFN features [r*F/T, (r+1)*F/T)  (column split of Wq/Wk/Wv/W1/W3,
+ *   row split of Wo/W2: the shard multiplies its column slice of Wo/W2).
+ * q head h uses kv head h / (Hq/Hkv) (contiguous groups).
+ *
+ * kind == TP_LLAMA_BLOCK: w_dtype TP_F32 or TP_BF16, kv_dtype likewise;
+ *   requires Hq % Hkv == 0, Hq % T == 0, Hkv % T == 0, F % T == 0, even hd,
+ *   dim, Hq_s*hd and F/T multiples of 8 (bf16) or 4 (fp32) elements,
+ *   dim % 32 == 0 when quant != 0, hd <= 256, quant_block == 32.
+ * kind == TP_FFN_2D: dim = E (the block's E slice), ffn_hidden = F (the
+ *   block's F slice), w_dtype TP_BF16, tp_size 1, heads ignored; the
+ *   decode step is Y = (silu(X W_gate^T) * (X W_in^T)) W_out^T.
+ */
+typedef struct {
+    int32_t kind;
+    int32_t dim, n_heads, n_kv_heads, head_dim, ffn_hidden;
+    int32_t tp_size, tp_rank;
+    int32_t max_batch, max_ctx; /* max_ctx = KV positions per sequence (cached + new) */
+    int32_t w_dtype, kv_dtype;
+    int32_t quant, quant_block;
+    float rope_theta; /* default 10000 */
+    float norm_eps;   /* default 1e-5 */
+} tp_config;
+
+/* Byte counts of the caller-owned device buffers. */
+typedef struct {
+    uint64_t packed_weights; /* the shard's packed weights, gains and RoPE table */
+    uint64_t kv_cache_each;  /* one of K or V: [max_batch][Hkv_s][max_ctx][hd] kv_dtype */
+    uint64_t workspace;      /* activations between kernels + the device error word */
+    uint64_t wire;           /* one shard's exchanged partial for max_batch rows */
+} tp_sizes;
+
+/* FULL layer weights on the device, (out, in) row-major, element type
+ * w_dtype: wq [Hq*hd][D], wk/wv [Hkv*hd][D], wo [D][Hq*hd], w1/w3 [F][D],
+ * w2 [D][F]; g_att/g_ffn fp32 [D] RMSNorm gains.
+ * For TP_FFN_2D: w1 = W_gate [F][E], w3 = W_in [F][E], w2 = W_out [E][F]
+ * (bf16); the others are ignored and may be NULL. */
+typedef struct {
+    const void *wq, *wk, *wv, *wo, *w1, *w3, *w2;
+    const float *g_att, *g_ffn;
+} tp_layer_weights;
+
+/* Optional fp32 device outputs of intermediate values (NULL = not written);
+ * rows are the batch:
+ *  xn   [B][D]          normalised stage input (after the int8 round trip if any)
+ *  q    [B][Hq_s*hd]    rotated queries            (attention stage)
+ *  k, v [B][Hkv_s*hd]   rotated keys, values        (attention stage)
+ *  att  [B][Hq_s*hd]    attention outputs           (attention stage)
+ *  a    [B][F_s]        SwiGLU activations          (FFN stage)
+ *  p_pre [B][D]         the stage's fp32 partial before quantisation */
+typedef struct {
+    float *xn, *q, *k, *v, *att, *a, *p_pre;
+} tp_taps;
+
+/*
+ * init_shard: validate cfg, plan the shard's slice and return a host handle
+ * and the device buffer sizes. Host only: enqueues nothing and needs no GPU.
+ * Errors: TP_EINVAL (null pointer, unknown enum, shape rule above broken).
+ */
+int32_t init_shard(const tp_config *cfg, tp_shard **out, tp_sizes *sizes);
+
+/*
+ * load_weights: slice the shard's part out of the FULL layer weights and
+ * pack it into `packed` (layout private to the library), compute the RoPE
+ * cos/sin table (fp64 on the device, stored fp32) into `packed`, clear the
+ * device error word in `workspace`, and remember k_cache / v_cache /
+ * workspace for later calls. Enqueued on hip_stream; the caller must keep
+ * `full` alive until the stream reaches this point.
+ * k_cache / v_cache hold [max_batch][Hkv_s][max_ctx][hd] kv_dtype each (the
+ * caller fills the cached past positions; the library appends); they are
+ * unused (may be NULL) for TP_FFN_2D.
+ * Errors: TP_EINVAL, TP_EALIGN, TP_ENODEV, TP_EHIP.
+ */
+int32_t load_weights(tp_shard *s, const tp_layer_weights *full, void *packed, void *k_cache,
+                     void *v_cache, void *workspace, void *hip_stream);
+
+/*
+ * decode_step: one stage of the shard's decode step for `batch` rows.
+ *  stage TP_STAGE_ATTN: x = fp32 [batch][D] residual input; lens = device
+ *    int32 [batch] cached positions per sequence: the new token's K/V are
+ *    written at slot lens[b] and attention covers lens[b] + 1 positions.
+ *    The library never advances lens. A sequence with lens[b] outside
+ *    [0, max_ctx) is skipped (attention output 0) and TP_DERR_LEN is set in
+ *    the device error word.
+ *  stage TP_STAGE_FFN: x = fp32 [batch][D] (the merged attention output);
+ *    lens unused (may be NULL).
+ *  For TP_FFN_2D only TP_STAGE_FFN is valid: x = bf16 [batch][E], and
+ *    wire_out receives Y fp32 [batch][E] (batch <= max_batch, any size).
+ *  wire_out: the partial this shard exchanges. With TP_Q_PARTIALS: int8
+ *    codes [batch][D] at offset 0, then fp32 scales [batch][D/32] at the
+ *    offset tp_wire_scales_offset(cfg, batch) (one scale per 32 consecutive
+ *    elements of a row: scale = max|p| / 127, code = p / scale rounded half
+ *    away from zero, clamped to +-127; an all-zero block has scale 0).
+ *    Otherwise fp32 [batch][D].
+ *  taps: NULL or optional intermediate outputs (tp_taps).
+ * Errors: TP_EINVAL, TP_EALIGN, TP_ESTATE (no load_weights yet), TP_EHIP.
+ */
+int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *lens,
+                    int32_t batch, void *wire_out, const tp_taps *taps, void *hip_stream);
+
+/*
+ * merge_partials: out = residual + sum_{i < n_wires} dequant(wires[i]) in the
+ * order of the array (shard order), per element, in fp32; `wires` is a HOST
+ * array of n_wires device pointers in this shard's wire format. out may
+ * alias residual. fp32 [batch][D] throughout.
+ * Errors: TP_EINVAL (n_wires < 1 or > 64, null pointers), TP_EALIGN, TP_EHIP.
+ */
+int32_t merge_partials(const tp_shard *s, int32_t stage, const void *const *wires,
+                       int32_t n_wires, const float *residual, float *out, int32_t batch,
+                       void *hip_stream);
+
+/* Byte offset of the fp32 scales inside a quantised wire of `batch` rows
+ * (16-byte aligned, right after the int8 codes). */
+uint64_t tp_wire_scales_offset(const tp_config *cfg, int32_t batch);
+
+/* Reads (and clears, when clear != 0) the device error word in the handle's
+ * workspace; synchronises hip_stream. */
+int32_t tp_read_error_word(tp_shard *s, uint32_t *word, int32_t clear, void *hip_stream);
+
+/*
+ * Kernel timing probe: while armed, the library records a HIP event pair on
+ * the launch stream around every launch of kernel `kernel_id` (see
+ * tp_kernel_name) it enqueues, and accumulates the elapsed time of
+ * completed pairs. tp_kernel_timing_arm(s, -1) disarms. Reading synchronises
+ * on the recorded events. Host-side HIP events only; no device memory.
+ */
+int32_t tp_kernel_timing_arm(tp_shard *s, int32_t kernel_id);
+int32_t tp_kernel_timing_read(tp_shard *s, double *total_ms, int32_t *launches);
+const char *tp_kernel_name(int32_t kernel_id); /* NULL past the last id */
+
+void destroy_shard(tp_shard *s);
+const char *tp_status_str(int32_t status);
+const char *tp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

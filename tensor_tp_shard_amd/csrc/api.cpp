@@ -1,0 +1,590 @@
+// api.cpp -- the C ABI of the shard library (include/tpshard.h): argument
+// validation, the shard's slice plan, weight packing, workspace layout and
+// the launch sequence of each stage on the caller's stream.
+//
+// The slice plan follows aiterms.tw "Tensor Parallelism", 核心概念 items 1-2:
+// column-split weights (Wq, Wk, Wv, W1, W3) keep whole output rows of the
+// shard's heads / FFN features; row-split weights (Wo, W2) keep the column
+// block that multiplies the shard's slice of the activation, giving a
+// full-size partial. The stage order follows distributed-llama issue
+// "[Feature Suggest] Tensor Parallellism for Accelerating LLM",
+// buildLlama2Arch (per layer: norm, quantise, QKV, attention, W_O, quantise,
+// dequantise + merge; then norm, quantise, SwiGLU FFN, W2, quantise,
+// dequantise + merge).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/tpshard.h"
+#include "common.h"
+
+using namespace tps;
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+int32_t hip_fail(hipError_t e, const char *what)
+{
+    return fail(TP_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+enum KernelId {
+    KID_RMSNORM = 0,
+    KID_GEMV_QKV,
+    KID_ATTN,
+    KID_COMBINE,
+    KID_GEMV_WO,
+    KID_WIRE,
+    KID_GEMV_W13,
+    KID_GEMV_W2,
+    KID_MERGE,
+    KID_FFN2D_UP,
+    KID_FFN2D_DOWN,
+    KID_ROPE_TABLE,
+    KID_COUNT
+};
+
+const char *const kKernelNames[KID_COUNT] = {
+    "rmsnorm",         "gemv_qkv",   "attn_split", "attn_combine", "gemv_wo",  "q8_wire",
+    "gemv_w13_swiglu", "gemv_w2",    "merge",      "ffn2d_up",     "ffn2d_down", "rope_table"};
+
+} // namespace
+
+struct tp_shard {
+    tp_config cfg;
+    // derived shape
+    int T, r, D, hd, Hq, Hkv, G, Hq_s, Hkv_s, F, Fs, n_qkv, esz, kv_esz;
+    // packed layout (byte offsets)
+    uint64_t o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn, o_rope, packed_bytes;
+    // workspace layout (byte offsets)
+    uint64_t w_err, w_xn, w_qkv, w_part, w_att, w_a, w_p, ws_bytes;
+    int n_chunks;
+    uint64_t kv_bytes, wire_bytes;
+    // bound buffers
+    char *packed = nullptr, *ws = nullptr;
+    void *kc = nullptr, *vc = nullptr;
+    bool loaded = false;
+    // kernel timing probe
+    int timing_kernel = -1;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_pool;
+    size_t ev_used = 0;
+};
+
+namespace {
+
+int32_t plan(const tp_config &c, tp_shard &s)
+{
+    if (c.kind != TP_LLAMA_BLOCK && c.kind != TP_FFN_2D)
+        return fail(TP_EINVAL, "unknown kind %d", c.kind);
+    if (c.w_dtype != TP_F32 && c.w_dtype != TP_BF16)
+        return fail(TP_EINVAL, "unknown w_dtype %d", c.w_dtype);
+    if (c.quant & ~(TP_Q_PARTIALS | TP_Q_INPUTS))
+        return fail(TP_EINVAL, "unknown quant bits 0x%x", c.quant);
+    if (c.quant && c.quant_block != kQBlock)
+        return fail(TP_EINVAL, "quant_block must be 32 (got %d)", c.quant_block);
+    if (c.max_batch < 1 || c.dim < 1 || c.ffn_hidden < 1)
+        return fail(TP_EINVAL, "dim, ffn_hidden and max_batch must be positive");
+    s.cfg = c;
+    s.D = c.dim;
+    s.F = c.ffn_hidden;
+    if (c.kind == TP_FFN_2D) {
+        if (c.w_dtype != TP_BF16)
+            return fail(TP_EINVAL, "TP_FFN_2D needs bf16 weights");
+        if (c.tp_size != 1 || c.tp_rank != 0)
+            return fail(TP_EINVAL, "TP_FFN_2D takes an already-cut block: tp_size 1, tp_rank 0");
+        if (c.quant)
+            return fail(TP_EINVAL, "TP_FFN_2D has no int8 exchange");
+        if (c.dim % 64 || c.ffn_hidden % 64)
+            return fail(TP_EINVAL, "TP_FFN_2D needs E and F multiples of 64");
+        s.T = 1;
+        s.r = 0;
+        s.esz = 2;
+        s.o_w13 = 0;
+        s.o_w2 = align_up(2ull * s.F * s.D * 2, 256);
+        s.packed_bytes = align_up(s.o_w2 + (uint64_t)s.D * s.F * 2, 256);
+        s.w_err = 0;
+        s.w_a = 256; // H = silu(X Wg^T) * (X Win^T), bf16 [max_batch][F]
+        s.ws_bytes = align_up(s.w_a + (uint64_t)c.max_batch * s.F * 2, 256);
+        s.kv_bytes = 0;
+        s.wire_bytes = (uint64_t)c.max_batch * s.D * 4;
+        return TP_OK;
+    }
+    if (c.kv_dtype != TP_F32 && c.kv_dtype != TP_BF16)
+        return fail(TP_EINVAL, "unknown kv_dtype %d", c.kv_dtype);
+    const int T = c.tp_size;
+    if (T < 1 || c.tp_rank < 0 || c.tp_rank >= T)
+        return fail(TP_EINVAL, "tp_rank %d outside [0, tp_size=%d)", c.tp_rank, T);
+    if (c.n_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 1 || c.max_ctx < 1)
+        return fail(TP_EINVAL, "heads, head_dim and max_ctx must be positive");
+    if (c.n_heads % c.n_kv_heads)
+        return fail(TP_EINVAL, "n_heads %% n_kv_heads != 0");
+    if (c.n_heads % T || c.n_kv_heads % T || c.ffn_hidden % T)
+        return fail(TP_EINVAL, "tp_size must divide n_heads, n_kv_heads and ffn_hidden");
+    if (c.head_dim % 16 || c.head_dim > 256)
+        return fail(TP_EINVAL, "head_dim must be a multiple of 16, at most 256");
+    if (c.n_heads / c.n_kv_heads > 8)
+        return fail(TP_EINVAL, "at most 8 q heads per kv head");
+    if (c.max_batch > 16)
+        return fail(TP_EINVAL, "decode batch is at most 16");
+    if (c.quant && c.dim % kQBlock)
+        return fail(TP_EINVAL, "dim must be a multiple of 32 when quantising");
+    if (!(c.norm_eps >= 0.f) || !(c.rope_theta > 0.f))
+        return fail(TP_EINVAL, "norm_eps must be >= 0 and rope_theta > 0");
+    s.T = T;
+    s.r = c.tp_rank;
+    s.hd = c.head_dim;
+    s.Hq = c.n_heads;
+    s.Hkv = c.n_kv_heads;
+    s.G = s.Hq / s.Hkv;
+    s.Hq_s = s.Hq / T;
+    s.Hkv_s = s.Hkv / T;
+    s.Fs = s.F / T;
+    s.n_qkv = (s.Hq_s + 2 * s.Hkv_s) * s.hd;
+    s.esz = c.w_dtype == TP_BF16 ? 2 : 4;
+    s.kv_esz = c.kv_dtype == TP_BF16 ? 2 : 4;
+    const int vec = 16 / s.esz;
+    if (s.D % vec || (s.Hq_s * s.hd) % vec || s.Fs % vec)
+        return fail(TP_EINVAL, "dim, Hq/T*head_dim and ffn_hidden/T must be multiples of %d", vec);
+    const uint64_t D = s.D, B = c.max_batch, e = s.esz;
+    uint64_t o = 0;
+    s.o_wqkv = o; o = align_up(o + (uint64_t)s.n_qkv * D * e, 256);
+    s.o_wo = o;   o = align_up(o + D * s.Hq_s * s.hd * e, 256);
+    s.o_w13 = o;  o = align_up(o + 2ull * s.Fs * D * e, 256);
+    s.o_w2 = o;   o = align_up(o + D * s.Fs * e, 256);
+    s.o_gatt = o; o = align_up(o + D * 4, 256);
+    s.o_gffn = o; o = align_up(o + D * 4, 256);
+    s.o_rope = o; o = align_up(o + (uint64_t)c.max_ctx * (s.hd / 2) * 8, 256);
+    s.packed_bytes = o;
+    s.n_chunks = (c.max_ctx + 63) / 64;
+    o = 0;
+    s.w_err = o;  o = 256;
+    s.w_xn = o;   o = align_up(o + B * D * 4, 256);
+    s.w_qkv = o;  o = align_up(o + B * s.n_qkv * 4, 256);
+    s.w_part = o; o = align_up(o + B * s.Hq_s * (uint64_t)s.n_chunks * (s.hd + 4) * 4, 256);
+    s.w_att = o;  o = align_up(o + B * s.Hq_s * s.hd * 4, 256);
+    s.w_a = o;    o = align_up(o + B * s.Fs * 4, 256);
+    s.w_p = o;    o = align_up(o + B * D * 4, 256);
+    s.ws_bytes = o;
+    s.kv_bytes = B * s.Hkv_s * (uint64_t)c.max_ctx * s.hd * s.kv_esz;
+    const uint64_t wq = align_up(B * D, 16) + B * (D / kQBlock) * 4;
+    s.wire_bytes = (c.quant & TP_Q_PARTIALS) ? wq : B * D * 4;
+    return TP_OK;
+}
+
+int32_t check_device()
+{
+    int dev = -1, n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n < 1)
+        return fail(TP_ENODEV, "no HIP device");
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(TP_ENODEV, "no current HIP device");
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess)
+        return fail(TP_ENODEV, "hipGetDeviceProperties failed");
+    if (strncmp(p.gcnArchName, "gfx950", 6) != 0)
+        return fail(TP_ENODEV, "device %d is %s, the library is built for gfx950", dev,
+                    p.gcnArchName);
+    return TP_OK;
+}
+
+// Runs `launch` with the timing probe's events around it when armed.
+template <typename F>
+int32_t timed(tp_shard *s, int kid, hipStream_t st, const char *what, F &&launch)
+{
+    const bool arm = s->timing_kernel == kid;
+    if (arm) {
+        if (s->ev_used == s->ev_pool.size()) {
+            hipEvent_t a, b;
+            if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess)
+                return fail(TP_EHIP, "hipEventCreate failed");
+            s->ev_pool.emplace_back(a, b);
+        }
+        hipEventRecord(s->ev_pool[s->ev_used].first, st);
+    }
+    const hipError_t e = launch();
+    if (e != hipSuccess)
+        return hip_fail(e, what);
+    if (arm) {
+        hipEventRecord(s->ev_pool[s->ev_used].second, st);
+        s->ev_used++;
+    }
+    return TP_OK;
+}
+
+hipError_t copy2d(void *dst, size_t dpitch, const void *src, size_t spitch, size_t width,
+                  size_t rows, hipStream_t st)
+{
+    return hipMemcpy2DAsync(dst, dpitch, src, spitch, width, rows, hipMemcpyDeviceToDevice, st);
+}
+
+} // namespace
+
+extern "C" {
+
+int32_t init_shard(const tp_config *cfg, tp_shard **out, tp_sizes *sizes)
+{
+    if (!cfg || !out || !sizes)
+        return fail(TP_EINVAL, "init_shard: null argument");
+    *out = nullptr;
+    tp_shard *s = new (std::nothrow) tp_shard();
+    if (!s)
+        return fail(TP_EINVAL, "init_shard: out of host memory");
+    const int32_t st = plan(*cfg, *s);
+    if (st != TP_OK) {
+        delete s;
+        return st;
+    }
+    sizes->packed_weights = s->packed_bytes;
+    sizes->kv_cache_each = s->kv_bytes;
+    sizes->workspace = s->ws_bytes;
+    sizes->wire = s->wire_bytes;
+    *out = s;
+    return TP_OK;
+}
+
+void destroy_shard(tp_shard *s)
+{
+    if (!s)
+        return;
+    for (auto &p : s->ev_pool) {
+        hipEventDestroy(p.first);
+        hipEventDestroy(p.second);
+    }
+    delete s;
+}
+
+uint64_t tp_wire_scales_offset(const tp_config *cfg, int32_t batch)
+{
+    if (!cfg || batch < 0)
+        return 0;
+    return align_up((uint64_t)batch * cfg->dim, 16);
+}
+
+int32_t load_weights(tp_shard *s, const tp_layer_weights *w, void *packed, void *k_cache,
+                     void *v_cache, void *workspace, void *hip_stream)
+{
+    if (!s || !w || !packed || !workspace)
+        return fail(TP_EINVAL, "load_weights: null argument");
+    const bool llama = s->cfg.kind == TP_LLAMA_BLOCK;
+    if (!w->w1 || !w->w3 || !w->w2 ||
+        (llama && (!w->wq || !w->wk || !w->wv || !w->wo || !w->g_att || !w->g_ffn || !k_cache ||
+                   !v_cache)))
+        return fail(TP_EINVAL, "load_weights: null weight or cache pointer");
+    const void *ptrs[] = {packed, workspace, w->w1, w->w3, w->w2};
+    for (const void *p : ptrs)
+        if (!aligned16(p))
+            return fail(TP_EALIGN, "load_weights: device buffer not 16-byte aligned");
+    if (llama) {
+        const void *lp[] = {w->wq, w->wk, w->wv, w->wo, w->g_att, w->g_ffn, k_cache, v_cache};
+        for (const void *p : lp)
+            if (!aligned16(p))
+                return fail(TP_EALIGN, "load_weights: device buffer not 16-byte aligned");
+    }
+    const int32_t dv = check_device();
+    if (dv != TP_OK)
+        return dv;
+    hipStream_t st = (hipStream_t)hip_stream;
+    char *P = (char *)packed;
+    const size_t e = s->esz, D = s->D;
+    hipError_t err = hipSuccess;
+    if (llama) {
+        const size_t hd = s->hd;
+        // column split: rows of the shard's q heads, kv heads (contiguous blocks)
+        err = hipMemcpyAsync(P + s->o_wqkv, (const char *)w->wq + (size_t)s->r * s->Hq_s * hd * D * e,
+                             (size_t)s->Hq_s * hd * D * e, hipMemcpyDeviceToDevice, st);
+        if (!err)
+            err = hipMemcpyAsync(P + s->o_wqkv + (size_t)s->Hq_s * hd * D * e,
+                                 (const char *)w->wk + (size_t)s->r * s->Hkv_s * hd * D * e,
+                                 (size_t)s->Hkv_s * hd * D * e, hipMemcpyDeviceToDevice, st);
+        if (!err)
+            err = hipMemcpyAsync(P + s->o_wqkv + (size_t)(s->Hq_s + s->Hkv_s) * hd * D * e,
+                                 (const char *)w->wv + (size_t)s->r * s->Hkv_s * hd * D * e,
+                                 (size_t)s->Hkv_s * hd * D * e, hipMemcpyDeviceToDevice, st);
+        // row split of W_O: columns [r*Hq_s*hd, (r+1)*Hq_s*hd) of every row
+        const size_t wo_cols = (size_t)s->Hq_s * hd;
+        if (!err)
+            err = copy2d(P + s->o_wo, wo_cols * e, (const char *)w->wo + s->r * wo_cols * e,
+                         (size_t)s->Hq * hd * e, wo_cols * e, D, st);
+        // up-projection: rows W1_f and W3_f interleaved (f in the shard's slice)
+        if (!err)
+            err = copy2d(P + s->o_w13, 2 * D * e, (const char *)w->w1 + (size_t)s->r * s->Fs * D * e,
+                         D * e, D * e, s->Fs, st);
+        if (!err)
+            err = copy2d(P + s->o_w13 + D * e, 2 * D * e,
+                         (const char *)w->w3 + (size_t)s->r * s->Fs * D * e, D * e, D * e, s->Fs,
+                         st);
+        // row split of W2: columns [r*Fs, (r+1)*Fs)
+        if (!err)
+            err = copy2d(P + s->o_w2, (size_t)s->Fs * e, (const char *)w->w2 + (size_t)s->r * s->Fs * e,
+                         (size_t)s->F * e, (size_t)s->Fs * e, D, st);
+        if (!err)
+            err = hipMemcpyAsync(P + s->o_gatt, w->g_att, D * 4, hipMemcpyDeviceToDevice, st);
+        if (!err)
+            err = hipMemcpyAsync(P + s->o_gffn, w->g_ffn, D * 4, hipMemcpyDeviceToDevice, st);
+        if (err)
+            return hip_fail(err, "load_weights: packing copy");
+        RopeArgs ra{(float2 *)(P + s->o_rope), s->cfg.max_ctx, s->hd, (double)s->cfg.rope_theta};
+        const int32_t rc =
+            timed(s, KID_ROPE_TABLE, st, "rope table", [&] { return launch_rope_table(ra, st); });
+        if (rc)
+            return rc;
+    } else {
+        // 2D FFN block: gate rows and up rows in groups of 16 ([F/16][2][16][E]),
+        // so one 16-row MFMA tile of each pair holds matching features
+        const size_t E = s->D, F = s->F;
+        err = copy2d(P + s->o_w13, 32 * E * e, w->w1, 16 * E * e, 16 * E * e, F / 16, st);
+        if (!err)
+            err = copy2d(P + s->o_w13 + 16 * E * e, 32 * E * e, w->w3, 16 * E * e, 16 * E * e,
+                         F / 16, st);
+        if (!err)
+            err = hipMemcpyAsync(P + s->o_w2, w->w2, E * F * e, hipMemcpyDeviceToDevice, st);
+        if (err)
+            return hip_fail(err, "load_weights: packing copy");
+    }
+    s->packed = P;
+    s->ws = (char *)workspace;
+    s->kc = k_cache;
+    s->vc = v_cache;
+    const hipError_t ce = launch_clear_u32((unsigned *)(s->ws + s->w_err), 1, st);
+    if (ce)
+        return hip_fail(ce, "load_weights: clear error word");
+    s->loaded = true;
+    return TP_OK;
+}
+
+int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *lens,
+                    int32_t batch, void *wire_out, const tp_taps *taps, void *hip_stream)
+{
+    if (!s)
+        return fail(TP_EINVAL, "decode_step: null handle");
+    if (!s->loaded)
+        return fail(TP_ESTATE, "decode_step before load_weights");
+    if (stage != TP_STAGE_ATTN && stage != TP_STAGE_FFN)
+        return fail(TP_EINVAL, "unknown stage %d", stage);
+    if (batch < 1 || batch > s->cfg.max_batch)
+        return fail(TP_EINVAL, "batch %d outside [1, max_batch=%d]", batch, s->cfg.max_batch);
+    if (!x || !wire_out)
+        return fail(TP_EINVAL, "decode_step: null x or wire_out");
+    if (!aligned16(x) || !aligned16(wire_out))
+        return fail(TP_EALIGN, "decode_step: x / wire_out not 16-byte aligned");
+    const tp_taps nt{};
+    const tp_taps &tp = taps ? *taps : nt;
+    const float *tp_ptrs[] = {tp.xn, tp.q, tp.k, tp.v, tp.att, tp.a, tp.p_pre};
+    for (const float *p : tp_ptrs)
+        if (p && !aligned16(p))
+            return fail(TP_EALIGN, "decode_step: tap not 16-byte aligned");
+    if ((tp.k == nullptr) != (tp.v == nullptr))
+        return fail(TP_EINVAL, "decode_step: taps k and v go together");
+    hipStream_t st = (hipStream_t)hip_stream;
+    const int B = batch;
+
+    if (s->cfg.kind == TP_FFN_2D) {
+        if (stage != TP_STAGE_FFN)
+            return fail(TP_EINVAL, "TP_FFN_2D has only the FFN stage");
+        return fail(TP_ENOTIMPL, "TP_FFN_2D decode step not built yet");
+    }
+
+    const bool wbf = s->cfg.w_dtype == TP_BF16;
+    const bool qin = s->cfg.quant & TP_Q_INPUTS, qpart = s->cfg.quant & TP_Q_PARTIALS;
+    float *xn = (float *)(s->ws + s->w_xn);
+    // the partial goes straight into the wire unless it is quantised first
+    float *p = qpart ? (float *)(s->ws + s->w_p) : (float *)wire_out;
+    const size_t D = s->D;
+    int32_t rc;
+
+    NormArgs na{(const float *)x,
+                (const float *)(s->packed + (stage == TP_STAGE_ATTN ? s->o_gatt : s->o_gffn)),
+                xn, tp.xn, B, s->D, s->cfg.norm_eps, qin ? 1 : 0};
+    rc = timed(s, KID_RMSNORM, st, "rmsnorm", [&] { return launch_rmsnorm(na, st); });
+    if (rc)
+        return rc;
+
+    if (stage == TP_STAGE_ATTN) {
+        if (!lens)
+            return fail(TP_EINVAL, "decode_step: attention stage needs lens");
+        float *qkv = (float *)(s->ws + s->w_qkv);
+        GemvArgs g{s->packed + s->o_wqkv, xn, qkv, nullptr, s->n_qkv, s->D, B, s->D, s->n_qkv};
+        rc = timed(s, KID_GEMV_QKV, st, "gemv qkv", [&] { return launch_gemv(g, wbf, EPI_STORE, st); });
+        if (rc)
+            return rc;
+        AttnArgs aa{qkv,
+                    lens,
+                    s->kc,
+                    s->vc,
+                    (const float2 *)(s->packed + s->o_rope),
+                    (float *)(s->ws + s->w_part),
+                    (unsigned *)(s->ws + s->w_err),
+                    tp.q,
+                    tp.k,
+                    tp.v,
+                    s->n_qkv,
+                    s->cfg.max_ctx,
+                    s->Hq_s,
+                    s->Hkv_s,
+                    s->G,
+                    s->hd,
+                    64,
+                    s->n_chunks,
+                    (float)(1.0 / std::sqrt((double)s->hd))};
+        rc = timed(s, KID_ATTN, st, "attention",
+                   [&] { return launch_attn(aa, s->cfg.kv_dtype == TP_BF16, B, st); });
+        if (rc)
+            return rc;
+        float *att = (float *)(s->ws + s->w_att);
+        CombineArgs ca{(const float *)(s->ws + s->w_part), lens, att, tp.att, s->Hq_s, s->hd, 64,
+                       s->n_chunks, s->cfg.max_ctx};
+        rc = timed(s, KID_COMBINE, st, "attention combine", [&] { return launch_combine(ca, B, st); });
+        if (rc)
+            return rc;
+        GemvArgs o{s->packed + s->o_wo, att, p, tp.p_pre, s->D, s->Hq_s * s->hd, B,
+                   s->Hq_s * s->hd, s->D};
+        rc = timed(s, KID_GEMV_WO, st, "gemv wo", [&] { return launch_gemv(o, wbf, EPI_STORE, st); });
+        if (rc)
+            return rc;
+    } else {
+        float *a = (float *)(s->ws + s->w_a);
+        GemvArgs u{s->packed + s->o_w13, xn, a, tp.a, 2 * s->Fs, s->D, B, s->D, s->Fs};
+        rc = timed(s, KID_GEMV_W13, st, "gemv w13",
+                   [&] { return launch_gemv(u, wbf, EPI_SWIGLU, st); });
+        if (rc)
+            return rc;
+        GemvArgs dn{s->packed + s->o_w2, a, p, tp.p_pre, s->D, s->Fs, B, s->Fs, s->D};
+        rc = timed(s, KID_GEMV_W2, st, "gemv w2", [&] { return launch_gemv(dn, wbf, EPI_STORE, st); });
+        if (rc)
+            return rc;
+    }
+
+    if (qpart) {
+        WireArgs wa{p, (int8_t *)wire_out,
+                    (float *)((char *)wire_out + tp_wire_scales_offset(&s->cfg, B)), B, s->D};
+        return timed(s, KID_WIRE, st, "q8 wire", [&] { return launch_wire(wa, st); });
+    }
+    return TP_OK;
+}
+
+int32_t merge_partials(const tp_shard *s, int32_t stage, const void *const *wires,
+                       int32_t n_wires, const float *residual, float *out, int32_t batch,
+                       void *hip_stream)
+{
+    if (!s)
+        return fail(TP_EINVAL, "merge_partials: null handle");
+    if (s->cfg.kind != TP_LLAMA_BLOCK)
+        return fail(TP_EINVAL, "merge_partials applies to TP_LLAMA_BLOCK shards");
+    if (stage != TP_STAGE_ATTN && stage != TP_STAGE_FFN)
+        return fail(TP_EINVAL, "unknown stage %d", stage);
+    if (!wires || n_wires < 1 || n_wires > kMaxWires)
+        return fail(TP_EINVAL, "merge_partials: n_wires %d outside [1, %d]", n_wires, kMaxWires);
+    if (batch < 1 || batch > s->cfg.max_batch)
+        return fail(TP_EINVAL, "batch %d outside [1, max_batch=%d]", batch, s->cfg.max_batch);
+    if (!residual || !out)
+        return fail(TP_EINVAL, "merge_partials: null residual / out");
+    if (!aligned16(residual) || !aligned16(out))
+        return fail(TP_EALIGN, "merge_partials: residual / out not 16-byte aligned");
+    MergeArgs m{};
+    for (int i = 0; i < n_wires; i++) {
+        if (!wires[i])
+            return fail(TP_EINVAL, "merge_partials: wire %d is null", i);
+        if (!aligned16(wires[i]))
+            return fail(TP_EALIGN, "merge_partials: wire %d not 16-byte aligned", i);
+        m.wires[i] = wires[i];
+    }
+    m.residual = residual;
+    m.out = out;
+    m.n_wires = n_wires;
+    m.B = batch;
+    m.D = s->D;
+    m.quant = (s->cfg.quant & TP_Q_PARTIALS) ? 1 : 0;
+    m.scales_off = tp_wire_scales_offset(&s->cfg, batch);
+    hipStream_t st = (hipStream_t)hip_stream;
+    return timed(const_cast<tp_shard *>(s), KID_MERGE, st, "merge",
+                 [&] { return launch_merge(m, st); });
+}
+
+int32_t tp_read_error_word(tp_shard *s, uint32_t *word, int32_t clear, void *hip_stream)
+{
+    if (!s || !word)
+        return fail(TP_EINVAL, "tp_read_error_word: null argument");
+    if (!s->loaded)
+        return fail(TP_ESTATE, "tp_read_error_word before load_weights");
+    hipStream_t st = (hipStream_t)hip_stream;
+    hipError_t e = hipMemcpyAsync(word, s->ws + s->w_err, 4, hipMemcpyDeviceToHost, st);
+    if (!e && clear)
+        e = launch_clear_u32((unsigned *)(s->ws + s->w_err), 1, st);
+    if (!e)
+        e = hipStreamSynchronize(st);
+    return e ? hip_fail(e, "tp_read_error_word") : TP_OK;
+}
+
+int32_t tp_kernel_timing_arm(tp_shard *s, int32_t kernel_id)
+{
+    if (!s)
+        return fail(TP_EINVAL, "tp_kernel_timing_arm: null handle");
+    if (kernel_id < -1 || kernel_id >= KID_COUNT)
+        return fail(TP_EINVAL, "unknown kernel id %d", kernel_id);
+    s->timing_kernel = kernel_id;
+    s->ev_used = 0;
+    return TP_OK;
+}
+
+int32_t tp_kernel_timing_read(tp_shard *s, double *total_ms, int32_t *launches)
+{
+    if (!s || !total_ms || !launches)
+        return fail(TP_EINVAL, "tp_kernel_timing_read: null argument");
+    double tot = 0.0;
+    for (size_t i = 0; i < s->ev_used; i++) {
+        if (hipEventSynchronize(s->ev_pool[i].second) != hipSuccess)
+            return fail(TP_EHIP, "hipEventSynchronize failed");
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, s->ev_pool[i].first, s->ev_pool[i].second) != hipSuccess)
+            return fail(TP_EHIP, "hipEventElapsedTime failed");
+        tot += ms;
+    }
+    *total_ms = tot;
+    *launches = (int32_t)s->ev_used;
+    return TP_OK;
+}
+
+const char *tp_kernel_name(int32_t kernel_id)
+{
+    return (kernel_id >= 0 && kernel_id < KID_COUNT) ? kKernelNames[kernel_id] : nullptr;
+}
+
+const char *tp_status_str(int32_t st)
+{
+    switch (st) {
+    case TP_OK: return "TP_OK";
+    case TP_EINVAL: return "TP_EINVAL";
+    case TP_EALIGN: return "TP_EALIGN";
+    case TP_ESTATE: return "TP_ESTATE";
+    case TP_ENODEV: return "TP_ENODEV";
+    case TP_EHIP: return "TP_EHIP";
+    case TP_ENOTIMPL: return "TP_ENOTIMPL";
+    default: return "TP_UNKNOWN";
+    }
+}
+
+const char *tp_last_error(void) { return g_err.c_str(); }
+
+} // extern "C"

@@ -1,0 +1,155 @@
+// common.h -- device helpers and launch-argument records shared by the
+// library's HIP sources (gfx950, wave64). Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tps {
+
+constexpr int kWave = 64;
+
+// 16-byte vector of a native vector type (usable with the nontemporal builtins)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kMaxWires = 64;
+constexpr int kQBlock = 32;
+
+// ---------------------------------------------------------------- bf16
+
+// bf16 is the upper half of an fp32: widening is a shift, exact.
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u)
+        return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---------------------------------------------------------------- wave reductions
+
+// butterfly over groups of W consecutive lanes (W a power of two <= 64)
+template <int W>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v)
+{
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------- block-32 int8 codec
+// scale = max|x| / 127 (IEEE fp32 division); code = round-half-away(x / scale)
+// clamped to +-127; zero scale -> zero code. `amax` is the block's max |x|.
+__device__ __forceinline__ float q8_scale(float amax) { return amax / 127.0f; }
+__device__ __forceinline__ int q8_code(float x, float scale)
+{
+    if (scale == 0.0f)
+        return 0;
+    float r = roundf(x / scale);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+// dequantisation: one rounded fp32 multiply (never contracted into an add)
+__device__ __forceinline__ float q8_dequant(int code, float scale) { return __fmul_rn((float)code, scale); }
+
+// ---------------------------------------------------------------- launch records
+
+struct NormArgs {
+    const float *x;      // [B][D]
+    const float *g;      // [D]
+    float *xn;           // [B][D]
+    float *tap;          // optional [B][D]
+    int B, D;
+    float eps;
+    int quant;           // int8 round trip of the normalised row
+};
+
+enum GemvEpi { EPI_STORE = 0, EPI_SWIGLU = 1 };
+
+struct GemvArgs {
+    const void *W;       // [N][K] row-major, 16-byte aligned rows
+    const float *x;      // [B][ldx]
+    float *y;            // [B][ldy]; SwiGLU: y[b][n/2]
+    float *tap;          // optional copy of y, same layout
+    int N, K, B, ldx, ldy;
+};
+
+struct AttnArgs {
+    const float *qkv;    // [B][ld_qkv]: q heads, then k heads, then v heads (raw, unrotated)
+    const int *lens;     // [B]
+    void *kc, *vc;       // [max_batch][Hkv_s][max_ctx][hd]
+    const float2 *rope;  // [max_ctx][hd/2] (cos, sin)
+    float *part;         // [B][Hq_s][n_chunks][hd + 4]: (m, l, -, -, o[hd])
+    unsigned *err;
+    float *tap_q, *tap_k, *tap_v;
+    int ld_qkv, max_ctx, Hq_s, Hkv_s, G, hd, chunk, n_chunks;
+    float scale;
+};
+
+struct CombineArgs {
+    const float *part;
+    const int *lens;
+    float *att;          // [B][Hq_s*hd]
+    float *tap;
+    int Hq_s, hd, chunk, n_chunks, max_ctx;
+};
+
+struct WireArgs {
+    const float *p;      // [B][D]
+    int8_t *codes;       // [B][D]
+    float *scales;       // [B][D/32]
+    int B, D;
+};
+
+struct MergeArgs {
+    const void *wires[kMaxWires];
+    const float *residual;
+    float *out;
+    int n_wires, B, D, quant;
+    uint64_t scales_off;
+};
+
+struct RopeArgs {
+    float2 *table;       // [max_ctx][hd/2]
+    int max_ctx, hd;
+    double theta;
+};
+
+struct Ffn2dArgs {
+    const uint16_t *x;   // [B][E] bf16
+    const uint16_t *w13; // [F/16][2][16][E] bf16: 16 gate rows, then the 16 matching up rows
+    const uint16_t *w2;  // [E][F] bf16
+    uint16_t *h;         // [B][F] bf16 workspace
+    float *y;            // [B][E]
+    int B, E, F;
+};
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st);
+hipError_t launch_gemv(const GemvArgs &a, int w_bf16, int epi, hipStream_t st);
+hipError_t launch_attn(const AttnArgs &a, int kv_bf16, int B, hipStream_t st);
+hipError_t launch_combine(const CombineArgs &a, int B, hipStream_t st);
+hipError_t launch_wire(const WireArgs &a, hipStream_t st);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
+hipError_t launch_rope_table(const RopeArgs &a, hipStream_t st);
+hipError_t launch_clear_u32(unsigned *p, int n, hipStream_t st);
+hipError_t launch_ffn2d(const Ffn2dArgs &a, hipStream_t st, int which);
+
+} // namespace tps

@@ -1,0 +1,140 @@
+"""Drives the HIP library through its C ABI (via the ctypes binding) for the
+GPU parity tests and the benchmark: uploads seeded synthetic inputs, runs
+every shard of a layer in turn on one GPU, merges on the device and brings
+the results back as numpy arrays. Imports nothing from oracle/."""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional
+
+import numpy as np
+
+import synth
+import tensor_tp_shard_amd as tp
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def dev_tensor(a: np.ndarray, bf16: bool = False):
+    t = torch()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return t.from_numpy(a.view(np.int16)).view(t.bfloat16).cuda()
+    return t.from_numpy(a).cuda()
+
+
+def to_np(t) -> np.ndarray:
+    tt = torch()
+    t = t.detach()
+    if t.dtype == tt.bfloat16:
+        return t.view(tt.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def config_of(w, rank: int = 0, max_batch: Optional[int] = None) -> tp.TpConfig:
+    dt = {synth.F32: tp.TP_F32, synth.BF16: tp.TP_BF16}
+    return tp.make_config(kind=tp.TP_LLAMA_BLOCK, dim=w.dim, n_heads=w.n_heads,
+                          n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn_hidden=w.ffn_hidden,
+                          tp_size=w.tp, tp_rank=rank, max_batch=max_batch or w.batch,
+                          max_ctx=w.max_ctx, w_dtype=dt[w.w_dtype], kv_dtype=dt[w.kv_dtype],
+                          quant=w.quant, quant_block=32, rope_theta=w.rope_theta,
+                          norm_eps=w.norm_eps)
+
+
+def shard_cache(w, full_cache: np.ndarray, rank: int) -> np.ndarray:
+    """The shard's slice [B][Hkv_s][max_ctx][hd] of a full cache."""
+    hs = w.n_kv_heads // w.tp
+    return np.ascontiguousarray(full_cache[:, rank * hs:(rank + 1) * hs])
+
+
+class Layer:
+    """All T shards of one layer on the GPU, with their caches."""
+
+    def __init__(self, w, d: Dict[str, np.ndarray], ranks: Optional[List[int]] = None):
+        self.w = w
+        self.ranks = list(range(w.tp)) if ranks is None else ranks
+        self.dw = {k: dev_tensor(d[k]) for k in ("wq", "wk", "wv", "wo", "w1", "w3", "w2",
+                                                 "g_att", "g_ffn")}
+        self.shards = {}
+        for r in self.ranks:
+            sh = tp.Shard(config_of(w, r), caches=False)
+            kc = dev_tensor(shard_cache(w, d["kcache"], r)).reshape(-1)
+            vc = dev_tensor(shard_cache(w, d["vcache"], r)).reshape(-1)
+            sh.load(self.dw, k_cache=kc, v_cache=vc)
+            self.shards[r] = sh
+        torch().cuda.synchronize()
+
+    def taps(self, stage: int, B: int) -> Dict[str, object]:
+        t = torch()
+        w = self.w
+        hd, T = w.head_dim, w.tp
+        f = lambda *s: t.full(s, float("nan"), dtype=t.float32, device="cuda")  # noqa: E731
+        if stage == tp.TP_STAGE_ATTN:
+            return {"xn": f(B, w.dim), "q": f(B, w.n_heads // T * hd), "k": f(B, w.n_kv_heads // T * hd),
+                    "v": f(B, w.n_kv_heads // T * hd), "att": f(B, w.n_heads // T * hd),
+                    "p_pre": f(B, w.dim)}
+        return {"xn": f(B, w.dim), "a": f(B, w.ffn_hidden // T), "p_pre": f(B, w.dim)}
+
+    def stage(self, stage: int, x, lens, B: int, with_taps: bool = True):
+        """Runs `stage` on every rank; returns (wires, taps) per rank."""
+        wires, taps = {}, {}
+        for r in self.ranks:
+            sh = self.shards[r]
+            wires[r] = sh.new_wire()
+            taps[r] = self.taps(stage, B) if with_taps else None
+            sh.step(stage, x, lens, B, wires[r], taps[r])
+        return wires, taps
+
+    def merge(self, stage: int, wires, residual, B: int):
+        out = torch().empty_like(residual)
+        self.shards[self.ranks[0]].merge(stage, [wires[r] for r in self.ranks], residual, out, B)
+        return out
+
+    def run(self, x_np: np.ndarray, lens_np: np.ndarray, with_taps: bool = True):
+        """The whole layer step: every shard's attention stage, merge, every
+        shard's FFN stage, merge. Returns numpy results."""
+        t = torch()
+        B = x_np.shape[0]
+        x = dev_tensor(np.ascontiguousarray(x_np, dtype=np.float32))
+        lens = dev_tensor(np.ascontiguousarray(lens_np, dtype=np.int32))
+        wa, ta = self.stage(tp.TP_STAGE_ATTN, x, lens, B, with_taps)
+        h = self.merge(tp.TP_STAGE_ATTN, wa, x, B)
+        wf, tf = self.stage(tp.TP_STAGE_FFN, h, None, B, with_taps)
+        out = self.merge(tp.TP_STAGE_FFN, wf, h, B)
+        t.cuda.synchronize()
+        res = {"h": to_np(h), "out": to_np(out),
+               "wire_att": {r: to_np(v) for r, v in wa.items()},
+               "wire_ffn": {r: to_np(v) for r, v in wf.items()}}
+        if with_taps:
+            res["taps_att"] = {r: {k: to_np(v) for k, v in ta[r].items()} for r in self.ranks}
+            res["taps_ffn"] = {r: {k: to_np(v) for k, v in tf[r].items()} for r in self.ranks}
+        return res
+
+    def cache(self, rank: int):
+        sh = self.shards[rank]
+        w = self.w
+        shape = (w.batch, w.n_kv_heads // w.tp, w.max_ctx, w.head_dim)
+        return to_np(sh.k_cache).reshape(shape), to_np(sh.v_cache).reshape(shape)
+
+    def error_word(self, rank: int) -> int:
+        return tp.read_error_word(self.shards[rank].handle)
+
+
+def split_wire(w, wire: np.ndarray, B: int):
+    """(codes int8 [B][D], scales fp32 [B][D/32]) of a quantised wire."""
+    D = w.dim
+    off = tp.wire_scales_offset(config_of(w), B)
+    codes = wire[:B * D].view(np.int8).reshape(B, D)
+    scales = wire[off:off + B * (D // 32) * 4].view(np.float32).reshape(B, D // 32)
+    return codes, scales
+
+
+def fp32_wire(w, wire: np.ndarray, B: int) -> np.ndarray:
+    return wire[:B * w.dim * 4].view(np.float32).reshape(B, w.dim)
+
+
+def with_batch(w, B: int):
+    return dataclasses.replace(w, batch=B)

@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute calls): the
+library loads, exports every function include/tpshard.h declares, and
+rejects bad arguments with the documented status before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tensor_tp_shard_amd as tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[a-z_][\w \*]*?\b(\w+)\s*\([^;{]*\)\s*;", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12, names
+    L = tp.lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing
+    assert set(names) == set(tp.EXPORTS)
+
+
+def cfg7b(**kw):
+    base = dict(dim=4096, n_heads=32, n_kv_heads=32, head_dim=128, ffn_hidden=11008, tp_size=4,
+                tp_rank=0, max_batch=1, max_ctx=2049)
+    base.update(kw)
+    return tp.make_config(**base)
+
+
+def test_sizes_of_the_7b_shard():
+    h, s = tp.init_shard(cfg7b())
+    D, hd = 4096, 128
+    weights = (3 * 8 * hd * D + D * 8 * hd + 2 * 2752 * D + D * 2752) * 2
+    assert s.packed_weights >= weights and s.packed_weights < weights + 2 * 2049 * 64 * 8 + 8192
+    assert s.kv_cache_each == 1 * 8 * 2049 * 128 * 2
+    assert s.wire == D * 4
+    tp.destroy_shard(h)
+    h, s = tp.init_shard(cfg7b(quant=tp.TP_Q_PARTIALS | tp.TP_Q_INPUTS))
+    assert s.wire == D + (D // 32) * 4
+    assert tp.wire_scales_offset(cfg7b(), 3) == 3 * D
+    tp.destroy_shard(h)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n_heads=30),                # n_heads % n_kv_heads
+    dict(tp_size=3),                 # T does not divide heads
+    dict(tp_rank=4),                 # rank outside [0, T)
+    dict(head_dim=120),              # not a multiple of 16
+    dict(max_batch=0),
+    dict(max_batch=17),
+    dict(quant=4),                   # unknown bit
+    dict(quant=1, quant_block=16),   # block must be 32
+    dict(w_dtype=7),
+    dict(kind=5),
+    dict(n_kv_heads=2, n_heads=32, tp_size=2),  # 16 q heads per kv head
+    dict(dim=4100, n_heads=32, quant=1),  # dim % 32 when quantising
+])
+def test_init_rejects_bad_config(kw):
+    with pytest.raises(tp.TpError) as e:
+        tp.init_shard(cfg7b(**kw))
+    assert e.value.status == tp.TP_EINVAL
+
+
+def test_order_alignment_and_device_errors():
+    h, s = tp.init_shard(tp.make_config(dim=288, n_heads=6, n_kv_heads=6, head_dim=48,
+                                        ffn_hidden=768, tp_size=2, max_batch=1, max_ctx=65,
+                                        w_dtype=tp.TP_F32, kv_dtype=tp.TP_F32))
+    fake = 0x10000  # never dereferenced: every call below fails on the host
+    W = {k: fake for k in ("wq", "wk", "wv", "wo", "w1", "w3", "w2", "g_att", "g_ffn")}
+    with pytest.raises(tp.TpError) as e:
+        tp.decode_step(h, tp.TP_STAGE_ATTN, fake, fake, 1, fake, stream=0)
+    assert e.value.status == tp.TP_ESTATE
+    with pytest.raises(tp.TpError) as e:
+        tp.load_weights(h, W, fake + 4, fake, fake, fake, stream=0)
+    assert e.value.status == tp.TP_EALIGN
+    W2 = dict(W)
+    W2["wo"] = None
+    with pytest.raises(tp.TpError) as e:
+        tp.load_weights(h, W2, fake, fake, fake, fake, stream=0)
+    assert e.value.status == tp.TP_EINVAL
+    import torch
+    if not torch.cuda.is_available():
+        with pytest.raises(tp.TpError) as e:
+            tp.load_weights(h, W, fake, fake, fake, fake, stream=0)
+        assert e.value.status == tp.TP_ENODEV
+    with pytest.raises(tp.TpError) as e:
+        tp.merge_partials(h, tp.TP_STAGE_FFN, [], fake, fake, 1, stream=0)
+    assert e.value.status == tp.TP_EINVAL
+    with pytest.raises(tp.TpError) as e:
+        tp.merge_partials(h, tp.TP_STAGE_FFN, [fake] * 65, fake, fake, 1, stream=0)
+    assert e.value.status == tp.TP_EINVAL
+    with pytest.raises(tp.TpError) as e:
+        tp.kernel_timing_arm(h, 99)
+    assert e.value.status == tp.TP_EINVAL
+    tp.destroy_shard(h)
+
+
+def test_null_arguments_and_status_strings():
+    L = tp.lib()
+    assert L.init_shard(None, None, None) == tp.TP_EINVAL
+    assert b"null" in L.tp_last_error()
+    assert L.tp_status_str(tp.TP_EALIGN) == b"TP_EALIGN"
+    names = tp.kernel_names()
+    assert "gemv_w13_swiglu" in names and len(names) == len(set(names))
+    L.destroy_shard(None)
