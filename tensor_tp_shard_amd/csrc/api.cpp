@@ -54,7 +54,6 @@ enum KernelId {
     KID_RMSNORM = 0,
     KID_GEMV_QKV,
     KID_ATTN,
-    KID_COMBINE,
     KID_GEMV_WO,
     KID_WIRE,
     KID_GEMV_W13,
@@ -67,8 +66,8 @@ enum KernelId {
 };
 
 const char *const kKernelNames[KID_COUNT] = {
-    "rmsnorm",         "gemv_qkv",   "attn_split", "attn_combine", "gemv_wo",  "q8_wire",
-    "gemv_w13_swiglu", "gemv_w2",    "merge",      "ffn2d_up",     "ffn2d_down", "rope_table"};
+    "rmsnorm",    "gemv_qkv", "attention", "gemv_wo",  "q8_wire",    "gemv_w13_swiglu",
+    "gemv_w2",    "merge",    "ffn2d_up",  "ffn2d_down", "rope_table"};
 
 } // namespace
 
@@ -142,8 +141,8 @@ int32_t plan(const tp_config &c, tp_shard &s)
         return fail(TP_EINVAL, "n_heads %% n_kv_heads != 0");
     if (c.n_heads % T || c.n_kv_heads % T || c.ffn_hidden % T)
         return fail(TP_EINVAL, "tp_size must divide n_heads, n_kv_heads and ffn_hidden");
-    if (c.head_dim % 16 || c.head_dim > 256)
-        return fail(TP_EINVAL, "head_dim must be a multiple of 16, at most 256");
+    if (c.head_dim % 16 || c.head_dim > 128)
+        return fail(TP_EINVAL, "head_dim must be a multiple of 16, at most 128");
     if (c.n_heads / c.n_kv_heads > 8)
         return fail(TP_EINVAL, "at most 8 q heads per kv head");
     if (c.max_batch > 16)
@@ -165,8 +164,12 @@ int32_t plan(const tp_config &c, tp_shard &s)
     s.esz = c.w_dtype == TP_BF16 ? 2 : 4;
     s.kv_esz = c.kv_dtype == TP_BF16 ? 2 : 4;
     const int vec = 16 / s.esz;
-    if (s.D % vec || (s.Hq_s * s.hd) % vec || s.Fs % vec)
-        return fail(TP_EINVAL, "dim, Hq/T*head_dim and ffn_hidden/T must be multiples of %d", vec);
+    if (s.D % 8 || (s.Hq_s * s.hd) % vec || s.Fs % vec)
+        return fail(TP_EINVAL, "dim must be a multiple of 8, Hq/T*head_dim and ffn_hidden/T of %d",
+                    vec);
+    s.n_chunks = (c.max_ctx + 63) / 64;
+    if (attn_lds_bytes(s.G, s.hd, c.kv_dtype == TP_BF16, s.n_chunks) > 64 * 1024)
+        return fail(TP_EINVAL, "attention workgroup would need more than 64 KiB of LDS");
     const uint64_t D = s.D, B = c.max_batch, e = s.esz;
     uint64_t o = 0;
     s.o_wqkv = o; o = align_up(o + (uint64_t)s.n_qkv * D * e, 256);
@@ -177,7 +180,6 @@ int32_t plan(const tp_config &c, tp_shard &s)
     s.o_gffn = o; o = align_up(o + D * 4, 256);
     s.o_rope = o; o = align_up(o + (uint64_t)c.max_ctx * (s.hd / 2) * 8, 256);
     s.packed_bytes = o;
-    s.n_chunks = (c.max_ctx + 63) / 64;
     o = 0;
     s.w_err = o;  o = 256;
     s.w_xn = o;   o = align_up(o + B * D * 4, 256);
@@ -408,77 +410,109 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
 
     const bool wbf = s->cfg.w_dtype == TP_BF16;
     const bool qin = s->cfg.quant & TP_Q_INPUTS, qpart = s->cfg.quant & TP_Q_PARTIALS;
-    float *xn = (float *)(s->ws + s->w_xn);
-    // the partial goes straight into the wire unless it is quantised first
+    const float *gain = (const float *)(s->packed + (stage == TP_STAGE_ATTN ? s->o_gatt : s->o_gffn));
+    // the partial goes straight into the wire unless it is quantised
     float *p = qpart ? (float *)(s->ws + s->w_p) : (float *)wire_out;
-    const size_t D = s->D;
+    int8_t *codes = qpart ? (int8_t *)wire_out : nullptr;
+    float *scales = qpart ? (float *)((char *)wire_out + tp_wire_scales_offset(&s->cfg, B)) : nullptr;
     int32_t rc;
 
-    NormArgs na{(const float *)x,
-                (const float *)(s->packed + (stage == TP_STAGE_ATTN ? s->o_gatt : s->o_gffn)),
-                xn, tp.xn, B, s->D, s->cfg.norm_eps, qin ? 1 : 0};
-    rc = timed(s, KID_RMSNORM, st, "rmsnorm", [&] { return launch_rmsnorm(na, st); });
-    if (rc)
-        return rc;
+    // RMSNorm: fused into the projection's prologue when the batch's rows fit
+    // in LDS, else a kernel of its own writing xn
+    const bool fuse_norm = gemv_fused_ok(B, s->D);
+    const float *in = (const float *)x;
+    GemvArgs up{};
+    up.x = in;
+    up.ldx = s->D;
+    up.K = s->D;
+    up.B = B;
+    if (fuse_norm) {
+        up.g = gain;
+        up.eps = s->cfg.norm_eps;
+        up.qin = qin ? 1 : 0;
+        up.xn_tap = tp.xn;
+    } else {
+        float *xn = (float *)(s->ws + s->w_xn);
+        NormArgs na{in, gain, xn, tp.xn, B, s->D, s->cfg.norm_eps, qin ? 1 : 0};
+        rc = timed(s, KID_RMSNORM, st, "rmsnorm", [&] { return launch_rmsnorm(na, st); });
+        if (rc)
+            return rc;
+        up.x = xn;
+    }
+    // row-split projection; its fp32 partial is quantised into the wire after it
+    GemvArgs down{};
+    down.y = p;
+    down.tap = tp.p_pre;
+    down.N = s->D;
+    down.ldy = s->D;
+    down.B = B;
+    const int Kd = stage == TP_STAGE_ATTN ? s->Hq_s * s->hd : s->Fs;
 
     if (stage == TP_STAGE_ATTN) {
         if (!lens)
             return fail(TP_EINVAL, "decode_step: attention stage needs lens");
         float *qkv = (float *)(s->ws + s->w_qkv);
-        GemvArgs g{s->packed + s->o_wqkv, xn, qkv, nullptr, s->n_qkv, s->D, B, s->D, s->n_qkv};
-        rc = timed(s, KID_GEMV_QKV, st, "gemv qkv", [&] { return launch_gemv(g, wbf, EPI_STORE, st); });
+        up.W = s->packed + s->o_wqkv;
+        up.y = qkv;
+        up.N = s->n_qkv;
+        up.ldy = s->n_qkv;
+        rc = timed(s, KID_GEMV_QKV, st, "gemv qkv", [&] { return launch_gemv(up, wbf, EPI_STORE, st); });
         if (rc)
             return rc;
-        AttnArgs aa{qkv,
-                    lens,
-                    s->kc,
-                    s->vc,
-                    (const float2 *)(s->packed + s->o_rope),
-                    (float *)(s->ws + s->w_part),
-                    (unsigned *)(s->ws + s->w_err),
-                    tp.q,
-                    tp.k,
-                    tp.v,
-                    s->n_qkv,
-                    s->cfg.max_ctx,
-                    s->Hq_s,
-                    s->Hkv_s,
-                    s->G,
-                    s->hd,
-                    64,
-                    s->n_chunks,
-                    (float)(1.0 / std::sqrt((double)s->hd))};
+        float *att = (float *)(s->ws + s->w_att);
+        AttnArgs aa{};
+        aa.qkv = qkv;
+        aa.lens = lens;
+        aa.kc = s->kc;
+        aa.vc = s->vc;
+        aa.rope = (const float2 *)(s->packed + s->o_rope);
+        aa.part = (float *)(s->ws + s->w_part);
+        aa.err = (unsigned *)(s->ws + s->w_err);
+        aa.att = att;
+        aa.tap_q = tp.q;
+        aa.tap_k = tp.k;
+        aa.tap_v = tp.v;
+        aa.tap_att = tp.att;
+        aa.ld_qkv = s->n_qkv;
+        aa.max_ctx = s->cfg.max_ctx;
+        aa.Hq_s = s->Hq_s;
+        aa.Hkv_s = s->Hkv_s;
+        aa.G = s->G;
+        aa.hd = s->hd;
+        aa.n_chunks = s->n_chunks;
+        aa.scale = (float)(1.0 / std::sqrt((double)s->hd));
         rc = timed(s, KID_ATTN, st, "attention",
                    [&] { return launch_attn(aa, s->cfg.kv_dtype == TP_BF16, B, st); });
         if (rc)
             return rc;
-        float *att = (float *)(s->ws + s->w_att);
-        CombineArgs ca{(const float *)(s->ws + s->w_part), lens, att, tp.att, s->Hq_s, s->hd, 64,
-                       s->n_chunks, s->cfg.max_ctx};
-        rc = timed(s, KID_COMBINE, st, "attention combine", [&] { return launch_combine(ca, B, st); });
-        if (rc)
-            return rc;
-        GemvArgs o{s->packed + s->o_wo, att, p, tp.p_pre, s->D, s->Hq_s * s->hd, B,
-                   s->Hq_s * s->hd, s->D};
-        rc = timed(s, KID_GEMV_WO, st, "gemv wo", [&] { return launch_gemv(o, wbf, EPI_STORE, st); });
+        down.W = s->packed + s->o_wo;
+        down.x = att;
+        down.K = Kd;
+        down.ldx = Kd;
+        rc = timed(s, KID_GEMV_WO, st, "gemv wo", [&] { return launch_gemv(down, wbf, EPI_STORE, st); });
         if (rc)
             return rc;
     } else {
         float *a = (float *)(s->ws + s->w_a);
-        GemvArgs u{s->packed + s->o_w13, xn, a, tp.a, 2 * s->Fs, s->D, B, s->D, s->Fs};
-        rc = timed(s, KID_GEMV_W13, st, "gemv w13",
-                   [&] { return launch_gemv(u, wbf, EPI_SWIGLU, st); });
+        up.W = s->packed + s->o_w13;
+        up.y = a;
+        up.tap = tp.a;
+        up.N = 2 * s->Fs;
+        up.ldy = s->Fs;
+        rc = timed(s, KID_GEMV_W13, st, "gemv w13", [&] { return launch_gemv(up, wbf, EPI_SWIGLU, st); });
         if (rc)
             return rc;
-        GemvArgs dn{s->packed + s->o_w2, a, p, tp.p_pre, s->D, s->Fs, B, s->Fs, s->D};
-        rc = timed(s, KID_GEMV_W2, st, "gemv w2", [&] { return launch_gemv(dn, wbf, EPI_STORE, st); });
+        down.W = s->packed + s->o_w2;
+        down.x = a;
+        down.K = Kd;
+        down.ldx = Kd;
+        rc = timed(s, KID_GEMV_W2, st, "gemv w2", [&] { return launch_gemv(down, wbf, EPI_STORE, st); });
         if (rc)
             return rc;
     }
 
     if (qpart) {
-        WireArgs wa{p, (int8_t *)wire_out,
-                    (float *)((char *)wire_out + tp_wire_scales_offset(&s->cfg, B)), B, s->D};
+        WireArgs wa{p, codes, scales, B, s->D};
         return timed(s, KID_WIRE, st, "q8 wire", [&] { return launch_wire(wa, st); });
     }
     return TP_OK;

@@ -88,6 +88,12 @@ struct GemvArgs {
     float *y;            // [B][ldy]; SwiGLU: y[b][n/2]
     float *tap;          // optional copy of y, same layout
     int N, K, B, ldx, ldy;
+    // fused RMSNorm prologue (g != null): x is the raw stage input and the
+    // product uses xn = g * x / sqrt(mean(x^2) + eps) [int8 round trip if qin]
+    const float *g;
+    float eps;
+    int qin;
+    float *xn_tap;       // [B][K]: the normalised rows, written by block 0
 };
 
 struct AttnArgs {
@@ -97,17 +103,10 @@ struct AttnArgs {
     const float2 *rope;  // [max_ctx][hd/2] (cos, sin)
     float *part;         // [B][Hq_s][n_chunks][hd + 4]: (m, l, -, -, o[hd])
     unsigned *err;
-    float *tap_q, *tap_k, *tap_v;
-    int ld_qkv, max_ctx, Hq_s, Hkv_s, G, hd, chunk, n_chunks;
+    float *att;          // [B][Hq_s*hd] combined attention output
+    float *tap_q, *tap_k, *tap_v, *tap_att;
+    int ld_qkv, max_ctx, Hq_s, Hkv_s, G, hd, n_chunks;
     float scale;
-};
-
-struct CombineArgs {
-    const float *part;
-    const int *lens;
-    float *att;          // [B][Hq_s*hd]
-    float *tap;
-    int Hq_s, hd, chunk, n_chunks, max_ctx;
 };
 
 struct WireArgs {
@@ -145,7 +144,9 @@ struct Ffn2dArgs {
 hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st);
 hipError_t launch_gemv(const GemvArgs &a, int w_bf16, int epi, hipStream_t st);
 hipError_t launch_attn(const AttnArgs &a, int kv_bf16, int B, hipStream_t st);
-hipError_t launch_combine(const CombineArgs &a, int B, hipStream_t st);
+size_t attn_lds_bytes(int G, int hd, int kv_bf16, int n_chunks);
+size_t gemv_lds_bytes(int B, int K);
+bool gemv_fused_ok(int B, int K);
 hipError_t launch_wire(const WireArgs &a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
 hipError_t launch_rope_table(const RopeArgs &a, hipStream_t st);

@@ -1,5 +1,5 @@
 // k_attn.hip -- RoPE, KV-cache append and split-KV grouped-query decode
-// attention over one shard's cache, then the fixed-order combine.
+// attention over one shard's cache, with the chunk combine fused in.
 //
 // Pages: distributed-llama issue "[Feature Suggest] Tensor Parallellism for
 // Accelerating LLM", buildLlama2Arch task llamaMultiheadAtt ("merge kv-cache,
@@ -18,28 +18,34 @@
 // Work split: one 256-thread workgroup per (sequence b, kv head g, chunk of
 // 64 positions). The workgroup serves all G query heads of kv head g, so each
 // K/V row is read from HBM once per step however many q heads share it.
-//  scores : 4 threads per position, each a 16-element stride of hd, butterfly
-//           over the 4 -> s[j][t] for the G heads
+//  load   : the chunk's K and V rows go to LDS in one round trip (16-byte
+//           loads, all issued before the first is used); the chunk holding
+//           position lens[b] rotates the new k, rounds k and v to the cache
+//           type, appends them to the cache and to its LDS rows
+//  scores : 4 threads per position, butterfly over the 4 -> s[j][t]
 //  softmax: one wave per head: chunk max m, p = exp(s - m), l = sum p
 //  values : hd/4 threads per row, 4 dims each, rows split into phases;
 //           phases summed in fixed order through LDS
-// The chunk holding position lens[b] rotates the new k, rounds k and v to the
-// cache type, appends them and uses the rounded values.
-// Partial record per (b, q head, chunk): m, l, -, -, o[hd] (unnormalised).
+//  combine: a second kernel (one workgroup per (b, g)) merges the chunk
+//           records in chunk order: att = sum_c o_c e^(m_c - M) / sum_c l_c
+//           e^(m_c - M). A separate launch is cheaper here than publishing
+//           through agent-scope fences, which on this chip write back and
+//           invalidate a whole XCD L2 per workgroup.
 #include "common.h"
 
 namespace tps {
 
 constexpr int kChunk = 64;
+constexpr int kMaxPieces = 8; // 16-byte pieces per thread per tensor (64 rows x hd <= 128 fp32)
 
 template <bool KBF16>
-__device__ __forceinline__ float4 load4(const void *base, size_t elem)
+__device__ __forceinline__ float4 lds4(const char *row, int d)
 {
     if constexpr (KBF16) {
-        const uint2 u = *(const uint2 *)((const uint16_t *)base + elem);
+        const uint2 u = *(const uint2 *)(row + 2 * d);
         return make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
     } else {
-        return *(const float4 *)((const float *)base + elem);
+        return *(const float4 *)(row + 4 * d);
     }
 }
 
@@ -61,6 +67,18 @@ __device__ __forceinline__ void store_kv(void *base, size_t elem, float v)
         ((float *)base)[elem] = v;
 }
 
+// bytes of one padded LDS row of K or V
+__host__ __device__ inline int attn_row_bytes(int hd, int kv_bf16) { return hd * (kv_bf16 ? 2 : 4) + 16; }
+
+__host__ __device__ inline size_t attn_smem_bytes(int G, int GM, int hd, int kv_bf16, int n_chunks)
+{
+    const int nph = 256 / (hd / 4);
+    const size_t rowb = attn_row_bytes(hd, kv_bf16);
+    const size_t kr = kChunk * rowb > (size_t)nph * G * hd * 4 ? kChunk * rowb : (size_t)nph * G * hd * 4;
+    (void)n_chunks;
+    return sizeof(float) * ((size_t)G * hd + (size_t)G * kChunk + 4 * GM) + kChunk * rowb + kr;
+}
+
 template <bool KBF16, int GM>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
 {
@@ -69,7 +87,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int L = a.lens[b];
-    if (L < 0 || L >= a.max_ctx) {
+    if (L < 0 || L >= a.max_ctx) { // skipped sequence: flagged here, zeroed by the combine
         if (c == 0 && g == 0 && tid == 0)
             atomicOr(a.err, 1u);
         return;
@@ -78,51 +96,99 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
     if (t0 > L)
         return;
     const int n = min(kChunk, L + 1 - t0); // positions in this chunk
+    const int nch = L / kChunk + 1;        // chunks of this sequence
     const bool owner = L < t0 + kChunk;
+    const int esz = KBF16 ? 2 : 4;
+    const int rowb = attn_row_bytes(hd, KBF16);
 
-    float *q_s = smem;                  // [G][hd]
-    float *s_s = q_s + G * hd;          // [G][64]
-    float *knew = s_s + G * kChunk;     // [hd]
-    float *vnew = knew + hd;            // [hd]
-    float *ml = vnew + hd;              // [G][2] (4*GM floats keep red 16-byte aligned)
-    float *red = ml + 4 * GM;           // [phases][G][hd]
+    float *q_s = smem;                            // [G][hd]
+    float *s_s = q_s + G * hd;                    // [G][64]
+    float *ml = s_s + G * kChunk;                 // [G][2] (4*GM floats)
+    char *V_s = (char *)(ml + 4 * GM);            // [64][rowb]
+    char *K_s = V_s + kChunk * rowb;              // [64][rowb], later the value-phase sums
+    float *red = (float *)K_s;
 
+    const size_t head_base = ((size_t)b * a.Hkv_s + g) * a.max_ctx * hd;
     const float *qkv = a.qkv + (size_t)b * a.ld_qkv;
     const float2 *rope = a.rope + (size_t)L * (hd / 2);
     const int half = hd / 2;
-
-    // rotated queries of the G heads served by kv head g
-    for (int i = tid; i < G * half; i += 256) {
-        const int j = i / half, p = i % half;
-        const int h = g * G + j;
-        const float x0 = qkv[h * hd + 2 * p], x1 = qkv[h * hd + 2 * p + 1];
-        const float2 cs = rope[p];
-        const float r0 = x0 * cs.x - x1 * cs.y, r1 = x0 * cs.y + x1 * cs.x;
-        q_s[j * hd + 2 * p] = r0;
-        q_s[j * hd + 2 * p + 1] = r1;
-        if (c == 0 && a.tap_q) {
-            a.tap_q[(size_t)b * a.Hq_s * hd + h * hd + 2 * p] = r0;
-            a.tap_q[(size_t)b * a.Hq_s * hd + h * hd + 2 * p + 1] = r1;
+    // 1) query pairs and their rotation factors first (they return first), then
+    //    the chunk's K and V rows: all 16-byte loads issued before any is used
+    constexpr int kQP = 4; // query pairs per thread: G * hd / 2 <= 8 * 64 = 512 <= 256 * kQP
+    float2 qp[kQP], cs[kQP];
+#pragma unroll
+    for (int u = 0; u < kQP; u++) {
+        const int i = tid + 256 * u;
+        if (i < G * half) {
+            const int j = i / half, p = i % half;
+            qp[u] = *(const float2 *)(qkv + (g * G + j) * hd + 2 * p);
+            cs[u] = rope[p];
         }
     }
-    const size_t head_base = ((size_t)b * a.Hkv_s + g) * a.max_ctx * hd;
-    if (owner) { // rotate and append the new key / value at slot L
+    const int ppr = hd * esz / 16; // 16-byte pieces per row
+    const int npc = n * ppr;
+    u32x4 kv[2][kMaxPieces];
+    {
+        const u32x4 *kg = (const u32x4 *)((const char *)a.kc + (head_base + (size_t)t0 * hd) * esz);
+        const u32x4 *vg = (const u32x4 *)((const char *)a.vc + (head_base + (size_t)t0 * hd) * esz);
+#pragma unroll
+        for (int i = 0; i < kMaxPieces; i++) {
+            const int p = tid + 256 * i;
+            if (p < npc) {
+                kv[0][i] = __builtin_nontemporal_load(kg + p);
+                kv[1][i] = __builtin_nontemporal_load(vg + p);
+            }
+        }
+    }
+    // 2) rotated queries of the G heads served by kv head g
+#pragma unroll
+    for (int u = 0; u < kQP; u++) {
+        const int i = tid + 256 * u;
+        if (i < G * half) {
+            const int j = i / half, p = i % half;
+            const float r0 = qp[u].x * cs[u].x - qp[u].y * cs[u].y;
+            const float r1 = qp[u].x * cs[u].y + qp[u].y * cs[u].x;
+            q_s[j * hd + 2 * p] = r0;
+            q_s[j * hd + 2 * p + 1] = r1;
+            if (c == 0 && a.tap_q) {
+                const int h = g * G + j;
+                a.tap_q[(size_t)b * a.Hq_s * hd + h * hd + 2 * p] = r0;
+                a.tap_q[(size_t)b * a.Hq_s * hd + h * hd + 2 * p + 1] = r1;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxPieces; i++) {
+        const int p = tid + 256 * i;
+        if (p < npc) {
+            const int row = p / ppr, col = p % ppr;
+            *(u32x4 *)(K_s + row * rowb + col * 16) = kv[0][i];
+            *(u32x4 *)(V_s + row * rowb + col * 16) = kv[1][i];
+        }
+    }
+    __syncthreads();
+    // 3) the owner rotates and appends the new key / value at slot L
+    if (owner) {
         const float *kq = qkv + (a.Hq_s + g) * hd;
         const float *vq = qkv + (a.Hq_s + a.Hkv_s + g) * hd;
+        char *krow = K_s + (L - t0) * rowb, *vrow = V_s + (L - t0) * rowb;
         for (int p = tid; p < half; p += 256) {
             const float x0 = kq[2 * p], x1 = kq[2 * p + 1];
-            const float2 cs = rope[p];
-            const float r0 = x0 * cs.x - x1 * cs.y, r1 = x0 * cs.y + x1 * cs.x;
+            const float2 cr = rope[p];
+            const float r0 = x0 * cr.x - x1 * cr.y, r1 = x0 * cr.y + x1 * cr.x;
             const float v0 = vq[2 * p], v1 = vq[2 * p + 1];
             const size_t e = head_base + (size_t)L * hd + 2 * p;
             store_kv<KBF16>(a.kc, e, r0);
             store_kv<KBF16>(a.kc, e + 1, r1);
             store_kv<KBF16>(a.vc, e, v0);
             store_kv<KBF16>(a.vc, e + 1, v1);
-            knew[2 * p] = round_kv<KBF16>(r0);
-            knew[2 * p + 1] = round_kv<KBF16>(r1);
-            vnew[2 * p] = round_kv<KBF16>(v0);
-            vnew[2 * p + 1] = round_kv<KBF16>(v1);
+            if constexpr (KBF16) {
+                *(uint32_t *)(krow + 4 * p) = (uint32_t)f32_to_bf16(r0) | ((uint32_t)f32_to_bf16(r1) << 16);
+                *(uint32_t *)(vrow + 4 * p) = (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+            } else {
+                *(float2 *)(krow + 8 * p) = make_float2(r0, r1);
+                *(float2 *)(vrow + 8 * p) = make_float2(v0, v1);
+            }
             if (a.tap_k) {
                 float *tk = a.tap_k + (size_t)b * a.Hkv_s * hd + g * hd;
                 float *tv = a.tap_v + (size_t)b * a.Hkv_s * hd + g * hd;
@@ -132,21 +198,20 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
                 tv[2 * p + 1] = v1;
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
 
-    // scores: 4 threads per position; thread quarter qt covers dims 4qt + 16i
+    // 4) scores: 4 threads per position; thread quarter qt covers dims 4qt + 16i
     {
         const int pl = tid >> 2, qt = tid & 3;
-        const int t = t0 + pl;
         float sacc[GM];
 #pragma unroll
         for (int j = 0; j < GM; j++)
             sacc[j] = 0.f;
         if (pl < n) {
+            const char *krow = K_s + pl * rowb;
             for (int d = 4 * qt; d < hd; d += 16) {
-                const float4 k4 = (t == L) ? *(const float4 *)(knew + d)
-                                           : load4<KBF16>(a.kc, head_base + (size_t)t * hd + d);
+                const float4 k4 = lds4<KBF16>(krow, d);
 #pragma unroll
                 for (int j = 0; j < GM; j++) {
                     if (j < G) {
@@ -165,7 +230,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
     }
     __syncthreads();
 
-    // chunk softmax statistics, one wave per head
+    // 5) chunk softmax statistics, one wave per head
     {
         const int w = tid >> 6, lane = tid & 63;
         for (int j = w; j < G; j += 4) {
@@ -182,20 +247,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
     }
     __syncthreads();
 
-    // o[j][d] = sum_t p[j][t] v[t][d]
-    const int tpr = hd / 4;       // threads per row
-    const int nph = 256 / tpr;    // row phases
+    // 6) o[j][d] = sum_t p[j][t] v[t][d]; K_s is dead, its space holds the phase sums
+    const int tpr = hd / 4;    // threads per row
+    const int nph = 256 / tpr; // row phases
     {
         const int ph = tid / tpr, d = (tid % tpr) * 4;
-        if (ph < nph) {
-            float4 acc[GM];
+        float4 acc[GM];
 #pragma unroll
-            for (int j = 0; j < GM; j++)
-                acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < GM; j++)
+            acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ph < nph) {
             for (int pl = ph; pl < n; pl += nph) {
-                const int t = t0 + pl;
-                const float4 v4 = (t == L) ? *(const float4 *)(vnew + d)
-                                           : load4<KBF16>(a.vc, head_base + (size_t)t * hd + d);
+                const float4 v4 = lds4<KBF16>(V_s + pl * rowb, d);
 #pragma unroll
                 for (int j = 0; j < GM; j++) {
                     if (j < G) {
@@ -207,6 +270,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
                     }
                 }
             }
+        }
+        __syncthreads(); // every thread is done with K_s before it is overwritten
+        if (ph < nph) {
 #pragma unroll
             for (int j = 0; j < GM; j++)
                 if (j < G)
@@ -214,59 +280,126 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
         }
     }
     __syncthreads();
+    const size_t rec_stride = (size_t)a.n_chunks * (hd + 4);
+    float *rec0 = a.part + ((size_t)b * a.Hq_s + (size_t)g * G) * rec_stride;
     for (int i = tid; i < G * hd; i += 256) {
         const int j = i / hd, d = i % hd;
         float o = 0.f;
         for (int ph = 0; ph < nph; ph++)
             o += red[((size_t)ph * G + j) * hd + d];
-        float *rec = a.part + (((size_t)b * a.Hq_s + g * G + j) * a.n_chunks + c) * (hd + 4);
+        float *rec = rec0 + j * rec_stride + (size_t)c * (hd + 4);
         rec[4 + d] = o;
         if (d == 0) {
             rec[0] = ml[2 * j];
             rec[1] = ml[2 * j + 1];
         }
     }
+
 }
 
-// att[b][h][d] = sum_c o_c[d] e^(m_c - M) / sum_c l_c e^(m_c - M), c in order.
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a)
+// Combine of the chunk partials of one (sequence b, kv head g): the G query
+// heads' outputs att = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M), chunks
+// summed in chunk order. All (m, l) and the first kCU chunks of every output
+// quad are loaded in one batch before any arithmetic.
+constexpr int kCombThreads = 512;
+
+__global__ __launch_bounds__(kCombThreads) void k_combine(AttnArgs a)
 {
-    const int h = blockIdx.x, b = blockIdx.y, hd = a.hd;
-    float *out = a.att + ((size_t)b * a.Hq_s + h) * hd;
-    float *tap = a.tap ? a.tap + ((size_t)b * a.Hq_s + h) * hd : nullptr;
+    extern __shared__ float smem[];
+    const int hd = a.hd, G = a.G, g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int L = a.lens[b];
-    if (L < 0 || L >= a.max_ctx) {
-        for (int d = threadIdx.x; d < hd; d += blockDim.x) {
-            out[d] = 0.f;
-            if (tap)
-                tap[d] = 0.f;
+    if (L < 0 || L >= a.max_ctx) { // skipped sequence: its attention output is 0
+        for (int i = tid; i < G * hd; i += kCombThreads) {
+            const size_t o = (size_t)b * a.Hq_s * hd + (size_t)g * G * hd + i;
+            a.att[o] = 0.f;
+            if (a.tap_att)
+                a.tap_att[o] = 0.f;
         }
         return;
     }
-    const int nch = L / a.chunk + 1;
-    const float *rec = a.part + ((size_t)b * a.Hq_s + h) * a.n_chunks * (hd + 4);
-    float M = -INFINITY;
-    for (int c = 0; c < nch; c++)
-        M = fmaxf(M, rec[(size_t)c * (hd + 4)]);
-    float l = 0.f;
-    for (int c = 0; c < nch; c++)
-        l += rec[(size_t)c * (hd + 4) + 1] * expf(rec[(size_t)c * (hd + 4)] - M);
-    const float inv = 1.0f / l;
-    for (int d = threadIdx.x; d < hd; d += blockDim.x) {
+    const int nch = L / kChunk + 1;
+    const int ws = a.n_chunks;
+    const size_t rec_stride = (size_t)a.n_chunks * (hd + 4);
+    const float *rec0 = a.part + ((size_t)b * a.Hq_s + (size_t)g * G) * rec_stride;
+    float *wts = smem;                                // [G][n_chunks] m_c, then e^(m_c - M)
+    float *lsv = wts + G * ws;                        // [G][n_chunks] l_c
+    float *inv_l = lsv + G * ws;                      // [G]
+    float *osum = smem + ((2 * G * ws + 8 + 3) & ~3); // [phases][G][hd]
+    const int quads = G * (hd / 4);
+    const int cph = kCombThreads / quads;             // chunk phases (quads <= 256)
+    constexpr int kCU = 16;                           // chunks per phase loaded together
+    const int qd = tid % quads, cp = tid / quads;
+    const bool qact = cp < cph;
+    const int j = qd / (hd / 4), d = (qd % (hd / 4)) * 4;
+    const float *rj = rec0 + j * rec_stride + 4 + d;
+    float4 v[kCU];
+#pragma unroll
+    for (int u = 0; u < kCU; u++) {
+        const int cc = cp + u * cph;
+        if (qact && cc < nch)
+            v[u] = *(const float4 *)(rj + (size_t)cc * (hd + 4));
+    }
+    for (int i = tid; i < G * nch; i += kCombThreads) {
+        const int jj = i / nch, cc = i % nch;
+        const float2 m_l = *(const float2 *)(rec0 + jj * rec_stride + (size_t)cc * (hd + 4));
+        wts[jj * ws + cc] = m_l.x;
+        lsv[jj * ws + cc] = m_l.y;
+    }
+    __syncthreads();
+    if (tid < G) {
+        float M = -INFINITY;
+        for (int cc = 0; cc < nch; cc++)
+            M = fmaxf(M, wts[tid * ws + cc]);
+        float l = 0.f;
+        for (int cc = 0; cc < nch; cc++) {
+            const float wv = expf(wts[tid * ws + cc] - M);
+            wts[tid * ws + cc] = wv;
+            l += wv * lsv[tid * ws + cc];
+        }
+        inv_l[tid] = 1.0f / l;
+    }
+    __syncthreads();
+    if (qact) {
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int c0 = cp; c0 < nch; c0 += cph * kCU) {
+            if (c0 != cp) { // chunks past the first batch (long sequences)
+#pragma unroll
+                for (int u = 0; u < kCU; u++) {
+                    const int cc = c0 + u * cph;
+                    if (cc < nch)
+                        v[u] = *(const float4 *)(rj + (size_t)cc * (hd + 4));
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kCU; u++) {
+                const int cc = c0 + u * cph;
+                if (cc < nch) {
+                    const float wv = wts[j * ws + cc];
+                    o.x += wv * v[u].x;
+                    o.y += wv * v[u].y;
+                    o.z += wv * v[u].z;
+                    o.w += wv * v[u].w;
+                }
+            }
+        }
+        *(float4 *)(osum + (size_t)cp * G * hd + j * hd + d) = o;
+    }
+    __syncthreads();
+    for (int i = tid; i < G * hd; i += kCombThreads) {
         float o = 0.f;
-        for (int c = 0; c < nch; c++)
-            o += rec[(size_t)c * (hd + 4) + 4 + d] * expf(rec[(size_t)c * (hd + 4)] - M);
-        out[d] = o * inv;
-        if (tap)
-            tap[d] = o * inv;
+        for (int p = 0; p < cph; p++)
+            o += osum[(size_t)p * G * hd + i];
+        const size_t oi = (size_t)b * a.Hq_s * hd + (size_t)g * G * hd + i;
+        a.att[oi] = o * inv_l[i / hd];
+        if (a.tap_att)
+            a.tap_att[oi] = o * inv_l[i / hd];
     }
 }
 
-static size_t attn_smem(int G, int GM, int hd)
+static size_t combine_smem_bytes(int G, int hd, int n_chunks)
 {
-    const int nph = 256 / (hd / 4);
-    return sizeof(float) * ((size_t)G * hd + (size_t)G * kChunk + 2 * hd + 4 * GM +
-                            (size_t)nph * G * hd);
+    const int cph = kCombThreads / (G * (hd / 4));
+    return (((size_t)2 * G * n_chunks + 8 + 3) / 4 * 4 + (size_t)cph * G * hd) * sizeof(float);
 }
 
 template <bool KBF16>
@@ -274,7 +407,8 @@ static hipError_t launch_attn_t(const AttnArgs &a, int B, hipStream_t st)
 {
     const dim3 grid(a.n_chunks, a.Hkv_s, B), block(256);
 #define TPS_ATTN(GM)                                                                          \
-    hipLaunchKernelGGL((k_attn<KBF16, GM>), grid, block, attn_smem(a.G, GM, a.hd), st, a)
+    hipLaunchKernelGGL((k_attn<KBF16, GM>), grid, block,                                       \
+                       attn_smem_bytes(a.G, GM, a.hd, KBF16, a.n_chunks), st, a)
     if (a.G <= 1)
         TPS_ATTN(1);
     else if (a.G <= 2)
@@ -287,17 +421,23 @@ static hipError_t launch_attn_t(const AttnArgs &a, int B, hipStream_t st)
     return hipGetLastError();
 }
 
-// Host-checked preconditions: 1 <= G <= 8, hd % 16 == 0, hd <= 256,
-// n_chunks = ceil(max_ctx / 64), chunk == 64.
+// Host-checked preconditions: 1 <= G <= 8, hd % 16 == 0, hd <= 128,
+// n_chunks = ceil(max_ctx / 64), attn_lds_bytes(...) <= 64 KiB.
 hipError_t launch_attn(const AttnArgs &a, int kv_bf16, int B, hipStream_t st)
 {
-    return kv_bf16 ? launch_attn_t<true>(a, B, st) : launch_attn_t<false>(a, B, st);
+    const hipError_t e = kv_bf16 ? launch_attn_t<true>(a, B, st) : launch_attn_t<false>(a, B, st);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_combine, dim3(a.Hkv_s, B), dim3(kCombThreads),
+                       combine_smem_bytes(a.G, a.hd, a.n_chunks), st, a);
+    return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineArgs &a, int B, hipStream_t st)
+size_t attn_lds_bytes(int G, int hd, int kv_bf16, int n_chunks)
 {
-    hipLaunchKernelGGL(k_combine, dim3(a.Hq_s, B), dim3(a.hd < 256 ? 128 : 256), 0, st, a);
-    return hipGetLastError();
+    const int GM = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+    const size_t a = attn_smem_bytes(G, GM, hd, kv_bf16, n_chunks), c = combine_smem_bytes(G, hd, n_chunks);
+    return a > c ? a : c;
 }
 
 } // namespace tps

@@ -1,67 +1,264 @@
 // k_gemv.hip -- weight-streaming matrix-vector products of the shard step
-// (small batch, B <= 16): y[b][n] = sum_k W[n][k] x[b][k].
+// (decode batch B <= 16): y[b][n] = sum_k W[n][k] x[b][k].
 //
 // Pages: aiterms.tw "Tensor Parallelism", 核心概念 items 1-2 (a column-split
 // shard owns whole output rows of Wq/Wk/Wv/W1/W3; a row-split shard owns a
 // column block of Wo/W2 and produces a full-size partial) and 運作原理 (the
 // FFN: column-split Linear1, elementwise activation, row-split Linear2);
 // distributed-llama issue "[Feature Suggest] Tensor Parallellism for
-// Accelerating LLM", buildLlama2Arch tasks llamaQkv, llamaAttOutput, llamaFfn
-// ("Compute SwiGLU activation"), llamaFfn2.
+// Accelerating LLM", buildLlama2Arch tasks llamaRmsAttNorm / llamaRmfFfnNorm
+// (fused here as the prologue of the projection that consumes the normalised
+// row), llamaQuantizeRmsAtt / llamaQuantizeRmfFfn (int8 round trip of that
+// row), llamaQkv, llamaAttOutput, llamaFfn ("Compute SwiGLU activation"),
+// llamaFfn2.
 //
-// Design (HBM-bound; one weight byte is used B times):
-//  - one wave per group of RPW consecutive rows; the 64 lanes stride the row
-//    in 16-byte vectors, so one wave instruction reads 1 KiB of contiguous
-//    weights (nontemporal: every weight is read once per step);
-//  - U chunk-iterations of loads are issued before any arithmetic, keeping
-//    U*RPW*1 KiB in flight per wave;
-//  - the activation rows x[b] (fp32, a few KiB, L1/L2 resident) are read
-//    with 16-byte loads matching the weight chunk;
-//  - fp32 accumulation, then a 64-lane butterfly per output;
+// Design (HBM-bound: every weight byte is read once and used B times):
+//  - one wave per RPW consecutive rows; the 64 lanes stride a row in 16-byte
+//    vectors, so one wave instruction reads 1 KiB of contiguous weights
+//    (nontemporal: read once per step);
+//  - all of a wave's weight vectors for up to KC x 1 KiB of each row are
+//    issued before anything waits on them;
+//  - the activation rows are staged once per workgroup in LDS (fp32) while
+//    the weights are in flight; with the fused RMSNorm every workgroup
+//    recomputes the row's sum of squares from L2 (B*K*4 bytes), which is
+//    cheaper than a separate launch;
+//  - fp32 accumulation, one 64-lane butterfly per output;
 //  - SwiGLU epilogue: the packed up-projection interleaves W1 row f and W3
-//    row f, so a wave with RPW = 2 holds both and writes silu(g) * u.
+//    row f, so a wave with RPW = 2 holds both and writes silu(g) * u;
 #include "common.h"
 
 namespace tps {
 
 template <bool BF16>
-__device__ __forceinline__ void load_x(const float *xrow, int c, float (&xv)[BF16 ? 8 : 4])
-{
-    const float4 *p = (const float4 *)xrow + c * (BF16 ? 2 : 1);
-    const float4 a = p[0];
-    xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
-    if constexpr (BF16) {
-        const float4 b = p[1];
-        xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
-    }
-}
-
-template <bool BF16>
-__device__ __forceinline__ float dot16(const u32x4 &w, const float (&xv)[BF16 ? 8 : 4], float acc)
+__device__ __forceinline__ float dot16(const u32x4 &w, const float4 &x0, const float4 &x1, float acc)
 {
     if constexpr (BF16) {
-        acc += bf16_lo(w.x) * xv[0];
-        acc += bf16_hi(w.x) * xv[1];
-        acc += bf16_lo(w.y) * xv[2];
-        acc += bf16_hi(w.y) * xv[3];
-        acc += bf16_lo(w.z) * xv[4];
-        acc += bf16_hi(w.z) * xv[5];
-        acc += bf16_lo(w.w) * xv[6];
-        acc += bf16_hi(w.w) * xv[7];
+        acc += bf16_lo(w.x) * x0.x;
+        acc += bf16_hi(w.x) * x0.y;
+        acc += bf16_lo(w.y) * x0.z;
+        acc += bf16_hi(w.y) * x0.w;
+        acc += bf16_lo(w.z) * x1.x;
+        acc += bf16_hi(w.z) * x1.y;
+        acc += bf16_lo(w.w) * x1.z;
+        acc += bf16_hi(w.w) * x1.w;
     } else {
-        acc += __uint_as_float(w.x) * xv[0];
-        acc += __uint_as_float(w.y) * xv[1];
-        acc += __uint_as_float(w.z) * xv[2];
-        acc += __uint_as_float(w.w) * xv[3];
+        acc += __uint_as_float(w.x) * x0.x;
+        acc += __uint_as_float(w.y) * x0.y;
+        acc += __uint_as_float(w.z) * x0.z;
+        acc += __uint_as_float(w.w) * x0.w;
     }
     return acc;
 }
 
+// sum over the 256 threads of a block, in a fixed order
+__device__ __forceinline__ float block_sum(float v, float *red4)
+{
+    v = group_sum<64>(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red4[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return (red4[0] + red4[1]) + (red4[2] + red4[3]);
+}
+
+// Staging of the activation rows x[b][0..K) (b < B) into LDS as fp32; with
+// a.g set, as the normalised row g * x * r (r = 1/sqrt(mean x^2 + eps)),
+// optionally through the int8 round trip (blocks of 32 = 8 consecutive
+// float4 = 8 lanes). Row 0 and the gains are loaded by stage_x_issue BEFORE
+// the weight loads are issued, so they return first (vector loads return in
+// order) and the norm is computed while the weights are still in flight.
+constexpr int kXV = 4; // float4 of a row per thread (K <= 4096)
+
+struct XRegs {
+    float4 x[kXV], g[kXV];
+};
+
+__device__ __forceinline__ void stage_x_issue(const GemvArgs &a, XRegs &r)
+{
+    const int n4 = a.K / 4;
+    const float4 *src = (const float4 *)a.x;
+#pragma unroll
+    for (int i = 0; i < kXV; i++) {
+        const int e = threadIdx.x + 256 * i;
+        if (e < n4) {
+            r.x[i] = src[e];
+            if (a.g)
+                r.g[i] = ((const float4 *)a.g)[e];
+        }
+    }
+}
+
+__device__ void stage_x_finish(const GemvArgs &a, XRegs &r, float *xs, float *red4)
+{
+    const int n4 = a.K / 4;
+    for (int b = 0; b < a.B; b++) {
+        float4 *dst = (float4 *)(xs + (size_t)b * a.K);
+        if (b > 0) {
+            const float4 *src = (const float4 *)(a.x + (size_t)b * a.ldx);
+#pragma unroll
+            for (int i = 0; i < kXV; i++) {
+                const int e = threadIdx.x + 256 * i;
+                if (e < n4)
+                    r.x[i] = src[e];
+            }
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < kXV; i++) {
+            const int e = threadIdx.x + 256 * i;
+            if (e < n4) {
+                const float4 v = r.x[i];
+                ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+            }
+        }
+        if (!a.g) {
+#pragma unroll
+            for (int i = 0; i < kXV; i++) {
+                const int e = threadIdx.x + 256 * i;
+                if (e < n4)
+                    dst[e] = r.x[i];
+            }
+            continue;
+        }
+        ss = block_sum(ss, red4);
+        const float rr = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+        float4 *tap = (a.xn_tap && blockIdx.x == 0) ? (float4 *)(a.xn_tap + (size_t)b * a.K) : nullptr;
+#pragma unroll
+        for (int i = 0; i < kXV; i++) {
+            const int e = threadIdx.x + 256 * i;
+            if (256 * i >= n4)
+                break; // uniform: no lane of this pass holds an element
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e < n4) {
+                const float4 x = r.x[i], g = r.g[i];
+                v = make_float4(g.x * x.x * rr, g.y * x.y * rr, g.z * x.z * rr, g.w * x.w * rr);
+            }
+            if (a.qin) { // every lane takes part; lanes past the row hold 0
+                const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+                const float s = q8_scale(group_max<8>(m));
+                v.x = q8_dequant(q8_code(v.x, s), s);
+                v.y = q8_dequant(q8_code(v.y, s), s);
+                v.z = q8_dequant(q8_code(v.z, s), s);
+                v.w = q8_dequant(q8_code(v.w, s), s);
+            }
+            if (e < n4) {
+                dst[e] = v;
+                if (tap)
+                    tap[e] = v;
+            }
+        }
+    }
+}
+
 template <bool BF16, int NB, int RPW, int EPI>
-__global__ __launch_bounds__(256) void k_gemv(GemvArgs a)
+__global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
 {
     constexpr int V = BF16 ? 8 : 4; // elements per 16-byte chunk
-    constexpr int U = 4;            // chunk iterations loaded ahead
+    constexpr int KC = 8;           // chunk iterations per lane kept in flight
+    extern __shared__ float xs[];   // [B][K]
+    __shared__ float red4[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int row0 = (blockIdx.x * 4 + wv) * RPW;
+    const bool active = row0 < a.N;
+    const int nchunk = a.K / V;
+    const u32x4 *Wr[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; r++)
+        Wr[r] = (const u32x4 *)((const char *)a.W + (size_t)(active ? row0 + r : 0) * a.K * (BF16 ? 2 : 4));
+
+    XRegs xr;
+    stage_x_issue(a, xr);
+    u32x4 w[RPW][KC];
+#pragma unroll
+    for (int i = 0; i < KC; i++) {
+        const int c = lane + 64 * i;
+#pragma unroll
+        for (int r = 0; r < RPW; r++)
+            if (active && c < nchunk)
+                w[r][i] = __builtin_nontemporal_load(Wr[r] + c);
+    }
+    stage_x_finish(a, xr, xs, red4);
+    __syncthreads();
+
+    float acc[RPW][NB];
+#pragma unroll
+    for (int r = 0; r < RPW; r++)
+#pragma unroll
+        for (int b = 0; b < NB; b++)
+            acc[r][b] = 0.f;
+    for (int kb = 0; kb < nchunk; kb += 64 * KC) {
+        if (kb > 0) {
+#pragma unroll
+            for (int i = 0; i < KC; i++) {
+                const int c = kb + lane + 64 * i;
+#pragma unroll
+                for (int r = 0; r < RPW; r++)
+                    if (active && c < nchunk)
+                        w[r][i] = __builtin_nontemporal_load(Wr[r] + c);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < KC; i++) {
+            const int c = kb + lane + 64 * i;
+            if (active && c < nchunk) {
+#pragma unroll
+                for (int b = 0; b < NB; b++) {
+                    if (b < a.B) {
+                        const float4 *xp = (const float4 *)(xs + (size_t)b * a.K) + c * (V / 4);
+                        const float4 x0 = xp[0];
+                        const float4 x1 = BF16 ? xp[1] : x0;
+#pragma unroll
+                        for (int r = 0; r < RPW; r++)
+                            acc[r][b] = dot16<BF16>(w[r][i], x0, x1, acc[r][b]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; r++)
+#pragma unroll
+        for (int b = 0; b < NB; b++)
+            acc[r][b] = group_sum<64>(acc[r][b]);
+
+    if (active) {
+        if constexpr (EPI == EPI_SWIGLU) {
+            static_assert(RPW == 2, "SwiGLU pairs rows (W1_f, W3_f)");
+            const int f = row0 / 2;
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                if (lane == b && b < a.B) {
+                    const float v = silu(acc[0][b]) * acc[1][b];
+                    a.y[(size_t)b * a.ldy + f] = v;
+                    if (a.tap)
+                        a.tap[(size_t)b * a.ldy + f] = v;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < RPW; r++)
+#pragma unroll
+                for (int b = 0; b < NB; b++) {
+                    if (lane == r * NB + b && b < a.B) {
+                        a.y[(size_t)b * a.ldy + row0 + r] = acc[r][b];
+                        if (a.tap)
+                            a.tap[(size_t)b * a.ldy + row0 + r] = acc[r][b];
+                    }
+                }
+        }
+    }
+
+}
+
+// ---------------------------------------------------------------- general-batch path
+// Activations read from global memory (L1/L2 resident), no fused prologue /
+// epilogue: used when the batch's activation rows do not fit in LDS.
+
+template <bool BF16, int NB, int RPW, int EPI>
+__global__ __launch_bounds__(256) void k_gemv_gx(GemvArgs a)
+{
+    constexpr int V = BF16 ? 8 : 4;
+    constexpr int U = 4;
     const int lane = threadIdx.x & 63;
     const int row0 = ((blockIdx.x * 256 + threadIdx.x) >> 6) * RPW;
     if (row0 >= a.N)
@@ -71,61 +268,44 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a)
 #pragma unroll
     for (int r = 0; r < RPW; r++)
         Wr[r] = (const u32x4 *)((const char *)a.W + (size_t)(row0 + r) * a.K * (BF16 ? 2 : 4));
-
     float acc[RPW][NB];
 #pragma unroll
     for (int r = 0; r < RPW; r++)
 #pragma unroll
         for (int b = 0; b < NB; b++)
             acc[r][b] = 0.f;
-
-    int c = lane;
-    for (; c + 64 * (U - 1) < nchunk; c += 64 * U) {
+    for (int c0 = lane; c0 < nchunk; c0 += 64 * U) {
         u32x4 w[U][RPW];
 #pragma unroll
         for (int u = 0; u < U; u++)
 #pragma unroll
             for (int r = 0; r < RPW; r++)
-                w[u][r] = __builtin_nontemporal_load(Wr[r] + c + 64 * u);
+                if (c0 + 64 * u < nchunk)
+                    w[u][r] = __builtin_nontemporal_load(Wr[r] + c0 + 64 * u);
 #pragma unroll
         for (int u = 0; u < U; u++) {
+            const int c = c0 + 64 * u;
+            if (c < nchunk) {
 #pragma unroll
-            for (int b = 0; b < NB; b++) {
-                if (b < a.B) {
-                    float xv[V];
-                    load_x<BF16>(a.x + (size_t)b * a.ldx, c + 64 * u, xv);
+                for (int b = 0; b < NB; b++) {
+                    if (b < a.B) {
+                        const float4 *xp = (const float4 *)(a.x + (size_t)b * a.ldx) + c * (V / 4);
+                        const float4 x0 = xp[0];
+                        const float4 x1 = BF16 ? xp[1] : x0;
 #pragma unroll
-                    for (int r = 0; r < RPW; r++)
-                        acc[r][b] = dot16<BF16>(w[u][r], xv, acc[r][b]);
+                        for (int r = 0; r < RPW; r++)
+                            acc[r][b] = dot16<BF16>(w[u][r], x0, x1, acc[r][b]);
+                    }
                 }
             }
         }
     }
-    for (; c < nchunk; c += 64) {
-        u32x4 w[RPW];
-#pragma unroll
-        for (int r = 0; r < RPW; r++)
-            w[r] = __builtin_nontemporal_load(Wr[r] + c);
-#pragma unroll
-        for (int b = 0; b < NB; b++) {
-            if (b < a.B) {
-                float xv[V];
-                load_x<BF16>(a.x + (size_t)b * a.ldx, c, xv);
-#pragma unroll
-                for (int r = 0; r < RPW; r++)
-                    acc[r][b] = dot16<BF16>(w[r], xv, acc[r][b]);
-            }
-        }
-    }
-
 #pragma unroll
     for (int r = 0; r < RPW; r++)
 #pragma unroll
         for (int b = 0; b < NB; b++)
             acc[r][b] = group_sum<64>(acc[r][b]);
-
     if constexpr (EPI == EPI_SWIGLU) {
-        static_assert(RPW == 2, "SwiGLU pairs rows (W1_f, W3_f)");
         const int f = row0 / 2;
 #pragma unroll
         for (int b = 0; b < NB; b++) {
@@ -150,35 +330,58 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a)
     }
 }
 
+// ---------------------------------------------------------------- launchers
+
+constexpr int kRPW = 2;
+
+size_t gemv_lds_bytes(int B, int K) { return (size_t)B * K * sizeof(float); }
+
+bool gemv_fused_ok(int B, int K) { return B <= 4 && K <= 4 * 256 * kXV && gemv_lds_bytes(B, K) <= 64 * 1024; }
+
 template <bool BF16, int NB>
-static hipError_t launch_nb(const GemvArgs &a, int epi, hipStream_t st)
+static hipError_t launch_lds(const GemvArgs &a, int epi, hipStream_t st)
 {
-    constexpr int RPW = 2;
-    const int waves = (a.N + RPW - 1) / RPW;
+    const dim3 grid((a.N + 4 * kRPW - 1) / (4 * kRPW)), block(256);
+    const size_t sm = gemv_lds_bytes(a.B, a.K);
+    if (epi == EPI_SWIGLU)
+        hipLaunchKernelGGL((k_gemv_lds<BF16, NB, kRPW, EPI_SWIGLU>), grid, block, sm, st, a);
+    else
+        hipLaunchKernelGGL((k_gemv_lds<BF16, NB, kRPW, EPI_STORE>), grid, block, sm, st, a);
+    return hipGetLastError();
+}
+
+template <bool BF16, int NB>
+static hipError_t launch_gx(const GemvArgs &a, int epi, hipStream_t st)
+{
+    const int waves = (a.N + kRPW - 1) / kRPW;
     const dim3 grid((waves + 3) / 4), block(256);
     if (epi == EPI_SWIGLU)
-        hipLaunchKernelGGL((k_gemv<BF16, NB, RPW, EPI_SWIGLU>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemv_gx<BF16, NB, kRPW, EPI_SWIGLU>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((k_gemv<BF16, NB, RPW, EPI_STORE>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemv_gx<BF16, NB, kRPW, EPI_STORE>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
 template <bool BF16>
 static hipError_t launch_t(const GemvArgs &a, int epi, hipStream_t st)
 {
-    if (a.B <= 1)
-        return launch_nb<BF16, 1>(a, epi, st);
-    if (a.B <= 2)
-        return launch_nb<BF16, 2>(a, epi, st);
-    if (a.B <= 4)
-        return launch_nb<BF16, 4>(a, epi, st);
+    if (gemv_fused_ok(a.B, a.K)) {
+        if (a.B <= 1)
+            return launch_lds<BF16, 1>(a, epi, st);
+        if (a.B <= 2)
+            return launch_lds<BF16, 2>(a, epi, st);
+        return launch_lds<BF16, 4>(a, epi, st);
+    }
+    if (a.g)
+        return hipErrorInvalidValue; // the fused norm needs the LDS path
     if (a.B <= 8)
-        return launch_nb<BF16, 8>(a, epi, st);
-    return launch_nb<BF16, 16>(a, epi, st);
+        return launch_gx<BF16, 8>(a, epi, st);
+    return launch_gx<BF16, 16>(a, epi, st);
 }
 
-// Host-checked preconditions: N even, K a multiple of the 16-byte vector,
-// rows 16-byte aligned, 1 <= B <= 16.
+// Host-checked preconditions: N a multiple of 8, K a
+// multiple of the 16-byte vector (of 32 with qin), rows 16-byte aligned,
+// 1 <= B <= 16.
 hipError_t launch_gemv(const GemvArgs &a, int w_bf16, int epi, hipStream_t st)
 {
     return w_bf16 ? launch_t<true>(a, epi, st) : launch_t<false>(a, epi, st);

@@ -72,29 +72,52 @@ __global__ __launch_bounds__(256) void k_wire(WireArgs a)
     }
 }
 
-// out = residual + d_0 + d_1 + ... (array order), 4 elements per thread.
+// out = residual + d_0 + d_1 + ... (array order), 4 elements per thread;
+// the wires are read 8 at a time so their loads are in flight together.
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a)
 {
+    constexpr int U = 8;
     const size_t n = (size_t)a.B * a.D;
     const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= n)
         return;
     float4 acc = *(const float4 *)(a.residual + i);
-    for (int s = 0; s < a.n_wires; s++) {
-        const char *w = (const char *)a.wires[s];
+    for (int s0 = 0; s0 < a.n_wires; s0 += U) {
         if (a.quant) {
-            const char4 c = *(const char4 *)(w + i);
-            const float sc = ((const float *)(w + a.scales_off))[i / kQBlock];
-            acc.x = acc.x + q8_dequant(c.x, sc);
-            acc.y = acc.y + q8_dequant(c.y, sc);
-            acc.z = acc.z + q8_dequant(c.z, sc);
-            acc.w = acc.w + q8_dequant(c.w, sc);
+            char4 c[U];
+            float sc[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                if (s0 + u < a.n_wires) {
+                    const char *w = (const char *)a.wires[s0 + u];
+                    c[u] = *(const char4 *)(w + i);
+                    sc[u] = ((const float *)(w + a.scales_off))[i / kQBlock];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                if (s0 + u < a.n_wires) {
+                    acc.x = acc.x + q8_dequant(c[u].x, sc[u]);
+                    acc.y = acc.y + q8_dequant(c[u].y, sc[u]);
+                    acc.z = acc.z + q8_dequant(c[u].z, sc[u]);
+                    acc.w = acc.w + q8_dequant(c[u].w, sc[u]);
+                }
+            }
         } else {
-            const float4 f = *(const float4 *)(w + i * 4);
-            acc.x = acc.x + f.x;
-            acc.y = acc.y + f.y;
-            acc.z = acc.z + f.z;
-            acc.w = acc.w + f.w;
+            float4 f[U];
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                if (s0 + u < a.n_wires)
+                    f[u] = *(const float4 *)((const char *)a.wires[s0 + u] + i * 4);
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                if (s0 + u < a.n_wires) {
+                    acc.x = acc.x + f[u].x;
+                    acc.y = acc.y + f[u].y;
+                    acc.z = acc.z + f[u].z;
+                    acc.w = acc.w + f[u].w;
+                }
+            }
         }
     }
     *(float4 *)(a.out + i) = acc;
