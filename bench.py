@@ -218,6 +218,101 @@ def cpu_baseline_llama(w, d, seconds):
                       f"FFN stage, wire, merge) by the single-threaded fp64 C oracle in {el:.1f} s"}
 
 
+def run_ffn2d(args, w):
+    """One step = the block's up-projection + SwiGLU and down-projection for
+    the workload's token count, over R rotating weight copies."""
+    import torch
+    import tensor_tp_shard_amd as tp
+    B, E, F = w.batch, w.e_blk, w.f_blk
+    d = synth.ffn2d_inputs(w)
+    W = {"w1": dev(d["w_gate"]), "w3": dev(d["w_in"]), "w2": dev(d["w_out"])}
+    cfg = tp.make_config(kind=tp.TP_FFN_2D, dim=E, ffn_hidden=F, tp_size=1, tp_rank=0,
+                         max_batch=B, w_dtype=tp.TP_BF16)
+    wbytes = 3 * E * F * 2
+    R = args.copies or max(2, int(np.ceil(3 * 256e6 / wbytes)))
+    copies = []
+    for _ in range(R):
+        sh = tp.Shard(cfg, caches=False)
+        sh.load(W)
+        copies.append(sh)
+    del W
+    x = dev(d["x"])
+    ys = [torch.empty((B, E), dtype=torch.float32, device="cuda") for _ in range(R)]
+    flops = 2.0 * B * E * F * 3
+    up_flops = 2.0 * B * E * 2 * F
+
+    def one_pass():
+        for r, c in enumerate(copies):
+            c.step(tp.TP_STAGE_FFN, x, None, B, ys[r])
+
+    passes = max(1, args.steps // R)
+    wpasses = max(1, args.warmup // R)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        one_pass()
+        graph = None
+        if args.mode == "graph":
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                one_pass()
+        run = graph.replay if graph is not None else one_pass
+        for _ in range(wpasses):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(passes):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        kid = tp.kernel_names().index("ffn2d_up")
+        for c in copies:
+            tp.kernel_timing_arm(c.handle, kid)
+        for _ in range(passes):
+            one_pass()
+        torch.cuda.synchronize()
+        tot, n = 0.0, 0
+        for c in copies:
+            t_, n_ = tp.kernel_timing_read(c.handle)
+            tot += t_
+            n += n_
+            tp.kernel_timing_arm(c.handle, -1)
+    steps = passes * R
+    ms_step = ms / steps
+    k_ms = tot / max(n, 1)
+    ach = up_flops / (k_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(1e3 / ms_step, 2), "unit": "ffn-block-steps/s",
+        "n_gpus": 1, "steps": steps, "warmup": wpasses * R, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": B, "E_block": E, "F_block": F, "layer_copies": R,
+                   "launch": args.mode},
+        "achieved_TFLOPs": round(flops / (ms_step * 1e-3) / 1e12, 1),
+        "mfma_frac": round(flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "roofline": {"kernel": "ffn2d_up", "bound": "mfma", "achieved": round(ach, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": up_flops, "avg_launch_us": round(k_ms * 1e3, 3),
+                     "launches": n},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.ffn2d(d["x"], d["w_gate"], d["w_in"], d["w_out"], row0=rows % B, nrows=1)
+            rows += 1
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(rows / el / B, 6), "unit": "ffn-block-steps/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{rows} token rows of {w.name} by the single-threaded "
+                                         f"fp64 C oracle in {el:.1f} s, scaled to {B} rows"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,7 +333,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w = synth.get(args.workload)
-    res = run_llama(args, w)
+    res = run_ffn2d(args, w) if w.kind == "ffn2d" else run_llama(args, w)
     print(json.dumps(res), flush=True)
 
 

@@ -80,7 +80,7 @@ struct tp_shard {
     // workspace layout (byte offsets)
     uint64_t w_err, w_xn, w_qkv, w_part, w_att, w_a, w_p, ws_bytes;
     int n_chunks;
-    uint64_t kv_bytes, wire_bytes;
+    uint64_t kv_bytes, wire_bytes, part_rows = 0;
     // bound buffers
     char *packed = nullptr, *ws = nullptr;
     void *kc = nullptr, *vc = nullptr;
@@ -103,7 +103,7 @@ int32_t plan(const tp_config &c, tp_shard &s)
         return fail(TP_EINVAL, "unknown quant bits 0x%x", c.quant);
     if (c.quant && c.quant_block != kQBlock)
         return fail(TP_EINVAL, "quant_block must be 32 (got %d)", c.quant_block);
-    if (c.max_batch < 1 || c.dim < 1 || c.ffn_hidden < 1)
+    if (c.max_batch < 1 || c.max_batch > (1 << 20) || c.dim < 1 || c.ffn_hidden < 1)
         return fail(TP_EINVAL, "dim, ffn_hidden and max_batch must be positive");
     s.cfg = c;
     s.D = c.dim;
@@ -115,8 +115,8 @@ int32_t plan(const tp_config &c, tp_shard &s)
             return fail(TP_EINVAL, "TP_FFN_2D takes an already-cut block: tp_size 1, tp_rank 0");
         if (c.quant)
             return fail(TP_EINVAL, "TP_FFN_2D has no int8 exchange");
-        if (c.dim % 64 || c.ffn_hidden % 64)
-            return fail(TP_EINVAL, "TP_FFN_2D needs E and F multiples of 64");
+        if (c.dim % 256 || c.ffn_hidden % 128)
+            return fail(TP_EINVAL, "TP_FFN_2D needs E a multiple of 256 and F of 128");
         s.T = 1;
         s.r = 0;
         s.esz = 2;
@@ -125,7 +125,15 @@ int32_t plan(const tp_config &c, tp_shard &s)
         s.packed_bytes = align_up(s.o_w2 + (uint64_t)s.D * s.F * 2, 256);
         s.w_err = 0;
         s.w_a = 256; // H = silu(X Wg^T) * (X Win^T), bf16 [max_batch][F]
-        s.ws_bytes = align_up(s.w_a + (uint64_t)c.max_batch * s.F * 2, 256);
+        s.w_p = align_up(s.w_a + (uint64_t)c.max_batch * s.F * 2, 256);
+        uint64_t part_rows = 0; // split-K partial rows: the most any batch <= max_batch needs
+        for (int b = 1; b <= c.max_batch; b++) {
+            const int S = ffn2d_splits(b, s.D, s.F);
+            if (S > 1 && (uint64_t)S * b > part_rows)
+                part_rows = (uint64_t)S * b;
+        }
+        s.part_rows = part_rows;
+        s.ws_bytes = align_up(s.w_p + part_rows * s.D * 4, 256);
         s.kv_bytes = 0;
         s.wire_bytes = (uint64_t)c.max_batch * s.D * 4;
         return TP_OK;
@@ -353,13 +361,14 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *w, void *packed, void 
         if (rc)
             return rc;
     } else {
-        // 2D FFN block: gate rows and up rows in groups of 16 ([F/16][2][16][E]),
-        // so one 16-row MFMA tile of each pair holds matching features
+        // 2D FFN block: gate rows and up rows interleaved in groups of 8
+        // ([F/8][2][8][E]), so every 16-row MFMA tile holds 8 features' gate
+        // and up rows
         const size_t E = s->D, F = s->F;
-        err = copy2d(P + s->o_w13, 32 * E * e, w->w1, 16 * E * e, 16 * E * e, F / 16, st);
+        err = copy2d(P + s->o_w13, 16 * E * e, w->w1, 8 * E * e, 8 * E * e, F / 8, st);
         if (!err)
-            err = copy2d(P + s->o_w13 + 16 * E * e, 32 * E * e, w->w3, 16 * E * e, 16 * E * e,
-                         F / 16, st);
+            err = copy2d(P + s->o_w13 + 8 * E * e, 16 * E * e, w->w3, 8 * E * e, 8 * E * e, F / 8,
+                         st);
         if (!err)
             err = hipMemcpyAsync(P + s->o_w2, w->w2, E * F * e, hipMemcpyDeviceToDevice, st);
         if (err)
@@ -405,7 +414,22 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
     if (s->cfg.kind == TP_FFN_2D) {
         if (stage != TP_STAGE_FFN)
             return fail(TP_EINVAL, "TP_FFN_2D has only the FFN stage");
-        return fail(TP_ENOTIMPL, "TP_FFN_2D decode step not built yet");
+        const int S = ffn2d_splits(B, s->D, s->F);
+        if (S > 1 && (uint64_t)S * B > s->part_rows) // cannot happen with plan()'s sizing
+            return fail(TP_EINVAL, "split-K partials of batch %d exceed the workspace", B);
+        Ffn2dArgs fa{(const uint16_t *)x,
+                     (const uint16_t *)(s->packed + s->o_w13),
+                     (const uint16_t *)(s->packed + s->o_w2),
+                     (uint16_t *)(s->ws + s->w_a),
+                     (float *)(s->ws + s->w_p),
+                     (float *)wire_out,
+                     B,
+                     s->D,
+                     s->F};
+        int32_t rc = timed(s, KID_FFN2D_UP, st, "ffn2d up", [&] { return launch_ffn2d(fa, st, 0); });
+        if (rc)
+            return rc;
+        return timed(s, KID_FFN2D_DOWN, st, "ffn2d down", [&] { return launch_ffn2d(fa, st, 1); });
     }
 
     const bool wbf = s->cfg.w_dtype == TP_BF16;

@@ -132,9 +132,10 @@ struct RopeArgs {
 
 struct Ffn2dArgs {
     const uint16_t *x;   // [B][E] bf16
-    const uint16_t *w13; // [F/16][2][16][E] bf16: 16 gate rows, then the 16 matching up rows
+    const uint16_t *w13; // [F/8][2][8][E] bf16: 8 gate rows, then the 8 matching up rows
     const uint16_t *w2;  // [E][F] bf16
     uint16_t *h;         // [B][F] bf16 workspace
+    float *part;         // [splits][B][E] fp32 workspace (split-K partials)
     float *y;            // [B][E]
     int B, E, F;
 };
@@ -152,5 +153,6 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
 hipError_t launch_rope_table(const RopeArgs &a, hipStream_t st);
 hipError_t launch_clear_u32(unsigned *p, int n, hipStream_t st);
 hipError_t launch_ffn2d(const Ffn2dArgs &a, hipStream_t st, int which);
+int ffn2d_splits(int B, int E, int F);
 
 } // namespace tps

@@ -1,0 +1,92 @@
+"""Parity of the MFMA FFN block (2D weight-stationary PaLM shape) with the
+fp64 oracle. The product stores H = silu(X Wg^T) * (X Win^T) in bf16 between
+the two GEMMs; the contract tolerance for bf16 paths is relative L2 2e-2 and
+these tests hold 5e-3 (bf16 rounding of H alone gives about 1e-3)."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import tensor_tp_shard_amd as tp
+from conftest import rel_l2
+
+pytestmark = pytest.mark.gpu
+TOL = 5e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X GPU")
+    tp.lib()
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def run_ffn2d(d, max_batch, batches):
+    import torch
+    B0, E = d["x"].shape
+    F = d["w_gate"].shape[0]
+    cfg = tp.make_config(kind=tp.TP_FFN_2D, dim=E, ffn_hidden=F, tp_size=1, tp_rank=0,
+                         max_batch=max_batch, w_dtype=tp.TP_BF16)
+    sh = tp.Shard(cfg, caches=False)
+    W = {"w1": dev(d["w_gate"]), "w3": dev(d["w_in"]), "w2": dev(d["w_out"])}
+    sh.load(W)
+    x = dev(d["x"])
+    outs = []
+    for B in batches:
+        y = torch.full((B, E), float("nan"), dtype=torch.float32, device="cuda")
+        sh.step(tp.TP_STAGE_FFN, x, None, B, y)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+    return outs
+
+
+def test_ffn2d_small_ragged():
+    """E = 256, F = 384, 200 rows (one full and one partial 128-row tile), and
+    a 5-row call on the same handle."""
+    w = synth.Ffn2D("ffn2d_small", e_blk=256, f_blk=384, batch=200, seed=91)
+    d = synth.ffn2d_inputs(w)
+    say("ffn2d small ragged")
+    y200, y5 = run_ffn2d(d, 200, [200, 5])
+    ref = oracle.ffn2d(d["x"], d["w_gate"], d["w_in"], d["w_out"])
+    assert np.all(np.isfinite(y200))
+    e = rel_l2(y200, ref)
+    say(f"ffn2d small rel-L2 {e:.3e}")
+    assert e <= TOL
+    assert rel_l2(y5, ref[:5]) <= TOL
+
+
+def _sampled_rows_check(w, rows):
+    d = synth.ffn2d_inputs(w)
+    say(f"{w.name} B={w.batch}")
+    (y,) = run_ffn2d(d, w.batch, [w.batch])
+    assert np.all(np.isfinite(y))
+    for r in rows:
+        ref = oracle.ffn2d(d["x"], d["w_gate"], d["w_in"], d["w_out"], row0=r, nrows=1)
+        e = rel_l2(y[r], ref[0])
+        assert e <= TOL, f"row {r} rel-L2 {e:.3e}"
+    return y
+
+
+def test_palm_ffn2d_decode_512_sampled_rows():
+    y = _sampled_rows_check(synth.PALM_DEC, [0, 1, 127, 128, 300, 511])
+    # deterministic: a second run is bitwise equal
+    d = synth.ffn2d_inputs(synth.PALM_DEC)
+    (y2,) = run_ffn2d(d, 512, [512])
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+def test_palm_ffn2d_prefill_8192_sampled_rows():
+    _sampled_rows_check(synth.PALM_PRE, [0, 4095, 8191])
