@@ -78,8 +78,9 @@ struct tp_shard {
     // packed layout (byte offsets)
     uint64_t o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn, o_rope, packed_bytes;
     // workspace layout (byte offsets)
-    uint64_t w_err, w_xn, w_qkv, w_part, w_att, w_a, w_p, ws_bytes;
+    uint64_t w_err, w_xfx, w_xfatt, w_xfa, w_xn, w_qkv, w_part, w_att, w_a, w_p, ws_bytes;
     int n_chunks;
+    bool mfma_ok = false; // the batch 5..16 MFMA path applies to this shape
     uint64_t kv_bytes, wire_bytes, part_rows = 0;
     // bound buffers
     char *packed = nullptr, *ws = nullptr;
@@ -149,8 +150,8 @@ int32_t plan(const tp_config &c, tp_shard &s)
         return fail(TP_EINVAL, "n_heads %% n_kv_heads != 0");
     if (c.n_heads % T || c.n_kv_heads % T || c.ffn_hidden % T)
         return fail(TP_EINVAL, "tp_size must divide n_heads, n_kv_heads and ffn_hidden");
-    if (c.head_dim % 16 || c.head_dim > 128)
-        return fail(TP_EINVAL, "head_dim must be a multiple of 16, at most 128");
+    if (!attn_hd_supported(c.head_dim))
+        return fail(TP_EINVAL, "head_dim must be 16, 32, 48, 64 or 128");
     if (c.n_heads / c.n_kv_heads > 8)
         return fail(TP_EINVAL, "at most 8 q heads per kv head");
     if (c.max_batch > 16)
@@ -188,8 +189,17 @@ int32_t plan(const tp_config &c, tp_shard &s)
     s.o_gffn = o; o = align_up(o + D * 4, 256);
     s.o_rope = o; o = align_up(o + (uint64_t)c.max_ctx * (s.hd / 2) * 8, 256);
     s.packed_bytes = o;
+    s.mfma_ok = c.w_dtype == TP_BF16 && c.max_batch > 4 && gemv_mfma_ok(16, s.n_qkv, s.D, 1) &&
+                gemv_mfma_ok(16, s.D, s.Hq_s * s.hd, 1) && gemv_mfma_ok(16, 2 * s.Fs, s.D, 1) &&
+                gemv_mfma_ok(16, s.D, s.Fs, 1);
     o = 0;
     s.w_err = o;  o = 256;
+    s.w_xfx = s.w_xfatt = s.w_xfa = 0;
+    if (s.mfma_ok) { // activations in the MFMA fragment layout
+        s.w_xfx = o;   o = align_up(o + xf_elems(s.D) * 2, 256);
+        s.w_xfatt = o; o = align_up(o + xf_elems(s.Hq_s * s.hd) * 2, 256);
+        s.w_xfa = o;   o = align_up(o + xf_elems(s.Fs) * 2, 256);
+    }
     s.w_xn = o;   o = align_up(o + B * D * 4, 256);
     s.w_qkv = o;  o = align_up(o + B * s.n_qkv * 4, 256);
     s.w_part = o; o = align_up(o + B * s.Hq_s * (uint64_t)s.n_chunks * (s.hd + 4) * 4, 256);
@@ -441,10 +451,15 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
     float *scales = qpart ? (float *)((char *)wire_out + tp_wire_scales_offset(&s->cfg, B)) : nullptr;
     int32_t rc;
 
-    // RMSNorm: fused into the projection's prologue when the batch's rows fit
-    // in LDS, else a kernel of its own writing xn
-    const bool fuse_norm = gemv_fused_ok(B, s->D);
+    // batch 5..16: RMSNorm kernel writing xn and its MFMA fragments, MFMA projections
+    const bool mfma = s->mfma_ok && B > 4;
+    // RMSNorm: otherwise fused into the projection's prologue when the batch's
+    // rows fit in LDS, else a kernel of its own writing xn
+    const bool fuse_norm = !mfma && gemv_fused_ok(B, s->D);
     const float *in = (const float *)x;
+    uint16_t *xfx = mfma ? (uint16_t *)(s->ws + s->w_xfx) : nullptr;
+    uint16_t *xfatt = mfma ? (uint16_t *)(s->ws + s->w_xfatt) : nullptr;
+    uint16_t *xfa = mfma ? (uint16_t *)(s->ws + s->w_xfa) : nullptr;
     GemvArgs up{};
     up.x = in;
     up.ldx = s->D;
@@ -457,7 +472,7 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
         up.xn_tap = tp.xn;
     } else {
         float *xn = (float *)(s->ws + s->w_xn);
-        NormArgs na{in, gain, xn, tp.xn, B, s->D, s->cfg.norm_eps, qin ? 1 : 0};
+        NormArgs na{in, gain, xn, tp.xn, xfx, B, s->D, s->cfg.norm_eps, qin ? 1 : 0};
         rc = timed(s, KID_RMSNORM, st, "rmsnorm", [&] { return launch_rmsnorm(na, st); });
         if (rc)
             return rc;
@@ -471,6 +486,12 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
     down.ldy = s->D;
     down.B = B;
     const int Kd = stage == TP_STAGE_ATTN ? s->Hq_s * s->hd : s->Fs;
+    auto run_gemv = [&](const GemvArgs &g, const uint16_t *xf, uint16_t *yf, int epi) {
+        if (!mfma)
+            return launch_gemv(g, wbf, epi, st);
+        MfmaGemvArgs m{(const uint16_t *)g.W, xf, g.y, g.tap, yf, g.N, g.K, g.B, g.ldy, 1};
+        return launch_gemv_mfma(m, epi, st);
+    };
 
     if (stage == TP_STAGE_ATTN) {
         if (!lens)
@@ -480,7 +501,7 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
         up.y = qkv;
         up.N = s->n_qkv;
         up.ldy = s->n_qkv;
-        rc = timed(s, KID_GEMV_QKV, st, "gemv qkv", [&] { return launch_gemv(up, wbf, EPI_STORE, st); });
+        rc = timed(s, KID_GEMV_QKV, st, "gemv qkv", [&] { return run_gemv(up, xfx, nullptr, EPI_STORE); });
         if (rc)
             return rc;
         float *att = (float *)(s->ws + s->w_att);
@@ -497,6 +518,7 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
         aa.tap_k = tp.k;
         aa.tap_v = tp.v;
         aa.tap_att = tp.att;
+        aa.att_xf = xfatt;
         aa.ld_qkv = s->n_qkv;
         aa.max_ctx = s->cfg.max_ctx;
         aa.Hq_s = s->Hq_s;
@@ -513,7 +535,7 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
         down.x = att;
         down.K = Kd;
         down.ldx = Kd;
-        rc = timed(s, KID_GEMV_WO, st, "gemv wo", [&] { return launch_gemv(down, wbf, EPI_STORE, st); });
+        rc = timed(s, KID_GEMV_WO, st, "gemv wo", [&] { return run_gemv(down, xfatt, nullptr, EPI_STORE); });
         if (rc)
             return rc;
     } else {
@@ -523,14 +545,14 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
         up.tap = tp.a;
         up.N = 2 * s->Fs;
         up.ldy = s->Fs;
-        rc = timed(s, KID_GEMV_W13, st, "gemv w13", [&] { return launch_gemv(up, wbf, EPI_SWIGLU, st); });
+        rc = timed(s, KID_GEMV_W13, st, "gemv w13", [&] { return run_gemv(up, xfx, xfa, EPI_SWIGLU); });
         if (rc)
             return rc;
         down.W = s->packed + s->o_w2;
         down.x = a;
         down.K = Kd;
         down.ldx = Kd;
-        rc = timed(s, KID_GEMV_W2, st, "gemv w2", [&] { return launch_gemv(down, wbf, EPI_STORE, st); });
+        rc = timed(s, KID_GEMV_W2, st, "gemv w2", [&] { return run_gemv(down, xfa, nullptr, EPI_STORE); });
         if (rc)
             return rc;
     }

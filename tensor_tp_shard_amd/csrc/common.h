@@ -75,9 +75,41 @@ struct NormArgs {
     const float *g;      // [D]
     float *xn;           // [B][D]
     float *tap;          // optional [B][D]
+    uint16_t *xf;        // optional: xn in the MFMA fragment layout (hi/lo bf16)
     int B, D;
     float eps;
     int quant;           // int8 round trip of the normalised row
+};
+
+// ---------------------------------------------------------------- MFMA fragment layout
+// Activations of a batch of <= 16 rows, K a multiple of 128, as the B operand
+// of v_mfma_f32_16x16x32_bf16: the fp32 value v is split into hi = bf16(v)
+// and lo = bf16(v - hi) (hi + lo carries ~16 mantissa bits). Element (b, k)
+// of part hl sits at [k/128][hl][s][q][b][e] with k % 128 = 32q + 8s + e, so
+// lane (q, b) of a wave reads its 8 values for step s as 16 contiguous bytes
+// and a wave reads 1 KiB contiguous per step.
+__host__ __device__ inline size_t xf_index(int b, int k, int hl)
+{
+    const int j = k >> 7, r = k & 127, q = r >> 5, s = (r >> 3) & 3, e = k & 7;
+    return ((((((size_t)j * 2 + hl) * 4 + s) * 4 + q) * 16 + b) << 3) + e;
+}
+__host__ __device__ inline size_t xf_elems(int K) { return (size_t)K * 32; } // 16 rows x K x {hi, lo}
+
+__device__ __forceinline__ void xf_store(uint16_t *xf, int b, int k, float v)
+{
+    const uint16_t hi = f32_to_bf16(v);
+    const uint16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+    xf[xf_index(b, k, 0)] = hi;
+    xf[xf_index(b, k, 1)] = lo;
+}
+
+struct MfmaGemvArgs {
+    const uint16_t *W;   // bf16 [N][K], N % 16 == 0, K % 128 == 0
+    const uint16_t *xf;  // activations in the fragment layout
+    float *y;            // EPI_STORE: y[b][n] (ld ldy); EPI_SWIGLU: y[b][n/2]
+    float *tap;          // optional copy of y
+    uint16_t *yf;        // EPI_SWIGLU: optional y in the fragment layout (K' = N/2)
+    int N, K, B, ldy, wk; // wk = waves per 16-row tile (K split)
 };
 
 enum GemvEpi { EPI_STORE = 0, EPI_SWIGLU = 1 };
@@ -105,6 +137,7 @@ struct AttnArgs {
     unsigned *err;
     float *att;          // [B][Hq_s*hd] combined attention output
     float *tap_q, *tap_k, *tap_v, *tap_att;
+    uint16_t *att_xf;    // optional: att in the MFMA fragment layout
     int ld_qkv, max_ctx, Hq_s, Hkv_s, G, hd, n_chunks;
     float scale;
 };
@@ -144,8 +177,11 @@ struct Ffn2dArgs {
 
 hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st);
 hipError_t launch_gemv(const GemvArgs &a, int w_bf16, int epi, hipStream_t st);
+hipError_t launch_gemv_mfma(const MfmaGemvArgs &a, int epi, hipStream_t st);
+bool gemv_mfma_ok(int B, int N, int K, int w_bf16);
 hipError_t launch_attn(const AttnArgs &a, int kv_bf16, int B, hipStream_t st);
 size_t attn_lds_bytes(int G, int hd, int kv_bf16, int n_chunks);
+bool attn_hd_supported(int hd);
 size_t gemv_lds_bytes(int B, int K);
 bool gemv_fused_ok(int B, int K);
 hipError_t launch_wire(const WireArgs &a, hipStream_t st);

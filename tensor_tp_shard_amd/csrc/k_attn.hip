@@ -79,11 +79,12 @@ __host__ __device__ inline size_t attn_smem_bytes(int G, int GM, int hd, int kv_
     return sizeof(float) * ((size_t)G * hd + (size_t)G * kChunk + 4 * GM) + kChunk * rowb + kr;
 }
 
-template <bool KBF16, int GM>
+template <bool KBF16, int GM, int HD>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
 {
     extern __shared__ float smem[];
-    const int hd = a.hd, G = a.G;
+    constexpr int hd = HD;
+    const int G = a.G;
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int L = a.lens[b];
@@ -98,8 +99,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
     const int n = min(kChunk, L + 1 - t0); // positions in this chunk
     const int nch = L / kChunk + 1;        // chunks of this sequence
     const bool owner = L < t0 + kChunk;
-    const int esz = KBF16 ? 2 : 4;
-    const int rowb = attn_row_bytes(hd, KBF16);
+    constexpr int esz = KBF16 ? 2 : 4;
+    constexpr int rowb = hd * esz + 16;
 
     float *q_s = smem;                            // [G][hd]
     float *s_s = q_s + G * hd;                    // [G][64]
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
             cs[u] = rope[p];
         }
     }
-    const int ppr = hd * esz / 16; // 16-byte pieces per row
+    constexpr int ppr = hd * esz / 16; // 16-byte pieces per row
     const int npc = n * ppr;
     u32x4 kv[2][kMaxPieces];
     {
@@ -210,7 +211,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
             sacc[j] = 0.f;
         if (pl < n) {
             const char *krow = K_s + pl * rowb;
-            for (int d = 4 * qt; d < hd; d += 16) {
+#pragma unroll
+            for (int it = 0; it < hd / 16; it++) {
+                const int d = 4 * qt + 16 * it;
                 const float4 k4 = lds4<KBF16>(krow, d);
 #pragma unroll
                 for (int j = 0; j < GM; j++) {
@@ -248,8 +251,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
     __syncthreads();
 
     // 6) o[j][d] = sum_t p[j][t] v[t][d]; K_s is dead, its space holds the phase sums
-    const int tpr = hd / 4;    // threads per row
-    const int nph = 256 / tpr; // row phases
+    constexpr int tpr = hd / 4;    // threads per row
+    constexpr int nph = 256 / tpr; // row phases
     {
         const int ph = tid / tpr, d = (tid % tpr) * 4;
         float4 acc[GM];
@@ -257,7 +260,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
         for (int j = 0; j < GM; j++)
             acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (ph < nph) {
-            for (int pl = ph; pl < n; pl += nph) {
+#pragma unroll
+            for (int it = 0; it < (kChunk + nph - 1) / nph; it++) {
+                const int pl = ph + it * nph;
+                if (pl >= n)
+                    break;
                 const float4 v4 = lds4<KBF16>(V_s + pl * rowb, d);
 #pragma unroll
                 for (int j = 0; j < GM; j++) {
@@ -285,6 +292,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
     for (int i = tid; i < G * hd; i += 256) {
         const int j = i / hd, d = i % hd;
         float o = 0.f;
+#pragma unroll
         for (int ph = 0; ph < nph; ph++)
             o += red[((size_t)ph * G + j) * hd + d];
         float *rec = rec0 + j * rec_stride + (size_t)c * (hd + 4);
@@ -314,6 +322,8 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(AttnArgs a)
             a.att[o] = 0.f;
             if (a.tap_att)
                 a.tap_att[o] = 0.f;
+            if (a.att_xf)
+                xf_store(a.att_xf, b, g * G * hd + i, 0.f);
         }
         return;
     }
@@ -393,6 +403,8 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(AttnArgs a)
         a.att[oi] = o * inv_l[i / hd];
         if (a.tap_att)
             a.tap_att[oi] = o * inv_l[i / hd];
+        if (a.att_xf)
+            xf_store(a.att_xf, b, g * G * hd + i, o * inv_l[i / hd]);
     }
 }
 
@@ -402,13 +414,13 @@ static size_t combine_smem_bytes(int G, int hd, int n_chunks)
     return (((size_t)2 * G * n_chunks + 8 + 3) / 4 * 4 + (size_t)cph * G * hd) * sizeof(float);
 }
 
-template <bool KBF16>
-static hipError_t launch_attn_t(const AttnArgs &a, int B, hipStream_t st)
+template <bool KBF16, int HD>
+static hipError_t launch_attn_hd(const AttnArgs &a, int B, hipStream_t st)
 {
     const dim3 grid(a.n_chunks, a.Hkv_s, B), block(256);
 #define TPS_ATTN(GM)                                                                          \
-    hipLaunchKernelGGL((k_attn<KBF16, GM>), grid, block,                                       \
-                       attn_smem_bytes(a.G, GM, a.hd, KBF16, a.n_chunks), st, a)
+    hipLaunchKernelGGL((k_attn<KBF16, GM, HD>), grid, block,                                   \
+                       attn_smem_bytes(a.G, GM, HD, KBF16, a.n_chunks), st, a)
     if (a.G <= 1)
         TPS_ATTN(1);
     else if (a.G <= 2)
@@ -421,7 +433,22 @@ static hipError_t launch_attn_t(const AttnArgs &a, int B, hipStream_t st)
     return hipGetLastError();
 }
 
-// Host-checked preconditions: 1 <= G <= 8, hd % 16 == 0, hd <= 128,
+template <bool KBF16>
+static hipError_t launch_attn_t(const AttnArgs &a, int B, hipStream_t st)
+{
+    switch (a.hd) {
+    case 16: return launch_attn_hd<KBF16, 16>(a, B, st);
+    case 32: return launch_attn_hd<KBF16, 32>(a, B, st);
+    case 48: return launch_attn_hd<KBF16, 48>(a, B, st);
+    case 64: return launch_attn_hd<KBF16, 64>(a, B, st);
+    case 128: return launch_attn_hd<KBF16, 128>(a, B, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool attn_hd_supported(int hd) { return hd == 16 || hd == 32 || hd == 48 || hd == 64 || hd == 128; }
+
+// Host-checked preconditions: 1 <= G <= 8, attn_hd_supported(hd),
 // n_chunks = ceil(max_ctx / 64), attn_lds_bytes(...) <= 64 KiB.
 hipError_t launch_attn(const AttnArgs &a, int kv_bf16, int B, hipStream_t st)
 {

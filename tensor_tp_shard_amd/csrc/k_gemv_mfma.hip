@@ -1,0 +1,129 @@
+// k_gemv_mfma.hip -- the shard's projections for a decode batch of 5..16
+// sequences on bf16 MFMA: y[b][n] = sum_k W[n][k] x[b][k].
+//
+// Pages: aiterms.tw "Tensor Parallelism", 核心概念 items 1-2 and 運作原理
+// (column- and row-split projections of one shard); distributed-llama issue
+// "[Feature Suggest] Tensor Parallellism for Accelerating LLM",
+// buildLlama2Arch tasks llamaQkv, llamaAttOutput, llamaFfn (SwiGLU),
+// llamaFfn2.
+//
+// Why MFMA here: with 16 sequences every weight feeds 16 multiply-adds, and
+// at the HBM rate (2.8 T bf16 weights/s at 70% of 8 TB/s) that is 45 T FMA/s,
+// more than the chip's non-packed fp32 vector rate (39 T FMA/s). A batch of
+// 16 times a weight block is a dense 16-row contraction, the shape of
+// v_mfma_f32_16x16x32_bf16. Weights are the A operand (16 rows per tile),
+// the 16 batch rows the B operand. The fp32 activations enter as bf16 hi and
+// lo parts (two MFMAs per step), so the product carries ~16 mantissa bits of
+// every activation with fp32 accumulation -- fp32-class accuracy. The
+// activations are written in the fragment layout once by their producer
+// (RMSNorm, attention combine, SwiGLU).
+//
+// Work split: one workgroup per 16-row tile, its wk waves split K in
+// 128-wide blocks; a wave keeps two blocks of weights (16-byte nontemporal
+// loads, 64 contiguous bytes per lane per block) and their activation
+// fragments in flight, then the waves' 16x16 accumulators are summed in wave
+// order through LDS. Epilogues: store, or SwiGLU of the interleaved
+// (W1_f, W3_f) rows (accumulator rows 4q..4q+3 of a lane are two pairs).
+#include "common.h"
+
+namespace tps {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxWk = 16;
+
+template <int EPI>
+__global__ __launch_bounds__(64 * kMaxWk) void k_gemv_mfma(MfmaGemvArgs a)
+{
+    constexpr int P = 2; // 128-wide K blocks in flight per wave
+    __shared__ f32x4 red[kMaxWk][64];
+    const int n0 = blockIdx.x * 16;
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
+    const int nb = a.K >> 7;
+    const int per = (nb + a.wk - 1) / a.wk;
+    const int j0 = wv * per, j1 = min(nb, j0 + per);
+    const u32x4 *wrow = (const u32x4 *)(a.W + (size_t)(n0 + r) * a.K + 32 * q);
+    const u32x4 *xf = (const u32x4 *)a.xf; // 16-byte units: [j][hl][s][q][b]
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = j0; j < j1; j += P) {
+        u32x4 w[P][4], xh[P][4], xl[P][4];
+#pragma unroll
+        for (int p = 0; p < P; p++)
+            if (j + p < j1)
+#pragma unroll
+                for (int s = 0; s < 4; s++)
+                    w[p][s] = __builtin_nontemporal_load(wrow + (size_t)(j + p) * 16 + s);
+#pragma unroll
+        for (int p = 0; p < P; p++)
+            if (j + p < j1)
+#pragma unroll
+                for (int s = 0; s < 4; s++) {
+                    xh[p][s] = xf[(((size_t)(j + p) * 2 + 0) * 4 + s) * 64 + lane];
+                    xl[p][s] = xf[(((size_t)(j + p) * 2 + 1) * 4 + s) * 64 + lane];
+                }
+#pragma unroll
+        for (int p = 0; p < P; p++)
+            if (j + p < j1)
+#pragma unroll
+                for (int s = 0; s < 4; s++) {
+                    const bf16x8 wa = __builtin_bit_cast(bf16x8, w[p][s]);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xh[p][s]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xl[p][s]), acc, 0, 0, 0);
+                }
+    }
+    red[wv][lane] = acc;
+    __syncthreads();
+    if (wv != 0)
+        return;
+    f32x4 c = red[0][lane];
+    for (int w = 1; w < a.wk; w++) {
+        const f32x4 v = red[w][lane];
+        c = f32x4{c[0] + v[0], c[1] + v[1], c[2] + v[2], c[3] + v[3]};
+    }
+    // lane holds rows n0 + 4q + i (i < 4) of batch column b = r
+    const int b = r;
+    if (b >= a.B)
+        return;
+    if constexpr (EPI == EPI_SWIGLU) {
+        const int f = (n0 >> 1) + 2 * q; // rows (4q, 4q+1) and (4q+2, 4q+3) are features f, f+1
+        const float h0 = silu(c[0]) * c[1], h1 = silu(c[2]) * c[3];
+        *(float2 *)(a.y + (size_t)b * a.ldy + f) = make_float2(h0, h1);
+        if (a.tap)
+            *(float2 *)(a.tap + (size_t)b * a.ldy + f) = make_float2(h0, h1);
+        if (a.yf) {
+            xf_store(a.yf, b, f, h0);
+            xf_store(a.yf, b, f + 1, h1);
+        }
+    } else {
+        const int n = n0 + 4 * q;
+        const float4 v = make_float4(c[0], c[1], c[2], c[3]);
+        *(float4 *)(a.y + (size_t)b * a.ldy + n) = v;
+        if (a.tap)
+            *(float4 *)(a.tap + (size_t)b * a.ldy + n) = v;
+    }
+}
+
+bool gemv_mfma_ok(int B, int N, int K, int w_bf16)
+{
+    return w_bf16 && B > 4 && B <= 16 && N % 16 == 0 && K % 128 == 0;
+}
+
+// Host-checked preconditions: gemv_mfma_ok; ldy and the float2/float4
+// stores 8/16-byte aligned (N and ldy multiples of 4).
+hipError_t launch_gemv_mfma(const MfmaGemvArgs &a0, int epi, hipStream_t st)
+{
+    MfmaGemvArgs a = a0;
+    const int nb = a.K / 128;
+    // K split so that each wave streams about 4 blocks (4 x 4 KiB of weights)
+    int wk = (nb + 3) / 4;
+    a.wk = wk < 1 ? 1 : wk > kMaxWk ? kMaxWk : wk;
+    const dim3 grid(a.N / 16), block(64 * a.wk);
+    if (epi == EPI_SWIGLU)
+        hipLaunchKernelGGL(k_gemv_mfma<EPI_SWIGLU>, grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL(k_gemv_mfma<EPI_STORE>, grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+} // namespace tps
