@@ -13,12 +13,16 @@
 // Both products are "NT": C[m][n] = sum_k A[m][k] B[n][k] with A and B stored
 // K-contiguous, which is the operand layout of v_mfma_f32_16x16x32_bf16
 // (each lane holds 8 consecutive k of one row of A and of one row of B).
-//  - workgroup tile 128 x 256, four waves as 2 x 2, wave tile 64 x 128
-//    (4 x 8 MFMA tiles, 128 fp32 accumulators per lane), K step 64;
-//  - the next K step's tiles are loaded into registers (16-byte global
-//    loads) while the current one is multiplied from LDS; LDS rows are 128
-//    bytes with the 16-byte chunk index XOR-swizzled by (row & 7), so the
-//    fragment reads (16 rows x 16 bytes per 8-lane phase) are conflict-free;
+//  - workgroup tile 128 x 288, four waves as 2 x 2, wave tile 64 x 144
+//    (4 x 9 MFMA tiles, 144 fp32 accumulators per lane), K step 64; 288
+//    divides the PaLM block's 2F = 18432 and E = 2304, so a 512-token
+//    up-projection is exactly 256 workgroups (one per CU) and the
+//    down-projection 32 tiles x 8 K splits;
+//  - a 5-stage LDS ring (K step 32 per stage, 26 KiB each) filled by direct
+//    global->LDS loads (global_load_lds_dwordx4), four stages ahead of the
+//    MFMAs, one barrier per stage and no register staging; 64-byte LDS rows
+//    with the 16-byte chunk index XOR-swizzled by (row >> 1) & 3, so the
+//    fragment reads are bank-conflict free;
 //  - tile order puts the M-tiles of one N-tile on the same XCD (linear
 //    workgroup id % 8), so a weight tile is fetched into one L2 once;
 //  - up-projection epilogue: the packed W_gate/W_in rows interleave in
@@ -33,10 +37,11 @@ namespace tps {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128, kBN = 256, kBK = 64;
-constexpr int kMT = 4, kNT = 8;                                // MFMA tiles per wave (64 x 128)
-constexpr int kChunksA = kBM * kBK / 8, kChunksB = kBN * kBK / 8; // 16-byte chunks per K step
-constexpr int kLoads = (kChunksA + kChunksB) / 256;            // per thread (12)
+constexpr int kBN = 288, kBK = 32;                              // N tile, K step per pipeline stage
+constexpr int kStages = 3;                                      // LDS ring of 3 stages
+constexpr int kNT = 9;                                          // MFMA tiles per wave in N (144)
+constexpr int kWN = kNT * 16;                                   // wave tile width
+constexpr int kRowB = kBK * 2;                                  // 64-byte LDS rows
 
 enum { FFN_UP = 0, FFN_DOWN = 1 };
 
@@ -48,17 +53,36 @@ struct GemmArgs {
     int M, N, K, ksteps_per_split;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK * 2 + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk q (of 4) of row r sits at chunk q ^ ((r >> 1) & 3): a
+// 16-row x 16-byte fragment read then touches every LDS bank once per
+// 8-lane phase.
+__device__ __forceinline__ int swz(int row, int q) { return row * kRowB + ((q ^ ((row >> 1) & 3)) << 4); }
 
-template <int EPI>
+// s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// BM = 64 (decode-sized M: more workgroups) or 128 (large M)
+template <int EPI, int BM>
 __global__ __launch_bounds__(256, 2) void k_gemm_nt(GemmArgs a)
 {
-    __shared__ __attribute__((aligned(16))) char As[kBM * kBK * 2];
-    __shared__ __attribute__((aligned(16))) char Bs[kBN * kBK * 2];
+    constexpr int kMT = BM / 32;                       // MFMA tiles per wave in M (BM/2 rows)
+    constexpr int kStageB = (BM + kBN) * kRowB;        // bytes per stage
+    constexpr int kSegs = kStageB / 1024;              // 1 KiB wave loads per stage
+    constexpr int kSegsA = BM * kRowB / 1024;          // of which A
+    constexpr int kMaxSegs = (kSegs + 3) / 4;          // per wave
+    constexpr int kMinSegs = kSegs / 4;
+    static_assert((BM * kRowB) % 1024 == 0 && kStageB % 1024 == 0, "whole wave loads");
+    static_assert(kMaxSegs - kMinSegs <= 1, "waves issue kMaxSegs or kMaxSegs - 1 segments");
+    __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageB];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wm = wv >> 1, wn = wv & 1;
     // grid: x = N-tile (fastest, so the M-tiles of one N-tile share id % 8), y = M-tile, z = split
-    const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
+    const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * BM;
     const int ks0 = blockIdx.z * a.ksteps_per_split;
     const int nks = min(a.ksteps_per_split, a.K / kBK - ks0);
 
@@ -69,70 +93,72 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(GemmArgs a)
         for (int j = 0; j < kNT; j++)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // global chunk ids of this thread: id < kChunksA are A chunks, the rest B
-    u32x4 pre[kLoads];
-    auto load_step = [&](int ks) {
-        const int kbase = (ks0 + ks) * kBK;
+    // Stage loads go straight from global memory to LDS (global_load_lds_dwordx4:
+    // lane i's 16 bytes land at base + 16 i). Wave w issues segments w, w+4, ...;
+    // lane i of segment t fills LDS slot 64 t + i = (row, physical chunk), so it
+    // loads the row's logical chunk q = physical ^ ((row >> 1) & 3). A rows past
+    // M read row M-1 (their outputs are never stored).
+    const int nseg = (kSegs - wv + 3) / 4; // kMaxSegs or kMaxSegs - 1
+    const uint16_t *src[kMaxSegs];
 #pragma unroll
-        for (int i = 0; i < kLoads; i++) {
-            const int id = tid + 256 * i;
-            if (id < kChunksA) {
-                const int row = id >> 3, ch = id & 7;
-                const int m = m0 + row;
-                if (m < a.M)
-                    pre[i] = *(const u32x4 *)(a.A + (size_t)m * a.K + kbase + ch * 8);
-                else
-                    pre[i] = u32x4{0u, 0u, 0u, 0u};
-            } else {
-                const int idb = id - kChunksA;
-                const int row = idb >> 3, ch = idb & 7;
-                pre[i] = __builtin_nontemporal_load(
-                    (const u32x4 *)(a.B + (size_t)(n0 + row) * a.K + kbase + ch * 8));
-            }
-        }
-    };
-    auto store_step = [&]() {
-#pragma unroll
-        for (int i = 0; i < kLoads; i++) {
-            const int id = tid + 256 * i;
-            if (id < kChunksA)
-                *(u32x4 *)(As + swz(id >> 3, id & 7)) = pre[i];
-            else
-                *(u32x4 *)(Bs + swz((id - kChunksA) >> 3, (id - kChunksA) & 7)) = pre[i];
-        }
-    };
-
-    if (nks > 0)
-        load_step(0);
-    for (int ks = 0; ks < nks; ks++) {
-        __syncthreads(); // the previous step's fragment reads are done
-        store_step();
-        __syncthreads();
-        if (ks + 1 < nks)
-            load_step(ks + 1);
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
-            const int ch = kk * 4 + (lane >> 4);
-            bf16x8 af[kMT], bfr[kNT];
-#pragma unroll
-            for (int i = 0; i < kMT; i++) {
-                const int row = wm * 64 + i * 16 + (lane & 15);
-                af[i] = *(const bf16x8 *)(As + swz(row, ch));
-            }
-#pragma unroll
-            for (int j = 0; j < kNT; j++) {
-                const int row = wn * 128 + j * 16 + (lane & 15);
-                bfr[j] = *(const bf16x8 *)(Bs + swz(row, ch));
-            }
-#pragma unroll
-            for (int i = 0; i < kMT; i++)
-#pragma unroll
-                for (int j = 0; j < kNT; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int u = 0; u < kMaxSegs; u++) {
+        const int t = wv + 4 * u;
+        const int p = lane, rs = p >> 2, phys = p & 3;
+        if (t < kSegsA) {
+            const int row = t * 16 + rs;
+            const int m = min(m0 + row, a.M - 1);
+            src[u] = a.A + (size_t)m * a.K + 8 * (phys ^ ((row >> 1) & 3));
+        } else {
+            const int row = (t - kSegsA) * 16 + rs;
+            src[u] = a.B + (size_t)(n0 + row) * a.K + 8 * (phys ^ ((row >> 1) & 3));
         }
     }
+    auto issue = [&](int ks) {
+        const int kbase = (ks0 + ks) * kBK;
+        char *base = lds + (ks % kStages) * kStageB;
+#pragma unroll
+        for (int u = 0; u < kMaxSegs; u++)
+            if (u < nseg)
+                __builtin_amdgcn_global_load_lds((const void *)(src[u] + kbase),
+                                                 (__attribute__((address_space(3))) void *)(base + (wv + 4 * u) * 1024),
+                                                 16, 0, 0);
+    };
 
-    // lane holds C[m0 + wm*64 + i*16 + 4*(lane/16) + r][n0 + wn*128 + j*16 + lane%16]
+    for (int s = 0; s < kStages - 1 && s < nks; s++)
+        issue(s);
+    const int q = lane >> 4;
+    for (int ks = 0; ks < nks; ks++) {
+        // this wave's loads of stage ks are done once at most the later stages'
+        // remain (kStages - 2 of them in the steady state; drain at the tail)
+        if (ks + kStages - 2 <= nks - 1) {
+            if (nseg == kMaxSegs)
+                wait_vmcnt<kMaxSegs * (kStages - 2)>();
+            else
+                wait_vmcnt<(kMaxSegs - 1) * (kStages - 2)>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        // every wave's stage ks is in LDS and stage ks-1's buffer is free; a bare
+        // barrier (no fence: a fence would also wait for the later stages' loads)
+        __builtin_amdgcn_s_barrier();
+        if (ks + kStages - 1 < nks)
+            issue(ks + kStages - 1);
+        const char *As = lds + (ks % kStages) * kStageB, *Bs = As + BM * kRowB;
+        bf16x8 af[kMT], bfr[kNT];
+#pragma unroll
+        for (int i = 0; i < kMT; i++)
+            af[i] = *(const bf16x8 *)(As + swz(wm * (BM / 2) + i * 16 + (lane & 15), q));
+#pragma unroll
+        for (int j = 0; j < kNT; j++)
+            bfr[j] = *(const bf16x8 *)(Bs + swz(wn * kWN + j * 16 + (lane & 15), q));
+#pragma unroll
+        for (int i = 0; i < kMT; i++)
+#pragma unroll
+            for (int j = 0; j < kNT; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+
+    // lane holds C[m0 + wm*BM/2 + i*16 + 4*(lane/16) + r][n0 + wn*kWN + j*16 + lane%16]
     const int col = lane & 15, rq = (lane >> 4) * 4;
     if constexpr (EPI == FFN_UP) {
         const int F = a.N / 2;
@@ -140,13 +166,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(GemmArgs a)
         for (int i = 0; i < kMT; i++)
 #pragma unroll
             for (int j = 0; j < kNT; j++) {
-                const int tile = (n0 + wn * 128 + j * 16) / 16;
+                const int tile = (n0 + wn * kWN + j * 16) / 16;
                 const int f = tile * 8 + (col & 7);
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     const float mine = acc[i][j][r];
                     const float other = __shfl_xor(mine, 8, 64); // lanes col and col ^ 8
-                    const int m = m0 + wm * 64 + i * 16 + rq + r;
+                    const int m = m0 + wm * (BM / 2) + i * 16 + rq + r;
                     if (col < 8 && m < a.M)
                         a.H[(size_t)m * F + f] = f32_to_bf16(silu(mine) * other);
                 }
@@ -157,10 +183,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(GemmArgs a)
         for (int i = 0; i < kMT; i++)
 #pragma unroll
             for (int j = 0; j < kNT; j++) {
-                const int n = n0 + wn * 128 + j * 16 + col;
+                const int n = n0 + wn * kWN + j * 16 + col;
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const int m = m0 + wm * 64 + i * 16 + rq + r;
+                    const int m = m0 + wm * (BM / 2) + i * 16 + rq + r;
                     if (m < a.M)
                         C[(size_t)m * a.N + n] = acc[i][j][r];
                 }
@@ -187,9 +213,12 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float *P, float *Y, 
 
 // Number of K splits of the down-projection for a batch of B rows: enough
 // workgroups for the 256 CUs when the output has few tiles.
+static int ffn2d_bm(int B) { return B <= 1024 ? 64 : 128; }
+
 int ffn2d_splits(int B, int E, int F)
 {
-    const int tiles = ((B + kBM - 1) / kBM) * (E / kBN);
+    const int bm = ffn2d_bm(B);
+    const int tiles = ((B + bm - 1) / bm) * (E / kBN);
     int s = 256 / (tiles > 0 ? tiles : 1);
     s = s < 1 ? 1 : s > 8 ? 8 : s;
     const int ksteps = F / kBK;
@@ -198,13 +227,18 @@ int ffn2d_splits(int B, int E, int F)
 
 // which = 0: up-projection + SwiGLU into a.h; which = 1: down-projection
 // into a.y (through the split partials in a.part when splitting).
-// Host-checked: E % 256 == 0, F % 128 == 0, E and F multiples of 64.
+// Host-checked: E % 288 == 0, (2F) % 288 == 0, E and F multiples of 64, F % 8 == 0.
 hipError_t launch_ffn2d(const Ffn2dArgs &f, hipStream_t st, int which)
 {
-    const int mt = (f.B + kBM - 1) / kBM;
+    const int bm = ffn2d_bm(f.B);
+    const int mt = (f.B + bm - 1) / bm;
     if (which == 0) {
         GemmArgs g{f.x, f.w13, f.h, nullptr, f.B, 2 * f.F, f.E, f.E / kBK};
-        hipLaunchKernelGGL(k_gemm_nt<FFN_UP>, dim3(2 * f.F / kBN, mt, 1), dim3(256), 0, st, g);
+        const dim3 grid(2 * f.F / kBN, mt, 1);
+        if (bm == 64)
+            hipLaunchKernelGGL((k_gemm_nt<FFN_UP, 64>), grid, dim3(256), 0, st, g);
+        else
+            hipLaunchKernelGGL((k_gemm_nt<FFN_UP, 128>), grid, dim3(256), 0, st, g);
         return hipGetLastError();
     }
     const int S = ffn2d_splits(f.B, f.E, f.F);
@@ -212,7 +246,11 @@ hipError_t launch_ffn2d(const Ffn2dArgs &f, hipStream_t st, int which)
     const int per = (ksteps + S - 1) / S;
     const int splits = (ksteps + per - 1) / per;
     GemmArgs g{f.h, f.w2, nullptr, splits > 1 ? f.part : f.y, f.B, f.E, f.F, per};
-    hipLaunchKernelGGL(k_gemm_nt<FFN_DOWN>, dim3(f.E / kBN, mt, splits), dim3(256), 0, st, g);
+    const dim3 grid(f.E / kBN, mt, splits);
+    if (bm == 64)
+        hipLaunchKernelGGL((k_gemm_nt<FFN_DOWN, 64>), grid, dim3(256), 0, st, g);
+    else
+        hipLaunchKernelGGL((k_gemm_nt<FFN_DOWN, 128>), grid, dim3(256), 0, st, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1)
         return e;

@@ -54,9 +54,9 @@ def run_ffn2d(d, max_batch, batches):
 
 
 def test_ffn2d_small_ragged():
-    """E = 256, F = 384, 200 rows (one full and one partial 128-row tile), and
+    """E = 576, F = 576, 200 rows (one full and one partial 128-row tile), and
     a 5-row call on the same handle."""
-    w = synth.Ffn2D("ffn2d_small", e_blk=256, f_blk=384, batch=200, seed=91)
+    w = synth.Ffn2D("ffn2d_small", e_blk=576, f_blk=576, batch=200, seed=91)
     d = synth.ffn2d_inputs(w)
     say("ffn2d small ragged")
     y200, y5 = run_ffn2d(d, 200, [200, 5])
