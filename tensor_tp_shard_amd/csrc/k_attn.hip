@@ -126,6 +126,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
             cs[u] = rope[p];
         }
     }
+    // the owner's new key / value pair p = tid (rotation factor cs[0] = rope[tid])
+    float2 nk = make_float2(0.f, 0.f), nv = make_float2(0.f, 0.f);
+    if (owner && tid < half) {
+        nk = *(const float2 *)(qkv + (a.Hq_s + g) * hd + 2 * tid);
+        nv = *(const float2 *)(qkv + (a.Hq_s + a.Hkv_s + g) * hd + 2 * tid);
+    }
     constexpr int ppr = hd * esz / 16; // 16-byte pieces per row
     const int npc = n * ppr;
     u32x4 kv[2][kMaxPieces];
@@ -170,14 +176,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
     __syncthreads();
     // 3) the owner rotates and appends the new key / value at slot L
     if (owner) {
-        const float *kq = qkv + (a.Hq_s + g) * hd;
-        const float *vq = qkv + (a.Hq_s + a.Hkv_s + g) * hd;
         char *krow = K_s + (L - t0) * rowb, *vrow = V_s + (L - t0) * rowb;
-        for (int p = tid; p < half; p += 256) {
-            const float x0 = kq[2 * p], x1 = kq[2 * p + 1];
-            const float2 cr = rope[p];
-            const float r0 = x0 * cr.x - x1 * cr.y, r1 = x0 * cr.y + x1 * cr.x;
-            const float v0 = vq[2 * p], v1 = vq[2 * p + 1];
+        if (tid < half) {
+            const int p = tid;
+            const float2 cr = cs[0];
+            const float r0 = nk.x * cr.x - nk.y * cr.y, r1 = nk.x * cr.y + nk.y * cr.x;
+            const float v0 = nv.x, v1 = nv.y;
             const size_t e = head_base + (size_t)L * hd + 2 * p;
             store_kv<KBF16>(a.kc, e, r0);
             store_kv<KBF16>(a.kc, e + 1, r1);
@@ -331,10 +335,15 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(AttnArgs a)
     const int ws = a.n_chunks;
     const size_t rec_stride = (size_t)a.n_chunks * (hd + 4);
     const float *rec0 = a.part + ((size_t)b * a.Hq_s + (size_t)g * G) * rec_stride;
-    float *wts = smem;                                // [G][n_chunks] m_c, then e^(m_c - M)
-    float *lsv = wts + G * ws;                        // [G][n_chunks] l_c
-    float *inv_l = lsv + G * ws;                      // [G]
-    float *osum = smem + ((2 * G * ws + 8 + 3) & ~3); // [phases][G][hd]
+    float *wts = smem;                                // [G][n_chunks] e^(m_c - M)
+    float *inv_l = wts + G * ws;                      // [G]
+    float *osum = smem + ((G * ws + 8 + 3) & ~3);     // [phases][G][hd]
+    const int w = tid >> 6, lane = tid & 63;
+    // 1) (m_c, l_c) of head w's first 64 chunks (wave w < G), then the first
+    //    kCU chunk outputs of every quad: all issued before anything waits
+    float2 ml0 = make_float2(-INFINITY, 0.f);
+    if (w < G && lane < nch)
+        ml0 = *(const float2 *)(rec0 + w * rec_stride + (size_t)lane * (hd + 4));
     const int quads = G * (hd / 4);
     const int cph = kCombThreads / quads;             // chunk phases (quads <= 256)
     constexpr int kCU = 16;                           // chunks per phase loaded together
@@ -349,24 +358,29 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(AttnArgs a)
         if (qact && cc < nch)
             v[u] = *(const float4 *)(rj + (size_t)cc * (hd + 4));
     }
-    for (int i = tid; i < G * nch; i += kCombThreads) {
-        const int jj = i / nch, cc = i % nch;
-        const float2 m_l = *(const float2 *)(rec0 + jj * rec_stride + (size_t)cc * (hd + 4));
-        wts[jj * ws + cc] = m_l.x;
-        lsv[jj * ws + cc] = m_l.y;
-    }
-    __syncthreads();
-    if (tid < G) {
-        float M = -INFINITY;
-        for (int cc = 0; cc < nch; cc++)
-            M = fmaxf(M, wts[tid * ws + cc]);
+    // 2) statistics of head w across the wave's lanes: M = max_c m_c,
+    //    w_c = e^(m_c - M), l = sum_c w_c l_c (lane partials, then the butterfly)
+    if (w < G) {
+        const float *rw = rec0 + w * rec_stride;
+        float m = ml0.x;
+        for (int cc = lane + 64; cc < nch; cc += 64) // sequences longer than 64 chunks
+            m = fmaxf(m, rw[(size_t)cc * (hd + 4)]);
+        const float M = group_max<64>(m);
         float l = 0.f;
-        for (int cc = 0; cc < nch; cc++) {
-            const float wv = expf(wts[tid * ws + cc] - M);
-            wts[tid * ws + cc] = wv;
-            l += wv * lsv[tid * ws + cc];
+        if (lane < nch) {
+            const float e = expf(ml0.x - M);
+            wts[w * ws + lane] = e;
+            l = e * ml0.y;
         }
-        inv_l[tid] = 1.0f / l;
+        for (int cc = lane + 64; cc < nch; cc += 64) {
+            const float2 q = *(const float2 *)(rw + (size_t)cc * (hd + 4));
+            const float e = expf(q.x - M);
+            wts[w * ws + cc] = e;
+            l += e * q.y;
+        }
+        l = group_sum<64>(l);
+        if (lane == 0)
+            inv_l[w] = 1.0f / l;
     }
     __syncthreads();
     if (qact) {
@@ -411,7 +425,7 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(AttnArgs a)
 static size_t combine_smem_bytes(int G, int hd, int n_chunks)
 {
     const int cph = kCombThreads / (G * (hd / 4));
-    return (((size_t)2 * G * n_chunks + 8 + 3) / 4 * 4 + (size_t)cph * G * hd) * sizeof(float);
+    return (((size_t)G * n_chunks + 8 + 3) / 4 * 4 + (size_t)cph * G * hd) * sizeof(float);
 }
 
 template <bool KBF16, int HD>
