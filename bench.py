@@ -4,8 +4,10 @@ A step is one pass of the whole shard step for rank 0 of the workload:
 attention stage (RMSNorm, QKV, RoPE + KV append, GQA attention, W_O, int8
 wire when configured) -> merge of the T shard partials (rank 0's own plus
 the T-1 wires the other ranks produced, standing in for what would arrive
-over xGMI) -> FFN stage (RMSNorm, W1/W3 + SwiGLU, W2) -> merge. The output of
-a step is the next step's input. R layer copies (distinct weights, caches
+over xGMI) -> FFN stage (RMSNorm, W1/W3 + SwiGLU, W2) -> merge. By default
+each merge is done by the kernel that produces rank 0's own partial
+(decode_merge_step); --merge separate runs it as a kernel of its own
+(merge_partials). The output of a step is the next step's input. R layer copies (distinct weights, caches
 and workspaces in HBM, R x step bytes > 2 x the 256 MB Infinity Cache) are
 used in rotation so no step reads what the previous one left in the cache.
 
@@ -114,7 +116,17 @@ def run_llama(args, w):
     hs_ = [torch.empty_like(x0) for _ in range(R)]
     xs[0].copy_(x0)
 
-    def one_pass():
+    def one_pass_fused():
+        # layer copy r reads xs[r] and writes xs[r+1]; each merge is done by
+        # the kernel that produces rank 0's own partial of that stage
+        for r, c in enumerate(copies):
+            xin, xout = xs[r], xs[(r + 1) % R]
+            c.step_merge(tp.TP_STAGE_ATTN, xin, lens, B, wires_a[r], [wires_a[r]] + other_att,
+                         hs_[r])
+            c.step_merge(tp.TP_STAGE_FFN, hs_[r], None, B, wires_f[r], [wires_f[r]] + other_ffn,
+                         xout)
+
+    def one_pass_separate():
         # layer copy r reads xs[r] and writes xs[r+1]; the pass ends where it began
         for r, c in enumerate(copies):
             xin, xout = xs[r], xs[(r + 1) % R]
@@ -122,6 +134,8 @@ def run_llama(args, w):
             c.merge(tp.TP_STAGE_ATTN, [wires_a[r]] + other_att, xin, hs_[r], B)
             c.step(tp.TP_STAGE_FFN, hs_[r], None, B, wires_f[r])
             c.merge(tp.TP_STAGE_FFN, [wires_f[r]] + other_ffn, hs_[r], xout, B)
+
+    one_pass = one_pass_fused if args.merge == "fused" else one_pass_separate
 
     passes = max(1, args.steps // R)
     steps = passes * R
@@ -182,6 +196,8 @@ def run_llama(args, w):
         "config": {"workload": w.name, "shard": f"rank 0 of TP={T}", "batch": B,
                    "kv_positions": [int(d["lens"].min()), int(d["lens"].max())],
                    "quant": w.quant, "layer_copies": R, "launch": args.mode,
+                   "merge": ("fused into the producer of rank 0's partial" if args.merge == "fused"
+                             else "kernel of its own"),
                    "step_bytes": int(step_bytes)},
         "achieved_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -321,6 +337,9 @@ def main():
     ap.add_argument("--workload", default="llama2_7b_tp4_b1", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--copies", type=int, default=0, help="layer copies in rotation (0 = auto)")
+    ap.add_argument("--merge", default="fused", choices=["fused", "separate"],
+                    help="merge of a stage's partials by the kernel that produces rank 0's own "
+                         "partial (decode_merge_step) or as a kernel of its own (merge_partials)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()

@@ -180,6 +180,27 @@ int32_t merge_partials(const tp_shard *s, int32_t stage, const void *const *wire
                        int32_t n_wires, const float *residual, float *out, int32_t batch,
                        void *hip_stream);
 
+/*
+ * decode_merge_step: decode_step, then merge_partials of this stage's
+ * partials onto x, with the merge done by the kernel that writes this shard's
+ * own partial (the down-projection's store, or the int8 quantiser) instead of
+ * a kernel of its own: the row-split partials' all-reduce fused into their
+ * producer (same passages as decode_step and merge_partials).
+ *  x_out = x + sum_{i < n_wires} dequant(wires[i]) in array order, bitwise
+ *    what merge_partials(wires, n_wires, residual = x) writes. Exactly one
+ *    wires[i] must equal wire_out: that term is this shard's partial, taken
+ *    from the producing kernel's registers; the others are read from memory
+ *    and must be complete when the call is enqueued (earlier work on the
+ *    stream). TP_LLAMA_BLOCK only.
+ *  x_out may alias x, but not a wire (TP_EINVAL).
+ *  Other arguments as in decode_step and merge_partials.
+ * Errors: those of decode_step and merge_partials; TP_EINVAL when wire_out is
+ * not in wires, appears twice, or x_out equals a wire.
+ */
+int32_t decode_merge_step(tp_shard *s, int32_t stage, const void *x, const int32_t *lens,
+                          int32_t batch, void *wire_out, const void *const *wires,
+                          int32_t n_wires, float *x_out, const tp_taps *taps, void *hip_stream);
+
 /* Byte offset of the fp32 scales inside a quantised wire of `batch` rows
  * (16-byte aligned, right after the int8 codes). */
 uint64_t tp_wire_scales_offset(const tp_config *cfg, int32_t batch);

@@ -4,7 +4,7 @@ Argument marshalling only: every step of the shard's decode step runs in the
 library's HIP kernels. PyTorch supplies device memory (``torch.empty``) and
 the stream (``torch.cuda.current_stream()``). The names mirror the C ABI:
 ``init_shard``, ``load_weights``, ``decode_step``, ``merge_partials``,
-``destroy_shard``; ``Shard`` bundles a handle with torch-allocated buffers.
+``decode_merge_step``, ``destroy_shard``; ``Shard`` bundles a handle with torch-allocated buffers.
 
 There is no fallback: if ``libtpshard.so`` is missing or fails to load,
 every call raises.
@@ -26,7 +26,8 @@ TP_OK, TP_EINVAL, TP_EALIGN, TP_ESTATE, TP_ENODEV, TP_EHIP, TP_ENOTIMPL = 0, -1,
 TP_DERR_LEN = 1
 
 # every symbol include/tpshard.h declares
-EXPORTS = ("init_shard", "load_weights", "decode_step", "merge_partials", "tp_wire_scales_offset",
+EXPORTS = ("init_shard", "load_weights", "decode_step", "merge_partials", "decode_merge_step",
+           "tp_wire_scales_offset",
            "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
            "tp_kernel_name", "destroy_shard", "tp_status_str", "tp_last_error")
 
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.load_weights.argtypes = [P, P, P, P, P, P, P]
         L.decode_step.argtypes = [P, I32, P, P, I32, P, P, P]
         L.merge_partials.argtypes = [P, I32, P, I32, P, P, I32, P]
+        L.decode_merge_step.argtypes = [P, I32, P, P, I32, P, P, I32, P, P, P]
         L.tp_wire_scales_offset.argtypes = [P, I32]
         L.tp_wire_scales_offset.restype = U64
         L.tp_read_error_word.argtypes = [P, P, I32, P]
@@ -86,7 +88,7 @@ def lib() -> ctypes.CDLL:
         L.tp_status_str.restype = ctypes.c_char_p
         L.tp_last_error.restype = ctypes.c_char_p
         for f in ("init_shard", "load_weights", "decode_step", "merge_partials",
-                  "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read"):
+                  "decode_merge_step", "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read"):
             getattr(L, f).restype = I32
         _lib = L
     return _lib
@@ -153,6 +155,18 @@ def merge_partials(handle, stage: int, wires: Sequence, residual, out, batch: in
     arr = (ctypes.c_void_p * len(wires))(*[_ptr(w) for w in wires])
     _check(lib().merge_partials(handle, stage, arr, len(wires), _ptr(residual), _ptr(out), batch,
                                 _stream(stream)), "merge_partials")
+
+
+def decode_merge_step(handle, stage: int, x, lens, batch: int, wire_out, wires: Sequence,
+                      x_out, taps: Optional[dict] = None, stream=None):
+    arr = (ctypes.c_void_p * len(wires))(*[_ptr(w) for w in wires])
+    t = None
+    if taps:
+        t = TpTaps(**{k: _ptr(v) for k, v in taps.items()})
+    _check(lib().decode_merge_step(handle, stage, _ptr(x), _ptr(lens), batch, _ptr(wire_out), arr,
+                                   len(wires), _ptr(x_out),
+                                   ctypes.byref(t) if t is not None else None, _stream(stream)),
+           "decode_merge_step")
 
 
 def wire_scales_offset(cfg: TpConfig, batch: int) -> int:
@@ -228,6 +242,9 @@ class Shard:
 
     def merge(self, stage, wires, residual, out, batch, stream=None):
         merge_partials(self.handle, stage, wires, residual, out, batch, stream)
+
+    def step_merge(self, stage, x, lens, batch, wire_out, wires, x_out, taps=None, stream=None):
+        decode_merge_step(self.handle, stage, x, lens, batch, wire_out, wires, x_out, taps, stream)
 
     def close(self):
         destroy_shard(self.handle)

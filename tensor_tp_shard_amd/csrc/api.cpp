@@ -395,8 +395,12 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *w, void *packed, void 
     return TP_OK;
 }
 
-int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *lens,
-                    int32_t batch, void *wire_out, const tp_taps *taps, void *hip_stream)
+// One stage of the shard step on input x. With mo (llama blocks only) the
+// stage's partials are also merged, mo->x_out = x + sum of mo's wires, by the
+// kernel that writes this shard's own partial (wire mo->own = wire_out).
+static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeIn *mo,
+                         const int32_t *lens, int32_t batch, void *wire_out, const tp_taps *taps,
+                         void *hip_stream)
 {
     if (!s)
         return fail(TP_EINVAL, "decode_step: null handle");
@@ -484,12 +488,14 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
     down.tap = tp.p_pre;
     down.N = s->D;
     down.ldy = s->D;
+    if (mo && !qpart) // fp32 wires: the down-projection's store epilogue merges
+        down.mo = *mo;
     down.B = B;
     const int Kd = stage == TP_STAGE_ATTN ? s->Hq_s * s->hd : s->Fs;
     auto run_gemv = [&](const GemvArgs &g, const uint16_t *xf, uint16_t *yf, int epi) {
         if (!mfma)
             return launch_gemv(g, wbf, epi, st);
-        MfmaGemvArgs m{(const uint16_t *)g.W, xf, g.y, g.tap, yf, g.N, g.K, g.B, g.ldy, 1};
+        MfmaGemvArgs m{(const uint16_t *)g.W, xf, g.y, g.tap, yf, g.N, g.K, g.B, g.ldy, 1, g.mo};
         return launch_gemv_mfma(m, epi, st);
     };
 
@@ -558,45 +564,92 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
     }
 
     if (qpart) {
-        WireArgs wa{p, codes, scales, B, s->D};
+        WireArgs wa{p, codes, scales, B, s->D, {}};
+        if (mo) // int8 wires: the quantiser merges
+            wa.mo = *mo;
         return timed(s, KID_WIRE, st, "q8 wire", [&] { return launch_wire(wa, st); });
     }
     return TP_OK;
+}
+
+int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *lens,
+                    int32_t batch, void *wire_out, const tp_taps *taps, void *hip_stream)
+{
+    return step_impl(s, stage, x, nullptr, lens, batch, wire_out, taps, hip_stream);
+}
+
+// Validates a merge request and fills mi (x_out = residual + sum of the wires).
+static int32_t merge_request(const tp_shard *s, int32_t stage, const void *const *wires,
+                             int32_t n_wires, const float *residual, float *x_out, int32_t batch,
+                             const char *fn, MergeIn &mi)
+{
+    if (!s)
+        return fail(TP_EINVAL, "%s: null handle", fn);
+    if (s->cfg.kind != TP_LLAMA_BLOCK)
+        return fail(TP_EINVAL, "%s applies to TP_LLAMA_BLOCK shards", fn);
+    if (stage != TP_STAGE_ATTN && stage != TP_STAGE_FFN)
+        return fail(TP_EINVAL, "unknown stage %d", stage);
+    if (!wires || n_wires < 1 || n_wires > kMaxWires)
+        return fail(TP_EINVAL, "%s: n_wires %d outside [1, %d]", fn, n_wires, kMaxWires);
+    if (batch < 1 || batch > s->cfg.max_batch)
+        return fail(TP_EINVAL, "batch %d outside [1, max_batch=%d]", batch, s->cfg.max_batch);
+    if (!residual || !x_out)
+        return fail(TP_EINVAL, "%s: null residual / out", fn);
+    if (!aligned16(residual) || !aligned16(x_out))
+        return fail(TP_EALIGN, "%s: residual / out not 16-byte aligned", fn);
+    mi = MergeIn{};
+    for (int i = 0; i < n_wires; i++) {
+        if (!wires[i])
+            return fail(TP_EINVAL, "%s: wire %d is null", fn, i);
+        if (!aligned16(wires[i]))
+            return fail(TP_EALIGN, "%s: wire %d not 16-byte aligned", fn, i);
+        mi.wires[i] = wires[i];
+    }
+    mi.residual = residual;
+    mi.x_out = x_out;
+    mi.n_wires = n_wires;
+    mi.quant = (s->cfg.quant & TP_Q_PARTIALS) ? 1 : 0;
+    mi.own = -1;
+    mi.scales_off = tp_wire_scales_offset(&s->cfg, batch);
+    return TP_OK;
+}
+
+int32_t decode_merge_step(tp_shard *s, int32_t stage, const void *x, const int32_t *lens,
+                          int32_t batch, void *wire_out, const void *const *wires,
+                          int32_t n_wires, float *x_out, const tp_taps *taps, void *hip_stream)
+{
+    MergeIn mo;
+    const int32_t rc = merge_request(s, stage, wires, n_wires, (const float *)x, x_out, batch,
+                                     "decode_merge_step", mo);
+    if (rc)
+        return rc;
+    mo.own = -1;
+    for (int i = 0; i < n_wires; i++) {
+        if (wires[i] == wire_out) {
+            if (mo.own >= 0)
+                return fail(TP_EINVAL, "decode_merge_step: wire_out appears twice in wires");
+            mo.own = i;
+        }
+        // the kernel that writes x_out still reads the other wires
+        if ((const void *)x_out == wires[i])
+            return fail(TP_EINVAL, "decode_merge_step: x_out aliases wire %d", i);
+    }
+    if (mo.own < 0)
+        return fail(TP_EINVAL, "decode_merge_step: wire_out is not one of the wires");
+    return step_impl(s, stage, x, &mo, lens, batch, wire_out, taps, hip_stream);
 }
 
 int32_t merge_partials(const tp_shard *s, int32_t stage, const void *const *wires,
                        int32_t n_wires, const float *residual, float *out, int32_t batch,
                        void *hip_stream)
 {
-    if (!s)
-        return fail(TP_EINVAL, "merge_partials: null handle");
-    if (s->cfg.kind != TP_LLAMA_BLOCK)
-        return fail(TP_EINVAL, "merge_partials applies to TP_LLAMA_BLOCK shards");
-    if (stage != TP_STAGE_ATTN && stage != TP_STAGE_FFN)
-        return fail(TP_EINVAL, "unknown stage %d", stage);
-    if (!wires || n_wires < 1 || n_wires > kMaxWires)
-        return fail(TP_EINVAL, "merge_partials: n_wires %d outside [1, %d]", n_wires, kMaxWires);
-    if (batch < 1 || batch > s->cfg.max_batch)
-        return fail(TP_EINVAL, "batch %d outside [1, max_batch=%d]", batch, s->cfg.max_batch);
-    if (!residual || !out)
-        return fail(TP_EINVAL, "merge_partials: null residual / out");
-    if (!aligned16(residual) || !aligned16(out))
-        return fail(TP_EALIGN, "merge_partials: residual / out not 16-byte aligned");
     MergeArgs m{};
-    for (int i = 0; i < n_wires; i++) {
-        if (!wires[i])
-            return fail(TP_EINVAL, "merge_partials: wire %d is null", i);
-        if (!aligned16(wires[i]))
-            return fail(TP_EALIGN, "merge_partials: wire %d not 16-byte aligned", i);
-        m.wires[i] = wires[i];
-    }
-    m.residual = residual;
-    m.out = out;
-    m.n_wires = n_wires;
+    const int32_t rc = merge_request(s, stage, wires, n_wires, residual, out, batch,
+                                     "merge_partials", m.m);
+    if (rc)
+        return rc;
     m.B = batch;
     m.D = s->D;
-    m.quant = (s->cfg.quant & TP_Q_PARTIALS) ? 1 : 0;
-    m.scales_off = tp_wire_scales_offset(&s->cfg, batch);
     hipStream_t st = (hipStream_t)hip_stream;
     return timed(const_cast<tp_shard *>(s), KID_MERGE, st, "merge",
                  [&] { return launch_merge(m, st); });

@@ -65,8 +65,106 @@ __device__ __forceinline__ int q8_code(float x, float scale)
     r = fminf(fmaxf(r, -127.0f), 127.0f);
     return (int)r;
 }
-// dequantisation: one rounded fp32 multiply (never contracted into an add)
-__device__ __forceinline__ float q8_dequant(int code, float scale) { return __fmul_rn((float)code, scale); }
+// dequantisation: one rounded fp32 multiply, never contracted into the add
+// that consumes it (the contract flag is off for this product, so the
+// compiler's default fp-contract cannot fuse it into an FMA)
+__device__ __forceinline__ float q8_dequant(int code, float scale)
+{
+#pragma clang fp contract(off)
+    return (float)code * scale;
+}
+
+// ---------------------------------------------------------------- merge of shard partials
+// x = residual + d_0 + d_1 + ... in wire order, one fp32 add per element and
+// wire, d_s the (dequantised) partial carried by wire s. The merge kernel and
+// the merge fused into the kernel that produces a shard's own partial both
+// use these helpers, so their results are bitwise equal.
+struct MergeIn {
+    const void *wires[kMaxWires];
+    const float *residual; // [B][D]
+    float *x_out;          // [B][D] merged rows
+    int n_wires;           // 0: no merge
+    int quant;             // wires hold int8 codes [B][D] + fp32 block scales
+    int own;               // wire whose values the producing kernel holds (-1: none)
+    uint64_t scales_off;   // byte offset of the scales inside a wire
+};
+
+// raw load of the 4 elements at flat index i (= b * D + k, i % 4 == 0) of wire s
+__device__ __forceinline__ u32x4 wire_load(const MergeIn &m, int s, size_t i)
+{
+    const char *w = (const char *)m.wires[s];
+    if (m.quant)
+        return u32x4{*(const uint32_t *)(w + i),
+                     __float_as_uint(((const float *)(w + m.scales_off))[i / kQBlock]), 0u, 0u};
+    return *(const u32x4 *)(w + 4 * i);
+}
+
+__device__ __forceinline__ void wire_add(float4 &acc, const MergeIn &m, const u32x4 &r)
+{
+    if (m.quant) {
+        const float sc = __uint_as_float(r.y);
+        acc.x = acc.x + q8_dequant((int)(int8_t)(r.x & 0xffu), sc);
+        acc.y = acc.y + q8_dequant((int)(int8_t)((r.x >> 8) & 0xffu), sc);
+        acc.z = acc.z + q8_dequant((int)(int8_t)((r.x >> 16) & 0xffu), sc);
+        acc.w = acc.w + q8_dequant((int)(int8_t)(r.x >> 24), sc);
+    } else {
+        acc.x = acc.x + __uint_as_float(r.x);
+        acc.y = acc.y + __uint_as_float(r.y);
+        acc.z = acc.z + __uint_as_float(r.z);
+        acc.w = acc.w + __uint_as_float(r.w);
+    }
+}
+
+// One element of wire s at flat index i: (code, scale) of an int8 wire (Q)
+// or the fp32 bits.
+template <bool Q>
+__device__ __forceinline__ uint2 wire_load1(const MergeIn &m, int s, size_t i)
+{
+    const char *w = (const char *)m.wires[s];
+    if constexpr (Q)
+        return make_uint2((uint32_t)(uint8_t)w[i], __float_as_uint(((const float *)(w + m.scales_off))[i / kQBlock]));
+    else
+        return make_uint2(((const uint32_t *)w)[i], 0u);
+}
+
+template <bool Q>
+__device__ __forceinline__ float wire_value1(uint2 r)
+{
+    if constexpr (Q)
+        return q8_dequant((int)(int8_t)(r.x & 0xffu), __uint_as_float(r.y));
+    else
+        return __uint_as_float(r.x);
+}
+
+// Fused merge of one element at flat index i by the lane that holds the own
+// partial's value v: the residual and wires 0..kMO-1 are requested by
+// merge_preload1 (early, so they are in flight with the kernel's other
+// loads), later wires by merge_finish1.
+constexpr int kMO = 8;
+
+template <bool Q>
+__device__ __forceinline__ void merge_preload1(const MergeIn &m, size_t i, float &res, uint2 (&pre)[kMO])
+{
+    res = m.residual[i];
+#pragma unroll
+    for (int k = 0; k < kMO; k++)
+        if (k < m.n_wires && k != m.own)
+            pre[k] = wire_load1<Q>(m, k, i);
+}
+
+template <bool Q>
+__device__ __forceinline__ void merge_finish1(const MergeIn &m, size_t i, float v, float res,
+                                              const uint2 (&pre)[kMO])
+{
+    float acc = res;
+#pragma unroll
+    for (int k = 0; k < kMO; k++)
+        if (k < m.n_wires)
+            acc = acc + (k == m.own ? v : wire_value1<Q>(pre[k]));
+    for (int k = kMO; k < m.n_wires; k++)
+        acc = acc + (k == m.own ? v : wire_value1<Q>(wire_load1<Q>(m, k, i)));
+    m.x_out[i] = acc;
+}
 
 // ---------------------------------------------------------------- launch records
 
@@ -110,6 +208,7 @@ struct MfmaGemvArgs {
     float *tap;          // optional copy of y
     uint16_t *yf;        // EPI_SWIGLU: optional y in the fragment layout (K' = N/2)
     int N, K, B, ldy, wk; // wk = waves per 16-row tile (K split)
+    MergeIn mo;          // EPI_STORE, fp32 wires: fused merge (y is wire mo.own)
 };
 
 enum GemvEpi { EPI_STORE = 0, EPI_SWIGLU = 1 };
@@ -126,6 +225,9 @@ struct GemvArgs {
     float eps;
     int qin;
     float *xn_tap;       // [B][K]: the normalised rows, written by block 0
+    // EPI_STORE, fp32 wires: merge of the stage's partials (this kernel's
+    // output y is wire mo.own), written to mo.x_out [B][ldy]
+    MergeIn mo;
 };
 
 struct AttnArgs {
@@ -147,14 +249,12 @@ struct WireArgs {
     int8_t *codes;       // [B][D]
     float *scales;       // [B][D/32]
     int B, D;
+    MergeIn mo;          // fused merge (codes/scales are wire mo.own), n_wires 0: none
 };
 
 struct MergeArgs {
-    const void *wires[kMaxWires];
-    const float *residual;
-    float *out;
-    int n_wires, B, D, quant;
-    uint64_t scales_off;
+    MergeIn m;           // out = m.x_out
+    int B, D;
 };
 
 struct RopeArgs {

@@ -150,7 +150,7 @@ __device__ void stage_x_finish(const GemvArgs &a, XRegs &r, float *xs, float *re
     }
 }
 
-template <bool BF16, int NB, int RPW, int EPI>
+template <bool BF16, int NB, int RPW, int EPI, bool MO>
 __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
 {
     constexpr int V = BF16 ? 8 : 4; // elements per 16-byte chunk
@@ -165,6 +165,15 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
 #pragma unroll
     for (int r = 0; r < RPW; r++)
         Wr[r] = (const u32x4 *)((const char *)a.W + (size_t)(active ? row0 + r : 0) * a.K * (BF16 ? 2 : 4));
+    // fused merge (MO): the lane that stores output (row0 + r, b) preloads the
+    // residual and the other wires' elements before the weights are requested
+    float mres = 0.f;
+    uint2 mpre[kMO];
+    if constexpr (MO) {
+        const int mr = lane / NB, mb = lane % NB;
+        if (active && lane < RPW * NB && mb < a.B)
+            merge_preload1<false>(a.mo, (size_t)mb * a.ldy + row0 + mr, mres, mpre);
+    }
 
     XRegs xr;
     stage_x_issue(a, xr);
@@ -243,18 +252,19 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
                         a.y[(size_t)b * a.ldy + row0 + r] = acc[r][b];
                         if (a.tap)
                             a.tap[(size_t)b * a.ldy + row0 + r] = acc[r][b];
+                        if constexpr (MO)
+                            merge_finish1<false>(a.mo, (size_t)b * a.ldy + row0 + r, acc[r][b], mres, mpre);
                     }
                 }
         }
     }
-
 }
 
 // ---------------------------------------------------------------- general-batch path
 // Activations read from global memory (L1/L2 resident), no fused prologue /
 // epilogue: used when the batch's activation rows do not fit in LDS.
 
-template <bool BF16, int NB, int RPW, int EPI>
+template <bool BF16, int NB, int RPW, int EPI, bool MO>
 __global__ __launch_bounds__(256) void k_gemv_gx(GemvArgs a)
 {
     constexpr int V = BF16 ? 8 : 4;
@@ -263,6 +273,13 @@ __global__ __launch_bounds__(256) void k_gemv_gx(GemvArgs a)
     const int row0 = ((blockIdx.x * 256 + threadIdx.x) >> 6) * RPW;
     if (row0 >= a.N)
         return;
+    float mres = 0.f;
+    uint2 mpre[kMO];
+    if constexpr (MO) {
+        const int mr = lane / NB, mb = lane % NB;
+        if (lane < RPW * NB && mb < a.B)
+            merge_preload1<false>(a.mo, (size_t)mb * a.ldy + row0 + mr, mres, mpre);
+    }
     const int nchunk = a.K / V;
     const u32x4 *Wr[RPW];
 #pragma unroll
@@ -325,6 +342,8 @@ __global__ __launch_bounds__(256) void k_gemv_gx(GemvArgs a)
                     a.y[(size_t)b * a.ldy + row0 + r] = acc[r][b];
                     if (a.tap)
                         a.tap[(size_t)b * a.ldy + row0 + r] = acc[r][b];
+                    if constexpr (MO)
+                        merge_finish1<false>(a.mo, (size_t)b * a.ldy + row0 + r, acc[r][b], mres, mpre);
                 }
             }
     }
@@ -344,9 +363,11 @@ static hipError_t launch_lds(const GemvArgs &a, int epi, hipStream_t st)
     const dim3 grid((a.N + 4 * kRPW - 1) / (4 * kRPW)), block(256);
     const size_t sm = gemv_lds_bytes(a.B, a.K);
     if (epi == EPI_SWIGLU)
-        hipLaunchKernelGGL((k_gemv_lds<BF16, NB, kRPW, EPI_SWIGLU>), grid, block, sm, st, a);
+        hipLaunchKernelGGL((k_gemv_lds<BF16, NB, kRPW, EPI_SWIGLU, false>), grid, block, sm, st, a);
+    else if (a.mo.n_wires)
+        hipLaunchKernelGGL((k_gemv_lds<BF16, NB, kRPW, EPI_STORE, true>), grid, block, sm, st, a);
     else
-        hipLaunchKernelGGL((k_gemv_lds<BF16, NB, kRPW, EPI_STORE>), grid, block, sm, st, a);
+        hipLaunchKernelGGL((k_gemv_lds<BF16, NB, kRPW, EPI_STORE, false>), grid, block, sm, st, a);
     return hipGetLastError();
 }
 
@@ -356,9 +377,11 @@ static hipError_t launch_gx(const GemvArgs &a, int epi, hipStream_t st)
     const int waves = (a.N + kRPW - 1) / kRPW;
     const dim3 grid((waves + 3) / 4), block(256);
     if (epi == EPI_SWIGLU)
-        hipLaunchKernelGGL((k_gemv_gx<BF16, NB, kRPW, EPI_SWIGLU>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemv_gx<BF16, NB, kRPW, EPI_SWIGLU, false>), grid, block, 0, st, a);
+    else if (a.mo.n_wires)
+        hipLaunchKernelGGL((k_gemv_gx<BF16, NB, kRPW, EPI_STORE, true>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((k_gemv_gx<BF16, NB, kRPW, EPI_STORE>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemv_gx<BF16, NB, kRPW, EPI_STORE, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
@@ -381,7 +404,8 @@ static hipError_t launch_t(const GemvArgs &a, int epi, hipStream_t st)
 
 // Host-checked preconditions: N a multiple of 8, K a
 // multiple of the 16-byte vector (of 32 with qin), rows 16-byte aligned,
-// 1 <= B <= 16.
+// 1 <= B <= 16; a fused merge (mo.n_wires > 0) only with EPI_STORE and fp32
+// wires.
 hipError_t launch_gemv(const GemvArgs &a, int w_bf16, int epi, hipStream_t st)
 {
     return w_bf16 ? launch_t<true>(a, epi, st) : launch_t<false>(a, epi, st);

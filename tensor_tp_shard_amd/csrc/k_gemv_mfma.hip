@@ -72,6 +72,19 @@ __global__ __launch_bounds__(64 * kMaxWk) void k_gemv_mfma(MfmaGemvArgs a)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xl[p][s]), acc, 0, 0, 0);
                 }
     }
+    // fused merge (EPI_STORE, fp32 wires): wave 0 requests the residual and
+    // the other wires' elements of its outputs before the reduction
+    constexpr int kM = EPI == EPI_STORE ? kMO : 1;
+    const bool mlane = EPI == EPI_STORE && a.mo.n_wires && wv == 0 && (lane & 15) < a.B;
+    const size_t mi = (size_t)(lane & 15) * a.ldy + n0 + 4 * q;
+    float4 mres = make_float4(0.f, 0.f, 0.f, 0.f), mpre[kM];
+    if (mlane) {
+        mres = *(const float4 *)(a.mo.residual + mi);
+#pragma unroll
+        for (int k = 0; k < kM; k++)
+            if (k < a.mo.n_wires && k != a.mo.own)
+                mpre[k] = *(const float4 *)((const float *)a.mo.wires[k] + mi);
+    }
     red[wv][lane] = acc;
     __syncthreads();
     if (wv != 0)
@@ -101,6 +114,26 @@ __global__ __launch_bounds__(64 * kMaxWk) void k_gemv_mfma(MfmaGemvArgs a)
         *(float4 *)(a.y + (size_t)b * a.ldy + n) = v;
         if (a.tap)
             *(float4 *)(a.tap + (size_t)b * a.ldy + n) = v;
+        if (mlane) {
+            float4 m = mres;
+#pragma unroll
+            for (int k = 0; k < kM; k++)
+                if (k < a.mo.n_wires) {
+                    const float4 d = k == a.mo.own ? v : mpre[k];
+                    m.x = m.x + d.x;
+                    m.y = m.y + d.y;
+                    m.z = m.z + d.z;
+                    m.w = m.w + d.w;
+                }
+            for (int k = kM; k < a.mo.n_wires; k++) {
+                const float4 d = k == a.mo.own ? v : *(const float4 *)((const float *)a.mo.wires[k] + mi);
+                m.x = m.x + d.x;
+                m.y = m.y + d.y;
+                m.z = m.z + d.z;
+                m.w = m.w + d.w;
+            }
+            *(float4 *)(a.mo.x_out + mi) = m;
+        }
     }
 }
 

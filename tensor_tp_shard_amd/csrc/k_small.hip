@@ -131,19 +131,30 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a)
 
 // One half-wave per block of 32 consecutive elements of p (rows are
 // D-contiguous and D % 32 == 0, so block j of the flat array is block
-// j % (D/32) of row j / (D/32)).
+// j % (D/32) of row j / (D/32)). With a fused merge, each lane also writes
+// x_out = residual + sum of the wires in order, its own wire's value being
+// the dequantised code it just wrote (the other wires' elements are requested
+// together with p). The wires of a quantised exchange are all int8.
 __global__ __launch_bounds__(256) void k_wire(WireArgs a)
 {
     const int blk = blockIdx.x * 8 + (threadIdx.x >> 5);
     const int nblk = a.B * (a.D / kQBlock);
     const int lane = threadIdx.x & 31;
     const bool ok = blk < nblk;
-    const float v = ok ? a.p[(size_t)blk * kQBlock + lane] : 0.f;
+    const size_t i = (size_t)blk * kQBlock + lane;
+    float mres = 0.f;
+    uint2 mpre[kMO];
+    if (ok && a.mo.n_wires)
+        merge_preload1<true>(a.mo, i, mres, mpre);
+    const float v = ok ? a.p[i] : 0.f;
     const float s = q8_scale(group_max<32>(fabsf(v)));
     if (ok) {
-        a.codes[(size_t)blk * kQBlock + lane] = (int8_t)q8_code(v, s);
+        const int c = q8_code(v, s);
+        a.codes[i] = (int8_t)c;
         if (lane == 0)
             a.scales[blk] = s;
+        if (a.mo.n_wires)
+            merge_finish1<true>(a.mo, i, q8_dequant(c, s), mres, mpre);
     }
 }
 
@@ -152,50 +163,24 @@ __global__ __launch_bounds__(256) void k_wire(WireArgs a)
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a)
 {
     constexpr int U = 8;
+    const MergeIn &m = a.m;
     const size_t n = (size_t)a.B * a.D;
     const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= n)
         return;
-    float4 acc = *(const float4 *)(a.residual + i);
-    for (int s0 = 0; s0 < a.n_wires; s0 += U) {
-        if (a.quant) {
-            char4 c[U];
-            float sc[U];
+    float4 acc = *(const float4 *)(m.residual + i);
+    for (int s0 = 0; s0 < m.n_wires; s0 += U) {
+        u32x4 r[U];
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                if (s0 + u < a.n_wires) {
-                    const char *w = (const char *)a.wires[s0 + u];
-                    c[u] = *(const char4 *)(w + i);
-                    sc[u] = ((const float *)(w + a.scales_off))[i / kQBlock];
-                }
-            }
+        for (int u = 0; u < U; u++)
+            if (s0 + u < m.n_wires)
+                r[u] = wire_load(m, s0 + u, i);
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                if (s0 + u < a.n_wires) {
-                    acc.x = acc.x + q8_dequant(c[u].x, sc[u]);
-                    acc.y = acc.y + q8_dequant(c[u].y, sc[u]);
-                    acc.z = acc.z + q8_dequant(c[u].z, sc[u]);
-                    acc.w = acc.w + q8_dequant(c[u].w, sc[u]);
-                }
-            }
-        } else {
-            float4 f[U];
-#pragma unroll
-            for (int u = 0; u < U; u++)
-                if (s0 + u < a.n_wires)
-                    f[u] = *(const float4 *)((const char *)a.wires[s0 + u] + i * 4);
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                if (s0 + u < a.n_wires) {
-                    acc.x = acc.x + f[u].x;
-                    acc.y = acc.y + f[u].y;
-                    acc.z = acc.z + f[u].z;
-                    acc.w = acc.w + f[u].w;
-                }
-            }
-        }
+        for (int u = 0; u < U; u++)
+            if (s0 + u < m.n_wires)
+                wire_add(acc, m, r[u]);
     }
-    *(float4 *)(a.out + i) = acc;
+    *(float4 *)(m.x_out + i) = acc;
 }
 
 // cos / sin of p * theta^(-2i/hd) in fp64, stored fp32: [max_ctx][hd/2].
@@ -233,6 +218,8 @@ hipError_t launch_wire(const WireArgs &a, hipStream_t st)
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st)
 {
     const size_t n4 = (size_t)a.B * a.D / 4;
+    if (n4 == 0)
+        return hipSuccess;
     hipLaunchKernelGGL(k_merge, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a);
     return hipGetLastError();
 }

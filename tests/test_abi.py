@@ -100,7 +100,38 @@ def test_order_alignment_and_device_errors():
     with pytest.raises(tp.TpError) as e:
         tp.kernel_timing_arm(h, 99)
     assert e.value.status == tp.TP_EINVAL
+    # decode_merge_step: the merge's checks, wire_out exactly once among the
+    # wires, x_out not a wire; then the stage's (no weights loaded yet)
+    other, own = fake + 0x100000, fake + 0x200000
+    dms = tp.decode_merge_step
+    with pytest.raises(tp.TpError) as e:
+        dms(h, tp.TP_STAGE_FFN, fake, None, 1, own, [], other, stream=0)
+    assert e.value.status == tp.TP_EINVAL
+    with pytest.raises(tp.TpError) as e:
+        dms(h, tp.TP_STAGE_FFN, fake, None, 1, own, [own, fake + 8], other, stream=0)
+    assert e.value.status == tp.TP_EALIGN
+    with pytest.raises(tp.TpError) as e:
+        dms(h, tp.TP_STAGE_FFN, fake, None, 1, own, [other, fake], fake + 0x300000, stream=0)
+    assert e.value.status == tp.TP_EINVAL and "not one of the wires" in str(e.value)
+    with pytest.raises(tp.TpError) as e:
+        dms(h, tp.TP_STAGE_FFN, fake, None, 1, own, [own, other, own], fake, stream=0)
+    assert e.value.status == tp.TP_EINVAL and "twice" in str(e.value)
+    with pytest.raises(tp.TpError) as e:
+        dms(h, tp.TP_STAGE_FFN, fake, None, 1, own, [own, other], other, stream=0)
+    assert e.value.status == tp.TP_EINVAL and "aliases wire 1" in str(e.value)
+    with pytest.raises(tp.TpError) as e:
+        dms(h, tp.TP_STAGE_FFN, fake, None, 2, own, [own, other], fake, stream=0)
+    assert e.value.status == tp.TP_EINVAL  # batch above max_batch
+    with pytest.raises(tp.TpError) as e:  # x_out may alias x; then: no weights yet
+        dms(h, tp.TP_STAGE_FFN, fake, None, 1, own, [own, other], fake, stream=0)
+    assert e.value.status == tp.TP_ESTATE
     tp.destroy_shard(h)
+    h2, _ = tp.init_shard(tp.make_config(kind=tp.TP_FFN_2D, dim=576, ffn_hidden=576,
+                                         max_batch=8, w_dtype=tp.TP_BF16))
+    with pytest.raises(tp.TpError) as e:
+        dms(h2, tp.TP_STAGE_FFN, fake, None, 1, own, [own], other, stream=0)
+    assert e.value.status == tp.TP_EINVAL and "TP_LLAMA_BLOCK" in str(e.value)
+    tp.destroy_shard(h2)
 
 
 def test_null_arguments_and_status_strings():
