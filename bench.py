@@ -18,10 +18,12 @@ timed region starts.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
 import time
+from typing import Optional
 
 import numpy as np
 
@@ -33,6 +35,56 @@ import synth  # noqa: E402
 METRIC = "decode layer-steps/s per TP shard + achieved HBM GB/s (% peak), 7B/70B shapes"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+
+
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def measured_traffic(profile: str, sources) -> Optional[int]:
+    """HBM bytes per launch of a kernel from its committed counter summary
+    (profiles/<profile>: FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a
+    copy of known size), or None when the summary is missing or the kernel's
+    sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, profile)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.split(":", 1)[0].strip() in ("traffic_bytes_per_launch",
+                                                                  "source_sha256"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if "traffic_bytes_per_launch" not in fields or "source_sha256" not in fields:
+        return None
+    if fields["source_sha256"] != sources_sha256(sources):
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
+def sources_sha256(sources) -> str:
+    h = hashlib.sha256()
+    for rel in sources:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+GEMV_SOURCES = ("tensor_tp_shard_amd/csrc/k_gemv.hip", "tensor_tp_shard_amd/csrc/common.h")
+FFN2D_SOURCES = ("tensor_tp_shard_amd/csrc/k_ffn2d.hip", "tensor_tp_shard_amd/csrc/common.h")
+
+
+def calib_copy(mib: int):
+    """A plain device-to-device copy of `mib` MiB (fp32, torch's copy kernel),
+    three times: the reference for scaling the HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n * 4, "copies": 3}), flush=True)
 
 
 def log(msg):
@@ -203,7 +255,8 @@ def run_llama(args, w):
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {"kernel": "gemv_w13_swiglu", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": int(w13bytes),
+                     "traffic": measured_traffic(f"traffic_gemv_w13_swiglu_{w.name}.md", GEMV_SOURCES),
+                     "bytes_per_launch": int(w13bytes),
                      "avg_launch_us": round(k_ms * 1e3, 3), "launches": n},
     }
     if not args.no_cpu_baseline:
@@ -311,7 +364,8 @@ def run_ffn2d(args, w):
         "mfma_frac": round(flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "roofline": {"kernel": "ffn2d_up", "bound": "mfma", "achieved": round(ach, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(f"traffic_ffn2d_up_{w.name}.md", FFN2D_SOURCES),
                      "flops_per_launch": up_flops, "avg_launch_us": round(k_ms * 1e3, 3),
                      "launches": n},
     }
@@ -340,6 +394,8 @@ def main():
     ap.add_argument("--merge", default="fused", choices=["fused", "separate"],
                     help="merge of a stage's partials by the kernel that produces rank 0's own "
                          "partial (decode_merge_step) or as a kernel of its own (merge_partials)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run a device copy of this many MiB (counter calibration) and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
@@ -351,6 +407,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calib_copy_mib:
+        calib_copy(args.calib_copy_mib)
+        return
     w = synth.get(args.workload)
     res = run_ffn2d(args, w) if w.kind == "ffn2d" else run_llama(args, w)
     print(json.dumps(res), flush=True)

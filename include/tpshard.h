@@ -210,10 +210,11 @@ uint64_t tp_wire_scales_offset(const tp_config *cfg, int32_t batch);
 int32_t tp_read_error_word(tp_shard *s, uint32_t *word, int32_t clear, void *hip_stream);
 
 /*
- * Kernel timing probe: while armed, the library records a HIP event pair on
- * the launch stream around every launch of kernel `kernel_id` (see
- * tp_kernel_name) it enqueues, and accumulates the elapsed time of
- * completed pairs. tp_kernel_timing_arm(s, -1) disarms. Reading synchronises
+ * Kernel timing probe: while armed, the library records a HIP event pair
+ * (created with hipEventDisableSystemFence, so the pair adds well under a
+ * microsecond to what it brackets) on the launch stream around every launch
+ * of kernel `kernel_id` (see tp_kernel_name) it enqueues, and accumulates the
+ * elapsed time of completed pairs. tp_kernel_timing_arm(s, -1) disarms. Reading synchronises
  * on the recorded events. Host-side HIP events only; no device memory.
  */
 int32_t tp_kernel_timing_arm(tp_shard *s, int32_t kernel_id);

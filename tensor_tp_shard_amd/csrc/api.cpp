@@ -237,7 +237,11 @@ int32_t timed(tp_shard *s, int kid, hipStream_t st, const char *what, F &&launch
     if (arm) {
         if (s->ev_used == s->ev_pool.size()) {
             hipEvent_t a, b;
-            if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess)
+            // no system-scope fence at the record: the pair then brackets the
+            // kernel within ~0.5 us of its execution time (a default event adds
+            // a few microseconds of its own)
+            if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess ||
+                hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess)
                 return fail(TP_EHIP, "hipEventCreate failed");
             s->ev_pool.emplace_back(a, b);
         }
