@@ -26,11 +26,12 @@
 //  softmax: one wave per head: chunk max m, p = exp(s - m), l = sum p
 //  values : hd/4 threads per row, 4 dims each, rows split into phases;
 //           phases summed in fixed order through LDS
-//  combine: a second kernel (one workgroup per (b, g)) merges the chunk
-//           records in chunk order: att = sum_c o_c e^(m_c - M) / sum_c l_c
-//           e^(m_c - M). A separate launch is cheaper here than publishing
-//           through agent-scope fences, which on this chip write back and
-//           invalidate a whole XCD L2 per workgroup.
+//  combine: a second kernel (one workgroup per (b, q head)) merges the
+//           chunk records in chunk order: att = sum_c o_c e^(m_c - M) /
+//           sum_c l_c e^(m_c - M). A separate launch is cheaper here than
+//           publishing through agent-scope fences (which on this chip write
+//           back and invalidate a whole XCD L2 per workgroup) or than a last-
+//           arriving chunk workgroup doing it (measured slower).
 #include "common.h"
 
 namespace tps {
@@ -309,123 +310,116 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
 
 }
 
-// Combine of the chunk partials of one (sequence b, kv head g): the G query
-// heads' outputs att = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M), chunks
-// summed in chunk order. All (m, l) and the first kCU chunks of every output
-// quad are loaded in one batch before any arithmetic.
+// Combine of the chunk partials of one (sequence b, query head h): its output
+// att = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M), chunks summed in chunk
+// order. The (m, l) of the first 64 chunks (wave 0) and the first kCU chunks
+// of every output quad are loaded in one batch before any arithmetic; wave 0
+// then forms M, the weights e^(m_c - M) and l across its lanes.
 constexpr int kCombThreads = 512;
 
 __global__ __launch_bounds__(kCombThreads) void k_combine(AttnArgs a)
 {
     extern __shared__ float smem[];
-    const int hd = a.hd, G = a.G, g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int hd = a.hd, h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int L = a.lens[b];
+    const size_t ob = (size_t)b * a.Hq_s * hd + (size_t)h * hd;
     if (L < 0 || L >= a.max_ctx) { // skipped sequence: its attention output is 0
-        for (int i = tid; i < G * hd; i += kCombThreads) {
-            const size_t o = (size_t)b * a.Hq_s * hd + (size_t)g * G * hd + i;
-            a.att[o] = 0.f;
+        for (int i = tid; i < hd; i += kCombThreads) {
+            a.att[ob + i] = 0.f;
             if (a.tap_att)
-                a.tap_att[o] = 0.f;
+                a.tap_att[ob + i] = 0.f;
             if (a.att_xf)
-                xf_store(a.att_xf, b, g * G * hd + i, 0.f);
+                xf_store(a.att_xf, b, h * hd + i, 0.f);
         }
         return;
     }
     const int nch = L / kChunk + 1;
-    const int ws = a.n_chunks;
-    const size_t rec_stride = (size_t)a.n_chunks * (hd + 4);
-    const float *rec0 = a.part + ((size_t)b * a.Hq_s + (size_t)g * G) * rec_stride;
-    float *wts = smem;                                // [G][n_chunks] e^(m_c - M)
-    float *inv_l = wts + G * ws;                      // [G]
-    float *osum = smem + ((G * ws + 8 + 3) & ~3);     // [phases][G][hd]
+    const float *rec = a.part + ((size_t)b * a.Hq_s + h) * (size_t)a.n_chunks * (hd + 4);
+    float *wts = smem;                                // [n_chunks] e^(m_c - M)
+    float *inv_l = wts + a.n_chunks;                  // [1]
+    float *osum = smem + ((a.n_chunks + 4 + 3) & ~3); // [phases][hd]
     const int w = tid >> 6, lane = tid & 63;
-    // 1) (m_c, l_c) of head w's first 64 chunks (wave w < G), then the first
-    //    kCU chunk outputs of every quad: all issued before anything waits
     float2 ml0 = make_float2(-INFINITY, 0.f);
-    if (w < G && lane < nch)
-        ml0 = *(const float2 *)(rec0 + w * rec_stride + (size_t)lane * (hd + 4));
-    const int quads = G * (hd / 4);
-    const int cph = kCombThreads / quads;             // chunk phases (quads <= 256)
+    if (w == 0 && lane < nch)
+        ml0 = *(const float2 *)(rec + (size_t)lane * (hd + 4));
+    const int quads = hd / 4;
+    const int cph = kCombThreads / quads;             // chunk phases (quads <= 32)
     constexpr int kCU = 16;                           // chunks per phase loaded together
-    const int qd = tid % quads, cp = tid / quads;
-    const bool qact = cp < cph;
-    const int j = qd / (hd / 4), d = (qd % (hd / 4)) * 4;
-    const float *rj = rec0 + j * rec_stride + 4 + d;
+    const int cp = tid / quads, d = (tid % quads) * 4;
+    const bool qact = cp < cph; // hd = 48: 512 is not a multiple of 12 quads
+    const float *rd = rec + 4 + d;
     float4 v[kCU];
 #pragma unroll
     for (int u = 0; u < kCU; u++) {
         const int cc = cp + u * cph;
         if (qact && cc < nch)
-            v[u] = *(const float4 *)(rj + (size_t)cc * (hd + 4));
+            v[u] = *(const float4 *)(rd + (size_t)cc * (hd + 4));
     }
-    // 2) statistics of head w across the wave's lanes: M = max_c m_c,
-    //    w_c = e^(m_c - M), l = sum_c w_c l_c (lane partials, then the butterfly)
-    if (w < G) {
-        const float *rw = rec0 + w * rec_stride;
+    if (w == 0) {
         float m = ml0.x;
         for (int cc = lane + 64; cc < nch; cc += 64) // sequences longer than 64 chunks
-            m = fmaxf(m, rw[(size_t)cc * (hd + 4)]);
+            m = fmaxf(m, rec[(size_t)cc * (hd + 4)]);
         const float M = group_max<64>(m);
         float l = 0.f;
         if (lane < nch) {
             const float e = expf(ml0.x - M);
-            wts[w * ws + lane] = e;
+            wts[lane] = e;
             l = e * ml0.y;
         }
         for (int cc = lane + 64; cc < nch; cc += 64) {
-            const float2 q = *(const float2 *)(rw + (size_t)cc * (hd + 4));
+            const float2 q = *(const float2 *)(rec + (size_t)cc * (hd + 4));
             const float e = expf(q.x - M);
-            wts[w * ws + cc] = e;
+            wts[cc] = e;
             l += e * q.y;
         }
         l = group_sum<64>(l);
         if (lane == 0)
-            inv_l[w] = 1.0f / l;
+            inv_l[0] = 1.0f / l;
     }
     __syncthreads();
-    if (qact) {
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int c0 = cp; c0 < nch; c0 += cph * kCU) {
-            if (c0 != cp) { // chunks past the first batch (long sequences)
-#pragma unroll
-                for (int u = 0; u < kCU; u++) {
-                    const int cc = c0 + u * cph;
-                    if (cc < nch)
-                        v[u] = *(const float4 *)(rj + (size_t)cc * (hd + 4));
-                }
-            }
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c0 = cp; qact && c0 < nch; c0 += cph * kCU) {
+        if (c0 != cp) { // chunks past the first batch (long sequences)
 #pragma unroll
             for (int u = 0; u < kCU; u++) {
                 const int cc = c0 + u * cph;
-                if (cc < nch) {
-                    const float wv = wts[j * ws + cc];
-                    o.x += wv * v[u].x;
-                    o.y += wv * v[u].y;
-                    o.z += wv * v[u].z;
-                    o.w += wv * v[u].w;
-                }
+                if (cc < nch)
+                    v[u] = *(const float4 *)(rd + (size_t)cc * (hd + 4));
             }
         }
-        *(float4 *)(osum + (size_t)cp * G * hd + j * hd + d) = o;
+#pragma unroll
+        for (int u = 0; u < kCU; u++) {
+            const int cc = c0 + u * cph;
+            if (cc < nch) {
+                const float wv = wts[cc];
+                o.x += wv * v[u].x;
+                o.y += wv * v[u].y;
+                o.z += wv * v[u].z;
+                o.w += wv * v[u].w;
+            }
+        }
     }
+    if (qact)
+        *(float4 *)(osum + (size_t)cp * hd + d) = o;
     __syncthreads();
-    for (int i = tid; i < G * hd; i += kCombThreads) {
-        float o = 0.f;
+    for (int i = tid; i < hd; i += kCombThreads) {
+        float t = 0.f;
         for (int p = 0; p < cph; p++)
-            o += osum[(size_t)p * G * hd + i];
-        const size_t oi = (size_t)b * a.Hq_s * hd + (size_t)g * G * hd + i;
-        a.att[oi] = o * inv_l[i / hd];
+            t += osum[(size_t)p * hd + i];
+        const float r = t * inv_l[0];
+        a.att[ob + i] = r;
         if (a.tap_att)
-            a.tap_att[oi] = o * inv_l[i / hd];
+            a.tap_att[ob + i] = r;
         if (a.att_xf)
-            xf_store(a.att_xf, b, g * G * hd + i, o * inv_l[i / hd]);
+            xf_store(a.att_xf, b, h * hd + i, r);
     }
 }
 
 static size_t combine_smem_bytes(int G, int hd, int n_chunks)
 {
-    const int cph = kCombThreads / (G * (hd / 4));
-    return (((size_t)G * n_chunks + 8 + 3) / 4 * 4 + (size_t)cph * G * hd) * sizeof(float);
+    (void)G;
+    const int cph = kCombThreads / (hd / 4);
+    return (((size_t)n_chunks + 4 + 3) / 4 * 4 + (size_t)cph * hd) * sizeof(float);
 }
 
 template <bool KBF16, int HD>
@@ -469,7 +463,7 @@ hipError_t launch_attn(const AttnArgs &a, int kv_bf16, int B, hipStream_t st)
     const hipError_t e = kv_bf16 ? launch_attn_t<true>(a, B, st) : launch_attn_t<false>(a, B, st);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(k_combine, dim3(a.Hkv_s, B), dim3(kCombThreads),
+    hipLaunchKernelGGL(k_combine, dim3(a.Hq_s, B), dim3(kCombThreads),
                        combine_smem_bytes(a.G, a.hd, a.n_chunks), st, a);
     return hipGetLastError();
 }

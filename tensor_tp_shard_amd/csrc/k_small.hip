@@ -15,37 +15,72 @@
 
 namespace tps {
 
-// One 256-thread block per row; a thread owns runs of 8 consecutive
-// elements (two float4), and all of a row's loads (x and gains, up to 4 runs
-// per thread for D <= 8192) are issued before any is used. Sum of squares in
-// fp32 (wave butterflies, then the 4 wave sums in order), y = g * x * r with
-// r = 1 / sqrt(ms + eps). With quant set, each block of 32 elements (4
-// consecutive threads) is quantised and dequantised in place (the receiver of
-// the broadcast sees these values). Optionally the row is also written in the
-// MFMA fragment layout (8 consecutive k are 16 contiguous bytes there).
+// One block of kNormThreads (1024) threads per row; a thread owns runs of 8
+// consecutive elements (two float4), up to kNormRuns runs (D <= 32768 in one
+// pass: all of the row's x and gain loads are issued before any is used and
+// the row stays in registers). Longer rows take further passes, re-reading x.
+// Sum of squares in fp32 (wave butterflies, then the 16 wave sums in order),
+// y = g * x * r with r = 1 / sqrt(ms + eps). With quant set, each block of 32
+// elements (4 consecutive threads) is quantised and dequantised in place (the
+// receiver of the broadcast sees these values). Optionally the row is also
+// written in the MFMA fragment layout (8 consecutive k are 16 contiguous bytes
+// there).
 constexpr int kNormRuns = 4;
+constexpr int kNormThreads = 1024;
+constexpr int kNormWaves = kNormThreads / 64;
 
-__global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a)
+__device__ __forceinline__ void norm_store_run(const NormArgs &a, int b, int run, float (&e)[8], float4 *y,
+                                               float4 *tap)
+{
+    const float4 lo4 = make_float4(e[0], e[1], e[2], e[3]);
+    const float4 hi4 = make_float4(e[4], e[5], e[6], e[7]);
+    y[2 * run] = lo4;
+    y[2 * run + 1] = hi4;
+    if (tap) {
+        tap[2 * run] = lo4;
+        tap[2 * run + 1] = hi4;
+    }
+    if (a.xf) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const uint16_t h0 = f32_to_bf16(e[2 * t]), h1 = f32_to_bf16(e[2 * t + 1]);
+            const uint16_t l0 = f32_to_bf16(e[2 * t] - bf16_to_f32(h0));
+            const uint16_t l1 = f32_to_bf16(e[2 * t + 1] - bf16_to_f32(h1));
+            hw[t] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lw[t] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        *(u32x4 *)(a.xf + xf_index(b, 8 * run, 0)) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+        *(u32x4 *)(a.xf + xf_index(b, 8 * run, 1)) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+    }
+}
+
+__global__ __launch_bounds__(kNormThreads) void k_rmsnorm(NormArgs a)
 {
     const int b = blockIdx.x, tid = threadIdx.x;
     const int nruns = a.D / 8;
+    const bool one_pass = nruns <= kNormThreads * kNormRuns;
     const float4 *x = (const float4 *)(a.x + (size_t)b * a.D);
     const float4 *g = (const float4 *)a.g;
-    __shared__ float red[4];
+    __shared__ float red[kNormWaves];
+    float4 v[kNormRuns][2], gv[kNormRuns][2];
     float ss = 0.f;
-    for (int r0 = 0; r0 < nruns; r0 += 256 * kNormRuns) { // one pass for D <= 8192
-        float4 v[kNormRuns][2];
+    for (int r0 = 0; r0 < nruns; r0 += kNormThreads * kNormRuns) {
 #pragma unroll
         for (int i = 0; i < kNormRuns; i++) {
-            const int run = r0 + tid + 256 * i;
+            const int run = r0 + tid + kNormThreads * i;
             if (run < nruns) {
                 v[i][0] = x[2 * run];
                 v[i][1] = x[2 * run + 1];
+                if (one_pass) {
+                    gv[i][0] = g[2 * run];
+                    gv[i][1] = g[2 * run + 1];
+                }
             }
         }
 #pragma unroll
         for (int i = 0; i < kNormRuns; i++) {
-            const int run = r0 + tid + 256 * i;
+            const int run = r0 + tid + kNormThreads * i;
             if (run < nruns)
 #pragma unroll
                 for (int h = 0; h < 2; h++)
@@ -57,35 +92,39 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a)
     if ((tid & 63) == 0)
         red[tid >> 6] = ss;
     __syncthreads();
-    ss = (red[0] + red[1]) + (red[2] + red[3]);
+    ss = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNormWaves; w++)
+        ss += red[w];
     const float r = 1.0f / sqrtf(ss / (float)a.D + a.eps);
     float4 *y = (float4 *)(a.xn + (size_t)b * a.D);
     float4 *tap = a.tap ? (float4 *)(a.tap + (size_t)b * a.D) : nullptr;
-    for (int r0 = 0; r0 < nruns; r0 += 256 * kNormRuns) {
-        float4 xv[kNormRuns][2], gv[kNormRuns][2];
+    for (int r0 = 0; r0 < nruns; r0 += kNormThreads * kNormRuns) {
+        if (!one_pass) {
 #pragma unroll
-        for (int i = 0; i < kNormRuns; i++) {
-            const int run = r0 + tid + 256 * i;
-            if (run < nruns) {
-                xv[i][0] = x[2 * run];
-                xv[i][1] = x[2 * run + 1];
-                gv[i][0] = g[2 * run];
-                gv[i][1] = g[2 * run + 1];
+            for (int i = 0; i < kNormRuns; i++) {
+                const int run = r0 + tid + kNormThreads * i;
+                if (run < nruns) {
+                    v[i][0] = x[2 * run];
+                    v[i][1] = x[2 * run + 1];
+                    gv[i][0] = g[2 * run];
+                    gv[i][1] = g[2 * run + 1];
+                }
             }
         }
 #pragma unroll
         for (int i = 0; i < kNormRuns; i++) {
-            const int run = r0 + tid + 256 * i;
-            if (r0 + 256 * i >= nruns)
+            const int run = r0 + tid + kNormThreads * i;
+            if (r0 + kNormThreads * i >= nruns)
                 break; // uniform: no thread of this pass holds a run
             float e[8];
             if (run < nruns) {
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
-                    e[4 * h + 0] = gv[i][h].x * xv[i][h].x * r;
-                    e[4 * h + 1] = gv[i][h].y * xv[i][h].y * r;
-                    e[4 * h + 2] = gv[i][h].z * xv[i][h].z * r;
-                    e[4 * h + 3] = gv[i][h].w * xv[i][h].w * r;
+                    e[4 * h + 0] = gv[i][h].x * v[i][h].x * r;
+                    e[4 * h + 1] = gv[i][h].y * v[i][h].y * r;
+                    e[4 * h + 2] = gv[i][h].z * v[i][h].z * r;
+                    e[4 * h + 3] = gv[i][h].w * v[i][h].w * r;
                 }
             } else {
 #pragma unroll
@@ -102,29 +141,8 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a)
                 for (int t = 0; t < 8; t++)
                     e[t] = q8_dequant(q8_code(e[t], sc), sc);
             }
-            if (run < nruns) {
-                const float4 lo4 = make_float4(e[0], e[1], e[2], e[3]);
-                const float4 hi4 = make_float4(e[4], e[5], e[6], e[7]);
-                y[2 * run] = lo4;
-                y[2 * run + 1] = hi4;
-                if (tap) {
-                    tap[2 * run] = lo4;
-                    tap[2 * run + 1] = hi4;
-                }
-                if (a.xf) {
-                    uint32_t hw[4], lw[4];
-#pragma unroll
-                    for (int t = 0; t < 4; t++) {
-                        const uint16_t h0 = f32_to_bf16(e[2 * t]), h1 = f32_to_bf16(e[2 * t + 1]);
-                        const uint16_t l0 = f32_to_bf16(e[2 * t] - bf16_to_f32(h0));
-                        const uint16_t l1 = f32_to_bf16(e[2 * t + 1] - bf16_to_f32(h1));
-                        hw[t] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                        lw[t] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-                    }
-                    *(u32x4 *)(a.xf + xf_index(b, 8 * run, 0)) = u32x4{hw[0], hw[1], hw[2], hw[3]};
-                    *(u32x4 *)(a.xf + xf_index(b, 8 * run, 1)) = u32x4{lw[0], lw[1], lw[2], lw[3]};
-                }
-            }
+            if (run < nruns)
+                norm_store_run(a, b, run, e, y, tap);
         }
     }
 }
@@ -204,7 +222,7 @@ __global__ void k_clear_u32(unsigned *p, int n)
 
 hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_rmsnorm, dim3(a.B), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_rmsnorm, dim3(a.B), dim3(kNormThreads), 0, st, a);
     return hipGetLastError();
 }
 
