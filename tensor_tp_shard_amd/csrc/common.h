@@ -183,12 +183,15 @@ struct NormArgs {
 // Activations of a batch of <= 16 rows, K a multiple of 128, as the B operand
 // of v_mfma_f32_16x16x32_bf16: the fp32 value v is split into hi = bf16(v)
 // and lo = bf16(v - hi) (hi + lo carries ~16 mantissa bits). Element (b, k)
-// of part hl sits at [k/128][hl][s][q][b][e] with k % 128 = 32q + 8s + e, so
+// of part hl sits at [k/128][hl][s][q][b][e] with k % 128 = 32s + 8q + e, so
 // lane (q, b) of a wave reads its 8 values for step s as 16 contiguous bytes
-// and a wave reads 1 KiB contiguous per step.
+// and a wave reads 1 KiB contiguous per step. The same k-slot order on the
+// weight side makes the 4 lanes that share a weight row read 64 contiguous
+// bytes of it per step (32s + 8q), half a 128-byte line, instead of 16
+// bytes from each of 4 places (measured: the 70B up-projection 48 -> 41 us).
 __host__ __device__ inline size_t xf_index(int b, int k, int hl)
 {
-    const int j = k >> 7, r = k & 127, q = r >> 5, s = (r >> 3) & 3, e = k & 7;
+    const int j = k >> 7, r = k & 127, q = (r >> 3) & 3, s = r >> 5, e = k & 7;
     return ((((((size_t)j * 2 + hl) * 4 + s) * 4 + q) * 16 + b) << 3) + e;
 }
 __host__ __device__ inline size_t xf_elems(int K) { return (size_t)K * 32; } // 16 rows x K x {hi, lo}

@@ -19,10 +19,10 @@
 // (RMSNorm, attention combine, SwiGLU).
 //
 // Work split: one workgroup per 16-row tile, its wk waves split K in
-// 128-wide blocks; a wave keeps two blocks of weights (16-byte nontemporal
-// loads, 64 contiguous bytes per lane per block) and their activation
-// fragments in flight, then the waves' 16x16 accumulators are summed in wave
-// order through LDS. Epilogues: store, or SwiGLU of the interleaved
+// 128-wide blocks (about 8 per wave); a wave keeps two blocks of weights
+// (16-byte nontemporal loads; per load instruction the 4 lanes of a row read
+// 64 contiguous bytes of it) and their activation fragments in flight, then
+// the waves' 16x16 accumulators are summed in wave order through LDS. Epilogues: store, or SwiGLU of the interleaved
 // (W1_f, W3_f) rows (accumulator rows 4q..4q+3 of a lane are two pairs).
 #include "common.h"
 
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(64 * kMaxWk) void k_gemv_mfma(MfmaGemvArgs a)
     const int nb = a.K >> 7;
     const int per = (nb + a.wk - 1) / a.wk;
     const int j0 = wv * per, j1 = min(nb, j0 + per);
-    const u32x4 *wrow = (const u32x4 *)(a.W + (size_t)(n0 + r) * a.K + 32 * q);
+    const u32x4 *wrow = (const u32x4 *)(a.W + (size_t)(n0 + r) * a.K + 8 * q);
     const u32x4 *xf = (const u32x4 *)a.xf; // 16-byte units: [j][hl][s][q][b]
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j = j0; j < j1; j += P) {
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(64 * kMaxWk) void k_gemv_mfma(MfmaGemvArgs a)
             if (j + p < j1)
 #pragma unroll
                 for (int s = 0; s < 4; s++)
-                    w[p][s] = __builtin_nontemporal_load(wrow + (size_t)(j + p) * 16 + s);
+                    w[p][s] = __builtin_nontemporal_load(wrow + (size_t)(j + p) * 16 + 4 * s);
 #pragma unroll
         for (int p = 0; p < P; p++)
             if (j + p < j1)
@@ -148,8 +148,10 @@ hipError_t launch_gemv_mfma(const MfmaGemvArgs &a0, int epi, hipStream_t st)
 {
     MfmaGemvArgs a = a0;
     const int nb = a.K / 128;
-    // K split so that each wave streams about 4 blocks (4 x 4 KiB of weights)
-    int wk = (nb + 3) / 4;
+    // K split so that each wave streams about 8 blocks (8 x 4 KiB of weights):
+    // fewer, longer waves keep every workgroup of a large projection resident
+    // at once (measured best of 4..16 blocks per wave on the 70B shapes)
+    int wk = (nb + 7) / 8;
     a.wk = wk < 1 ? 1 : wk > kMaxWk ? kMaxWk : wk;
     const dim3 grid(a.N / 16), block(64 * a.wk);
     if (epi == EPI_SWIGLU)
