@@ -13,16 +13,14 @@
 // Both products are "NT": C[m][n] = sum_k A[m][k] B[n][k] with A and B stored
 // K-contiguous, which is the operand layout of v_mfma_f32_16x16x32_bf16
 // (each lane holds 8 consecutive k of one row of A and of one row of B).
-//  - workgroup tile 128 x 288, four waves as 2 x 2, wave tile 64 x 144
-//    (4 x 9 MFMA tiles, 144 fp32 accumulators per lane), K step 64; 288
-//    divides the PaLM block's 2F = 18432 and E = 2304, so a 512-token
-//    up-projection is exactly 256 workgroups (one per CU) and the
-//    down-projection 32 tiles x 8 K splits;
-//  - a 5-stage LDS ring (K step 32 per stage, 26 KiB each) filled by direct
-//    global->LDS loads (global_load_lds_dwordx4), four stages ahead of the
-//    MFMAs, one barrier per stage and no register staging; 64-byte LDS rows
-//    with the 16-byte chunk index XOR-swizzled by (row >> 1) & 3, so the
-//    fragment reads are bank-conflict free;
+//  - workgroup tile BM x 288 (BM = 64 up to 1024 rows, else 128), four
+//    waves as 2 x 2, wave tile BM/2 x 144 (BM/32 x 9 MFMA tiles); 288
+//    divides the PaLM block's 2F = 18432 and E = 2304;
+//  - a 3-stage LDS ring (K step 32 per stage) filled by direct global->LDS
+//    loads (global_load_lds_dwordx4), two stages ahead of the MFMAs, one
+//    barrier per stage, waits by vmcnt and no register staging; occupancy 2;
+//    64-byte LDS rows with the 16-byte chunk index XOR-swizzled by
+//    (row >> 1) & 3, so the fragment reads are bank-conflict free;
 //  - tile order puts the M-tiles of one N-tile on the same XCD (linear
 //    workgroup id % 8), so a weight tile is fetched into one L2 once;
 //  - up-projection epilogue: the packed W_gate/W_in rows interleave in
