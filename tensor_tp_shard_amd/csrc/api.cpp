@@ -116,8 +116,8 @@ int32_t plan(const tp_config &c, tp_shard &s)
             return fail(TP_EINVAL, "TP_FFN_2D takes an already-cut block: tp_size 1, tp_rank 0");
         if (c.quant)
             return fail(TP_EINVAL, "TP_FFN_2D has no int8 exchange");
-        if (c.dim % 288 || (2 * c.ffn_hidden) % 288 || c.ffn_hidden % 64)
-            return fail(TP_EINVAL, "TP_FFN_2D needs E a multiple of 288, 2F of 288 and F of 64");
+        if (c.dim % 288 || c.dim % 64 || (2 * c.ffn_hidden) % 288 || c.ffn_hidden % 64)
+            return fail(TP_EINVAL, "TP_FFN_2D needs E a multiple of 576, 2F of 288 and F of 64");
         s.T = 1;
         s.r = 0;
         s.esz = 2;

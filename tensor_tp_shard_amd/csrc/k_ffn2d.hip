@@ -16,11 +16,15 @@
 //  - workgroup tile BM x 288 (BM = 64 up to 1024 rows, else 128), four
 //    waves as 2 x 2, wave tile BM/2 x 144 (BM/32 x 9 MFMA tiles); 288
 //    divides the PaLM block's 2F = 18432 and E = 2304;
-//  - a 3-stage LDS ring (K step 32 per stage) filled by direct global->LDS
-//    loads (global_load_lds_dwordx4), two stages ahead of the MFMAs, one
-//    barrier per stage, waits by vmcnt and no register staging; occupancy 2;
-//    64-byte LDS rows with the 16-byte chunk index XOR-swizzled by
-//    (row >> 1) & 3, so the fragment reads are bank-conflict free;
+//  - a 3-stage LDS ring filled by direct global->LDS loads
+//    (global_load_lds_dwordx4), two stages ahead of the MFMAs, one barrier
+//    per stage, waits by vmcnt and no register staging. Up to 1024 rows a
+//    stage holds 64 K values (128 bytes of every row, occupancy 1): each
+//    1 KiB wave load is 8 full 128-byte lines, where 64-byte rows made it 16
+//    half-used lines and the L2 delivered about half the bytes per request
+//    (512 tokens: 124.6 -> 118.4 us per block). Larger M keeps 32 K values
+//    per stage at occupancy 2, which hides more latency there. 16-byte chunks
+//    are XOR-swizzled per row against bank conflicts;
 //  - tile order puts the M-tiles of one N-tile on the same XCD (linear
 //    workgroup id % 8), so a weight tile is fetched into one L2 once;
 //  - up-projection epilogue: the packed W_gate/W_in rows interleave in
@@ -35,11 +39,10 @@ namespace tps {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBN = 288, kBK = 32;                              // N tile, K step per pipeline stage
+constexpr int kBN = 288;                                        // N tile
 constexpr int kStages = 3;                                      // LDS ring of 3 stages
 constexpr int kNT = 9;                                          // MFMA tiles per wave in N (144)
 constexpr int kWN = kNT * 16;                                   // wave tile width
-constexpr int kRowB = kBK * 2;                                  // 64-byte LDS rows
 
 enum { FFN_UP = 0, FFN_DOWN = 1 };
 
@@ -51,10 +54,13 @@ struct GemmArgs {
     int M, N, K, ksteps_per_split;
 };
 
-// 16-byte chunk q (of 4) of row r sits at chunk q ^ ((r >> 1) & 3): a
-// 16-row x 16-byte fragment read then touches every LDS bank once per
-// 8-lane phase.
-__device__ __forceinline__ int swz(int row, int q) { return row * kRowB + ((q ^ ((row >> 1) & 3)) << 4); }
+// An LDS row holds the stage's KB values of a matrix row (2 KB bytes); its
+// 16-byte chunk c sits at chunk c ^ ((r >> 1) & (chunks - 1)), so that the 16
+// rows of a fragment read (same logical chunk) spread over the LDS banks.
+template <int KB>
+__device__ __forceinline__ int swx(int row) { return (row >> 1) & (KB / 8 - 1); }
+template <int KB>
+__device__ __forceinline__ int swz(int row, int c) { return row * (KB * 2) + ((c ^ swx<KB>(row)) << 4); }
 
 // s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding)
 template <int N>
@@ -64,10 +70,17 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// BM = 64 (decode-sized M: more workgroups) or 128 (large M)
-template <int EPI, int BM>
-__global__ __launch_bounds__(256, 2) void k_gemm_nt(GemmArgs a)
+// BM = 64 or 128 rows of A per workgroup; KB = 32 or 64 K values per stage.
+// KB = 64 (occupancy 1) makes every wave load 8 full 128-byte lines and suits
+// decode-sized M, where the L2 delivery of the weights is the limit; KB = 32
+// (64-byte rows, occupancy 2) hides more latency for large, compute-bound M.
+template <int EPI, int BM, int KB>
+__global__ __launch_bounds__(256, KB == 32 ? 2 : 1) void k_gemm_nt(GemmArgs a)
 {
+    constexpr int kBK = KB;
+    constexpr int kRowB = KB * 2;                      // bytes of a row per stage
+    constexpr int kRowsSeg = 1024 / kRowB;             // rows per 1 KiB wave load
+    constexpr int kChunks = kRowB / 16;                // 16-byte chunks per row
     constexpr int kMT = BM / 32;                       // MFMA tiles per wave in M (BM/2 rows)
     constexpr int kStageB = (BM + kBN) * kRowB;        // bytes per stage
     constexpr int kSegs = kStageB / 1024;              // 1 KiB wave loads per stage
@@ -92,23 +105,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(GemmArgs a)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Stage loads go straight from global memory to LDS (global_load_lds_dwordx4:
-    // lane i's 16 bytes land at base + 16 i). Wave w issues segments w, w+4, ...;
+    // lane i's 16 bytes land at base + 16 i), each wave instruction a segment of
+    // 8 rows x 128 bytes (full cache lines). Wave w issues segments w, w+4, ...;
     // lane i of segment t fills LDS slot 64 t + i = (row, physical chunk), so it
-    // loads the row's logical chunk q = physical ^ ((row >> 1) & 3). A rows past
-    // M read row M-1 (their outputs are never stored).
+    // loads the row's logical chunk physical ^ swx(row). A rows past M read row
+    // M-1 (their outputs are never stored).
     const int nseg = (kSegs - wv + 3) / 4; // kMaxSegs or kMaxSegs - 1
     const uint16_t *src[kMaxSegs];
 #pragma unroll
     for (int u = 0; u < kMaxSegs; u++) {
         const int t = wv + 4 * u;
-        const int p = lane, rs = p >> 2, phys = p & 3;
+        const int p = lane, rs = p / kChunks, phys = p % kChunks;
         if (t < kSegsA) {
-            const int row = t * 16 + rs;
+            const int row = t * kRowsSeg + rs;
             const int m = min(m0 + row, a.M - 1);
-            src[u] = a.A + (size_t)m * a.K + 8 * (phys ^ ((row >> 1) & 3));
+            src[u] = a.A + (size_t)m * a.K + 8 * (phys ^ swx<KB>(row));
         } else {
-            const int row = (t - kSegsA) * 16 + rs;
-            src[u] = a.B + (size_t)(n0 + row) * a.K + 8 * (phys ^ ((row >> 1) & 3));
+            const int row = (t - kSegsA) * kRowsSeg + rs;
+            src[u] = a.B + (size_t)(n0 + row) * a.K + 8 * (phys ^ swx<KB>(row));
         }
     }
     auto issue = [&](int ks) {
@@ -142,18 +156,22 @@ __global__ __launch_bounds__(256, 2) void k_gemm_nt(GemmArgs a)
         if (ks + kStages - 1 < nks)
             issue(ks + kStages - 1);
         const char *As = lds + (ks % kStages) * kStageB, *Bs = As + BM * kRowB;
-        bf16x8 af[kMT], bfr[kNT];
+        // two MFMA k-steps of 32 per stage: lane quarter q takes chunk 4 kk + q
 #pragma unroll
-        for (int i = 0; i < kMT; i++)
-            af[i] = *(const bf16x8 *)(As + swz(wm * (BM / 2) + i * 16 + (lane & 15), q));
+        for (int kk = 0; kk < kBK / 32; kk++) {
+            bf16x8 af[kMT], bfr[kNT];
 #pragma unroll
-        for (int j = 0; j < kNT; j++)
-            bfr[j] = *(const bf16x8 *)(Bs + swz(wn * kWN + j * 16 + (lane & 15), q));
-#pragma unroll
-        for (int i = 0; i < kMT; i++)
+            for (int i = 0; i < kMT; i++)
+                af[i] = *(const bf16x8 *)(As + swz<KB>(wm * (BM / 2) + i * 16 + (lane & 15), 4 * kk + q));
 #pragma unroll
             for (int j = 0; j < kNT; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                bfr[j] = *(const bf16x8 *)(Bs + swz<KB>(wn * kWN + j * 16 + (lane & 15), 4 * kk + q));
+#pragma unroll
+            for (int i = 0; i < kMT; i++)
+#pragma unroll
+                for (int j = 0; j < kNT; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
     }
 
     // lane holds C[m0 + wm*BM/2 + i*16 + 4*(lane/16) + r][n0 + wn*kWN + j*16 + lane%16]
@@ -209,46 +227,66 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float *P, float *Y, 
     *(float4 *)(Y + i) = acc;
 }
 
+// Tile rows and K values per stage for a batch of B rows (see k_gemm_nt).
+struct Ffn2dCfg {
+    int bm, kb;
+};
+static Ffn2dCfg ffn2d_cfg(int B)
+{
+    if (B <= 256)
+        return {64, 64};
+    if (B <= 1024)
+        return {128, 64};
+    return {128, 32};
+}
+
 // Number of K splits of the down-projection for a batch of B rows: enough
 // workgroups for the 256 CUs when the output has few tiles.
-static int ffn2d_bm(int B) { return B <= 1024 ? 64 : 128; }
-
 int ffn2d_splits(int B, int E, int F)
 {
-    const int bm = ffn2d_bm(B);
-    const int tiles = ((B + bm - 1) / bm) * (E / kBN);
+    const Ffn2dCfg c = ffn2d_cfg(B);
+    const int tiles = ((B + c.bm - 1) / c.bm) * (E / kBN);
     int s = 256 / (tiles > 0 ? tiles : 1);
     s = s < 1 ? 1 : s > 8 ? 8 : s;
-    const int ksteps = F / kBK;
+    const int ksteps = F / c.kb;
     return s > ksteps ? ksteps : s;
+}
+
+template <int EPI, int BM, int KB>
+static void launch_gemm(const GemmArgs &g, dim3 grid, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_gemm_nt<EPI, BM, KB>), grid, dim3(256), 0, st, g);
+}
+
+template <int EPI>
+static void launch_gemm_cfg(const Ffn2dCfg &c, const GemmArgs &g, dim3 grid, hipStream_t st)
+{
+    if (c.bm == 64)
+        launch_gemm<EPI, 64, 64>(g, grid, st);
+    else if (c.kb == 64)
+        launch_gemm<EPI, 128, 64>(g, grid, st);
+    else
+        launch_gemm<EPI, 128, 32>(g, grid, st);
 }
 
 // which = 0: up-projection + SwiGLU into a.h; which = 1: down-projection
 // into a.y (through the split partials in a.part when splitting).
-// Host-checked: E % 288 == 0, (2F) % 288 == 0, E and F multiples of 64, F % 8 == 0.
+// Host-checked: E % 288 == 0, (2F) % 288 == 0, E and F multiples of 64.
 hipError_t launch_ffn2d(const Ffn2dArgs &f, hipStream_t st, int which)
 {
-    const int bm = ffn2d_bm(f.B);
-    const int mt = (f.B + bm - 1) / bm;
+    const Ffn2dCfg c = ffn2d_cfg(f.B);
+    const int mt = (f.B + c.bm - 1) / c.bm;
     if (which == 0) {
-        GemmArgs g{f.x, f.w13, f.h, nullptr, f.B, 2 * f.F, f.E, f.E / kBK};
-        const dim3 grid(2 * f.F / kBN, mt, 1);
-        if (bm == 64)
-            hipLaunchKernelGGL((k_gemm_nt<FFN_UP, 64>), grid, dim3(256), 0, st, g);
-        else
-            hipLaunchKernelGGL((k_gemm_nt<FFN_UP, 128>), grid, dim3(256), 0, st, g);
+        GemmArgs g{f.x, f.w13, f.h, nullptr, f.B, 2 * f.F, f.E, f.E / c.kb};
+        launch_gemm_cfg<FFN_UP>(c, g, dim3(2 * f.F / kBN, mt, 1), st);
         return hipGetLastError();
     }
     const int S = ffn2d_splits(f.B, f.E, f.F);
-    const int ksteps = f.F / kBK;
+    const int ksteps = f.F / c.kb;
     const int per = (ksteps + S - 1) / S;
     const int splits = (ksteps + per - 1) / per;
     GemmArgs g{f.h, f.w2, nullptr, splits > 1 ? f.part : f.y, f.B, f.E, f.F, per};
-    const dim3 grid(f.E / kBN, mt, splits);
-    if (bm == 64)
-        hipLaunchKernelGGL((k_gemm_nt<FFN_DOWN, 64>), grid, dim3(256), 0, st, g);
-    else
-        hipLaunchKernelGGL((k_gemm_nt<FFN_DOWN, 128>), grid, dim3(256), 0, st, g);
+    launch_gemm_cfg<FFN_DOWN>(c, g, dim3(f.E / kBN, mt, splits), st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1)
         return e;
