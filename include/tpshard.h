@@ -75,11 +75,14 @@ enum { TP_DERR_LEN = 1 }; /* some lens[b] was < 0 or >= max_ctx; that sequence w
  * q head h uses kv head h / (Hq/Hkv) (contiguous groups).
  *
  * kind == TP_LLAMA_BLOCK: w_dtype TP_F32 or TP_BF16, kv_dtype likewise;
- *   requires Hq % Hkv == 0, Hq % T == 0, Hkv % T == 0, F % T == 0, even hd,
- *   dim, Hq_s*hd and F/T multiples of 8 (bf16) or 4 (fp32) elements,
- *   dim % 32 == 0 when quant != 0, hd <= 256, quant_block == 32.
+ *   requires Hq % Hkv == 0, Hq % T == 0, Hkv % T == 0, F % T == 0,
+ *   hd in {16, 32, 48, 64, 128}, at most 8 q heads per kv head,
+ *   max_batch <= 16, dim, Hq_s*hd and F/T multiples of 8 (bf16) or 4 (fp32)
+ *   elements, dim % 32 == 0 when quant != 0, quant_block == 32, and the
+ *   attention workgroup's LDS (which grows with max_ctx) within 64 KiB.
  * kind == TP_FFN_2D: dim = E (the block's E slice), ffn_hidden = F (the
- *   block's F slice), w_dtype TP_BF16, tp_size 1, heads ignored; the
+ *   block's F slice), w_dtype TP_BF16, tp_size 1, heads ignored, quant 0;
+ *   E a multiple of 576, 2F of 288 and F of 64; any max_batch >= 1. The
  *   decode step is Y = (silu(X W_gate^T) * (X W_in^T)) W_out^T.
  */
 typedef struct {
