@@ -13,9 +13,9 @@
 // llamaFfn2.
 //
 // Design (HBM-bound: every weight byte is read once and used B times):
-//  - one wave per RPW consecutive rows; the 64 lanes stride a row in 16-byte
-//    vectors, so one wave instruction reads 1 KiB of contiguous weights
-//    (nontemporal: read once per step);
+//  - one wave per RPW consecutive rows (1, or 2 for SwiGLU); the 64 lanes
+//    stride a row in 16-byte vectors, so one wave instruction reads 1 KiB of
+//    contiguous weights (nontemporal: read once per step);
 //  - all of a wave's weight vectors for up to KC x 1 KiB of each row are
 //    issued before anything waits on them;
 //  - the activation rows are staged once per workgroup in LDS (fp32) while
@@ -357,17 +357,25 @@ size_t gemv_lds_bytes(int B, int K) { return (size_t)B * K * sizeof(float); }
 
 bool gemv_fused_ok(int B, int K) { return B <= 4 && K <= 4 * 256 * kXV && gemv_lds_bytes(B, K) <= 64 * 1024; }
 
+// One row per wave for the plain-store projections (QKV, W_O, W2): twice the
+// waves of two rows per wave, each with a whole row of loads in flight
+// (7B shard step 42.2 -> 41.1 us); the SwiGLU projection pairs W1_f / W3_f
+// rows in one wave.
 template <bool BF16, int NB>
 static hipError_t launch_lds(const GemvArgs &a, int epi, hipStream_t st)
 {
-    const dim3 grid((a.N + 4 * kRPW - 1) / (4 * kRPW)), block(256);
     const size_t sm = gemv_lds_bytes(a.B, a.K);
-    if (epi == EPI_SWIGLU)
+    const dim3 block(256);
+    if (epi == EPI_SWIGLU) {
+        const dim3 grid((a.N + 4 * kRPW - 1) / (4 * kRPW));
         hipLaunchKernelGGL((k_gemv_lds<BF16, NB, kRPW, EPI_SWIGLU, false>), grid, block, sm, st, a);
-    else if (a.mo.n_wires)
-        hipLaunchKernelGGL((k_gemv_lds<BF16, NB, kRPW, EPI_STORE, true>), grid, block, sm, st, a);
-    else
-        hipLaunchKernelGGL((k_gemv_lds<BF16, NB, kRPW, EPI_STORE, false>), grid, block, sm, st, a);
+    } else {
+        const dim3 grid((a.N + 3) / 4);
+        if (a.mo.n_wires)
+            hipLaunchKernelGGL((k_gemv_lds<BF16, NB, 1, EPI_STORE, true>), grid, block, sm, st, a);
+        else
+            hipLaunchKernelGGL((k_gemv_lds<BF16, NB, 1, EPI_STORE, false>), grid, block, sm, st, a);
+    }
     return hipGetLastError();
 }
 

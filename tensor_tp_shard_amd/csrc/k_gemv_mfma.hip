@@ -18,11 +18,13 @@
 // activations are written in the fragment layout once by their producer
 // (RMSNorm, attention combine, SwiGLU).
 //
-// Work split: one workgroup per 16-row tile, its wk waves split K in
-// 128-wide blocks (about 8 per wave); a wave keeps two blocks of weights
-// (16-byte nontemporal loads; per load instruction the 4 lanes of a row read
-// 64 contiguous bytes of it) and their activation fragments in flight, then
-// the waves' 16x16 accumulators are summed in wave order through LDS. Epilogues: store, or SwiGLU of the interleaved
+// Work split: one workgroup per T 16-row tiles (T = 2 for the large
+// projections, sharing each activation fragment between two tiles), its wk
+// waves split K in 128-wide blocks (about 8 per wave); a wave keeps two
+// blocks of weights (16-byte nontemporal loads; per load instruction the 4
+// lanes of a row read 64 contiguous bytes of it) and their activation
+// fragments in flight, then the waves' 16x16 accumulators are summed in wave
+// order through LDS. Epilogues: store, or SwiGLU of the interleaved
 // (W1_f, W3_f) rows (accumulator rows 4q..4q+3 of a lane are two pairs).
 #include "common.h"
 
@@ -33,27 +35,38 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxWk = 16;
 
-template <int EPI>
-__global__ __launch_bounds__(64 * kMaxWk) void k_gemv_mfma(MfmaGemvArgs a)
+// T = 16-row weight tiles per wave sharing each activation fragment (1 or
+// 2): two tiles halve the activation bytes the waves pull from L2 per weight
+// byte; the register cost limits such workgroups to 8 waves.
+template <int EPI, int T>
+__global__ __launch_bounds__(64 * (T == 1 ? kMaxWk : 8)) void k_gemv_mfma(MfmaGemvArgs a)
 {
     constexpr int P = 2; // 128-wide K blocks in flight per wave
-    __shared__ f32x4 red[kMaxWk][64];
-    const int n0 = blockIdx.x * 16;
+    __shared__ f32x4 red[T == 1 ? kMaxWk : 8][T][64];
+    const int n0 = blockIdx.x * 16 * T;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
     const int nb = a.K >> 7;
     const int per = (nb + a.wk - 1) / a.wk;
     const int j0 = wv * per, j1 = min(nb, j0 + per);
-    const u32x4 *wrow = (const u32x4 *)(a.W + (size_t)(n0 + r) * a.K + 8 * q);
+    const u32x4 *wrow[T];
+#pragma unroll
+    for (int t = 0; t < T; t++)
+        wrow[t] = (const u32x4 *)(a.W + (size_t)(n0 + 16 * t + r) * a.K + 8 * q);
     const u32x4 *xf = (const u32x4 *)a.xf; // 16-byte units: [j][hl][s][q][b]
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; t++)
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j = j0; j < j1; j += P) {
-        u32x4 w[P][4], xh[P][4], xl[P][4];
+        u32x4 w[P][T][4], xh[P][4], xl[P][4];
 #pragma unroll
         for (int p = 0; p < P; p++)
             if (j + p < j1)
 #pragma unroll
-                for (int s = 0; s < 4; s++)
-                    w[p][s] = __builtin_nontemporal_load(wrow + (size_t)(j + p) * 16 + 4 * s);
+                for (int t = 0; t < T; t++)
+#pragma unroll
+                    for (int s = 0; s < 4; s++)
+                        w[p][t][s] = __builtin_nontemporal_load(wrow[t] + (size_t)(j + p) * 16 + 4 * s);
 #pragma unroll
         for (int p = 0; p < P; p++)
             if (j + p < j1)
@@ -66,73 +79,83 @@ __global__ __launch_bounds__(64 * kMaxWk) void k_gemv_mfma(MfmaGemvArgs a)
         for (int p = 0; p < P; p++)
             if (j + p < j1)
 #pragma unroll
-                for (int s = 0; s < 4; s++) {
-                    const bf16x8 wa = __builtin_bit_cast(bf16x8, w[p][s]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xh[p][s]), acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xl[p][s]), acc, 0, 0, 0);
-                }
+                for (int s = 0; s < 4; s++)
+#pragma unroll
+                    for (int t = 0; t < T; t++) {
+                        const bf16x8 wa = __builtin_bit_cast(bf16x8, w[p][t][s]);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xh[p][s]), acc[t], 0, 0, 0);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xl[p][s]), acc[t], 0, 0, 0);
+                    }
     }
+    // lane holds rows n0 + 16 t + 4q + i (i < 4) of batch column b = r
+    const int b = r;
     // fused merge (EPI_STORE, fp32 wires): wave 0 requests the residual and
     // the other wires' elements of its outputs before the reduction
     constexpr int kM = EPI == EPI_STORE ? kMO : 1;
-    const bool mlane = EPI == EPI_STORE && a.mo.n_wires && wv == 0 && (lane & 15) < a.B;
-    const size_t mi = (size_t)(lane & 15) * a.ldy + n0 + 4 * q;
-    float4 mres = make_float4(0.f, 0.f, 0.f, 0.f), mpre[kM];
+    const bool mlane = EPI == EPI_STORE && a.mo.n_wires && wv == 0 && b < a.B;
+    float4 mres[T], mpre[T][kM];
     if (mlane) {
-        mres = *(const float4 *)(a.mo.residual + mi);
 #pragma unroll
-        for (int k = 0; k < kM; k++)
-            if (k < a.mo.n_wires && k != a.mo.own)
-                mpre[k] = *(const float4 *)((const float *)a.mo.wires[k] + mi);
-    }
-    red[wv][lane] = acc;
-    __syncthreads();
-    if (wv != 0)
-        return;
-    f32x4 c = red[0][lane];
-    for (int w = 1; w < a.wk; w++) {
-        const f32x4 v = red[w][lane];
-        c = f32x4{c[0] + v[0], c[1] + v[1], c[2] + v[2], c[3] + v[3]};
-    }
-    // lane holds rows n0 + 4q + i (i < 4) of batch column b = r
-    const int b = r;
-    if (b >= a.B)
-        return;
-    if constexpr (EPI == EPI_SWIGLU) {
-        const int f = (n0 >> 1) + 2 * q; // rows (4q, 4q+1) and (4q+2, 4q+3) are features f, f+1
-        const float h0 = silu(c[0]) * c[1], h1 = silu(c[2]) * c[3];
-        *(float2 *)(a.y + (size_t)b * a.ldy + f) = make_float2(h0, h1);
-        if (a.tap)
-            *(float2 *)(a.tap + (size_t)b * a.ldy + f) = make_float2(h0, h1);
-        if (a.yf) {
-            xf_store(a.yf, b, f, h0);
-            xf_store(a.yf, b, f + 1, h1);
-        }
-    } else {
-        const int n = n0 + 4 * q;
-        const float4 v = make_float4(c[0], c[1], c[2], c[3]);
-        *(float4 *)(a.y + (size_t)b * a.ldy + n) = v;
-        if (a.tap)
-            *(float4 *)(a.tap + (size_t)b * a.ldy + n) = v;
-        if (mlane) {
-            float4 m = mres;
+        for (int t = 0; t < T; t++) {
+            const size_t mi = (size_t)b * a.ldy + n0 + 16 * t + 4 * q;
+            mres[t] = *(const float4 *)(a.mo.residual + mi);
 #pragma unroll
             for (int k = 0; k < kM; k++)
-                if (k < a.mo.n_wires) {
-                    const float4 d = k == a.mo.own ? v : mpre[k];
+                if (k < a.mo.n_wires && k != a.mo.own)
+                    mpre[t][k] = *(const float4 *)((const float *)a.mo.wires[k] + mi);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < T; t++)
+        red[wv][t][lane] = acc[t];
+    __syncthreads();
+    if (wv != 0 || b >= a.B)
+        return;
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+        const int nt = n0 + 16 * t;
+        const size_t mi = (size_t)b * a.ldy + nt + 4 * q;
+        f32x4 c = red[0][t][lane];
+        for (int w = 1; w < a.wk; w++) {
+            const f32x4 v = red[w][t][lane];
+            c = f32x4{c[0] + v[0], c[1] + v[1], c[2] + v[2], c[3] + v[3]};
+        }
+        if constexpr (EPI == EPI_SWIGLU) {
+            const int f = (nt >> 1) + 2 * q; // rows (4q, 4q+1) and (4q+2, 4q+3) are features f, f+1
+            const float h0 = silu(c[0]) * c[1], h1 = silu(c[2]) * c[3];
+            *(float2 *)(a.y + (size_t)b * a.ldy + f) = make_float2(h0, h1);
+            if (a.tap)
+                *(float2 *)(a.tap + (size_t)b * a.ldy + f) = make_float2(h0, h1);
+            if (a.yf) {
+                xf_store(a.yf, b, f, h0);
+                xf_store(a.yf, b, f + 1, h1);
+            }
+        } else {
+            const int n = nt + 4 * q;
+            const float4 v = make_float4(c[0], c[1], c[2], c[3]);
+            *(float4 *)(a.y + (size_t)b * a.ldy + n) = v;
+            if (a.tap)
+                *(float4 *)(a.tap + (size_t)b * a.ldy + n) = v;
+            if (mlane) {
+                float4 m = mres[t];
+#pragma unroll
+                for (int k = 0; k < kM; k++)
+                    if (k < a.mo.n_wires) {
+                        const float4 d = k == a.mo.own ? v : mpre[t][k];
+                        m.x = m.x + d.x;
+                        m.y = m.y + d.y;
+                        m.z = m.z + d.z;
+                        m.w = m.w + d.w;
+                    }
+                for (int k = kM; k < a.mo.n_wires; k++) {
+                    const float4 d = k == a.mo.own ? v : *(const float4 *)((const float *)a.mo.wires[k] + mi);
                     m.x = m.x + d.x;
                     m.y = m.y + d.y;
                     m.z = m.z + d.z;
                     m.w = m.w + d.w;
                 }
-            for (int k = kM; k < a.mo.n_wires; k++) {
-                const float4 d = k == a.mo.own ? v : *(const float4 *)((const float *)a.mo.wires[k] + mi);
-                m.x = m.x + d.x;
-                m.y = m.y + d.y;
-                m.z = m.z + d.z;
-                m.w = m.w + d.w;
+                *(float4 *)(a.mo.x_out + mi) = m;
             }
-            *(float4 *)(a.mo.x_out + mi) = m;
         }
     }
 }
@@ -148,16 +171,27 @@ hipError_t launch_gemv_mfma(const MfmaGemvArgs &a0, int epi, hipStream_t st)
 {
     MfmaGemvArgs a = a0;
     const int nb = a.K / 128;
-    // K split so that each wave streams about 8 blocks (8 x 4 KiB of weights):
-    // fewer, longer waves keep every workgroup of a large projection resident
-    // at once (measured best of 4..16 blocks per wave on the 70B shapes)
-    int wk = (nb + 7) / 8;
-    a.wk = wk < 1 ? 1 : wk > kMaxWk ? kMaxWk : wk;
-    const dim3 grid(a.N / 16), block(64 * a.wk);
-    if (epi == EPI_SWIGLU)
-        hipLaunchKernelGGL(k_gemv_mfma<EPI_SWIGLU>, grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL(k_gemv_mfma<EPI_STORE>, grid, block, 0, st, a);
+    // K split so that each wave streams about 8 blocks (8 x 4 KiB of weights
+    // per tile): fewer, longer waves keep every workgroup of a large
+    // projection resident at once (measured best of 4..16 blocks per wave on
+    // the 70B shapes). Two tiles per wave when that still gives every SIMD a
+    // wave (the 70B W1/W3 and W2), else one (few rows: QKV; short K: W_O).
+    const int wk8 = (nb + 7) / 8;
+    const int wk2 = wk8 < 1 ? 1 : wk8 > 8 ? 8 : wk8;
+    const bool two = a.N % 32 == 0 && (long)(a.N / 32) * wk2 >= 1024;
+    a.wk = two ? wk2 : (wk8 < 1 ? 1 : wk8 > kMaxWk ? kMaxWk : wk8);
+    const dim3 grid(a.N / (two ? 32 : 16)), block(64 * a.wk);
+    if (two) {
+        if (epi == EPI_SWIGLU)
+            hipLaunchKernelGGL((k_gemv_mfma<EPI_SWIGLU, 2>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((k_gemv_mfma<EPI_STORE, 2>), grid, block, 0, st, a);
+    } else {
+        if (epi == EPI_SWIGLU)
+            hipLaunchKernelGGL((k_gemv_mfma<EPI_SWIGLU, 1>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((k_gemv_mfma<EPI_STORE, 1>), grid, block, 0, st, a);
+    }
     return hipGetLastError();
 }
 
