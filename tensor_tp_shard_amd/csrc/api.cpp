@@ -78,7 +78,7 @@ struct tp_shard {
     // packed layout (byte offsets)
     uint64_t o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn, o_rope, packed_bytes;
     // workspace layout (byte offsets)
-    uint64_t w_err, w_xfx, w_xfatt, w_xfa, w_xn, w_qkv, w_part, w_att, w_a, w_p, ws_bytes;
+    uint64_t w_err, w_xfx, w_xfatt, w_xfa, w_skp, w_xn, w_qkv, w_part, w_att, w_a, w_p, ws_bytes;
     int n_chunks;
     bool mfma_ok = false; // the batch 5..16 MFMA path applies to this shape
     uint64_t kv_bytes, wire_bytes, part_rows = 0;
@@ -194,11 +194,20 @@ int32_t plan(const tp_config &c, tp_shard &s)
                 gemv_mfma_ok(16, s.D, s.Fs, 1);
     o = 0;
     s.w_err = o;  o = 256;
-    s.w_xfx = s.w_xfatt = s.w_xfa = 0;
+    s.w_xfx = s.w_xfatt = s.w_xfa = s.w_skp = 0;
     if (s.mfma_ok) { // activations in the MFMA fragment layout
         s.w_xfx = o;   o = align_up(o + xf_elems(s.D) * 2, 256);
         s.w_xfatt = o; o = align_up(o + xf_elems(s.Hq_s * s.hd) * 2, 256);
         s.w_xfa = o;   o = align_up(o + xf_elems(s.Fs) * 2, 256);
+        // split-K partials of the largest batch-16 projection
+        size_t skp = gemv_sk_part_floats(s.n_qkv, s.D, c.max_batch);
+        const size_t sk[] = {gemv_sk_part_floats(s.D, s.Hq_s * s.hd, c.max_batch),
+                             gemv_sk_part_floats(2 * s.Fs, s.D, c.max_batch),
+                             gemv_sk_part_floats(s.D, s.Fs, c.max_batch)};
+        for (size_t v : sk)
+            skp = v > skp ? v : skp;
+        s.w_skp = skp ? o : 0;
+        o = align_up(o + skp * 4, 256);
     }
     s.w_xn = o;   o = align_up(o + B * D * 4, 256);
     s.w_qkv = o;  o = align_up(o + B * s.n_qkv * 4, 256);
@@ -499,7 +508,8 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
     auto run_gemv = [&](const GemvArgs &g, const uint16_t *xf, uint16_t *yf, int epi) {
         if (!mfma)
             return launch_gemv(g, wbf, epi, st);
-        MfmaGemvArgs m{(const uint16_t *)g.W, xf, g.y, g.tap, yf, g.N, g.K, g.B, g.ldy, 1, g.mo};
+        MfmaGemvArgs m{(const uint16_t *)g.W, xf, g.y, g.tap, yf, g.N, g.K, g.B, g.ldy, 1, g.mo,
+                       s->w_skp ? (float *)(s->ws + s->w_skp) : nullptr, 0, 0};
         return launch_gemv_mfma(m, epi, st);
     };
 

@@ -212,6 +212,8 @@ struct MfmaGemvArgs {
     uint16_t *yf;        // EPI_SWIGLU: optional y in the fragment layout (K' = N/2)
     int N, K, B, ldy, wk; // wk = waves per 16-row tile (K split)
     MergeIn mo;          // EPI_STORE, fp32 wires: fused merge (y is wire mo.own)
+    float *part;         // split-K partials [S][B][N] (gemv_sk_part_floats), or null
+    int nbs, S;          // split-K: 128-blocks per K slice, number of slices (set by the launcher)
 };
 
 enum GemvEpi { EPI_STORE = 0, EPI_SWIGLU = 1 };
@@ -281,6 +283,7 @@ struct Ffn2dArgs {
 hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st);
 hipError_t launch_gemv(const GemvArgs &a, int w_bf16, int epi, hipStream_t st);
 hipError_t launch_gemv_mfma(const MfmaGemvArgs &a, int epi, hipStream_t st);
+size_t gemv_sk_part_floats(int N, int K, int B);
 bool gemv_mfma_ok(int B, int N, int K, int w_bf16);
 hipError_t launch_attn(const AttnArgs &a, int kv_bf16, int B, hipStream_t st);
 size_t attn_lds_bytes(int G, int hd, int kv_bf16, int n_chunks);

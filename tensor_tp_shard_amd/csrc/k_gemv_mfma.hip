@@ -160,6 +160,201 @@ __global__ __launch_bounds__(64 * (T == 1 ? kMaxWk : 8)) void k_gemv_mfma(MfmaGe
     }
 }
 
+// ---------------------------------------------------------------- split K
+// The batch-16 projections with many rows and a long K: a workgroup of 8
+// waves takes 8 x T 16-row tiles and one K slice of nbs 128-blocks. The
+// slice's activation fragments (nbs x 8 KiB) go to LDS once per workgroup
+// (direct global->LDS loads, issued before the weights) and every wave reads
+// its MFMA B operands there, so each activation byte leaves L2 once per
+// workgroup instead of once per tile; the weights stream from HBM into
+// registers as in k_gemv_mfma. Each slice's fp32 partial goes to a.part
+// [S][B][N]; k_gemv_sk_epi sums the slices in order and applies the
+// epilogue. (In a probe on the 70B up-projection shape the activations in
+// LDS took the stream from 38 to 26 us.)
+constexpr int kSkWaves = 8, kSkMaxNbs = 8;
+
+// s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int T>
+__global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
+{
+    constexpr int P = 2; // 128-wide K blocks in flight per wave
+    __shared__ __attribute__((aligned(1024))) char lds[kSkMaxNbs * 8192];
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
+    const int ks = blockIdx.y, jb = ks * a.nbs;
+    const int nbl = min(a.nbs, (a.K >> 7) - jb); // blocks in this slice
+    // the slice's fragments: nbl x 8 KiB = 8 nbl wave loads of 1 KiB
+    const u32x4 *xf = (const u32x4 *)a.xf + (size_t)jb * 512;
+    for (int seg = wv; seg < 8 * nbl; seg += kSkWaves)
+        __builtin_amdgcn_global_load_lds((const void *)(xf + (size_t)seg * 64 + lane),
+                                         (__attribute__((address_space(3))) void *)(lds + seg * 1024), 16, 0, 0);
+    const int n0 = (blockIdx.x * kSkWaves + wv) * 16 * T;
+    const u32x4 *wrow[T];
+#pragma unroll
+    for (int t = 0; t < T; t++)
+        wrow[t] = (const u32x4 *)(a.W + (size_t)(n0 + 16 * t + r) * a.K + 8 * q) + (size_t)jb * 16;
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; t++)
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jl = 0; jl < nbl; jl += P) {
+        u32x4 w[P][T][4];
+#pragma unroll
+        for (int p = 0; p < P; p++)
+            if (jl + p < nbl)
+#pragma unroll
+                for (int t = 0; t < T; t++)
+#pragma unroll
+                    for (int s = 0; s < 4; s++)
+                        w[p][t][s] = __builtin_nontemporal_load(wrow[t] + (size_t)(jl + p) * 16 + 4 * s);
+        if (jl == 0) {
+            // this wave's fragment loads (issued before these weight loads,
+            // loads complete in order) are done once only the weight loads
+            // remain; after the barrier every wave's fragments are in LDS
+            if (nbl >= P)
+                wait_vmcnt<P * T * 4>();
+            else
+                wait_vmcnt<T * 4>();
+            __builtin_amdgcn_s_barrier();
+        }
+#pragma unroll
+        for (int p = 0; p < P; p++)
+            if (jl + p < nbl)
+#pragma unroll
+                for (int s = 0; s < 4; s++) {
+                    const u32x4 xh = *(const u32x4 *)(lds + (((jl + p) * 2 + 0) * 4 + s) * 1024 + lane * 16);
+                    const u32x4 xl = *(const u32x4 *)(lds + (((jl + p) * 2 + 1) * 4 + s) * 1024 + lane * 16);
+#pragma unroll
+                    for (int t = 0; t < T; t++) {
+                        const bf16x8 wa = __builtin_bit_cast(bf16x8, w[p][t][s]);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xh), acc[t], 0, 0, 0);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xl), acc[t], 0, 0, 0);
+                    }
+                }
+    }
+    // lane (q, b = r) holds rows n0 + 16 t + 4q + i (i < 4) of batch column b
+    if (r < a.B)
+#pragma unroll
+        for (int t = 0; t < T; t++)
+            *(f32x4 *)(a.part + ((size_t)ks * a.B + r) * a.N + n0 + 16 * t + 4 * q) = acc[t];
+}
+
+// y[b][n] = sum_s part[s][b][n] in slice order, then the projection's
+// epilogue: store (+ tap, + fused merge), or SwiGLU of the interleaved
+// (W1_f, W3_f) rows (+ tap, + fragment copy for the next projection).
+// One thread per 4 consecutive n of one batch row.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemv_sk_epi(MfmaGemvArgs a)
+{
+    const int n4 = a.N / 4;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.B * n4)
+        return;
+    const int b = i / n4, n = (i % n4) * 4;
+    const size_t slice = (size_t)a.B * a.N;
+    const float *p = a.part + (size_t)b * a.N + n;
+    // slices 8 at a time, all 8 loads in flight before the in-order adds
+    constexpr int U = 8;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < a.S; s0 += U) {
+        float4 u[U];
+#pragma unroll
+        for (int k = 0; k < U; k++)
+            if (s0 + k < a.S)
+                u[k] = *(const float4 *)(p + (s0 + k) * slice);
+#pragma unroll
+        for (int k = 0; k < U; k++)
+            if (s0 + k < a.S) {
+                if (s0 + k == 0) {
+                    v = u[0];
+                } else {
+                    v.x += u[k].x;
+                    v.y += u[k].y;
+                    v.z += u[k].z;
+                    v.w += u[k].w;
+                }
+            }
+    }
+    if constexpr (EPI == EPI_SWIGLU) {
+        const int f = n >> 1; // rows (n, n+1) and (n+2, n+3) are features f, f+1
+        const float h0 = silu(v.x) * v.y, h1 = silu(v.z) * v.w;
+        *(float2 *)(a.y + (size_t)b * a.ldy + f) = make_float2(h0, h1);
+        if (a.tap)
+            *(float2 *)(a.tap + (size_t)b * a.ldy + f) = make_float2(h0, h1);
+        if (a.yf) {
+            xf_store(a.yf, b, f, h0);
+            xf_store(a.yf, b, f + 1, h1);
+        }
+    } else {
+        const size_t o = (size_t)b * a.ldy + n;
+        *(float4 *)(a.y + o) = v;
+        if (a.tap)
+            *(float4 *)(a.tap + o) = v;
+        if (a.mo.n_wires) {
+            float4 m = *(const float4 *)(a.mo.residual + o);
+            for (int k0 = 0; k0 < a.mo.n_wires; k0 += kMO) {
+                float4 d[kMO];
+#pragma unroll
+                for (int k = 0; k < kMO; k++)
+                    if (k0 + k < a.mo.n_wires && k0 + k != a.mo.own)
+                        d[k] = *(const float4 *)((const float *)a.mo.wires[k0 + k] + o);
+#pragma unroll
+                for (int k = 0; k < kMO; k++)
+                    if (k0 + k < a.mo.n_wires) {
+                        const float4 e = k0 + k == a.mo.own ? v : d[k];
+                        m.x = m.x + e.x;
+                        m.y = m.y + e.y;
+                        m.z = m.z + e.z;
+                        m.w = m.w + e.w;
+                    }
+            }
+            *(float4 *)(a.mo.x_out + o) = m;
+        }
+    }
+}
+
+// Split-K shape for an N x K projection: tiles per wave T, 128-blocks per
+// slice and slices, aiming at about 256 workgroups; T = 0 when the shape
+// does not tile (the per-tile kernel takes it).
+struct SkShape {
+    int T, nbs, S, R;
+};
+static SkShape sk_shape(int N, int K)
+{
+    const int nb = K / 128;
+    SkShape sh{0, 0, 0, 0};
+    // only long K: with K < 4096 the per-tile kernel's activation traffic is
+    // small and the reduce launch would cost more than it saves (70B W_O and
+    // W2 measured slower split)
+    if (K % 128 || K < 4096)
+        return sh;
+    if (N % 256 == 0 && N / 256 >= 16)
+        sh.T = 2;
+    else if (N % 128 == 0)
+        sh.T = 1;
+    else
+        return sh;
+    sh.R = N / (128 * sh.T);
+    const int st = (256 + sh.R - 1) / sh.R;
+    int nbs = (nb + st - 1) / st;
+    nbs = nbs < 2 ? 2 : nbs > kSkMaxNbs ? kSkMaxNbs : nbs;
+    sh.nbs = nbs;
+    sh.S = (nb + nbs - 1) / nbs;
+    return sh;
+}
+
+size_t gemv_sk_part_floats(int N, int K, int B)
+{
+    const SkShape sh = sk_shape(N, K);
+    return sh.T ? (size_t)sh.S * B * N : 0;
+}
+
 bool gemv_mfma_ok(int B, int N, int K, int w_bf16)
 {
     return w_bf16 && B > 4 && B <= 16 && N % 16 == 0 && K % 128 == 0;
@@ -171,11 +366,30 @@ hipError_t launch_gemv_mfma(const MfmaGemvArgs &a0, int epi, hipStream_t st)
 {
     MfmaGemvArgs a = a0;
     const int nb = a.K / 128;
+    const SkShape sh = sk_shape(a.N, a.K);
+    if (a.part && sh.T) {
+        a.nbs = sh.nbs;
+        a.S = sh.S;
+        const dim3 grid(sh.R, sh.S), block(64 * kSkWaves);
+        if (sh.T == 2)
+            hipLaunchKernelGGL(k_gemv_sk<2>, grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL(k_gemv_sk<1>, grid, block, 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        const dim3 eg((unsigned)((a.B * (a.N / 4) + 255) / 256));
+        if (epi == EPI_SWIGLU)
+            hipLaunchKernelGGL(k_gemv_sk_epi<EPI_SWIGLU>, eg, dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL(k_gemv_sk_epi<EPI_STORE>, eg, dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
     // K split so that each wave streams about 8 blocks (8 x 4 KiB of weights
     // per tile): fewer, longer waves keep every workgroup of a large
     // projection resident at once (measured best of 4..16 blocks per wave on
     // the 70B shapes). Two tiles per wave when that still gives every SIMD a
-    // wave (the 70B W1/W3 and W2), else one (few rows: QKV; short K: W_O).
+    // wave, else one.
     const int wk8 = (nb + 7) / 8;
     const int wk2 = wk8 < 1 ? 1 : wk8 > 8 ? 8 : wk8;
     const bool two = a.N % 32 == 0 && (long)(a.N / 32) * wk2 >= 1024;

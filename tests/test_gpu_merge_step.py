@@ -4,10 +4,10 @@ merge_partials. Both use the same per-element fp32 sum in wire order, so the
 merged rows and the stage's own wire must be bitwise equal. Cases cover every
 producer that can carry the merge: the down-projection with LDS-staged
 activations (batch <= 4), the one reading activations from global memory
-(fp32 batch 8), the MFMA one (bf16 batch 16, one and two 16-row tiles per
-wave), and the int8 quantiser; the own wire at the first, the last and a
-middle position, x_out aliasing x, and more wires than the producer requests
-ahead of time (8)."""
+(fp32 batch 8), the MFMA ones (bf16 batch 16: one and two 16-row tiles per
+wave, and split K with the merge in the reduce), and the int8 quantiser; the
+own wire at the first, the last and a middle position, x_out aliasing x, and
+more wires than the producer requests ahead of time (8)."""
 import sys
 
 import numpy as np
@@ -68,6 +68,11 @@ CASES = {
                                        head_dim=128, ffn_hidden=7168, tp=2, batch=16,
                                        past=(1, 40), w_dtype=synth.BF16, kv_dtype=synth.BF16,
                                        seed=305),
+    # split-K MFMA down-projection (F/T 4096: long K) with the merge in its reduce
+    "splitk_bf16_b16": synth.small_llama(name="splitk_b16", dim=1024, n_heads=8, n_kv_heads=8,
+                                         head_dim=128, ffn_hidden=8192, tp=2, batch=16,
+                                         past=(1, 40), w_dtype=synth.BF16, kv_dtype=synth.BF16,
+                                         seed=306),
     # dim > 8192 with int8 wires
     "wide_q8_b2": synth.small_llama(name="wide_q8", dim=8448, n_heads=4, n_kv_heads=4,
                                     head_dim=32, ffn_hidden=256, tp=2, batch=2, past=(2, 40),
