@@ -310,6 +310,237 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
 
 }
 
+// ---------------------------------------------------------------- GQA on MFMA
+// The same work split and chunk records for a bf16 cache with G >= 4 q heads
+// per kv head, where the VALU version spends its time re-reading the G
+// queries from LDS for every position. Scores and values are dense
+// contractions: S^T[t][j] = K[t][:] . q_j (A = the K chunk, B = the queries)
+// and O[j][d] = sum_t p[j][t] V[t][d] (A = the probabilities, B = V, stored
+// transposed in LDS), each on v_mfma_f32_16x16x32_bf16 with the fp32
+// operand (queries, probabilities) split into bf16 hi + lo parts (two MFMAs,
+// ~16 mantissa bits) and fp32 accumulation. K and V are used as stored.
+// Positions past the sequence are zero in LDS (the cache may hold anything
+// there) and masked out of the softmax. One wave per 16 positions for the
+// scores, per 16-wide dim tiles for the values.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16 bits, round to nearest even (the hardware conversion)
+__device__ __forceinline__ uint16_t bf16_rn(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+__device__ __forceinline__ uint32_t bf16_pair(float lo_elem, float hi_elem)
+{
+    return (uint32_t)bf16_rn(lo_elem) | ((uint32_t)bf16_rn(hi_elem) << 16);
+}
+
+// LDS: queries and probabilities as bf16 hi / lo parts in 16-row MFMA
+// operand form (rows past G zero), the K chunk row-major with padded rows,
+// V in 8-position groups [t/8][dim][t%8] so that a B fragment (8 consecutive
+// positions of one dim) is one aligned 16-byte read.
+__host__ __device__ inline size_t attn_mfma_smem_bytes(int G, int hd)
+{
+    return (size_t)2 * 16 * hd * 2 +          // q hi, lo
+           sizeof(float) * (size_t)G * kChunk + // scores
+           (size_t)2 * 16 * kChunk * 2 +       // p hi, lo
+           sizeof(float) * 2 * 16 +            // (m, l)
+           (size_t)kChunk * (hd * 2 + 16) +    // K
+           (size_t)kChunk * hd * 2;            // V groups
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    constexpr int hd = HD;
+    constexpr int rowb = hd * 2 + 16; // padded K row
+    const int G = a.G;
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, q = lane >> 4, r = lane & 15;
+    const int L = a.lens[b];
+    if (L < 0 || L >= a.max_ctx) { // skipped sequence: flagged here, zeroed by the combine
+        if (c == 0 && g == 0 && tid == 0)
+            atomicOr(a.err, 1u);
+        return;
+    }
+    const int t0 = c * kChunk;
+    if (t0 > L)
+        return;
+    const int n = min(kChunk, L + 1 - t0);
+    const bool owner = L < t0 + kChunk;
+
+    uint16_t *qh_s = (uint16_t *)lds_raw;          // [16][hd]
+    uint16_t *ql_s = qh_s + 16 * hd;               // [16][hd]
+    float *s_s = (float *)(ql_s + 16 * hd);        // [G][64]
+    uint16_t *ph_s = (uint16_t *)(s_s + G * kChunk); // [16][64]
+    uint16_t *pl_s = ph_s + 16 * kChunk;           // [16][64]
+    float *ml = (float *)(pl_s + 16 * kChunk);     // [16][2]
+    char *K_s = (char *)(ml + 2 * 16);             // [64][rowb]
+    uint16_t *V_g = (uint16_t *)(K_s + kChunk * rowb); // [8][hd][8]
+
+    const size_t head_base = ((size_t)b * a.Hkv_s + g) * a.max_ctx * hd;
+    const float *qkv = a.qkv + (size_t)b * a.ld_qkv;
+    const float2 *rope = a.rope + (size_t)L * (hd / 2);
+    const int half = hd / 2;
+    constexpr int kQP = 16 * (HD / 2) / 256; // q pairs per thread over all 16 operand rows
+    float2 qp[kQP], cs[kQP];
+#pragma unroll
+    for (int u = 0; u < kQP; u++) {
+        const int i = tid + 256 * u;
+        const int j = i / half, p = i % half;
+        cs[u] = rope[p];
+        if (j < G)
+            qp[u] = *(const float2 *)(qkv + (g * G + j) * hd + 2 * p);
+    }
+    float2 nk = make_float2(0.f, 0.f), nv = make_float2(0.f, 0.f);
+    if (owner && tid < half) {
+        nk = *(const float2 *)(qkv + (a.Hq_s + g) * hd + 2 * tid);
+        nv = *(const float2 *)(qkv + (a.Hq_s + a.Hkv_s + g) * hd + 2 * tid);
+    }
+    constexpr int ppr = hd / 8;                 // 16-byte pieces per row
+    constexpr int kPieces = kChunk * ppr / 256; // per thread (64 rows)
+    u32x4 kv[2][kPieces];
+    {
+        const u32x4 *kg = (const u32x4 *)((const char *)a.kc + (head_base + (size_t)t0 * hd) * 2);
+        const u32x4 *vg = (const u32x4 *)((const char *)a.vc + (head_base + (size_t)t0 * hd) * 2);
+#pragma unroll
+        for (int i = 0; i < kPieces; i++) {
+            const int p = tid + 256 * i;
+            if (p < n * ppr) {
+                kv[0][i] = __builtin_nontemporal_load(kg + p);
+                kv[1][i] = __builtin_nontemporal_load(vg + p);
+            } else {
+                kv[0][i] = kv[1][i] = u32x4{0u, 0u, 0u, 0u}; // positions past the sequence
+            }
+        }
+    }
+    // rotated queries -> hi / lo operand rows (rows >= G zero); p rows >= G zero
+#pragma unroll
+    for (int u = 0; u < kQP; u++) {
+        const int i = tid + 256 * u;
+        const int j = i / half, p = i % half;
+        float r0 = 0.f, r1 = 0.f;
+        if (j < G) {
+            r0 = qp[u].x * cs[u].x - qp[u].y * cs[u].y;
+            r1 = qp[u].x * cs[u].y + qp[u].y * cs[u].x;
+            if (c == 0 && a.tap_q) {
+                const int h = g * G + j;
+                a.tap_q[(size_t)b * a.Hq_s * hd + h * hd + 2 * p] = r0;
+                a.tap_q[(size_t)b * a.Hq_s * hd + h * hd + 2 * p + 1] = r1;
+            }
+        }
+        const uint16_t h0 = bf16_rn(r0), h1 = bf16_rn(r1);
+        *(uint32_t *)(qh_s + j * hd + 2 * p) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        *(uint32_t *)(ql_s + j * hd + 2 * p) = bf16_pair(r0 - bf16_to_f32(h0), r1 - bf16_to_f32(h1));
+    }
+    for (int i = tid; i < (16 - G) * kChunk / 2; i += 256) {
+        const int e = G * kChunk + 2 * i;
+        *(uint32_t *)(ph_s + e) = 0u;
+        *(uint32_t *)(pl_s + e) = 0u;
+    }
+    // K rows as loaded; V into 8-position groups, the element order rotated by
+    // the piece's column so the 16 lanes of a row write 8 different banks
+#pragma unroll
+    for (int i = 0; i < kPieces; i++) {
+        const int p = tid + 256 * i;
+        const int row = p / ppr, col = p % ppr;
+        *(u32x4 *)(K_s + row * rowb + col * 16) = kv[0][i];
+        const u32x4 v = kv[1][i];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        uint16_t *vb = V_g + (size_t)(row >> 3) * hd * 8 + (row & 7);
+#pragma unroll
+        for (int e0 = 0; e0 < 8; e0++) {
+            const int e = (e0 + col) & 7;
+            vb[(8 * col + e) * 8] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+    __syncthreads();
+    if (owner) { // rotate and append the new key / value at slot L (cache and LDS)
+        if (tid < half) {
+            const int p = tid, tl = L - t0;
+            const float2 cr = cs[0];
+            const float r0 = nk.x * cr.x - nk.y * cr.y, r1 = nk.x * cr.y + nk.y * cr.x;
+            const size_t e = head_base + (size_t)L * hd + 2 * p;
+            const uint16_t k0 = bf16_rn(r0), k1 = bf16_rn(r1);
+            const uint16_t v0 = bf16_rn(nv.x), v1 = bf16_rn(nv.y);
+            ((uint16_t *)a.kc)[e] = k0;
+            ((uint16_t *)a.kc)[e + 1] = k1;
+            ((uint16_t *)a.vc)[e] = v0;
+            ((uint16_t *)a.vc)[e + 1] = v1;
+            *(uint32_t *)(K_s + tl * rowb + 4 * p) = (uint32_t)k0 | ((uint32_t)k1 << 16);
+            uint16_t *vb = V_g + (size_t)(tl >> 3) * hd * 8 + (tl & 7);
+            vb[(2 * p) * 8] = v0;
+            vb[(2 * p + 1) * 8] = v1;
+            if (a.tap_k) {
+                float *tk = a.tap_k + (size_t)b * a.Hkv_s * hd + g * hd;
+                float *tv = a.tap_v + (size_t)b * a.Hkv_s * hd + g * hd;
+                tk[2 * p] = r0;
+                tk[2 * p + 1] = r1;
+                tv[2 * p] = nv.x;
+                tv[2 * p + 1] = nv.y;
+            }
+        }
+        __syncthreads();
+    }
+
+    // scores: wave wv takes positions 16 wv .. 16 wv + 15; column r = head r
+    {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < hd / 32; s++) {
+            const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(K_s + (16 * wv + r) * rowb + (4 * s + q) * 16));
+            const bf16x8_t qh = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(qh_s + r * hd + 32 * s + 8 * q));
+            const bf16x8_t ql = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(ql_s + r * hd + 32 * s + 8 * q));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql, acc, 0, 0, 0);
+        }
+        if (r < G) // acc[i] = score of position 16 wv + 4q + i for head r
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int pl = 16 * wv + 4 * q + i;
+                s_s[r * kChunk + pl] = pl < n ? acc[i] * a.scale : -INFINITY;
+            }
+    }
+    __syncthreads();
+    // chunk softmax statistics, one wave per head; p as hi / lo operand rows
+    for (int j = wv; j < G; j += 4) {
+        const float sv = s_s[j * kChunk + lane];
+        const float m = group_max<64>(sv);
+        const float p = (lane < n) ? expf(sv - m) : 0.f;
+        const float l = group_sum<64>(p);
+        const uint16_t h = bf16_rn(p);
+        ph_s[j * kChunk + lane] = h;
+        pl_s[j * kChunk + lane] = bf16_rn(p - bf16_to_f32(h));
+        if (lane == 0) {
+            ml[2 * j] = m;
+            ml[2 * j + 1] = l;
+        }
+    }
+    __syncthreads();
+    // values: wave wv takes dim tiles dt = wv, wv + 4, ...; row (4q + i) = head
+    const size_t rec_stride = (size_t)a.n_chunks * (hd + 4);
+    float *rec0 = a.part + ((size_t)b * a.Hq_s + (size_t)g * G) * rec_stride + (size_t)c * (hd + 4);
+    for (int dt = wv; dt < hd / 16; dt += 4) {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kChunk / 32; ks++) {
+            const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(ph_s + r * kChunk + 32 * ks + 8 * q));
+            const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(pl_s + r * kChunk + 32 * ks + 8 * q));
+            const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(V_g + ((size_t)(4 * ks + q) * hd + 16 * dt + r) * 8));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int j = 4 * q + i;
+            if (j < G)
+                rec0[j * rec_stride + 4 + 16 * dt + r] = acc[i];
+        }
+    }
+    if (tid < G) {
+        rec0[tid * rec_stride] = ml[2 * tid];
+        rec0[tid * rec_stride + 1] = ml[2 * tid + 1];
+    }
+}
+
 // Combine of the chunk partials of one (sequence b, query head h): its output
 // att = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M), chunks summed in chunk
 // order. The (m, l) of the first 64 chunks (wave 0) and the first kCU chunks
@@ -441,9 +672,20 @@ static hipError_t launch_attn_hd(const AttnArgs &a, int B, hipStream_t st)
     return hipGetLastError();
 }
 
+static bool attn_use_mfma(int G, int hd, int kv_bf16) { return kv_bf16 && G >= 4 && (hd == 64 || hd == 128); }
+
 template <bool KBF16>
 static hipError_t launch_attn_t(const AttnArgs &a, int B, hipStream_t st)
 {
+    if (attn_use_mfma(a.G, a.hd, KBF16)) {
+        const dim3 grid(a.n_chunks, a.Hkv_s, B), block(256);
+        const size_t sm = attn_mfma_smem_bytes(a.G, a.hd);
+        if (a.hd == 128)
+            hipLaunchKernelGGL(k_attn_mfma<128>, grid, block, sm, st, a);
+        else
+            hipLaunchKernelGGL(k_attn_mfma<64>, grid, block, sm, st, a);
+        return hipGetLastError();
+    }
     switch (a.hd) {
     case 16: return launch_attn_hd<KBF16, 16>(a, B, st);
     case 32: return launch_attn_hd<KBF16, 32>(a, B, st);
@@ -470,6 +712,10 @@ hipError_t launch_attn(const AttnArgs &a, int kv_bf16, int B, hipStream_t st)
 
 size_t attn_lds_bytes(int G, int hd, int kv_bf16, int n_chunks)
 {
+    if (attn_use_mfma(G, hd, kv_bf16)) {
+        const size_t a = attn_mfma_smem_bytes(G, hd), c = combine_smem_bytes(G, hd, n_chunks);
+        return a > c ? a : c;
+    }
     const int GM = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
     const size_t a = attn_smem_bytes(G, GM, hd, kv_bf16, n_chunks), c = combine_smem_bytes(G, hd, n_chunks);
     return a > c ? a : c;

@@ -132,10 +132,12 @@ def test_tiny_shard_counts(T):
     check_layer(dataclasses.replace(synth.TINY, name=f"tiny_tp{T}", tp=T))
 
 
-def test_micro_gqa_ragged_batch():
+@pytest.mark.parametrize("hd", [32, 64])
+def test_micro_gqa_ragged_batch(hd):
     """GQA (G=4), batch 5, lengths 0, 1, 63, 64 and 130: chunk edges and the
-    attention of a sequence whose only position is the new token."""
-    w = synth.small_llama(name="micro_gqa", dim=128, n_heads=8, n_kv_heads=2, head_dim=32,
+    attention of a sequence whose only position is the new token; head_dim 64
+    takes the MFMA attention kernel, 32 the vector one."""
+    w = synth.small_llama(name=f"micro_gqa{hd}", dim=128, n_heads=8, n_kv_heads=2, head_dim=hd,
                           ffn_hidden=256, tp=2, batch=5, past=(0, 130), w_dtype=synth.BF16,
                           kv_dtype=synth.BF16, seed=77)
     d = synth.llama_inputs(w)
