@@ -21,14 +21,9 @@ __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u)
-        return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
+// fp32 -> bf16, round to nearest, ties to even (gfx950's conversion
+// instruction, v_cvt_pk_bf16_f32; NaN gives a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // ---------------------------------------------------------------- wave reductions
 

@@ -325,11 +325,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// fp32 -> bf16 bits, round to nearest even (the hardware conversion)
-__device__ __forceinline__ uint16_t bf16_rn(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
 __device__ __forceinline__ uint32_t bf16_pair(float lo_elem, float hi_elem)
 {
-    return (uint32_t)bf16_rn(lo_elem) | ((uint32_t)bf16_rn(hi_elem) << 16);
+    return (uint32_t)f32_to_bf16(lo_elem) | ((uint32_t)f32_to_bf16(hi_elem) << 16);
 }
 
 // LDS: queries and probabilities as bf16 hi / lo parts in 16-row MFMA
@@ -427,7 +425,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
                 a.tap_q[(size_t)b * a.Hq_s * hd + h * hd + 2 * p + 1] = r1;
             }
         }
-        const uint16_t h0 = bf16_rn(r0), h1 = bf16_rn(r1);
+        const uint16_t h0 = f32_to_bf16(r0), h1 = f32_to_bf16(r1);
         *(uint32_t *)(qh_s + j * hd + 2 * p) = (uint32_t)h0 | ((uint32_t)h1 << 16);
         *(uint32_t *)(ql_s + j * hd + 2 * p) = bf16_pair(r0 - bf16_to_f32(h0), r1 - bf16_to_f32(h1));
     }
@@ -459,8 +457,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
             const float2 cr = cs[0];
             const float r0 = nk.x * cr.x - nk.y * cr.y, r1 = nk.x * cr.y + nk.y * cr.x;
             const size_t e = head_base + (size_t)L * hd + 2 * p;
-            const uint16_t k0 = bf16_rn(r0), k1 = bf16_rn(r1);
-            const uint16_t v0 = bf16_rn(nv.x), v1 = bf16_rn(nv.y);
+            const uint16_t k0 = f32_to_bf16(r0), k1 = f32_to_bf16(r1);
+            const uint16_t v0 = f32_to_bf16(nv.x), v1 = f32_to_bf16(nv.y);
             ((uint16_t *)a.kc)[e] = k0;
             ((uint16_t *)a.kc)[e + 1] = k1;
             ((uint16_t *)a.vc)[e] = v0;
@@ -506,9 +504,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
         const float m = group_max<64>(sv);
         const float p = (lane < n) ? expf(sv - m) : 0.f;
         const float l = group_sum<64>(p);
-        const uint16_t h = bf16_rn(p);
+        const uint16_t h = f32_to_bf16(p);
         ph_s[j * kChunk + lane] = h;
-        pl_s[j * kChunk + lane] = bf16_rn(p - bf16_to_f32(h));
+        pl_s[j * kChunk + lane] = f32_to_bf16(p - bf16_to_f32(h));
         if (lane == 0) {
             ml[2 * j] = m;
             ml[2 * j + 1] = l;
