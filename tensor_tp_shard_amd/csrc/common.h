@@ -25,6 +25,27 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 // instruction, v_cvt_pk_bf16_f32; NaN gives a quiet NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
+// ---------------------------------------------------------------- buffer loads
+// A raw buffer resource over [p, p + bytes): a load at an offset at or past
+// `bytes` returns zeros without touching memory. Kernels use these to issue
+// loads unconditionally (out-of-range lanes get kOob), which lets the
+// compiler count outstanding loads exactly: a wait for an early small load
+// (an activation row) then does not also wait for the weights behind it.
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes)
+{
+    // 0x00020000: the third descriptor word of a raw 32-bit-format buffer on CDNA
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2); // nontemporal
+}
+
 // ---------------------------------------------------------------- wave reductions
 
 // butterfly over groups of W consecutive lanes (W a power of two <= 64)
