@@ -90,3 +90,12 @@ def test_palm_ffn2d_decode_512_sampled_rows():
 
 def test_palm_ffn2d_prefill_8192_sampled_rows():
     _sampled_rows_check(synth.PALM_PRE, [0, 4095, 8191])
+
+
+def test_ffn2d_large_batch_tiles_and_ragged_tail():
+    """2100 rows (the 128-row, 32-K-per-stage tiles of large batches: 16 full
+    M-tiles and a 52-row tail). Rows at tile edges and the whole tail against
+    the oracle."""
+    w = synth.Ffn2D("ffn2d_big", e_blk=576, f_blk=1152, batch=2100, seed=92)
+    rows = [0, 1, 127, 128, 255, 256, 1023, 1024, 1791, 2047] + list(range(2048, 2100))
+    _sampled_rows_check(w, rows)
