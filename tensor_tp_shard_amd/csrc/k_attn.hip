@@ -336,9 +336,9 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo_elem, float hi_elem)
 // positions of one dim) is one aligned 16-byte read.
 __host__ __device__ inline size_t attn_mfma_smem_bytes(int G, int hd)
 {
-    return (size_t)2 * 16 * hd * 2 +          // q hi, lo
+    return (size_t)2 * 16 * (hd + 8) * 2 +    // q hi, lo (rows padded by 16 bytes)
            sizeof(float) * (size_t)G * kChunk + // scores
-           (size_t)2 * 16 * kChunk * 2 +       // p hi, lo
+           (size_t)2 * 16 * (kChunk + 8) * 2 + // p hi, lo (rows padded by 16 bytes)
            sizeof(float) * 2 * 16 +            // (m, l)
            (size_t)kChunk * (hd * 2 + 16) +    // K
            (size_t)kChunk * hd * 2;            // V groups
@@ -365,12 +365,16 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
     const int n = min(kChunk, L + 1 - t0);
     const bool owner = L < t0 + kChunk;
 
-    uint16_t *qh_s = (uint16_t *)lds_raw;          // [16][hd]
-    uint16_t *ql_s = qh_s + 16 * hd;               // [16][hd]
-    float *s_s = (float *)(ql_s + 16 * hd);        // [G][64]
-    uint16_t *ph_s = (uint16_t *)(s_s + G * kChunk); // [16][64]
-    uint16_t *pl_s = ph_s + 16 * kChunk;           // [16][64]
-    float *ml = (float *)(pl_s + 16 * kChunk);     // [16][2]
+    // operand rows padded by 16 bytes: the 16 lanes that read one 16-byte
+    // slice of 16 consecutive rows then hit 16 different bank groups (with
+    // 256- and 128-byte rows they hit one or two)
+    constexpr int qld = hd + 8, pld = kChunk + 8;
+    uint16_t *qh_s = (uint16_t *)lds_raw;          // [16][qld]
+    uint16_t *ql_s = qh_s + 16 * qld;              // [16][qld]
+    float *s_s = (float *)(ql_s + 16 * qld);       // [G][64]
+    uint16_t *ph_s = (uint16_t *)(s_s + G * kChunk); // [16][pld]
+    uint16_t *pl_s = ph_s + 16 * pld;              // [16][pld]
+    float *ml = (float *)(pl_s + 16 * pld);        // [16][2]
     char *K_s = (char *)(ml + 2 * 16);             // [64][rowb]
     uint16_t *V_g = (uint16_t *)(K_s + kChunk * rowb); // [8][hd][8]
 
@@ -426,11 +430,11 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
             }
         }
         const uint16_t h0 = f32_to_bf16(r0), h1 = f32_to_bf16(r1);
-        *(uint32_t *)(qh_s + j * hd + 2 * p) = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        *(uint32_t *)(ql_s + j * hd + 2 * p) = bf16_pair(r0 - bf16_to_f32(h0), r1 - bf16_to_f32(h1));
+        *(uint32_t *)(qh_s + j * qld + 2 * p) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        *(uint32_t *)(ql_s + j * qld + 2 * p) = bf16_pair(r0 - bf16_to_f32(h0), r1 - bf16_to_f32(h1));
     }
     for (int i = tid; i < (16 - G) * kChunk / 2; i += 256) {
-        const int e = G * kChunk + 2 * i;
+        const int e = (G + 2 * i / kChunk) * pld + (2 * i) % kChunk;
         *(uint32_t *)(ph_s + e) = 0u;
         *(uint32_t *)(pl_s + e) = 0u;
     }
@@ -485,8 +489,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
 #pragma unroll
         for (int s = 0; s < hd / 32; s++) {
             const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(K_s + (16 * wv + r) * rowb + (4 * s + q) * 16));
-            const bf16x8_t qh = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(qh_s + r * hd + 32 * s + 8 * q));
-            const bf16x8_t ql = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(ql_s + r * hd + 32 * s + 8 * q));
+            const bf16x8_t qh = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(qh_s + r * qld + 32 * s + 8 * q));
+            const bf16x8_t ql = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(ql_s + r * qld + 32 * s + 8 * q));
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql, acc, 0, 0, 0);
         }
@@ -505,8 +509,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
         const float p = (lane < n) ? expf(sv - m) : 0.f;
         const float l = group_sum<64>(p);
         const uint16_t h = f32_to_bf16(p);
-        ph_s[j * kChunk + lane] = h;
-        pl_s[j * kChunk + lane] = f32_to_bf16(p - bf16_to_f32(h));
+        ph_s[j * pld + lane] = h;
+        pl_s[j * pld + lane] = f32_to_bf16(p - bf16_to_f32(h));
         if (lane == 0) {
             ml[2 * j] = m;
             ml[2 * j + 1] = l;
@@ -520,8 +524,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
         f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < kChunk / 32; ks++) {
-            const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(ph_s + r * kChunk + 32 * ks + 8 * q));
-            const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(pl_s + r * kChunk + 32 * ks + 8 * q));
+            const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(ph_s + r * pld + 32 * ks + 8 * q));
+            const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(pl_s + r * pld + 32 * ks + 8 * q));
             const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(V_g + ((size_t)(4 * ks + q) * hd + 16 * dt + r) * 8));
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, acc, 0, 0, 0);
