@@ -13,9 +13,13 @@
 // Both products are "NT": C[m][n] = sum_k A[m][k] B[n][k] with A and B stored
 // K-contiguous, which is the operand layout of v_mfma_f32_16x16x32_bf16
 // (each lane holds 8 consecutive k of one row of A and of one row of B).
-//  - workgroup tile BM x 288 (BM = 64 up to 1024 rows, else 128), four
-//    waves as 2 x 2, wave tile BM/2 x 144 (BM/32 x 9 MFMA tiles); 288
-//    divides the PaLM block's 2F = 18432 and E = 2304;
+//  - workgroup tile BM x 288 (BM = 64 up to 256 rows, 128 up to 4095, else
+//    256), waves as (BM/64) x 2 (four, or eight for BM = 256), wave tile
+//    64 x 144 (4 x 9 MFMA tiles; BM/2 x 144 for BM = 64); 288 divides the
+//    PaLM block's 2F = 18432 and E = 2304. The 256-row tiles fetch each
+//    operand tile from L2 for half as many partner tiles as 128-row tiles,
+//    and give the 8192-token down-projection exactly one workgroup per CU
+//    (8 N-tiles x 32 M-tiles): 8192-token block 1.133 -> 1.080 ms;
 //  - a 3-stage LDS ring filled by direct global->LDS loads
 //    (global_load_lds_dwordx4), two stages ahead of the MFMAs, one barrier
 //    per stage, waits by vmcnt and no register staging. Up to 1024 rows a
@@ -40,7 +44,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBN = 288;                                        // N tile
-constexpr int kStages = 3;                                      // LDS ring of 3 stages
 constexpr int kNT = 9;                                          // MFMA tiles per wave in N (144)
 constexpr int kWN = kNT * 16;                                   // wave tile width
 
@@ -74,24 +77,26 @@ __device__ __forceinline__ void wait_vmcnt()
 // KB = 64 (occupancy 1) makes every wave load 8 full 128-byte lines and suits
 // decode-sized M, where the L2 delivery of the weights is the limit; KB = 32
 // (64-byte rows, occupancy 2) hides more latency for large, compute-bound M.
-template <int EPI, int BM, int KB>
-__global__ __launch_bounds__(256, KB == 32 ? 2 : 1) void k_gemm_nt(GemmArgs a)
+template <int EPI, int BM, int KB, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV, (KB == 32 && NWV == 4) ? 2 : 1) void k_gemm_nt(GemmArgs a)
 {
     constexpr int kBK = KB;
+    constexpr int kStages = 3;                         // LDS ring of 3 stages
+    constexpr int kWM = NWV / 2;                       // waves in M (2 in N)
     constexpr int kRowB = KB * 2;                      // bytes of a row per stage
     constexpr int kRowsSeg = 1024 / kRowB;             // rows per 1 KiB wave load
     constexpr int kChunks = kRowB / 16;                // 16-byte chunks per row
-    constexpr int kMT = BM / 32;                       // MFMA tiles per wave in M (BM/2 rows)
+    constexpr int kMT = BM / (16 * kWM);               // MFMA tiles per wave in M (BM/kWM rows)
     constexpr int kStageB = (BM + kBN) * kRowB;        // bytes per stage
     constexpr int kSegs = kStageB / 1024;              // 1 KiB wave loads per stage
     constexpr int kSegsA = BM * kRowB / 1024;          // of which A
-    constexpr int kMaxSegs = (kSegs + 3) / 4;          // per wave
-    constexpr int kMinSegs = kSegs / 4;
+    constexpr int kMaxSegs = (kSegs + NWV - 1) / NWV;  // per wave
+    constexpr int kMinSegs = kSegs / NWV;
     static_assert((BM * kRowB) % 1024 == 0 && kStageB % 1024 == 0, "whole wave loads");
     static_assert(kMaxSegs - kMinSegs <= 1, "waves issue kMaxSegs or kMaxSegs - 1 segments");
     __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageB];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv >> 1, wn = wv & 1;
+    const int wm = wv >> 1, wn = wv & 1; // wave grid kWM x 2
     // grid: x = N-tile (fastest, so the M-tiles of one N-tile share id % 8), y = M-tile, z = split
     const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * BM;
     const int ks0 = blockIdx.z * a.ksteps_per_split;
@@ -110,11 +115,11 @@ __global__ __launch_bounds__(256, KB == 32 ? 2 : 1) void k_gemm_nt(GemmArgs a)
     // lane i of segment t fills LDS slot 64 t + i = (row, physical chunk), so it
     // loads the row's logical chunk physical ^ swx(row). A rows past M read row
     // M-1 (their outputs are never stored).
-    const int nseg = (kSegs - wv + 3) / 4; // kMaxSegs or kMaxSegs - 1
+    const int nseg = (kSegs - wv + NWV - 1) / NWV; // kMaxSegs or kMaxSegs - 1
     const uint16_t *src[kMaxSegs];
 #pragma unroll
     for (int u = 0; u < kMaxSegs; u++) {
-        const int t = wv + 4 * u;
+        const int t = wv + NWV * u;
         const int p = lane, rs = p / kChunks, phys = p % kChunks;
         if (t < kSegsA) {
             const int row = t * kRowsSeg + rs;
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(256, KB == 32 ? 2 : 1) void k_gemm_nt(GemmArgs a)
         for (int u = 0; u < kMaxSegs; u++)
             if (u < nseg)
                 __builtin_amdgcn_global_load_lds((const void *)(src[u] + kbase),
-                                                 (__attribute__((address_space(3))) void *)(base + (wv + 4 * u) * 1024),
+                                                 (__attribute__((address_space(3))) void *)(base + (wv + NWV * u) * 1024),
                                                  16, 0, 0);
     };
 
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(256, KB == 32 ? 2 : 1) void k_gemm_nt(GemmArgs a)
             bf16x8 af[kMT], bfr[kNT];
 #pragma unroll
             for (int i = 0; i < kMT; i++)
-                af[i] = *(const bf16x8 *)(As + swz<KB>(wm * (BM / 2) + i * 16 + (lane & 15), 4 * kk + q));
+                af[i] = *(const bf16x8 *)(As + swz<KB>(wm * (BM / kWM) + i * 16 + (lane & 15), 4 * kk + q));
 #pragma unroll
             for (int j = 0; j < kNT; j++)
                 bfr[j] = *(const bf16x8 *)(Bs + swz<KB>(wn * kWN + j * 16 + (lane & 15), 4 * kk + q));
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(256, KB == 32 ? 2 : 1) void k_gemm_nt(GemmArgs a)
         }
     }
 
-    // lane holds C[m0 + wm*BM/2 + i*16 + 4*(lane/16) + r][n0 + wn*kWN + j*16 + lane%16]
+    // lane holds C[m0 + wm*BM/kWM + i*16 + 4*(lane/16) + r][n0 + wn*kWN + j*16 + lane%16]
     const int col = lane & 15, rq = (lane >> 4) * 4;
     if constexpr (EPI == FFN_UP) {
         const int F = a.N / 2;
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(256, KB == 32 ? 2 : 1) void k_gemm_nt(GemmArgs a)
                 for (int r = 0; r < 4; r++) {
                     const float mine = acc[i][j][r];
                     const float other = __shfl_xor(mine, 8, 64); // lanes col and col ^ 8
-                    const int m = m0 + wm * (BM / 2) + i * 16 + rq + r;
+                    const int m = m0 + wm * (BM / kWM) + i * 16 + rq + r;
                     if (col < 8 && m < a.M)
                         a.H[(size_t)m * F + f] = f32_to_bf16(silu(mine) * other);
                 }
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(256, KB == 32 ? 2 : 1) void k_gemm_nt(GemmArgs a)
                 const int n = n0 + wn * kWN + j * 16 + col;
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const int m = m0 + wm * (BM / 2) + i * 16 + rq + r;
+                    const int m = m0 + wm * (BM / kWM) + i * 16 + rq + r;
                     if (m < a.M)
                         C[(size_t)m * a.N + n] = acc[i][j][r];
                 }
@@ -229,15 +234,19 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float *P, float *Y, 
 
 // Tile rows and K values per stage for a batch of B rows (see k_gemm_nt).
 struct Ffn2dCfg {
-    int bm, kb;
+    int bm, kb, nwv;
 };
 static Ffn2dCfg ffn2d_cfg(int B)
 {
     if (B <= 256)
-        return {64, 64};
+        return {64, 64, 4};
     if (B <= 1024)
-        return {128, 64};
-    return {128, 32};
+        return {128, 64, 4};
+    if (B < 4096)
+        return {128, 32, 4};
+    // 256 x 288 tiles, 8 waves of 64 x 144: each operand tile is fetched from
+    // L2 for half as many partner tiles in M as with 128-row tiles
+    return {256, 32, 8};
 }
 
 // Number of K splits of the down-projection for a batch of B rows: enough
@@ -252,10 +261,10 @@ int ffn2d_splits(int B, int E, int F)
     return s > ksteps ? ksteps : s;
 }
 
-template <int EPI, int BM, int KB>
+template <int EPI, int BM, int KB, int NWV = 4>
 static void launch_gemm(const GemmArgs &g, dim3 grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((k_gemm_nt<EPI, BM, KB>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_nt<EPI, BM, KB, NWV>), grid, dim3(64 * NWV), 0, st, g);
 }
 
 template <int EPI>
@@ -265,8 +274,10 @@ static void launch_gemm_cfg(const Ffn2dCfg &c, const GemmArgs &g, dim3 grid, hip
         launch_gemm<EPI, 64, 64>(g, grid, st);
     else if (c.kb == 64)
         launch_gemm<EPI, 128, 64>(g, grid, st);
-    else
+    else if (c.bm == 128)
         launch_gemm<EPI, 128, 32>(g, grid, st);
+    else
+        launch_gemm<EPI, 256, 32, 8>(g, grid, st);
 }
 
 // which = 0: up-projection + SwiGLU into a.h; which = 1: down-projection

@@ -92,10 +92,12 @@ def test_palm_ffn2d_prefill_8192_sampled_rows():
     _sampled_rows_check(synth.PALM_PRE, [0, 4095, 8191])
 
 
-def test_ffn2d_large_batch_tiles_and_ragged_tail():
-    """2100 rows (the 128-row, 32-K-per-stage tiles of large batches: 16 full
-    M-tiles and a 52-row tail). Rows at tile edges and the whole tail against
-    the oracle."""
-    w = synth.Ffn2D("ffn2d_big", e_blk=576, f_blk=1152, batch=2100, seed=92)
-    rows = [0, 1, 127, 128, 255, 256, 1023, 1024, 1791, 2047] + list(range(2048, 2100))
+@pytest.mark.parametrize("B,tile", [(2100, 128), (4100, 256)])
+def test_ffn2d_large_batch_tiles_and_ragged_tail(B, tile):
+    """Large batches: 2100 rows on the 128-row tiles with 32 K values per
+    stage, 4100 rows on the 256-row tiles of 8 waves; rows at tile edges and
+    the whole ragged tail against the oracle."""
+    w = synth.Ffn2D(f"ffn2d_big{B}", e_blk=576, f_blk=1152, batch=B, seed=92)
+    full = B // tile * tile
+    rows = sorted({0, 1, tile - 1, tile, 2 * tile - 1, full - tile, full - 1} | set(range(full, B)))
     _sampled_rows_check(w, rows)
