@@ -263,6 +263,7 @@ struct AttnArgs {
     uint16_t *att_xf;    // optional: att in the MFMA fragment layout
     int ld_qkv, max_ctx, Hq_s, Hkv_s, G, hd, n_chunks;
     float scale;
+    int B;               // sequences (set by launch_attn)
 };
 
 struct WireArgs {

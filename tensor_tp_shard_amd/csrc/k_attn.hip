@@ -351,17 +351,35 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
     constexpr int hd = HD;
     constexpr int rowb = hd * 2 + 16; // padded K row
     const int G = a.G;
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int g = blockIdx.y;
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, q = lane >> 4, r = lane & 15;
-    const int L = a.lens[b];
-    if (L < 0 || L >= a.max_ctx) { // skipped sequence: flagged here, zeroed by the combine
-        if (c == 0 && g == 0 && tid == 0)
-            atomicOr(a.err, 1u);
-        return;
+    // Compact chunk numbering: workgroup x takes the x-th chunk in the order
+    // (sequence, chunk) over the chunks the sequences actually have, so the
+    // working workgroups are the first ones dispatched and the surplus of the
+    // n_chunks x B grid exits at its end. (With x = chunk and z = sequence,
+    // the chunks past each sequence's end sat between working ones, and at
+    // 3 workgroups per CU the last sequences' chunks waited for a second
+    // round of slots.) A skipped sequence (lens outside [0, max_ctx)) has no
+    // chunks; workgroup 0 of kv head 0 flags it, the combine zeroes its rows.
+    int b = -1, c = 0, L = 0, before = 0;
+    bool bad = false;
+    for (int i = 0; i < a.B; i++) {
+        const int Li = a.lens[i];
+        const bool ok = Li >= 0 && Li < a.max_ctx;
+        bad |= !ok;
+        const int ni = ok ? Li / kChunk + 1 : 0;
+        if (b < 0 && (int)blockIdx.x < before + ni) {
+            b = i;
+            c = blockIdx.x - before;
+            L = Li;
+        }
+        before += ni;
     }
-    const int t0 = c * kChunk;
-    if (t0 > L)
+    if (bad && blockIdx.x == 0 && g == 0 && tid == 0)
+        atomicOr(a.err, 1u);
+    if (b < 0)
         return;
+    const int t0 = c * kChunk;
     const int n = min(kChunk, L + 1 - t0);
     const bool owner = L < t0 + kChunk;
 
@@ -680,7 +698,7 @@ template <bool KBF16>
 static hipError_t launch_attn_t(const AttnArgs &a, int B, hipStream_t st)
 {
     if (attn_use_mfma(a.G, a.hd, KBF16)) {
-        const dim3 grid(a.n_chunks, a.Hkv_s, B), block(256);
+        const dim3 grid(a.n_chunks * B, a.Hkv_s), block(256);
         const size_t sm = attn_mfma_smem_bytes(a.G, a.hd);
         if (a.hd == 128)
             hipLaunchKernelGGL(k_attn_mfma<128>, grid, block, sm, st, a);
@@ -702,8 +720,10 @@ bool attn_hd_supported(int hd) { return hd == 16 || hd == 32 || hd == 48 || hd =
 
 // Host-checked preconditions: 1 <= G <= 8, attn_hd_supported(hd),
 // n_chunks = ceil(max_ctx / 64), attn_lds_bytes(...) <= 64 KiB.
-hipError_t launch_attn(const AttnArgs &a, int kv_bf16, int B, hipStream_t st)
+hipError_t launch_attn(const AttnArgs &args, int kv_bf16, int B, hipStream_t st)
 {
+    AttnArgs a = args;
+    a.B = B;
     const hipError_t e = kv_bf16 ? launch_attn_t<true>(a, B, st) : launch_attn_t<false>(a, B, st);
     if (e != hipSuccess)
         return e;

@@ -214,6 +214,28 @@ def test_bad_length_sets_error_word_and_skips_row():
     assert L.error_word(0) == 0  # read clears
 
 
+def test_bad_length_mfma_attention_skips_row():
+    """Same contract on the MFMA attention path (bf16 cache, 4 q heads per kv
+    head, hd 64): the other sequences' chunks still run and match the oracle."""
+    w = synth.small_llama(name="micro_err_mfma", dim=512, n_heads=8, n_kv_heads=2, head_dim=64,
+                          ffn_hidden=256, tp=1, batch=3, past=(70, 200), w_dtype=synth.BF16,
+                          kv_dtype=synth.BF16, seed=81)
+    d = synth.llama_inputs(w)
+    say("error word, MFMA attention")
+    L = Layer(w, d)
+    bad = d["lens"].copy()
+    bad[1] = -1
+    g = L.run(d["x"], bad, with_taps=True)
+    assert L.error_word(0) == tp.TP_DERR_LEN
+    att = g["taps_att"][0]["att"]
+    assert np.all(att[1] == 0)
+    kc, vc = d["kcache"].copy(), d["vcache"].copy()
+    o = oracle.llama_layer(w, d, d["x"], d["lens"], kc, vc)
+    for b in (0, 2):
+        e = rel_l2(att[b], o["att"][0][b])
+        assert e <= 1e-3, f"row {b} rel-L2 {e:.3e}"
+
+
 def test_graph_replay_matches_eager():
     import torch
     w = synth.small_llama(name="micro_graph", dim=256, n_heads=8, n_kv_heads=8, head_dim=32,
