@@ -27,19 +27,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_
 
 // ---------------------------------------------------------------- buffer loads
 // A raw buffer resource over [p, p + bytes): a load at an offset at or past
-// `bytes` returns zeros without touching memory. Kernels use these to issue
-// loads unconditionally (out-of-range lanes get kOob), which lets the
-// compiler count outstanding loads exactly: a wait for an early small load
-// (an activation row) then does not also wait for the weights behind it.
+// `bytes` returns zeros without touching memory. The decode projections issue
+// their weight loads through these unconditionally (out-of-range lanes get
+// kOob), which lets the compiler count outstanding loads exactly: a wait for
+// an earlier small load (an activation row) then does not also wait for the
+// weights behind it.
 constexpr uint32_t kOob = 0x80000000u;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes)
 {
     // 0x00020000: the third descriptor word of a raw 32-bit-format buffer on CDNA
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 __device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
