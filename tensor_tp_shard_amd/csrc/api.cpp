@@ -468,10 +468,15 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
     float *scales = qpart ? (float *)((char *)wire_out + tp_wire_scales_offset(&s->cfg, B)) : nullptr;
     int32_t rc;
 
-    // batch 5..16: RMSNorm kernel writing xn and its MFMA fragments, MFMA projections
+    // batch 5..16: MFMA projections. A split-K up-projection folds the
+    // RMSNorm in (fragments of x g built per K slice, each row scaled by its
+    // 1 / rms in the epilogue); otherwise a RMSNorm kernel writes xn and its
+    // fragments. The int8 round trip of quantised inputs needs the kernel.
     const bool mfma = s->mfma_ok && B > 4;
-    // RMSNorm: otherwise fused into the projection's prologue when the batch's
-    // rows fit in LDS, else a kernel of its own writing xn
+    const int up_n = stage == TP_STAGE_ATTN ? s->n_qkv : 2 * s->Fs;
+    const bool sk_norm = mfma && !qin && s->w_skp && gemv_sk_used(up_n, s->D);
+    // RMSNorm below batch 5: fused into the projection's prologue when the
+    // batch's rows fit in LDS, else a kernel of its own writing xn
     const bool fuse_norm = !mfma && gemv_fused_ok(B, s->D);
     const float *in = (const float *)x;
     uint16_t *xfx = mfma ? (uint16_t *)(s->ws + s->w_xfx) : nullptr;
@@ -487,7 +492,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         up.eps = s->cfg.norm_eps;
         up.qin = qin ? 1 : 0;
         up.xn_tap = tp.xn;
-    } else {
+    } else if (!sk_norm || tp.xn) { // with sk_norm only for the xn tap
         float *xn = (float *)(s->ws + s->w_xn);
         NormArgs na{in, gain, xn, tp.xn, xfx, B, s->D, s->cfg.norm_eps, qin ? 1 : 0};
         rc = timed(s, KID_RMSNORM, st, "rmsnorm", [&] { return launch_rmsnorm(na, st); });
@@ -505,11 +510,12 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         down.mo = *mo;
     down.B = B;
     const int Kd = stage == TP_STAGE_ATTN ? s->Hq_s * s->hd : s->Fs;
-    auto run_gemv = [&](const GemvArgs &g, const uint16_t *xf, uint16_t *yf, int epi) {
+    auto run_gemv = [&](const GemvArgs &g, const uint16_t *xf, uint16_t *yf, int epi, bool norm) {
         if (!mfma)
             return launch_gemv(g, wbf, epi, st);
         MfmaGemvArgs m{(const uint16_t *)g.W, xf, g.y, g.tap, yf, g.N, g.K, g.B, g.ldy, 1, g.mo,
-                       s->w_skp ? (float *)(s->ws + s->w_skp) : nullptr, 0, 0};
+                       s->w_skp ? (float *)(s->ws + s->w_skp) : nullptr, 0, 0,
+                       norm ? in : nullptr, norm ? gain : nullptr, s->cfg.norm_eps};
         return launch_gemv_mfma(m, epi, st);
     };
 
@@ -521,7 +527,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         up.y = qkv;
         up.N = s->n_qkv;
         up.ldy = s->n_qkv;
-        rc = timed(s, KID_GEMV_QKV, st, "gemv qkv", [&] { return run_gemv(up, xfx, nullptr, EPI_STORE); });
+        rc = timed(s, KID_GEMV_QKV, st, "gemv qkv", [&] { return run_gemv(up, xfx, nullptr, EPI_STORE, sk_norm); });
         if (rc)
             return rc;
         float *att = (float *)(s->ws + s->w_att);
@@ -555,7 +561,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         down.x = att;
         down.K = Kd;
         down.ldx = Kd;
-        rc = timed(s, KID_GEMV_WO, st, "gemv wo", [&] { return run_gemv(down, xfatt, nullptr, EPI_STORE); });
+        rc = timed(s, KID_GEMV_WO, st, "gemv wo", [&] { return run_gemv(down, xfatt, nullptr, EPI_STORE, false); });
         if (rc)
             return rc;
     } else {
@@ -565,14 +571,14 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         up.tap = tp.a;
         up.N = 2 * s->Fs;
         up.ldy = s->Fs;
-        rc = timed(s, KID_GEMV_W13, st, "gemv w13", [&] { return run_gemv(up, xfx, xfa, EPI_SWIGLU); });
+        rc = timed(s, KID_GEMV_W13, st, "gemv w13", [&] { return run_gemv(up, xfx, xfa, EPI_SWIGLU, sk_norm); });
         if (rc)
             return rc;
         down.W = s->packed + s->o_w2;
         down.x = a;
         down.K = Kd;
         down.ldx = Kd;
-        rc = timed(s, KID_GEMV_W2, st, "gemv w2", [&] { return run_gemv(down, xfa, nullptr, EPI_STORE); });
+        rc = timed(s, KID_GEMV_W2, st, "gemv w2", [&] { return run_gemv(down, xfa, nullptr, EPI_STORE, false); });
         if (rc)
             return rc;
     }

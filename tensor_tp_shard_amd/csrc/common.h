@@ -38,6 +38,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32
     // 0x00020000: the third descriptor word of a raw 32-bit-format buffer on CDNA
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
 __device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2); // nontemporal
@@ -225,8 +229,15 @@ struct MfmaGemvArgs {
     uint16_t *yf;        // EPI_SWIGLU: optional y in the fragment layout (K' = N/2)
     int N, K, B, ldy, wk; // wk = waves per 16-row tile (K split)
     MergeIn mo;          // EPI_STORE, fp32 wires: fused merge (y is wire mo.own)
-    float *part;         // split-K partials [S][B][N] (gemv_sk_part_floats), or null
+    float *part;         // split-K partials [S][B][N] then [S][16] row sums of squares
+                         // (gemv_sk_part_floats floats), or null
     int nbs, S;          // split-K: 128-blocks per K slice, number of slices (set by the launcher)
+    // split-K with the RMSNorm folded in (xs != null, instead of xf): the
+    // operand is xs[b][k] * g[k] (xs the raw fp32 stage input, row stride K)
+    // and the epilogue scales row b by 1 / sqrt(mean_k xs[b][k]^2 + eps)
+    const float *xs;
+    const float *g;
+    float eps;
 };
 
 enum GemvEpi { EPI_STORE = 0, EPI_SWIGLU = 1 };
@@ -298,6 +309,7 @@ hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st);
 hipError_t launch_gemv(const GemvArgs &a, int w_bf16, int epi, hipStream_t st);
 hipError_t launch_gemv_mfma(const MfmaGemvArgs &a, int epi, hipStream_t st);
 size_t gemv_sk_part_floats(int N, int K, int B);
+bool gemv_sk_used(int N, int K); // the batch-16 N x K projection takes the split-K kernels
 bool gemv_mfma_ok(int B, int N, int K, int w_bf16);
 hipError_t launch_attn(const AttnArgs &a, int kv_bf16, int B, hipStream_t st);
 size_t attn_lds_bytes(int G, int hd, int kv_bf16, int n_chunks);

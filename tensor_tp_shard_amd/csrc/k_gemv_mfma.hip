@@ -171,6 +171,14 @@ __global__ __launch_bounds__(64 * (T == 1 ? kMaxWk : 8)) void k_gemv_mfma(MfmaGe
 // [S][B][N]; k_gemv_sk_epi sums the slices in order and applies the
 // epilogue. (In a probe on the 70B up-projection shape the activations in
 // LDS took the stream from 38 to 26 us.)
+//
+// RMSNorm folded in (the up-projections, xs set): RMSNorm is a per-row
+// scale of x g, so W (g x / rms(x)) = (W (g x)) / rms(x). Each workgroup
+// builds its slice's fragments of x g from the raw fp32 input (same bytes
+// as the ready fragments), the workgroups of tile column 0 also store each
+// row's sum of squares over their slice, and the reduce scales row b by
+// 1 / sqrt(sum / K + eps). This drops the RMSNorm launch that had to finish
+// before the projection (70B step 97.4 -> 88.9 us with the reduce below).
 constexpr int kSkWaves = 8, kSkMaxNbs = 8;
 
 // s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding)
@@ -181,24 +189,60 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int T>
+// NORM: the fragments are built here from the raw fp32 input (RMSNorm
+// folded in, see MfmaGemvArgs::xs): thread u of the slice takes the 8
+// consecutive k = 128 (jb + jl) + 32 s + 8 q of row b, where u = ((jl * 4 +
+// s) * 4 + q) * 16 + b is also its 16-byte unit in the fragment layout;
+// the workgroups of tile column 0 add up each row's squares over the slice.
+constexpr int kSkUnits = kSkMaxNbs * 256 / (64 * kSkWaves); // 8-element units per thread
+
+template <int T, bool NORM>
 __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
 {
     constexpr int P = 2; // 128-wide K blocks in flight per wave
     __shared__ __attribute__((aligned(1024))) char lds[kSkMaxNbs * 8192];
+    __shared__ float ssr[NORM ? 64 * kSkWaves : 1];
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
     const int ks = blockIdx.y, jb = ks * a.nbs;
     const int nbl = min(a.nbs, (a.K >> 7) - jb); // blocks in this slice
-    // the slice's fragments: nbl x 8 KiB = 8 nbl wave loads of 1 KiB
-    const u32x4 *xf = (const u32x4 *)a.xf + (size_t)jb * 512;
-    for (int seg = wv; seg < 8 * nbl; seg += kSkWaves)
-        __builtin_amdgcn_global_load_lds((const void *)(xf + (size_t)seg * 64 + lane),
-                                         (__attribute__((address_space(3))) void *)(lds + seg * 1024), 16, 0, 0);
+    // every load below is unconditional (buffer loads, kOob past the data):
+    // the compiler then counts outstanding loads exactly, so a wait for the
+    // activations never also waits for weights issued after them
+    u32x4 xv[NORM ? kSkUnits : 1][2], gv[NORM ? kSkUnits : 1][2];
+    if constexpr (NORM) {
+        const int b = threadIdx.x & 15;
+        const __amdgpu_buffer_rsrc_t xr = buf_rsrc(a.xs, (uint32_t)a.B * a.K * 4);
+        const __amdgpu_buffer_rsrc_t gr = buf_rsrc(a.g, (uint32_t)a.K * 4);
+#pragma unroll
+        for (int i = 0; i < kSkUnits; i++) {
+            const int u = threadIdx.x + 64 * kSkWaves * i;
+            const uint32_t k = (uint32_t)(jb << 7) + (u >> 4) * 8;
+            const bool in = u < 256 * nbl;
+            const uint32_t xo = in && b < a.B ? ((uint32_t)b * a.K + k) * 4 : kOob;
+            xv[i][0] = buf_load16(xr, xo);
+            xv[i][1] = buf_load16(xr, xo + 16);
+            gv[i][0] = buf_load16(gr, in ? k * 4 : kOob);
+            gv[i][1] = buf_load16(gr, in ? k * 4 + 16 : kOob);
+        }
+        __builtin_amdgcn_sched_barrier(0); // the activation loads stay ahead of the weights
+    } else {
+        // the slice's fragments: nbl x 8 KiB = 8 nbl wave loads of 1 KiB
+        const u32x4 *xf = (const u32x4 *)a.xf + (size_t)jb * 512;
+        for (int seg = wv; seg < 8 * nbl; seg += kSkWaves)
+            __builtin_amdgcn_global_load_lds((const void *)(xf + (size_t)seg * 64 + lane),
+                                             (__attribute__((address_space(3))) void *)(lds + seg * 1024), 16, 0, 0);
+    }
     const int n0 = (blockIdx.x * kSkWaves + wv) * 16 * T;
-    const u32x4 *wrow[T];
+    // one resource per 16-row tile from the slice start of its first row (wave
+    // uniform, so the descriptor stays in scalar registers); lane (q, r) reads
+    // row r at r K + 128 (block) + 32 s + 8 q elements, blocks past the slice
+    // at kOob
+    const int n0u = (blockIdx.x * kSkWaves + __builtin_amdgcn_readfirstlane(wv)) * 16 * T;
+    __amdgpu_buffer_rsrc_t Wr[T];
 #pragma unroll
     for (int t = 0; t < T; t++)
-        wrow[t] = (const u32x4 *)(a.W + (size_t)(n0 + 16 * t + r) * a.K + 8 * q) + (size_t)jb * 16;
+        Wr[t] = buf_rsrc(a.W + (size_t)(n0u + 16 * t) * a.K + (size_t)jb * 128, (uint32_t)(16 * a.K - jb * 128) * 2);
+    const uint32_t lofs = (uint32_t)r * a.K * 2 + 16 * q;
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; t++)
@@ -207,21 +251,62 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
         u32x4 w[P][T][4];
 #pragma unroll
         for (int p = 0; p < P; p++)
-            if (jl + p < nbl)
 #pragma unroll
-                for (int t = 0; t < T; t++)
+            for (int t = 0; t < T; t++)
 #pragma unroll
-                    for (int s = 0; s < 4; s++)
-                        w[p][t][s] = __builtin_nontemporal_load(wrow[t] + (size_t)(jl + p) * 16 + 4 * s);
+                for (int s = 0; s < 4; s++)
+                    w[p][t][s] = buf_load16_nt(Wr[t], jl + p < nbl ? lofs + (uint32_t)(jl + p) * 256 + 64 * s : kOob);
+        // all P blocks' loads are issued before the first MFMA waits on one
+        // (else the scheduler moves each load next to its use)
+        __builtin_amdgcn_sched_barrier(0);
         if (jl == 0) {
-            // this wave's fragment loads (issued before these weight loads,
-            // loads complete in order) are done once only the weight loads
-            // remain; after the barrier every wave's fragments are in LDS
-            if (nbl >= P)
+            if constexpr (NORM) {
+                // x g as bf16 hi / lo fragments into LDS (the compiler waits
+                // for the activation loads only, issued before the weights)
+                float ss = 0.f;
+#pragma unroll
+                for (int i = 0; i < kSkUnits; i++) {
+                    const int u = threadIdx.x + 64 * kSkWaves * i;
+                    if (u < 256 * nbl) {
+                        float e[8], f[8];
+#pragma unroll
+                        for (int c = 0; c < 4; c++) {
+                            e[c] = __uint_as_float(xv[i][0][c]);
+                            e[4 + c] = __uint_as_float(xv[i][1][c]);
+                            f[c] = __uint_as_float(gv[i][0][c]);
+                            f[4 + c] = __uint_as_float(gv[i][1][c]);
+                        }
+                        uint32_t hw[4], lw[4];
+#pragma unroll
+                        for (int t2 = 0; t2 < 4; t2++) {
+                            const float v0 = e[2 * t2] * f[2 * t2], v1 = e[2 * t2 + 1] * f[2 * t2 + 1];
+                            const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+                            hw[t2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                            lw[t2] = (uint32_t)f32_to_bf16(v0 - bf16_to_f32(h0)) |
+                                     ((uint32_t)f32_to_bf16(v1 - bf16_to_f32(h1)) << 16);
+                            ss += e[2 * t2] * e[2 * t2] + e[2 * t2 + 1] * e[2 * t2 + 1];
+                        }
+                        const int jl2 = u >> 8, s2 = (u >> 6) & 3, ln = u & 63;
+                        *(u32x4 *)(lds + ((jl2 * 2 + 0) * 4 + s2) * 1024 + ln * 16) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                        *(u32x4 *)(lds + ((jl2 * 2 + 1) * 4 + s2) * 1024 + ln * 16) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+                    }
+                }
+                ssr[threadIdx.x] = ss;
+                __syncthreads(); // LDS only: the weight loads stay in flight
+                if (blockIdx.x == 0 && threadIdx.x < 16) {
+                    // row b's squares over the slice, threads b, b + 16, ... in order
+                    float t3 = 0.f;
+                    for (int i = 0; i < 4 * kSkWaves; i++)
+                        t3 += ssr[threadIdx.x + 16 * i];
+                    a.part[(size_t)a.S * a.B * a.N + ks * 16 + threadIdx.x] = t3;
+                }
+            } else {
+                // this wave's fragment loads (issued before these weight loads,
+                // loads complete in order) are done once only the weight loads
+                // remain; after the barrier every wave's fragments are in LDS
                 wait_vmcnt<P * T * 4>();
-            else
-                wait_vmcnt<T * 4>();
-            __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_s_barrier();
+            }
         }
 #pragma unroll
         for (int p = 0; p < P; p++)
@@ -249,6 +334,8 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
 // epilogue: store (+ tap, + fused merge), or SwiGLU of the interleaved
 // (W1_f, W3_f) rows (+ tap, + fragment copy for the next projection).
 // One thread per 4 consecutive n of one batch row.
+constexpr int kSkEpiU = 32;
+
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemv_sk_epi(MfmaGemvArgs a)
 {
@@ -259,17 +346,24 @@ __global__ __launch_bounds__(256) void k_gemv_sk_epi(MfmaGemvArgs a)
     const int b = i / n4, n = (i % n4) * 4;
     const size_t slice = (size_t)a.B * a.N;
     const float *p = a.part + (size_t)b * a.N + n;
-    // slices 8 at a time, all 8 loads in flight before the in-order adds
-    constexpr int U = 8;
+    const float *ssp = a.part + (size_t)a.S * slice + b; // [S][16] row sums of squares
+    // up to kSkEpiU slices per round, all their loads (and, with the RMSNorm
+    // folded in, the slices' sums of squares of row b) in flight before the
+    // in-order adds: one round trip for every shape with S <= kSkEpiU
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < a.S; s0 += U) {
-        float4 u[U];
+    float t = 0.f;
+    for (int s0 = 0; s0 < a.S; s0 += kSkEpiU) {
+        float4 u[kSkEpiU];
+        float q2[kSkEpiU];
 #pragma unroll
-        for (int k = 0; k < U; k++)
-            if (s0 + k < a.S)
+        for (int k = 0; k < kSkEpiU; k++)
+            if (s0 + k < a.S) {
                 u[k] = *(const float4 *)(p + (s0 + k) * slice);
+                if (a.xs)
+                    q2[k] = ssp[16 * (s0 + k)];
+            }
 #pragma unroll
-        for (int k = 0; k < U; k++)
+        for (int k = 0; k < kSkEpiU; k++)
             if (s0 + k < a.S) {
                 if (s0 + k == 0) {
                     v = u[0];
@@ -279,8 +373,16 @@ __global__ __launch_bounds__(256) void k_gemv_sk_epi(MfmaGemvArgs a)
                     v.z += u[k].z;
                     v.w += u[k].w;
                 }
+                if (a.xs)
+                    t += q2[k];
             }
     }
+    // RMSNorm folded in: row b times 1 / rms of input row b
+    const float rs = a.xs ? 1.0f / sqrtf(t / (float)a.K + a.eps) : 1.f;
+    v.x *= rs;
+    v.y *= rs;
+    v.z *= rs;
+    v.w *= rs;
     if constexpr (EPI == EPI_SWIGLU) {
         const int f = n >> 1; // rows (n, n+1) and (n+2, n+3) are features f, f+1
         const float h0 = silu(v.x) * v.y, h1 = silu(v.z) * v.w;
@@ -320,7 +422,7 @@ __global__ __launch_bounds__(256) void k_gemv_sk_epi(MfmaGemvArgs a)
 }
 
 // Split-K shape for an N x K projection: tiles per wave T, 128-blocks per
-// slice and slices, aiming at about 256 workgroups; T = 0 when the shape
+// slice and slices, aiming at up to 256 workgroups; T = 0 when the shape
 // does not tile (the per-tile kernel takes it).
 struct SkShape {
     int T, nbs, S, R;
@@ -341,7 +443,10 @@ static SkShape sk_shape(int N, int K)
     else
         return sh;
     sh.R = N / (128 * sh.T);
-    const int st = (256 + sh.R - 1) / sh.R;
+    // at most 256 workgroups: the folded-RMSNorm kernel holds one 8-wave
+    // workgroup per CU, so a 257th would run in a second round (70B
+    // up-projection: 280 -> 224 workgroups, 34.8 -> 33.5 us)
+    const int st = 256 / sh.R > 1 ? 256 / sh.R : 1;
     int nbs = (nb + st - 1) / st;
     nbs = nbs < 2 ? 2 : nbs > kSkMaxNbs ? kSkMaxNbs : nbs;
     sh.nbs = nbs;
@@ -352,8 +457,10 @@ static SkShape sk_shape(int N, int K)
 size_t gemv_sk_part_floats(int N, int K, int B)
 {
     const SkShape sh = sk_shape(N, K);
-    return sh.T ? (size_t)sh.S * B * N : 0;
+    return sh.T ? (size_t)sh.S * (B * N + 16) : 0;
 }
+
+bool gemv_sk_used(int N, int K) { return sk_shape(N, K).T != 0; }
 
 bool gemv_mfma_ok(int B, int N, int K, int w_bf16)
 {
@@ -367,14 +474,23 @@ hipError_t launch_gemv_mfma(const MfmaGemvArgs &a0, int epi, hipStream_t st)
     MfmaGemvArgs a = a0;
     const int nb = a.K / 128;
     const SkShape sh = sk_shape(a.N, a.K);
+    if (a.xs && !(a.part && sh.T)) // the folded RMSNorm exists on the split-K path only
+        return hipErrorInvalidValue;
     if (a.part && sh.T) {
         a.nbs = sh.nbs;
         a.S = sh.S;
         const dim3 grid(sh.R, sh.S), block(64 * kSkWaves);
-        if (sh.T == 2)
-            hipLaunchKernelGGL(k_gemv_sk<2>, grid, block, 0, st, a);
-        else
-            hipLaunchKernelGGL(k_gemv_sk<1>, grid, block, 0, st, a);
+        if (a.xs) {
+            if (sh.T == 2)
+                hipLaunchKernelGGL((k_gemv_sk<2, true>), grid, block, 0, st, a);
+            else
+                hipLaunchKernelGGL((k_gemv_sk<1, true>), grid, block, 0, st, a);
+        } else {
+            if (sh.T == 2)
+                hipLaunchKernelGGL((k_gemv_sk<2, false>), grid, block, 0, st, a);
+            else
+                hipLaunchKernelGGL((k_gemv_sk<1, false>), grid, block, 0, st, a);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

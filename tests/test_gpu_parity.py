@@ -147,6 +147,22 @@ def test_micro_gqa_ragged_batch(hd):
     check_layer(w, d)
 
 
+def test_splitk_folded_norm_ragged_batch():
+    """Batch 7 at dim 4096: both up-projections take the split-K kernels with
+    the RMSNorm folded in (QKV with one 16-row tile per wave, W1/W3 with
+    two), and operand rows 7..15 are zero. Checked against the oracle (with
+    taps, where a RMSNorm kernel also runs for the xn tap alone), then the
+    output without taps must be bitwise the same."""
+    w = synth.small_llama(name="splitk_norm_b7", dim=4096, n_heads=8, n_kv_heads=2, head_dim=128,
+                          ffn_hidden=4096, tp=2, batch=7, past=(1, 100), w_dtype=synth.BF16,
+                          kv_dtype=synth.BF16, seed=79)
+    d = synth.llama_inputs(w)
+    _, g, _ = check_layer(w, d)
+    say("splitk_norm_b7 without taps")
+    r = Layer(w, d).run(d["x"], d["lens"], with_taps=False)
+    assert np.array_equal(r["out"].view(np.uint32), g["out"].view(np.uint32))
+
+
 def test_determinism_and_batch_rows():
     w = synth.small_llama(name="micro_b16", dim=256, n_heads=8, n_kv_heads=4, head_dim=32,
                           ffn_hidden=512, tp=2, batch=16, past=(1, 200), w_dtype=synth.BF16,
