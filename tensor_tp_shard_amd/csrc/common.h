@@ -49,23 +49,56 @@ __device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_
 
 // ---------------------------------------------------------------- wave reductions
 
-// butterfly over groups of W consecutive lanes (W a power of two <= 64)
+// Rotation right by N lanes inside each 16-lane row (DPP row_ror:N, a VALU
+// operand modifier: no LDS round trip).
+template <int N>
+__device__ __forceinline__ float row_ror(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_value(float v, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Reductions over groups of W consecutive lanes (W a power of two <= 64),
+// result in every lane of the group; all lanes of the wave active. W = 64:
+// rotations by 8, 4, 2, 1 leave each 16-lane row's total in its lanes, then
+// the four row totals (lanes 0, 16, 32, 48) are combined as wave-uniform
+// values, (r0 + r1) + (r2 + r3). Smaller W: xor butterfly through
+// ds_bpermute.
 template <int W>
 __device__ __forceinline__ float group_sum(float v)
 {
+    if constexpr (W == 64) {
+        v += row_ror<8>(v);
+        v += row_ror<4>(v);
+        v += row_ror<2>(v);
+        v += row_ror<1>(v);
+        return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+    } else {
 #pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, kWave);
-    return v;
+        for (int o = W / 2; o > 0; o >>= 1)
+            v += __shfl_xor(v, o, kWave);
+        return v;
+    }
 }
 
 template <int W>
 __device__ __forceinline__ float group_max(float v)
 {
+    if constexpr (W == 64) {
+        v = fmaxf(v, row_ror<8>(v));
+        v = fmaxf(v, row_ror<4>(v));
+        v = fmaxf(v, row_ror<2>(v));
+        v = fmaxf(v, row_ror<1>(v));
+        return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+    } else {
 #pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1)
-        v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+        for (int o = W / 2; o > 0; o >>= 1)
+            v = fmaxf(v, __shfl_xor(v, o, kWave));
+        return v;
+    }
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }

@@ -361,20 +361,38 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
     // 3 workgroups per CU the last sequences' chunks waited for a second
     // round of slots.) A skipped sequence (lens outside [0, max_ctx)) has no
     // chunks; workgroup 0 of kv head 0 flags it, the combine zeroes its rows.
+    // Each wave reads 64 lengths per load (lane i: sequence i0 + i) and an
+    // inclusive scan of their chunk counts gives every sequence's chunk
+    // range: one load round trip for up to 64 sequences, where a loop over
+    // scalar loads waited for each length in turn (2-6 us at batch 16).
     int b = -1, c = 0, L = 0, before = 0;
     bool bad = false;
-    for (int i = 0; i < a.B; i++) {
-        const int Li = a.lens[i];
+    for (int i0 = 0; i0 < a.B; i0 += 64) {
+        const int i = i0 + lane;
+        const int Li = i < a.B ? a.lens[i] : 0;
         const bool ok = Li >= 0 && Li < a.max_ctx;
-        bad |= !ok;
-        const int ni = ok ? Li / kChunk + 1 : 0;
-        if (b < 0 && (int)blockIdx.x < before + ni) {
-            b = i;
-            c = blockIdx.x - before;
-            L = Li;
+        bad |= __ballot(i < a.B && !ok) != 0ull;
+        const int ni = i < a.B && ok ? Li / kChunk + 1 : 0;
+        int inc = ni;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(inc, o, 64);
+            inc += lane >= o ? t : 0;
         }
-        before += ni;
+        inc += before;
+        const int x = blockIdx.x;
+        const unsigned long long m = __ballot(x >= inc - ni && x < inc);
+        if (b < 0 && m) {
+            const int ln = __ffsll((unsigned long long)m) - 1;
+            b = i0 + ln;
+            L = __shfl(Li, ln, 64);
+            c = x - (__shfl(inc, ln, 64) - __shfl(ni, ln, 64));
+        }
+        before = __shfl(inc, 63, 64);
     }
+    b = __builtin_amdgcn_readfirstlane(b);
+    c = __builtin_amdgcn_readfirstlane(c);
+    L = __builtin_amdgcn_readfirstlane(L);
     if (bad && blockIdx.x == 0 && g == 0 && tid == 0)
         atomicOr(a.err, 1u);
     if (b < 0)
