@@ -71,6 +71,8 @@ def sources_sha256(sources) -> str:
 
 
 GEMV_SOURCES = ("tensor_tp_shard_amd/csrc/k_gemv.hip", "tensor_tp_shard_amd/csrc/common.h")
+# batch 5..16 with bf16 weights: the MFMA projections
+GEMV_MFMA_SOURCES = ("tensor_tp_shard_amd/csrc/k_gemv_mfma.hip", "tensor_tp_shard_amd/csrc/common.h")
 FFN2D_SOURCES = ("tensor_tp_shard_amd/csrc/k_ffn2d.hip", "tensor_tp_shard_amd/csrc/common.h")
 
 
@@ -255,7 +257,9 @@ def run_llama(args, w):
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {"kernel": "gemv_w13_swiglu", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(f"traffic_gemv_w13_swiglu_{w.name}.md", GEMV_SOURCES),
+                     "traffic": measured_traffic(
+                         f"traffic_gemv_w13_swiglu_{w.name}.md",
+                         GEMV_MFMA_SOURCES if w.w_dtype == synth.BF16 and B > 4 else GEMV_SOURCES),
                      "bytes_per_launch": int(w13bytes),
                      "avg_launch_us": round(k_ms * 1e3, 3), "launches": n},
     }

@@ -501,15 +501,16 @@ hipError_t launch_gemv_mfma(const MfmaGemvArgs &a0, int epi, hipStream_t st)
             hipLaunchKernelGGL(k_gemv_sk_epi<EPI_STORE>, eg, dim3(256), 0, st, a);
         return hipGetLastError();
     }
-    // K split so that each wave streams about 8 blocks (8 x 4 KiB of weights
-    // per tile): fewer, longer waves keep every workgroup of a large
-    // projection resident at once (measured best of 4..16 blocks per wave on
-    // the 70B shapes). Two tiles per wave when that still gives every SIMD a
-    // wave, else one.
-    const int wk8 = (nb + 7) / 8;
-    const int wk2 = wk8 < 1 ? 1 : wk8 > 8 ? 8 : wk8;
+    // K split so that each wave streams about 2 blocks (2 x 4 KiB of weights
+    // per tile), one round of loads: a wave that must wait for one round
+    // before issuing the next falls behind in the queue at the HBM, and the
+    // last waves then stream alone (70B W_O 9.6 -> 8.3 us with 2 instead of 8
+    // blocks per wave, W2 19.1 -> 17.6 us). Two tiles per wave when that
+    // still gives every SIMD a wave, else one.
+    const int wkb = (nb + 1) / 2;
+    const int wk2 = wkb < 1 ? 1 : wkb > 8 ? 8 : wkb;
     const bool two = a.N % 32 == 0 && (long)(a.N / 32) * wk2 >= 1024;
-    a.wk = two ? wk2 : (wk8 < 1 ? 1 : wk8 > kMaxWk ? kMaxWk : wk8);
+    a.wk = two ? wk2 : (wkb < 1 ? 1 : wkb > kMaxWk ? kMaxWk : wkb);
     const dim3 grid(a.N / (two ? 32 : 16)), block(64 * a.wk);
     if (two) {
         if (epi == EPI_SWIGLU)

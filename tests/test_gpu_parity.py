@@ -163,6 +163,16 @@ def test_splitk_folded_norm_ragged_batch():
     assert np.array_equal(r["out"].view(np.uint32), g["out"].view(np.uint32))
 
 
+def test_mfma_gemv_one_tile_sixteen_waves():
+    """Batch 12, dim 1024, FFN slice 3968: W2 (N 1024, K 3968 < 4096) takes the
+    per-tile MFMA kernel with one 16-row tile per wave and 16 waves splitting
+    K (31 blocks, the last wave one block short)."""
+    w = synth.small_llama(name="mfma_t1_wk16", dim=1024, n_heads=8, n_kv_heads=8, head_dim=128,
+                          ffn_hidden=7936, tp=2, batch=12, past=(1, 60), w_dtype=synth.BF16,
+                          kv_dtype=synth.BF16, seed=80)
+    check_layer(w)
+
+
 def test_determinism_and_batch_rows():
     w = synth.small_llama(name="micro_b16", dim=256, n_heads=8, n_kv_heads=4, head_dim=32,
                           ffn_hidden=512, tp=2, batch=16, past=(1, 200), w_dtype=synth.BF16,
