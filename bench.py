@@ -114,13 +114,14 @@ def llama_bytes(w, lens):
     """Algorithmic HBM bytes of rank 0's layer step: every packed weight of the
     shard once, plus the cached K and V of the past positions of the shard's
     kv heads (each kv head once, however many q heads share it)."""
-    e = 2 if w.w_dtype == synth.BF16 else 4
+    # int8 weights: one byte per weight plus a 4-byte scale per 32
+    e = 1.125 if w.quant & synth.Q_WEIGHTS else 2 if w.w_dtype == synth.BF16 else 4
     kve = 2 if w.kv_dtype == synth.BF16 else 4
     T, D, hd = w.tp, w.dim, w.head_dim
     Hq_s, Hkv_s, Fs = w.n_heads // T, w.n_kv_heads // T, w.ffn_hidden // T
-    weights = ((Hq_s + 2 * Hkv_s) * hd * D + D * Hq_s * hd + 2 * Fs * D + D * Fs) * e
+    weights = int(((Hq_s + 2 * Hkv_s) * hd * D + D * Hq_s * hd + 2 * Fs * D + D * Fs) * e)
     kv = int(np.sum(lens)) * Hkv_s * hd * 2 * kve
-    w13 = 2 * Fs * D * e
+    w13 = int(2 * Fs * D * e)
     return weights, kv, w13
 
 
@@ -245,7 +246,7 @@ def run_llama(args, w):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.w_dtype == synth.BF16 else "f32",
+        "dtype": "int8" if w.quant & synth.Q_WEIGHTS else "bf16" if w.w_dtype == synth.BF16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "shard": f"rank 0 of TP={T}", "batch": B,
                    "kv_positions": [int(d["lens"].min()), int(d["lens"].max())],
@@ -270,9 +271,17 @@ def run_llama(args, w):
 
 def cpu_baseline_llama(w, d, seconds):
     """The fp64 oracle, as it stands, doing rank 0's layer step on the host."""
+    import dataclasses
     import oracle
     x = d["x"].astype(np.float64)
     kc, vc = d["kcache"].copy(), d["vcache"].copy()
+    if w.quant & synth.Q_WEIGHTS:
+        # the weights' int8 round trip is a load-time step (as in load_weights):
+        # done once, the timed steps then run on the dequantised weights
+        d = dict(d)
+        for k in ("wq", "wk", "wv", "wo", "w1", "w3", "w2"):
+            d[k] = oracle.q8_weights(d[k], w.w_dtype)[2]
+        w = dataclasses.replace(w, w_dtype=synth.F32, quant=w.quant & ~synth.Q_WEIGHTS)
     zeros = np.zeros((w.tp - 1, w.batch, w.dim))
     n, t0 = 0, time.perf_counter()
     while True:

@@ -51,7 +51,18 @@ typedef struct tp_shard tp_shard; /* opaque host-side handle; owns no device mem
 enum { TP_F32 = 0, TP_BF16 = 1 };                         /* element types */
 enum { TP_LLAMA_BLOCK = 0, TP_FFN_2D = 1 };                /* tp_config.kind */
 enum { TP_STAGE_ATTN = 0, TP_STAGE_FFN = 1 };              /* decode_step / merge_partials stage */
-enum { TP_Q_NONE = 0, TP_Q_PARTIALS = 1, TP_Q_INPUTS = 2 }; /* tp_config.quant bit mask */
+/* tp_config.quant bit mask. TP_Q_PARTIALS / TP_Q_INPUTS: the block-32 int8
+ * round trip of the exchanged partials / the normalised stage inputs
+ * (distributed-llama issue, buildLlama2Arch: the quantise / sync / dequantise
+ * tasks). TP_Q_WEIGHTS: weight-only int8 projections (CS349E lecture 4,
+ * 03_pope_partitioning.py, demo 4: small-batch decode is bound by the weight
+ * bytes, and int8 weights cut the measured PaLM decode time): load_weights
+ * cuts every row of Wq/Wk/Wv/Wo/W1/W3/W2 (the shard's slice, given in
+ * w_dtype) into blocks of 32 along k and stores each block with the same
+ * codec as an fp32 scale and 32 int8 codes; the projections then accumulate
+ * sum_blocks scale * sum_k code * x in fp32. Needs dim, Hq/T*head_dim and F/T
+ * multiples of 32. Not for TP_FFN_2D. */
+enum { TP_Q_NONE = 0, TP_Q_PARTIALS = 1, TP_Q_INPUTS = 2, TP_Q_WEIGHTS = 4 };
 
 enum {
     TP_OK = 0,
@@ -207,6 +218,15 @@ int32_t decode_merge_step(tp_shard *s, int32_t stage, const void *x, const int32
 /* Byte offset of the fp32 scales inside a quantised wire of `batch` rows
  * (16-byte aligned, right after the int8 codes). */
 uint64_t tp_wire_scales_offset(const tp_config *cfg, int32_t batch);
+
+/* TP_Q_WEIGHTS: where projection `proj` (0 = Wqkv, 1 = Wo, 2 = W13 with the
+ * W1_f / W3_f rows interleaved, 3 = W2) sits inside the packed weights: its
+ * int8 codes [rows][cols] at byte *codes_off, its fp32 scales
+ * [rows][cols / 32] at byte *scales_off, both row-major (scale j of a row
+ * covers codes 32 j .. 32 j + 31). TP_EINVAL for a handle without int8
+ * weights, an unknown proj or a null output. */
+int32_t tp_packed_int8_view(const tp_shard *s, int32_t proj, uint64_t *codes_off,
+                            uint64_t *scales_off, int32_t *rows, int32_t *cols);
 
 /* Reads (and clears, when clear != 0) the device error word in the handle's
  * workspace; synchronises hip_stream. */

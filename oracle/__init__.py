@@ -32,7 +32,7 @@ LIB = os.environ.get("TP_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
 F32, BF16 = 0, 1
-Q_PARTIALS, Q_INPUTS = 1, 2
+Q_PARTIALS, Q_INPUTS, Q_WEIGHTS = 1, 2, 4
 QBLOCK = 32
 
 _lib = None
@@ -145,6 +145,24 @@ def q8_dequantize(codes, scales) -> np.ndarray:
     return y
 
 
+def q8_weights(W, dtype="bf16"):
+    """Weight-only int8 (CS349E lecture 4, 03_pope_partitioning.py, demo 4:
+    int8 weights for the weight-bound small-batch decode). The pages give no
+    weight format; the reading taken here: each row of W [N][K] is cut into
+    blocks of 32 consecutive k and every block goes through the exchange
+    codec above (one fp32 scale, 32 int8 codes). Returns (codes [N][K] int8,
+    scales [N][K/32] fp32, dequantised weights [N][K] fp32); the layer stages
+    with TP_Q_WEIGHTS use the dequantised weights."""
+    dt = _dt(dtype)
+    W = _typed(W, dt)
+    N, K = W.shape
+    assert K % QBLOCK == 0
+    f = W if dt == F32 else (W.astype(np.uint32) << 16).view(np.float32)
+    codes, scales = q8_quantize(f.reshape(-1))
+    deq = q8_dequantize(codes, scales)
+    return codes.reshape(N, K), scales.reshape(N, K // QBLOCK), deq.reshape(N, K)
+
+
 def matvec(W, x, dtype="f32", col0: int = 0, K: Optional[int] = None) -> np.ndarray:
     dt = _dt(dtype)
     W = _typed(W, dt)
@@ -188,16 +206,22 @@ def silu(z: float) -> float:
 # ---------------------------------------------------------------- block stages
 
 def _cfg(w) -> LlamaCfg:
+    # int8 weights: the stages see the dequantised fp32 weights (_Weights)
+    w8 = bool(w.quant & Q_WEIGHTS)
     return LlamaCfg(dim=w.dim, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
                     ffn_hidden=w.ffn_hidden, tp_size=w.tp, batch=w.batch, max_ctx=w.max_ctx,
-                    w_dtype=_dt(w.w_dtype), kv_dtype=_dt(w.kv_dtype), quant=w.quant, pad_=0,
-                    rope_theta=w.rope_theta, norm_eps=w.norm_eps)
+                    w_dtype=F32 if w8 else _dt(w.w_dtype), kv_dtype=_dt(w.kv_dtype),
+                    quant=w.quant & ~Q_WEIGHTS, pad_=0, rope_theta=w.rope_theta, norm_eps=w.norm_eps)
 
 
 class _Weights:
     def __init__(self, w, weights: Dict[str, np.ndarray]):
         dt = _dt(w.w_dtype)
-        self.keep = {k: _typed(weights[k], dt) for k in ("wq", "wk", "wv", "wo", "w1", "w3", "w2")}
+        names = ("wq", "wk", "wv", "wo", "w1", "w3", "w2")
+        if w.quant & Q_WEIGHTS:
+            self.keep = {k: q8_weights(weights[k], w.w_dtype)[2] for k in names}
+        else:
+            self.keep = {k: _typed(weights[k], dt) for k in names}
         self.keep["g_att"] = np.ascontiguousarray(weights["g_att"], dtype=np.float32)
         self.keep["g_ffn"] = np.ascontiguousarray(weights["g_ffn"], dtype=np.float32)
         self.s = LlamaWeights(**{k: _ptr(v) for k, v in self.keep.items()})

@@ -36,6 +36,7 @@ BF16 = "bf16"
 Q_NONE = 0
 Q_PARTIALS = 1
 Q_INPUTS = 2
+Q_WEIGHTS = 4
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -108,6 +109,10 @@ L7B_Q8 = _add(dataclasses.replace(L7B, name="llama2_7b_tp4_b1_q8", quant=Q_PARTI
 L70B = _add(LlamaBlock("llama2_70b_tp8_b16", dim=8192, n_heads=64, n_kv_heads=8, head_dim=128,
                        ffn_hidden=28672, tp=8, batch=16, past=(1024, 4096), w_dtype=BF16,
                        kv_dtype=BF16, quant=Q_NONE, seed=1004))
+# the 7B and 70B shards with weight-only int8 projections (block-32 codes and
+# scales made from the same seeded bf16 weights at load time)
+L7B_W8 = _add(dataclasses.replace(L7B, name="llama2_7b_tp4_b1_w8", quant=Q_WEIGHTS, seed=1006))
+L70B_W8 = _add(dataclasses.replace(L70B, name="llama2_70b_tp8_b16_w8", quant=Q_WEIGHTS, seed=1007))
 # PaLM-540B FFN block of an 8x8 2D weight-stationary grid: E=18432/8, F=73728/8
 PALM_DEC = _add(Ffn2D("palm540b_ffn2d_b512", e_blk=2304, f_blk=9216, batch=512, seed=1005))
 PALM_PRE = _add(Ffn2D("palm540b_ffn2d_prefill8192", e_blk=2304, f_blk=9216, batch=8192, seed=1005))

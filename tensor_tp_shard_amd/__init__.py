@@ -21,13 +21,14 @@ LIB_PATH = os.path.join(HERE, "libtpshard.so")
 TP_F32, TP_BF16 = 0, 1
 TP_LLAMA_BLOCK, TP_FFN_2D = 0, 1
 TP_STAGE_ATTN, TP_STAGE_FFN = 0, 1
-TP_Q_NONE, TP_Q_PARTIALS, TP_Q_INPUTS = 0, 1, 2
+TP_Q_NONE, TP_Q_PARTIALS, TP_Q_INPUTS, TP_Q_WEIGHTS = 0, 1, 2, 4
 TP_OK, TP_EINVAL, TP_EALIGN, TP_ESTATE, TP_ENODEV, TP_EHIP, TP_ENOTIMPL = 0, -1, -2, -3, -4, -5, -6
 TP_DERR_LEN = 1
 
 # every symbol include/tpshard.h declares
 EXPORTS = ("init_shard", "load_weights", "decode_step", "merge_partials", "decode_merge_step",
            "tp_wire_scales_offset",
+           "tp_packed_int8_view",
            "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
            "tp_kernel_name", "destroy_shard", "tp_status_str", "tp_last_error")
 
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
         L.tp_wire_scales_offset.argtypes = [P, I32]
         L.tp_wire_scales_offset.restype = U64
         L.tp_read_error_word.argtypes = [P, P, I32, P]
+        L.tp_packed_int8_view.argtypes = [P, I32, P, P, P, P]
         L.tp_kernel_timing_arm.argtypes = [P, I32]
         L.tp_kernel_timing_read.argtypes = [P, P, P]
         L.tp_kernel_name.argtypes = [I32]
@@ -88,7 +90,8 @@ def lib() -> ctypes.CDLL:
         L.tp_status_str.restype = ctypes.c_char_p
         L.tp_last_error.restype = ctypes.c_char_p
         for f in ("init_shard", "load_weights", "decode_step", "merge_partials",
-                  "decode_merge_step", "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read"):
+                  "decode_merge_step", "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
+                  "tp_packed_int8_view"):
             getattr(L, f).restype = I32
         _lib = L
     return _lib
@@ -178,6 +181,17 @@ def read_error_word(handle, clear: bool = True, stream=None) -> int:
     _check(lib().tp_read_error_word(handle, ctypes.byref(w), 1 if clear else 0, _stream(stream)),
            "tp_read_error_word")
     return w.value
+
+
+def packed_int8_view(handle, proj: int):
+    """(codes byte offset, scales byte offset, rows, cols) of projection proj
+    (0 Wqkv, 1 Wo, 2 W13 interleaved, 3 W2) inside the packed weights of a
+    shard with int8 weights."""
+    co, so = ctypes.c_uint64(), ctypes.c_uint64()
+    r, c = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().tp_packed_int8_view(handle, proj, ctypes.byref(co), ctypes.byref(so), ctypes.byref(r),
+                                     ctypes.byref(c)), "tp_packed_int8_view")
+    return co.value, so.value, r.value, c.value
 
 
 def kernel_timing_arm(handle, kernel_id: int):

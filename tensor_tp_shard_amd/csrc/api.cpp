@@ -75,8 +75,10 @@ struct tp_shard {
     tp_config cfg;
     // derived shape
     int T, r, D, hd, Hq, Hkv, G, Hq_s, Hkv_s, F, Fs, n_qkv, esz, kv_esz;
+    bool w8; // TP_Q_WEIGHTS: packed projections are int8 codes + fp32 scales per 32 k
     // packed layout (byte offsets)
     uint64_t o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn, o_rope, packed_bytes;
+    uint64_t o_sqkv, o_swo, o_sw13, o_sw2; // w8: scale arrays [N][K/32]
     // workspace layout (byte offsets)
     uint64_t w_err, w_xfx, w_xfatt, w_xfa, w_skp, w_xn, w_qkv, w_part, w_att, w_a, w_p, ws_bytes;
     int n_chunks;
@@ -100,7 +102,7 @@ int32_t plan(const tp_config &c, tp_shard &s)
         return fail(TP_EINVAL, "unknown kind %d", c.kind);
     if (c.w_dtype != TP_F32 && c.w_dtype != TP_BF16)
         return fail(TP_EINVAL, "unknown w_dtype %d", c.w_dtype);
-    if (c.quant & ~(TP_Q_PARTIALS | TP_Q_INPUTS))
+    if (c.quant & ~(TP_Q_PARTIALS | TP_Q_INPUTS | TP_Q_WEIGHTS))
         return fail(TP_EINVAL, "unknown quant bits 0x%x", c.quant);
     if (c.quant && c.quant_block != kQBlock)
         return fail(TP_EINVAL, "quant_block must be 32 (got %d)", c.quant_block);
@@ -172,6 +174,9 @@ int32_t plan(const tp_config &c, tp_shard &s)
     s.n_qkv = (s.Hq_s + 2 * s.Hkv_s) * s.hd;
     s.esz = c.w_dtype == TP_BF16 ? 2 : 4;
     s.kv_esz = c.kv_dtype == TP_BF16 ? 2 : 4;
+    s.w8 = (c.quant & TP_Q_WEIGHTS) != 0;
+    if (s.w8 && (s.D % kQBlock || (s.Hq_s * s.hd) % kQBlock || s.Fs % kQBlock))
+        return fail(TP_EINVAL, "int8 weights need dim, Hq/T*head_dim and ffn_hidden/T multiples of 32");
     const int vec = 16 / s.esz;
     if (s.D % 8 || (s.Hq_s * s.hd) % vec || s.Fs % vec)
         return fail(TP_EINVAL, "dim must be a multiple of 8, Hq/T*head_dim and ffn_hidden/T of %d",
@@ -179,17 +184,24 @@ int32_t plan(const tp_config &c, tp_shard &s)
     s.n_chunks = (c.max_ctx + 63) / 64;
     if (attn_lds_bytes(s.G, s.hd, c.kv_dtype == TP_BF16, s.n_chunks) > 64 * 1024)
         return fail(TP_EINVAL, "attention workgroup would need more than 64 KiB of LDS");
-    const uint64_t D = s.D, B = c.max_batch, e = s.esz;
+    const uint64_t D = s.D, B = c.max_batch, e = s.w8 ? 1 : s.esz; // packed bytes per weight
     uint64_t o = 0;
     s.o_wqkv = o; o = align_up(o + (uint64_t)s.n_qkv * D * e, 256);
     s.o_wo = o;   o = align_up(o + D * s.Hq_s * s.hd * e, 256);
     s.o_w13 = o;  o = align_up(o + 2ull * s.Fs * D * e, 256);
     s.o_w2 = o;   o = align_up(o + D * s.Fs * e, 256);
+    s.o_sqkv = s.o_swo = s.o_sw13 = s.o_sw2 = 0;
+    if (s.w8) { // one fp32 scale per 32 weights of a row
+        s.o_sqkv = o; o = align_up(o + (uint64_t)s.n_qkv * (D / kQBlock) * 4, 256);
+        s.o_swo = o;  o = align_up(o + D * (s.Hq_s * s.hd / kQBlock) * 4, 256);
+        s.o_sw13 = o; o = align_up(o + 2ull * s.Fs * (D / kQBlock) * 4, 256);
+        s.o_sw2 = o;  o = align_up(o + D * (s.Fs / kQBlock) * 4, 256);
+    }
     s.o_gatt = o; o = align_up(o + D * 4, 256);
     s.o_gffn = o; o = align_up(o + D * 4, 256);
     s.o_rope = o; o = align_up(o + (uint64_t)c.max_ctx * (s.hd / 2) * 8, 256);
     s.packed_bytes = o;
-    s.mfma_ok = c.w_dtype == TP_BF16 && c.max_batch > 4 && gemv_mfma_ok(16, s.n_qkv, s.D, 1) &&
+    s.mfma_ok = (c.w_dtype == TP_BF16 || s.w8) && c.max_batch > 4 && gemv_mfma_ok(16, s.n_qkv, s.D, 1) &&
                 gemv_mfma_ok(16, s.D, s.Hq_s * s.hd, 1) && gemv_mfma_ok(16, 2 * s.Fs, s.D, 1) &&
                 gemv_mfma_ok(16, s.D, s.Fs, 1);
     o = 0;
@@ -342,7 +354,51 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *w, void *packed, void 
     char *P = (char *)packed;
     const size_t e = s->esz, D = s->D;
     hipError_t err = hipSuccess;
-    if (llama) {
+    if (llama && s->w8) {
+        // int8 weights: the same slices and interleave as below, each row cut
+        // into blocks of 32 along k and quantised (codes and scales packed
+        // separately, [N][K] and [N][K/32]); the shard's column slices start at
+        // multiples of 32, so the blocks are those of the unsharded rows
+        const size_t hd = s->hd, nb = D / kQBlock, wo_cols = (size_t)s->Hq_s * hd;
+        const int bf = s->cfg.w_dtype == TP_BF16;
+        auto quant = [&](const void *src, size_t src_pitch, size_t rows, size_t cols, uint64_t code_off,
+                         size_t code_pitch, uint64_t scale_off, size_t scale_pitch) {
+            const QuantRowsArgs qa{src, bf, src_pitch, (int)rows, (int)cols, (int8_t *)(P + code_off),
+                                   code_pitch, (float *)(P + scale_off), scale_pitch};
+            return launch_quant_rows(qa, st);
+        };
+        const size_t nq = (size_t)s->Hq_s * hd, nk = (size_t)s->Hkv_s * hd;
+        err = quant((const char *)w->wq + s->r * nq * D * e, D, nq, D, s->o_wqkv, D, s->o_sqkv, nb);
+        if (!err)
+            err = quant((const char *)w->wk + s->r * nk * D * e, D, nk, D, s->o_wqkv + nq * D, D,
+                        s->o_sqkv + nq * nb * 4, nb);
+        if (!err)
+            err = quant((const char *)w->wv + s->r * nk * D * e, D, nk, D, s->o_wqkv + (nq + nk) * D, D,
+                        s->o_sqkv + (nq + nk) * nb * 4, nb);
+        if (!err) // W_O: columns [r*Hq_s*hd, (r+1)*Hq_s*hd) of every row
+            err = quant((const char *)w->wo + s->r * wo_cols * e, (size_t)s->Hq * hd, D, wo_cols, s->o_wo,
+                        wo_cols, s->o_swo, wo_cols / kQBlock);
+        if (!err) // W1_f and W3_f rows interleaved
+            err = quant((const char *)w->w1 + (size_t)s->r * s->Fs * D * e, D, s->Fs, D, s->o_w13, 2 * D,
+                        s->o_sw13, 2 * nb);
+        if (!err)
+            err = quant((const char *)w->w3 + (size_t)s->r * s->Fs * D * e, D, s->Fs, D, s->o_w13 + D,
+                        2 * D, s->o_sw13 + nb * 4, 2 * nb);
+        if (!err) // W2: columns [r*Fs, (r+1)*Fs)
+            err = quant((const char *)w->w2 + (size_t)s->r * s->Fs * e, (size_t)s->F, D, s->Fs, s->o_w2,
+                        s->Fs, s->o_sw2, s->Fs / kQBlock);
+        if (!err)
+            err = hipMemcpyAsync(P + s->o_gatt, w->g_att, D * 4, hipMemcpyDeviceToDevice, st);
+        if (!err)
+            err = hipMemcpyAsync(P + s->o_gffn, w->g_ffn, D * 4, hipMemcpyDeviceToDevice, st);
+        if (err)
+            return hip_fail(err, "load_weights: int8 packing");
+        RopeArgs ra{(float2 *)(P + s->o_rope), s->cfg.max_ctx, s->hd, (double)s->cfg.rope_theta};
+        const int32_t rc =
+            timed(s, KID_ROPE_TABLE, st, "rope table", [&] { return launch_rope_table(ra, st); });
+        if (rc)
+            return rc;
+    } else if (llama) {
         const size_t hd = s->hd;
         // column split: rows of the shard's q heads, kv heads (contiguous blocks)
         err = hipMemcpyAsync(P + s->o_wqkv, (const char *)w->wq + (size_t)s->r * s->Hq_s * hd * D * e,
@@ -460,6 +516,9 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
     }
 
     const bool wbf = s->cfg.w_dtype == TP_BF16;
+    const int wt = s->w8 ? WT_I8 : wbf ? WT_BF16 : WT_F32;
+    const char *Pk = s->packed;
+    auto wscales = [&](uint64_t off) { return s->w8 ? (const float *)(Pk + off) : nullptr; };
     const bool qin = s->cfg.quant & TP_Q_INPUTS, qpart = s->cfg.quant & TP_Q_PARTIALS;
     const float *gain = (const float *)(s->packed + (stage == TP_STAGE_ATTN ? s->o_gatt : s->o_gffn));
     // the partial goes straight into the wire unless it is quantised
@@ -512,10 +571,10 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
     const int Kd = stage == TP_STAGE_ATTN ? s->Hq_s * s->hd : s->Fs;
     auto run_gemv = [&](const GemvArgs &g, const uint16_t *xf, uint16_t *yf, int epi, bool norm) {
         if (!mfma)
-            return launch_gemv(g, wbf, epi, st);
+            return launch_gemv(g, wt, epi, st);
         MfmaGemvArgs m{(const uint16_t *)g.W, xf, g.y, g.tap, yf, g.N, g.K, g.B, g.ldy, 1, g.mo,
                        s->w_skp ? (float *)(s->ws + s->w_skp) : nullptr, 0, 0,
-                       norm ? in : nullptr, norm ? gain : nullptr, s->cfg.norm_eps};
+                       norm ? in : nullptr, norm ? gain : nullptr, s->cfg.norm_eps, g.ws};
         return launch_gemv_mfma(m, epi, st);
     };
 
@@ -524,6 +583,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
             return fail(TP_EINVAL, "decode_step: attention stage needs lens");
         float *qkv = (float *)(s->ws + s->w_qkv);
         up.W = s->packed + s->o_wqkv;
+        up.ws = wscales(s->o_sqkv);
         up.y = qkv;
         up.N = s->n_qkv;
         up.ldy = s->n_qkv;
@@ -558,6 +618,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         if (rc)
             return rc;
         down.W = s->packed + s->o_wo;
+        down.ws = wscales(s->o_swo);
         down.x = att;
         down.K = Kd;
         down.ldx = Kd;
@@ -567,6 +628,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
     } else {
         float *a = (float *)(s->ws + s->w_a);
         up.W = s->packed + s->o_w13;
+        up.ws = wscales(s->o_sw13);
         up.y = a;
         up.tap = tp.a;
         up.N = 2 * s->Fs;
@@ -575,6 +637,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         if (rc)
             return rc;
         down.W = s->packed + s->o_w2;
+        down.ws = wscales(s->o_sw2);
         down.x = a;
         down.K = Kd;
         down.ldx = Kd;
@@ -673,6 +736,23 @@ int32_t merge_partials(const tp_shard *s, int32_t stage, const void *const *wire
     hipStream_t st = (hipStream_t)hip_stream;
     return timed(const_cast<tp_shard *>(s), KID_MERGE, st, "merge",
                  [&] { return launch_merge(m, st); });
+}
+
+int32_t tp_packed_int8_view(const tp_shard *s, int32_t proj, uint64_t *codes_off,
+                            uint64_t *scales_off, int32_t *rows, int32_t *cols)
+{
+    if (!s || !codes_off || !scales_off || !rows || !cols)
+        return fail(TP_EINVAL, "tp_packed_int8_view: null argument");
+    if (!s->w8)
+        return fail(TP_EINVAL, "tp_packed_int8_view: the shard has no int8 weights");
+    switch (proj) {
+    case 0: *codes_off = s->o_wqkv; *scales_off = s->o_sqkv; *rows = s->n_qkv; *cols = s->D; break;
+    case 1: *codes_off = s->o_wo; *scales_off = s->o_swo; *rows = s->D; *cols = s->Hq_s * s->hd; break;
+    case 2: *codes_off = s->o_w13; *scales_off = s->o_sw13; *rows = 2 * s->Fs; *cols = s->D; break;
+    case 3: *codes_off = s->o_w2; *scales_off = s->o_sw2; *rows = s->D; *cols = s->Fs; break;
+    default: return fail(TP_EINVAL, "tp_packed_int8_view: unknown projection %d", proj);
+    }
+    return TP_OK;
 }
 
 int32_t tp_read_error_word(tp_shard *s, uint32_t *word, int32_t clear, void *hip_stream)

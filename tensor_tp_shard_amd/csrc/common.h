@@ -38,9 +38,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32
     // 0x00020000: the third descriptor word of a raw 32-bit-format buffer on CDNA
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 buf_load8_nt(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2); // nontemporal
 }
 __device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
@@ -255,7 +264,7 @@ __device__ __forceinline__ void xf_store(uint16_t *xf, int b, int k, float v)
 }
 
 struct MfmaGemvArgs {
-    const uint16_t *W;   // bf16 [N][K], N % 16 == 0, K % 128 == 0
+    const uint16_t *W;   // bf16 [N][K] (or int8 codes [N][K] with ws), N % 16 == 0, K % 128 == 0
     const uint16_t *xf;  // activations in the fragment layout
     float *y;            // EPI_STORE: y[b][n] (ld ldy); EPI_SWIGLU: y[b][n/2]
     float *tap;          // optional copy of y
@@ -271,12 +280,20 @@ struct MfmaGemvArgs {
     const float *xs;
     const float *g;
     float eps;
+    const float *ws;     // int8 weights: W holds the codes, ws the scales [N][K/32]
 };
 
 enum GemvEpi { EPI_STORE = 0, EPI_SWIGLU = 1 };
 
+// Weight types of the projections: fp32, bf16, or int8 codes with one fp32
+// scale per 32 consecutive k of a row (the block-32 codec applied to the
+// weights at load time).
+enum WeightType { WT_F32 = 0, WT_BF16 = 1, WT_I8 = 2 };
+__host__ __device__ constexpr int wt_per_chunk(int wt) { return wt == WT_I8 ? 16 : wt == WT_BF16 ? 8 : 4; }
+
 struct GemvArgs {
     const void *W;       // [N][K] row-major, 16-byte aligned rows
+    const float *ws;     // WT_I8: scales [N][K/32]
     const float *x;      // [B][ldx]
     float *y;            // [B][ldy]; SwiGLU: y[b][n/2]
     float *tap;          // optional copy of y, same layout
@@ -320,6 +337,18 @@ struct MergeArgs {
     int B, D;
 };
 
+// int8 weight packing: rows x cols (cols % 32 == 0) of src -> codes / scales
+struct QuantRowsArgs {
+    const void *src;
+    int src_bf16;
+    size_t src_pitch;   // elements
+    int rows, cols;
+    int8_t *codes;
+    size_t code_pitch;  // bytes
+    float *scales;
+    size_t scale_pitch; // floats
+};
+
 struct RopeArgs {
     float2 *table;       // [max_ctx][hd/2]
     int max_ctx, hd;
@@ -339,7 +368,7 @@ struct Ffn2dArgs {
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st);
-hipError_t launch_gemv(const GemvArgs &a, int w_bf16, int epi, hipStream_t st);
+hipError_t launch_gemv(const GemvArgs &a, int wt, int epi, hipStream_t st);
 hipError_t launch_gemv_mfma(const MfmaGemvArgs &a, int epi, hipStream_t st);
 size_t gemv_sk_part_floats(int N, int K, int B);
 bool gemv_sk_used(int N, int K); // the batch-16 N x K projection takes the split-K kernels
@@ -352,6 +381,7 @@ bool gemv_fused_ok(int B, int K);
 hipError_t launch_wire(const WireArgs &a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
 hipError_t launch_rope_table(const RopeArgs &a, hipStream_t st);
+hipError_t launch_quant_rows(const QuantRowsArgs &a, hipStream_t st);
 hipError_t launch_clear_u32(unsigned *p, int n, hipStream_t st);
 hipError_t launch_ffn2d(const Ffn2dArgs &a, hipStream_t st, int which);
 int ffn2d_splits(int B, int E, int F);

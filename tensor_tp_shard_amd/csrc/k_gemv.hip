@@ -34,10 +34,14 @@
 
 namespace tps {
 
-template <bool BF16>
-__device__ __forceinline__ float dot16(const u32x4 &w, const float4 &x0, const float4 &x1, float acc)
+// One 16-byte chunk of a weight row against the matching activations xp
+// (fp32: 4 weights, bf16: 8, int8: 16 codes of one half of a 32-block whose
+// scale is sc: the codes' dot product, then one multiply by the scale).
+template <int WT>
+__device__ __forceinline__ float dot_chunk(const u32x4 &w, const float4 *xp, float sc, float acc)
 {
-    if constexpr (BF16) {
+    if constexpr (WT == WT_BF16) {
+        const float4 x0 = xp[0], x1 = xp[1];
         acc += bf16_lo(w.x) * x0.x;
         acc += bf16_hi(w.x) * x0.y;
         acc += bf16_lo(w.y) * x0.z;
@@ -46,7 +50,20 @@ __device__ __forceinline__ float dot16(const u32x4 &w, const float4 &x0, const f
         acc += bf16_hi(w.z) * x1.y;
         acc += bf16_lo(w.w) * x1.z;
         acc += bf16_hi(w.w) * x1.w;
+    } else if constexpr (WT == WT_I8) {
+        float p = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+            const uint32_t u = w[d];
+            const float4 x = xp[d];
+            p += (float)(int8_t)(u & 0xffu) * x.x;
+            p += (float)(int8_t)((u >> 8) & 0xffu) * x.y;
+            p += (float)(int8_t)((u >> 16) & 0xffu) * x.z;
+            p += (float)(int8_t)(u >> 24) * x.w;
+        }
+        acc += sc * p;
     } else {
+        const float4 x0 = xp[0];
         acc += __uint_as_float(w.x) * x0.x;
         acc += __uint_as_float(w.y) * x0.y;
         acc += __uint_as_float(w.z) * x0.z;
@@ -154,10 +171,10 @@ __device__ void stage_x_finish(const GemvArgs &a, XRegs &r, float *xs, float *re
     }
 }
 
-template <bool BF16, int NB, int RPW, int EPI, bool MO>
+template <int WT, int NB, int RPW, int EPI, bool MO>
 __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
 {
-    constexpr int V = BF16 ? 8 : 4; // elements per 16-byte chunk
+    constexpr int V = wt_per_chunk(WT); // elements per 16-byte chunk
     constexpr int KC = 8;           // chunk iterations per lane kept in flight
     extern __shared__ float xs[];   // [B][K]
     __shared__ float red4[4];
@@ -172,11 +189,15 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
     const bool active = row0 < a.N;
     const int nchunk = a.K / V;
     // one buffer per weight row (an inactive wave's covers nothing)
-    const uint32_t rowb = (uint32_t)a.K * (BF16 ? 2 : 4);
-    __amdgpu_buffer_rsrc_t Wr[RPW];
+    const uint32_t rowb = (uint32_t)a.K * 16 / V;
+    __amdgpu_buffer_rsrc_t Wr[RPW], Sr[RPW];
 #pragma unroll
-    for (int r = 0; r < RPW; r++)
+    for (int r = 0; r < RPW; r++) {
         Wr[r] = buf_rsrc((const char *)a.W + (size_t)(active ? row0 + r : 0) * rowb, active ? rowb : 0u);
+        // int8: the row's fp32 scales, one per 32 codes (two chunks)
+        if constexpr (WT == WT_I8)
+            Sr[r] = buf_rsrc(a.ws + (size_t)(active ? row0 + r : 0) * (a.K / 32), active ? (uint32_t)a.K / 8 : 0u);
+    }
     // fused merge (MO): the lane that stores output (row0 + r, b) preloads the
     // residual and the other wires' elements before the weights are requested
     float mres = 0.f;
@@ -191,13 +212,22 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
     stage_x_issue(a, xr);
     __builtin_amdgcn_sched_barrier(0); // the activation loads stay ahead of the weights
     u32x4 w[RPW][KC];
+    float sc[RPW][KC];
+    auto load_w = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < KC; i++) {
-        const int c = lane + 64 * i;
+        for (int i = 0; i < KC; i++) {
+            const int c = kb + lane + 64 * i;
 #pragma unroll
-        for (int r = 0; r < RPW; r++)
-            w[r][i] = buf_load16_nt(Wr[r], c < nchunk ? 16u * c : kOob);
-    }
+            for (int r = 0; r < RPW; r++) {
+                w[r][i] = buf_load16_nt(Wr[r], c < nchunk ? 16u * c : kOob);
+                if constexpr (WT == WT_I8)
+                    sc[r][i] = __uint_as_float(buf_load4(Sr[r], c < nchunk ? 4u * (c >> 1) : kOob));
+                else
+                    sc[r][i] = 1.f;
+            }
+        }
+    };
+    load_w(0);
     stage_x_finish(a, xr, xs, red4);
     __syncthreads();
 
@@ -208,15 +238,8 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
         for (int b = 0; b < NB; b++)
             acc[r][b] = 0.f;
     for (int kb = 0; kb < nchunk; kb += 64 * KC) {
-        if (kb > 0) {
-#pragma unroll
-            for (int i = 0; i < KC; i++) {
-                const int c = kb + lane + 64 * i;
-#pragma unroll
-                for (int r = 0; r < RPW; r++)
-                    w[r][i] = buf_load16_nt(Wr[r], c < nchunk ? 16u * c : kOob);
-            }
-        }
+        if (kb > 0)
+            load_w(kb);
 #pragma unroll
         for (int i = 0; i < KC; i++) {
             const int c = kb + lane + 64 * i;
@@ -225,11 +248,9 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
                 for (int b = 0; b < NB; b++) {
                     if (b < a.B) {
                         const float4 *xp = (const float4 *)(xs + (size_t)b * a.K) + c * (V / 4);
-                        const float4 x0 = xp[0];
-                        const float4 x1 = BF16 ? xp[1] : x0;
 #pragma unroll
                         for (int r = 0; r < RPW; r++)
-                            acc[r][b] = dot16<BF16>(w[r][i], x0, x1, acc[r][b]);
+                            acc[r][b] = dot_chunk<WT>(w[r][i], xp, sc[r][i], acc[r][b]);
                     }
                 }
             }
@@ -275,10 +296,10 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
 // Activations read from global memory (L1/L2 resident), no fused prologue /
 // epilogue: used when the batch's activation rows do not fit in LDS.
 
-template <bool BF16, int NB, int RPW, int EPI, bool MO>
+template <int WT, int NB, int RPW, int EPI, bool MO>
 __global__ __launch_bounds__(256) void k_gemv_gx(GemvArgs a)
 {
-    constexpr int V = BF16 ? 8 : 4;
+    constexpr int V = wt_per_chunk(WT);
     constexpr int U = 4;
     const int lane = threadIdx.x & 63;
     const int row0 = ((blockIdx.x * 256 + threadIdx.x) >> 6) * RPW;
@@ -295,7 +316,7 @@ __global__ __launch_bounds__(256) void k_gemv_gx(GemvArgs a)
     const u32x4 *Wr[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; r++)
-        Wr[r] = (const u32x4 *)((const char *)a.W + (size_t)(row0 + r) * a.K * (BF16 ? 2 : 4));
+        Wr[r] = (const u32x4 *)((const char *)a.W + (size_t)(row0 + r) * a.K * 16 / V);
     float acc[RPW][NB];
 #pragma unroll
     for (int r = 0; r < RPW; r++)
@@ -318,11 +339,11 @@ __global__ __launch_bounds__(256) void k_gemv_gx(GemvArgs a)
                 for (int b = 0; b < NB; b++) {
                     if (b < a.B) {
                         const float4 *xp = (const float4 *)(a.x + (size_t)b * a.ldx) + c * (V / 4);
-                        const float4 x0 = xp[0];
-                        const float4 x1 = BF16 ? xp[1] : x0;
 #pragma unroll
                         for (int r = 0; r < RPW; r++)
-                            acc[r][b] = dot16<BF16>(w[u][r], x0, x1, acc[r][b]);
+                            acc[r][b] = dot_chunk<WT>(w[u][r], xp,
+                                                      WT == WT_I8 ? a.ws[(size_t)(row0 + r) * (a.K / 32) + (c >> 1)] : 1.f,
+                                                      acc[r][b]);
                     }
                 }
             }
@@ -372,62 +393,64 @@ bool gemv_fused_ok(int B, int K) { return B <= 4 && K <= 4 * 256 * kXV && gemv_l
 // waves of two rows per wave, each with a whole row of loads in flight
 // (7B shard step 42.2 -> 41.1 us); the SwiGLU projection pairs W1_f / W3_f
 // rows in one wave.
-template <bool BF16, int NB>
+template <int WT, int NB>
 static hipError_t launch_lds(const GemvArgs &a, int epi, hipStream_t st)
 {
     const size_t sm = gemv_lds_bytes(a.B, a.K);
     const dim3 block(256);
     if (epi == EPI_SWIGLU) {
         const dim3 grid((a.N + 4 * kRPW - 1) / (4 * kRPW));
-        hipLaunchKernelGGL((k_gemv_lds<BF16, NB, kRPW, EPI_SWIGLU, false>), grid, block, sm, st, a);
+        hipLaunchKernelGGL((k_gemv_lds<WT, NB, kRPW, EPI_SWIGLU, false>), grid, block, sm, st, a);
     } else {
         const dim3 grid((a.N + 3) / 4);
         if (a.mo.n_wires)
-            hipLaunchKernelGGL((k_gemv_lds<BF16, NB, 1, EPI_STORE, true>), grid, block, sm, st, a);
+            hipLaunchKernelGGL((k_gemv_lds<WT, NB, 1, EPI_STORE, true>), grid, block, sm, st, a);
         else
-            hipLaunchKernelGGL((k_gemv_lds<BF16, NB, 1, EPI_STORE, false>), grid, block, sm, st, a);
+            hipLaunchKernelGGL((k_gemv_lds<WT, NB, 1, EPI_STORE, false>), grid, block, sm, st, a);
     }
     return hipGetLastError();
 }
 
-template <bool BF16, int NB>
+template <int WT, int NB>
 static hipError_t launch_gx(const GemvArgs &a, int epi, hipStream_t st)
 {
     const int waves = (a.N + kRPW - 1) / kRPW;
     const dim3 grid((waves + 3) / 4), block(256);
     if (epi == EPI_SWIGLU)
-        hipLaunchKernelGGL((k_gemv_gx<BF16, NB, kRPW, EPI_SWIGLU, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemv_gx<WT, NB, kRPW, EPI_SWIGLU, false>), grid, block, 0, st, a);
     else if (a.mo.n_wires)
-        hipLaunchKernelGGL((k_gemv_gx<BF16, NB, kRPW, EPI_STORE, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemv_gx<WT, NB, kRPW, EPI_STORE, true>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((k_gemv_gx<BF16, NB, kRPW, EPI_STORE, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_gemv_gx<WT, NB, kRPW, EPI_STORE, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
-template <bool BF16>
+template <int WT>
 static hipError_t launch_t(const GemvArgs &a, int epi, hipStream_t st)
 {
     if (gemv_fused_ok(a.B, a.K)) {
         if (a.B <= 1)
-            return launch_lds<BF16, 1>(a, epi, st);
+            return launch_lds<WT, 1>(a, epi, st);
         if (a.B <= 2)
-            return launch_lds<BF16, 2>(a, epi, st);
-        return launch_lds<BF16, 4>(a, epi, st);
+            return launch_lds<WT, 2>(a, epi, st);
+        return launch_lds<WT, 4>(a, epi, st);
     }
     if (a.g)
         return hipErrorInvalidValue; // the fused norm needs the LDS path
     if (a.B <= 8)
-        return launch_gx<BF16, 8>(a, epi, st);
-    return launch_gx<BF16, 16>(a, epi, st);
+        return launch_gx<WT, 8>(a, epi, st);
+    return launch_gx<WT, 16>(a, epi, st);
 }
 
 // Host-checked preconditions: N a multiple of 8, K a
 // multiple of the 16-byte vector (of 32 with qin), rows 16-byte aligned,
 // 1 <= B <= 16; a fused merge (mo.n_wires > 0) only with EPI_STORE and fp32
 // wires.
-hipError_t launch_gemv(const GemvArgs &a, int w_bf16, int epi, hipStream_t st)
+hipError_t launch_gemv(const GemvArgs &a, int wt, int epi, hipStream_t st)
 {
-    return w_bf16 ? launch_t<true>(a, epi, st) : launch_t<false>(a, epi, st);
+    if (wt == WT_I8)
+        return launch_t<WT_I8>(a, epi, st);
+    return wt == WT_BF16 ? launch_t<WT_BF16>(a, epi, st) : launch_t<WT_F32>(a, epi, st);
 }
 
 } // namespace tps

@@ -35,23 +35,53 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxWk = 16;
 
+// Eight int8 codes -> the bf16 MFMA operand (exact: |code| <= 127 has at
+// most 7 significant bits).
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(u32x2 v)
+{
+    uint32_t o[4];
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+        const uint32_t u = (h < 2 ? v.x : v.y) >> (16 * (h & 1));
+        const float f0 = (float)(int8_t)(u & 0xffu), f1 = (float)(int8_t)((u >> 8) & 0xffu);
+        o[h] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+    }
+    return __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+}
+
 // T = 16-row weight tiles per wave sharing each activation fragment (1 or
 // 2): two tiles halve the activation bytes the waves pull from L2 per weight
 // byte; the register cost limits such workgroups to 8 waves.
-template <int EPI, int T>
-__global__ __launch_bounds__(64 * (T == 1 ? kMaxWk : 8)) void k_gemv_mfma(MfmaGemvArgs a)
+// W8: int8 codes with a scale per 32 k of a row. MFMA step s of 128-block j
+// then covers exactly the 32-block 4j + s (lane q holds its codes 8q..8q+7,
+// 8 contiguous bytes), so each step's product goes through a fresh
+// accumulator and is added times the scale. The operands swap roles
+// (activations A, weights B): lane (q, r) then holds batches 4q..4q+3 of the
+// single weight row r, whose scale is one value per step; the partial sums
+// go to the reduction buffer in the usual (row 4q + i, batch r) places.
+// (At most 8 waves for W8: its conversions need more than the 128 registers
+// a 16-wave workgroup leaves.)
+constexpr int mfma_max_waves(int T, bool W8) { return T == 1 && !W8 ? kMaxWk : 8; }
+
+template <int EPI, int T, bool W8>
+__global__ __launch_bounds__(64 * mfma_max_waves(T, W8)) void k_gemv_mfma(MfmaGemvArgs a)
 {
     constexpr int P = 2; // 128-wide K blocks in flight per wave
-    __shared__ f32x4 red[T == 1 ? kMaxWk : 8][T][64];
+    __shared__ f32x4 red[mfma_max_waves(T, W8)][T][64];
     const int n0 = blockIdx.x * 16 * T;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
     const int nb = a.K >> 7;
     const int per = (nb + a.wk - 1) / a.wk;
     const int j0 = wv * per, j1 = min(nb, j0 + per);
     const u32x4 *wrow[T];
+    const u32x2 *w8row[T];
+    const float *srow[T]; // W8: scales of the lane's weight row r of tile t
 #pragma unroll
-    for (int t = 0; t < T; t++)
+    for (int t = 0; t < T; t++) {
         wrow[t] = (const u32x4 *)(a.W + (size_t)(n0 + 16 * t + r) * a.K + 8 * q);
+        w8row[t] = (const u32x2 *)((const int8_t *)a.W + (size_t)(n0 + 16 * t + r) * a.K + 8 * q);
+        srow[t] = W8 ? a.ws + (size_t)(n0 + 16 * t + r) * (a.K / 32) : nullptr;
+    }
     const u32x4 *xf = (const u32x4 *)a.xf; // 16-byte units: [j][hl][s][q][b]
     f32x4 acc[T];
 #pragma unroll
@@ -59,14 +89,23 @@ __global__ __launch_bounds__(64 * (T == 1 ? kMaxWk : 8)) void k_gemv_mfma(MfmaGe
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j = j0; j < j1; j += P) {
         u32x4 w[P][T][4], xh[P][4], xl[P][4];
+        u32x2 w8[P][T][4];
+        float4 sc[P][T]; // W8: row r's scales of the block's four 32-blocks
 #pragma unroll
         for (int p = 0; p < P; p++)
             if (j + p < j1)
 #pragma unroll
                 for (int t = 0; t < T; t++)
 #pragma unroll
-                    for (int s = 0; s < 4; s++)
-                        w[p][t][s] = __builtin_nontemporal_load(wrow[t] + (size_t)(j + p) * 16 + 4 * s);
+                    for (int s = 0; s < 4; s++) {
+                        if constexpr (W8) {
+                            w8[p][t][s] = __builtin_nontemporal_load(w8row[t] + (size_t)(j + p) * 16 + 4 * s);
+                            if (s == 0)
+                                sc[p][t] = *(const float4 *)(srow[t] + 4 * (j + p));
+                        } else {
+                            w[p][t][s] = __builtin_nontemporal_load(wrow[t] + (size_t)(j + p) * 16 + 4 * s);
+                        }
+                    }
 #pragma unroll
         for (int p = 0; p < P; p++)
             if (j + p < j1)
@@ -82,9 +121,22 @@ __global__ __launch_bounds__(64 * (T == 1 ? kMaxWk : 8)) void k_gemv_mfma(MfmaGe
                 for (int s = 0; s < 4; s++)
 #pragma unroll
                     for (int t = 0; t < T; t++) {
-                        const bf16x8 wa = __builtin_bit_cast(bf16x8, w[p][t][s]);
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xh[p][s]), acc[t], 0, 0, 0);
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xl[p][s]), acc[t], 0, 0, 0);
+                        if constexpr (W8) {
+                            const bf16x8 wb = i8x8_to_bf16(w8[p][t][s]);
+                            // d[i] = batch 4q + i of weight row r over 32-block 4 (j + p) + s
+                            f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xh[p][s]), wb,
+                                                                              f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xl[p][s]), wb, d, 0, 0, 0);
+                            const float scv = sc[p][t][s];
+                            acc[t][0] += scv * d[0];
+                            acc[t][1] += scv * d[1];
+                            acc[t][2] += scv * d[2];
+                            acc[t][3] += scv * d[3];
+                        } else {
+                            const bf16x8 wa = __builtin_bit_cast(bf16x8, w[p][t][s]);
+                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xh[p][s]), acc[t], 0, 0, 0);
+                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xl[p][s]), acc[t], 0, 0, 0);
+                        }
                     }
     }
     // lane holds rows n0 + 16 t + 4q + i (i < 4) of batch column b = r
@@ -105,9 +157,18 @@ __global__ __launch_bounds__(64 * (T == 1 ? kMaxWk : 8)) void k_gemv_mfma(MfmaGe
                     mpre[t][k] = *(const float4 *)((const float *)a.mo.wires[k] + mi);
         }
     }
+    if constexpr (W8) {
+        // acc[t][i] = (row r, batch 4q + i) -> the place of lane (r / 4, b), element r % 4
 #pragma unroll
-    for (int t = 0; t < T; t++)
-        red[wv][t][lane] = acc[t];
+        for (int t = 0; t < T; t++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                ((float *)&red[wv][t][(r >> 2) * 16 + 4 * q + i])[r & 3] = acc[t][i];
+    } else {
+#pragma unroll
+        for (int t = 0; t < T; t++)
+            red[wv][t][lane] = acc[t];
+    }
     __syncthreads();
     if (wv != 0 || b >= a.B)
         return;
@@ -196,10 +257,13 @@ __device__ __forceinline__ void wait_vmcnt()
 // the workgroups of tile column 0 add up each row's squares over the slice.
 constexpr int kSkUnits = kSkMaxNbs * 256 / (64 * kSkWaves); // 8-element units per thread
 
-template <int T, bool NORM>
+// W8: int8 weights as in k_gemv_mfma (each MFMA step one 32-block, operands
+// swapped, the step's product times the row's scale); the lane's partials
+// (row r, batches 4q..4q+3) are stored one by one.
+template <int T, bool NORM, bool W8>
 __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
 {
-    constexpr int P = 2; // 128-wide K blocks in flight per wave
+    constexpr int P = W8 ? 4 : 2; // 128-wide K blocks in flight per wave (the same bytes)
     __shared__ __attribute__((aligned(1024))) char lds[kSkMaxNbs * 8192];
     __shared__ float ssr[NORM ? 64 * kSkWaves : 1];
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
@@ -238,24 +302,45 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
     // row r at r K + 128 (block) + 32 s + 8 q elements, blocks past the slice
     // at kOob
     const int n0u = (blockIdx.x * kSkWaves + __builtin_amdgcn_readfirstlane(wv)) * 16 * T;
-    __amdgpu_buffer_rsrc_t Wr[T];
+    // (W8: codes K bytes a row, the lane's 8 bytes of a step at 32 s + 8 q;
+    // scales K / 32 floats a row, the block's four at 16 bytes)
+    constexpr uint32_t eb = W8 ? 1 : 2; // bytes per weight
+    __amdgpu_buffer_rsrc_t Wr[T], Sr[T];
 #pragma unroll
-    for (int t = 0; t < T; t++)
-        Wr[t] = buf_rsrc(a.W + (size_t)(n0u + 16 * t) * a.K + (size_t)jb * 128, (uint32_t)(16 * a.K - jb * 128) * 2);
-    const uint32_t lofs = (uint32_t)r * a.K * 2 + 16 * q;
+    for (int t = 0; t < T; t++) {
+        Wr[t] = buf_rsrc((const char *)a.W + ((size_t)(n0u + 16 * t) * a.K + (size_t)jb * 128) * eb,
+                         (uint32_t)(16 * a.K - jb * 128) * eb);
+        if constexpr (W8)
+            Sr[t] = buf_rsrc(a.ws + (size_t)(n0u + 16 * t) * (a.K / 32) + (size_t)jb * 4,
+                             (uint32_t)(16 * (a.K / 32) - jb * 4) * 4);
+    }
+    const uint32_t lofs = W8 ? (uint32_t)r * a.K + 8 * q : (uint32_t)r * a.K * 2 + 16 * q;
+    const uint32_t sofs = (uint32_t)r * (a.K / 32) * 4;
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; t++)
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int jl = 0; jl < nbl; jl += P) {
         u32x4 w[P][T][4];
+        u32x2 w8[P][T][4];
+        float4 sc[P][T];
 #pragma unroll
         for (int p = 0; p < P; p++)
 #pragma unroll
-            for (int t = 0; t < T; t++)
+            for (int t = 0; t < T; t++) {
 #pragma unroll
-                for (int s = 0; s < 4; s++)
-                    w[p][t][s] = buf_load16_nt(Wr[t], jl + p < nbl ? lofs + (uint32_t)(jl + p) * 256 + 64 * s : kOob);
+                for (int s = 0; s < 4; s++) {
+                    if constexpr (W8)
+                        w8[p][t][s] = buf_load8_nt(Wr[t], jl + p < nbl ? lofs + (uint32_t)(jl + p) * 128 + 32 * s : kOob);
+                    else
+                        w[p][t][s] = buf_load16_nt(Wr[t], jl + p < nbl ? lofs + (uint32_t)(jl + p) * 256 + 64 * s : kOob);
+                }
+                if constexpr (W8) {
+                    const u32x4 v = buf_load16(Sr[t], jl + p < nbl ? sofs + (uint32_t)(jl + p) * 16 : kOob);
+                    sc[p][t] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                                           __uint_as_float(v.w));
+                }
+            }
         // all P blocks' loads are issued before the first MFMA waits on one
         // (else the scheduler moves each load next to its use)
         __builtin_amdgcn_sched_barrier(0);
@@ -304,7 +389,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
                 // this wave's fragment loads (issued before these weight loads,
                 // loads complete in order) are done once only the weight loads
                 // remain; after the barrier every wave's fragments are in LDS
-                wait_vmcnt<P * T * 4>();
+                wait_vmcnt<P * T * (W8 ? 5 : 4)>(); // W8: 4 code loads + 1 scale load per (p, t)
                 __builtin_amdgcn_s_barrier();
             }
         }
@@ -317,17 +402,38 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
                     const u32x4 xl = *(const u32x4 *)(lds + (((jl + p) * 2 + 1) * 4 + s) * 1024 + lane * 16);
 #pragma unroll
                     for (int t = 0; t < T; t++) {
-                        const bf16x8 wa = __builtin_bit_cast(bf16x8, w[p][t][s]);
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xh), acc[t], 0, 0, 0);
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xl), acc[t], 0, 0, 0);
+                        if constexpr (W8) {
+                            const bf16x8 wb = i8x8_to_bf16(w8[p][t][s]);
+                            f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xh), wb,
+                                                                              f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xl), wb, d, 0, 0, 0);
+                            const float scv = sc[p][t][s];
+                            acc[t][0] += scv * d[0];
+                            acc[t][1] += scv * d[1];
+                            acc[t][2] += scv * d[2];
+                            acc[t][3] += scv * d[3];
+                        } else {
+                            const bf16x8 wa = __builtin_bit_cast(bf16x8, w[p][t][s]);
+                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xh), acc[t], 0, 0, 0);
+                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xl), acc[t], 0, 0, 0);
+                        }
                     }
                 }
     }
-    // lane (q, b = r) holds rows n0 + 16 t + 4q + i (i < 4) of batch column b
-    if (r < a.B)
+    if constexpr (W8) {
+        // lane (q, r) holds batches 4q + i (i < 4) of row n0 + 16 t + r
+#pragma unroll
+        for (int t = 0; t < T; t++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                if (4 * q + i < a.B)
+                    a.part[((size_t)ks * a.B + 4 * q + i) * a.N + n0 + 16 * t + r] = acc[t][i];
+    } else if (r < a.B) {
+        // lane (q, b = r) holds rows n0 + 16 t + 4q + i (i < 4) of batch column b
 #pragma unroll
         for (int t = 0; t < T; t++)
             *(f32x4 *)(a.part + ((size_t)ks * a.B + r) * a.N + n0 + 16 * t + 4 * q) = acc[t];
+    }
 }
 
 // y[b][n] = sum_s part[s][b][n] in slice order, then the projection's
@@ -480,17 +586,25 @@ hipError_t launch_gemv_mfma(const MfmaGemvArgs &a0, int epi, hipStream_t st)
         a.nbs = sh.nbs;
         a.S = sh.S;
         const dim3 grid(sh.R, sh.S), block(64 * kSkWaves);
+#define TPS_SK(NORM, W8)                                                           \
+    do {                                                                           \
+        if (sh.T == 2)                                                             \
+            hipLaunchKernelGGL((k_gemv_sk<2, NORM, W8>), grid, block, 0, st, a);   \
+        else                                                                       \
+            hipLaunchKernelGGL((k_gemv_sk<1, NORM, W8>), grid, block, 0, st, a);   \
+    } while (0)
         if (a.xs) {
-            if (sh.T == 2)
-                hipLaunchKernelGGL((k_gemv_sk<2, true>), grid, block, 0, st, a);
+            if (a.ws)
+                TPS_SK(true, true);
             else
-                hipLaunchKernelGGL((k_gemv_sk<1, true>), grid, block, 0, st, a);
+                TPS_SK(true, false);
         } else {
-            if (sh.T == 2)
-                hipLaunchKernelGGL((k_gemv_sk<2, false>), grid, block, 0, st, a);
+            if (a.ws)
+                TPS_SK(false, true);
             else
-                hipLaunchKernelGGL((k_gemv_sk<1, false>), grid, block, 0, st, a);
+                TPS_SK(false, false);
         }
+#undef TPS_SK
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -510,19 +624,29 @@ hipError_t launch_gemv_mfma(const MfmaGemvArgs &a0, int epi, hipStream_t st)
     const int wkb = (nb + 1) / 2;
     const int wk2 = wkb < 1 ? 1 : wkb > 8 ? 8 : wkb;
     const bool two = a.N % 32 == 0 && (long)(a.N / 32) * wk2 >= 1024;
-    a.wk = two ? wk2 : (wkb < 1 ? 1 : wkb > kMaxWk ? kMaxWk : wkb);
+    const int wmax = a.ws ? 8 : kMaxWk;
+    a.wk = two ? wk2 : (wkb < 1 ? 1 : wkb > wmax ? wmax : wkb);
     const dim3 grid(a.N / (two ? 32 : 16)), block(64 * a.wk);
+#define TPS_MFMA(TT, W8)                                                              \
+    do {                                                                              \
+        if (epi == EPI_SWIGLU)                                                        \
+            hipLaunchKernelGGL((k_gemv_mfma<EPI_SWIGLU, TT, W8>), grid, block, 0, st, a); \
+        else                                                                          \
+            hipLaunchKernelGGL((k_gemv_mfma<EPI_STORE, TT, W8>), grid, block, 0, st, a);  \
+    } while (0)
+    const bool w8 = a.ws != nullptr;
     if (two) {
-        if (epi == EPI_SWIGLU)
-            hipLaunchKernelGGL((k_gemv_mfma<EPI_SWIGLU, 2>), grid, block, 0, st, a);
+        if (w8)
+            TPS_MFMA(2, true);
         else
-            hipLaunchKernelGGL((k_gemv_mfma<EPI_STORE, 2>), grid, block, 0, st, a);
+            TPS_MFMA(2, false);
     } else {
-        if (epi == EPI_SWIGLU)
-            hipLaunchKernelGGL((k_gemv_mfma<EPI_SWIGLU, 1>), grid, block, 0, st, a);
+        if (w8)
+            TPS_MFMA(1, true);
         else
-            hipLaunchKernelGGL((k_gemv_mfma<EPI_STORE, 1>), grid, block, 0, st, a);
+            TPS_MFMA(1, false);
     }
+#undef TPS_MFMA
     return hipGetLastError();
 }
 

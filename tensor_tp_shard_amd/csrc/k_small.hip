@@ -176,6 +176,40 @@ __global__ __launch_bounds__(256) void k_wire(WireArgs a)
     }
 }
 
+// Weight quantisation at load time: rows of a bf16 or fp32 matrix (pitch
+// src_pitch elements) to int8 codes and one fp32 scale per 32 consecutive
+// elements of a row, with the block-32 codec of the exchanged activations.
+// One 32-lane group per block (the group's max |w| by butterfly), as k_wire.
+__global__ __launch_bounds__(256) void k_quant_rows(QuantRowsArgs a)
+{
+    const int nb = a.cols / kQBlock;
+    const long blk = (long)blockIdx.x * 8 + (threadIdx.x >> 5);
+    const int lane = threadIdx.x & 31;
+    const bool ok = blk < (long)a.rows * nb;
+    const long row = ok ? blk / nb : 0;
+    const int c = ok ? (int)(blk % nb) * kQBlock + lane : 0;
+    float v = 0.f;
+    if (ok) {
+        const size_t e = (size_t)row * a.src_pitch + c;
+        v = a.src_bf16 ? bf16_to_f32(((const uint16_t *)a.src)[e]) : ((const float *)a.src)[e];
+    }
+    const float s = q8_scale(group_max<32>(fabsf(v)));
+    if (ok) {
+        a.codes[(size_t)row * a.code_pitch + c] = (int8_t)q8_code(v, s);
+        if (lane == 0)
+            a.scales[(size_t)row * a.scale_pitch + c / kQBlock] = s;
+    }
+}
+
+hipError_t launch_quant_rows(const QuantRowsArgs &a, hipStream_t st)
+{
+    const long n = (long)a.rows * (a.cols / kQBlock);
+    if (n == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_quant_rows, dim3((unsigned)((n + 7) / 8)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 // out = residual + d_0 + d_1 + ... (array order), 4 elements per thread;
 // the wires are read 8 at a time so their loads are in flight together.
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a)

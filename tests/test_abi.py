@@ -47,6 +47,30 @@ def test_sizes_of_the_7b_shard():
     assert s.wire == D + (D // 32) * 4
     assert tp.wire_scales_offset(cfg7b(), 3) == 3 * D
     tp.destroy_shard(h)
+    # int8 weights: one byte per weight plus an fp32 scale per 32
+    h, s = tp.init_shard(cfg7b(quant=tp.TP_Q_WEIGHTS))
+    n_w = weights // 2
+    w8 = n_w + n_w // 32 * 4
+    assert s.packed_weights >= w8 and s.packed_weights < w8 + 2 * 2049 * 64 * 8 + 8192
+    tp.destroy_shard(h)
+
+
+def test_packed_int8_view():
+    h, _ = tp.init_shard(cfg7b())
+    with pytest.raises(tp.TpError):
+        tp.packed_int8_view(h, 0)  # no int8 weights
+    tp.destroy_shard(h)
+    h, s = tp.init_shard(cfg7b(quant=tp.TP_Q_WEIGHTS))
+    views = [tp.packed_int8_view(h, p) for p in range(4)]
+    assert [v[2:] for v in views] == [(3072, 4096), (4096, 1024), (5504, 4096), (4096, 2752)]
+    ends = sorted((co, co + r * c) for co, _, r, c in views) + \
+        sorted((so, so + r * c // 8) for _, so, r, c in views)
+    for (a0, a1), (b0, _) in zip(ends, ends[1:]):
+        assert a1 <= b0 and a0 % 256 == 0  # disjoint, 256-byte aligned, codes before scales
+    assert ends[-1][1] <= s.packed_weights
+    with pytest.raises(tp.TpError):
+        tp.packed_int8_view(h, 4)
+    tp.destroy_shard(h)
 
 
 @pytest.mark.parametrize("kw", [
@@ -56,7 +80,8 @@ def test_sizes_of_the_7b_shard():
     dict(head_dim=120),              # not a multiple of 16
     dict(max_batch=0),
     dict(max_batch=17),
-    dict(quant=4),                   # unknown bit
+    dict(quant=8),                   # unknown bit
+    dict(quant=4, ffn_hidden=11072),  # int8 weights: F/T = 2768 not a multiple of 32
     dict(quant=1, quant_block=16),   # block must be 32
     dict(w_dtype=7),
     dict(kind=5),

@@ -147,15 +147,16 @@ def test_micro_gqa_ragged_batch(hd):
     check_layer(w, d)
 
 
-def test_splitk_folded_norm_ragged_batch():
+@pytest.mark.parametrize("quant", [synth.Q_NONE, synth.Q_WEIGHTS])
+def test_splitk_folded_norm_ragged_batch(quant):
     """Batch 7 at dim 4096: both up-projections take the split-K kernels with
     the RMSNorm folded in (QKV with one 16-row tile per wave, W1/W3 with
-    two), and operand rows 7..15 are zero. Checked against the oracle (with
-    taps, where a RMSNorm kernel also runs for the xn tap alone), then the
-    output without taps must be bitwise the same."""
-    w = synth.small_llama(name="splitk_norm_b7", dim=4096, n_heads=8, n_kv_heads=2, head_dim=128,
+    two), and operand rows 7..15 are zero; bf16 and int8 weights. Checked
+    against the oracle (with taps, where a RMSNorm kernel also runs for the xn
+    tap alone), then the output without taps must be bitwise the same."""
+    w = synth.small_llama(name=f"splitk_norm_b7_q{quant}", dim=4096, n_heads=8, n_kv_heads=2, head_dim=128,
                           ffn_hidden=4096, tp=2, batch=7, past=(1, 100), w_dtype=synth.BF16,
-                          kv_dtype=synth.BF16, seed=79)
+                          kv_dtype=synth.BF16, quant=quant, seed=79)
     d = synth.llama_inputs(w)
     _, g, _ = check_layer(w, d)
     say("splitk_norm_b7 without taps")
@@ -171,6 +172,60 @@ def test_mfma_gemv_one_tile_sixteen_waves():
                           ffn_hidden=7936, tp=2, batch=12, past=(1, 60), w_dtype=synth.BF16,
                           kv_dtype=synth.BF16, seed=80)
     check_layer(w)
+
+
+def test_llama7b_tp4_w8_layer():
+    """7B shard shapes with int8 weights, batch 1: the LDS-staged GEMVs read
+    16 codes per 16-byte load and one scale per 32."""
+    check_layer(synth.L7B_W8)
+
+
+def _w8_expected(w, d, r):
+    """The oracle's codes and scales of shard r's four packed projections."""
+    T, hd, D = w.tp, w.head_dim, w.dim
+    nq, nk, Fs = w.n_heads // T * hd, w.n_kv_heads // T * hd, w.ffn_hidden // T
+    q = {k: oracle.q8_weights(d[k], w.w_dtype) for k in ("wq", "wk", "wv", "wo", "w1", "w3", "w2")}
+    c_qkv = np.concatenate([q["wq"][0][r * nq:(r + 1) * nq], q["wk"][0][r * nk:(r + 1) * nk],
+                            q["wv"][0][r * nk:(r + 1) * nk]])
+    s_qkv = np.concatenate([q["wq"][1][r * nq:(r + 1) * nq], q["wk"][1][r * nk:(r + 1) * nk],
+                            q["wv"][1][r * nk:(r + 1) * nk]])
+    c_wo, s_wo = q["wo"][0][:, r * nq:(r + 1) * nq], q["wo"][1][:, r * nq // 32:(r + 1) * nq // 32]
+    c13 = np.empty((2 * Fs, D), np.int8)
+    s13 = np.empty((2 * Fs, D // 32), np.float32)
+    c13[0::2], c13[1::2] = q["w1"][0][r * Fs:(r + 1) * Fs], q["w3"][0][r * Fs:(r + 1) * Fs]
+    s13[0::2], s13[1::2] = q["w1"][1][r * Fs:(r + 1) * Fs], q["w3"][1][r * Fs:(r + 1) * Fs]
+    c_w2, s_w2 = q["w2"][0][:, r * Fs:(r + 1) * Fs], q["w2"][1][:, r * Fs // 32:(r + 1) * Fs // 32]
+    return [(c_qkv, s_qkv), (c_wo, s_wo), (c13, s13), (c_w2, s_w2)]
+
+
+@pytest.mark.parametrize("case", ["mfma_b16", "lds_b3", "global_b2"])
+def test_int8_weights_codes_and_layer(case):
+    """int8 weights on each projection kernel: batch 16 (MFMA, operands
+    swapped so each lane's scale is one per step; W2 with 16-wave K split
+    capped at 8), batch 3 (activations staged in LDS), batch 2 at dim 4224
+    (activations read from global memory). The packed codes and scales of
+    every shard equal the oracle's codec bit for bit; the layer matches the
+    oracle's layer on the dequantised weights."""
+    shapes = {
+        "mfma_b16": dict(dim=1024, n_heads=8, n_kv_heads=2, head_dim=128, ffn_hidden=7936, batch=16),
+        "lds_b3": dict(dim=256, n_heads=8, n_kv_heads=4, head_dim=32, ffn_hidden=512, batch=3),
+        "global_b2": dict(dim=4224, n_heads=4, n_kv_heads=4, head_dim=32, ffn_hidden=512, batch=2),
+    }
+    w = synth.small_llama(name=f"w8_{case}", tp=2, past=(1, 70), w_dtype=synth.BF16, kv_dtype=synth.BF16,
+                          quant=synth.Q_WEIGHTS, seed=81, **shapes[case])
+    d = synth.llama_inputs(w)
+    L, _, _ = check_layer(w, d)
+    from gpu_harness import to_np
+    for r in range(w.tp):
+        sh = L.shards[r]
+        packed = to_np(sh.packed)
+        for proj, (ce, se) in enumerate(_w8_expected(w, d, r)):
+            co, so, rows, cols = tp.packed_int8_view(sh.handle, proj)
+            assert (rows, cols) == ce.shape, (proj, rows, cols, ce.shape)
+            got_c = packed[co:co + rows * cols].view(np.int8).reshape(rows, cols)
+            got_s = packed[so:so + rows * (cols // 32) * 4].view(np.uint32).reshape(rows, cols // 32)
+            assert np.array_equal(got_c, ce), f"{case} shard {r} projection {proj}: codes differ"
+            assert np.array_equal(got_s, se.view(np.uint32)), f"{case} shard {r} projection {proj}: scales"
 
 
 def test_determinism_and_batch_rows():

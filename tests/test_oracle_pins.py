@@ -218,6 +218,64 @@ def test_q8_multiples_of_scale_are_exact(orc):
     assert np.array_equal(orc.q8_dequantize(codes, scales), x.reshape(-1))
 
 
+# ---------------------------------------------------------------- int8 weights
+
+def test_q8_weights_block_rows_along_k(orc):
+    """Blocks run along each row (k), never across rows: row i's codes and
+    scales equal the codec applied to row i alone; |DQ - W| stays within
+    half a step of the row block's scale."""
+    W = synth.f32_to_bf16_bits(_rng(31).normal(0, 0.02, size=(6, 96)).astype(np.float32))
+    codes, scales, deq = orc.q8_weights(W, "bf16")
+    assert codes.shape == (6, 96) and scales.shape == (6, 3) and deq.shape == (6, 96)
+    wf = synth.bf16_bits_to_f32(W).astype(np.float64)
+    for i in range(6):
+        ci, si = orc.q8_quantize(synth.bf16_bits_to_f32(W[i]))
+        assert np.array_equal(codes[i], ci) and np.array_equal(scales[i].view(np.uint32), si.view(np.uint32))
+    s = np.repeat(scales.astype(np.float64), 32, axis=1)
+    assert np.all(np.abs(deq - wf) <= s * (0.5 + 127 * 2.0 ** -22))
+    # a block of one row holding a single nonzero weight keeps it exactly
+    W1 = np.zeros((2, 64), np.float32)
+    W1[1, 37] = -0.375
+    c1, s1, d1 = orc.q8_weights(W1, "f32")
+    assert np.array_equal(d1, W1) and c1[1, 37] == -127 and np.count_nonzero(c1) == 1
+    assert s1[0].tolist() == [0.0, 0.0] and s1[1, 0] == 0.0
+
+
+def _lossless_int8_weights(w, d, rng):
+    """Weights m * 2^-9 with integer |m| <= 127 and 127 in every 32-block of
+    every row: the codec stores them exactly (scale 2^-9, code m)."""
+    for k in ("wq", "wk", "wv", "wo", "w1", "w3", "w2"):
+        N, K = d[k].shape
+        m = rng.integers(-126, 127, size=(N, K))
+        m[:, ::32] = 127 * rng.choice([-1, 1], size=(N, K // 32))
+        d[k] = synth.f32_to_bf16_bits((m * 2.0 ** -9).astype(np.float32))
+    return d
+
+
+def test_int8_weight_layer_is_exact_when_the_codec_is_lossless(orc):
+    """With every row block holding its own maximum on the 2^-9 grid the int8
+    layer must equal the bf16 layer bit for bit; blocks taken down the
+    columns instead would not be lossless for these weights (checked)."""
+    w = synth.small_llama(name="pin_w8", dim=64, n_heads=4, n_kv_heads=2, head_dim=16, ffn_hidden=128,
+                          tp=2, batch=2, past=(3, 9), w_dtype=synth.BF16, kv_dtype=synth.BF16, seed=41)
+    d = _lossless_int8_weights(w, synth.llama_inputs(w), _rng(42))
+    import dataclasses
+    w8 = dataclasses.replace(w, quant=synth.Q_WEIGHTS)
+    o16 = orc.llama_layer(w, d, d["x"], d["lens"], d["kcache"].copy(), d["vcache"].copy())
+    o8 = orc.llama_layer(w8, d, d["x"], d["lens"], d["kcache"].copy(), d["vcache"].copy())
+    for key in ("q", "att", "p_att", "a", "p_ffn", "out"):
+        assert np.array_equal(o16[key], o8[key]), key
+    wt = synth.bf16_bits_to_f32(d["w2"]).T.copy()  # columns as rows
+    _, _, dq = orc.q8_weights(wt, "f32")
+    assert not np.array_equal(dq, wt)
+    # and with ordinary weights the int8 layer differs by about the codec's error
+    d2 = synth.llama_inputs(w)
+    o16 = orc.llama_layer(w, d2, d2["x"], d2["lens"], d2["kcache"].copy(), d2["vcache"].copy())
+    o8 = orc.llama_layer(w8, d2, d2["x"], d2["lens"], d2["kcache"].copy(), d2["vcache"].copy())
+    e = rel_l2(o8["out"] - o8["h"], o16["out"] - o16["h"])
+    assert 1e-4 < e < 3e-2, e
+
+
 # ---------------------------------------------------------------- merge / wire
 
 def test_merge_integer_sums_exact(orc):
