@@ -9,6 +9,7 @@ survive. Residual deltas (h - x, out - h) are compared, not h and out, so the
 N(0, 1) residual cannot mask an error in the small partials.
 """
 import dataclasses
+import math
 import sys
 
 import numpy as np
@@ -94,12 +95,26 @@ def check_layer(w, d=None, ranks=None):
         for key, tk in (("xn", "taps_att"), ("hn", "taps_ffn")):
             got = g[tk][0]["xn"].astype(np.float64).reshape(B, -1, 32)
             ref = o[key][0].reshape(B, -1, 32)
+            if key == "hn" and w.quant & synth.Q_PARTIALS:
+                # the FFN input is the merge of int8 wires, whose codes may flip at a
+                # tie between the GPU's fp32 and the oracle's fp64 partials (the
+                # wires are checked against the codec of the GPU's own partial): so
+                # is hn, against the oracle's norm + round trip of the GPU's own h
+                hn = np.stack([oracle.rmsnorm(g["h"][b], d["g_ffn"], w.norm_eps) for b in range(B)])
+                c_, s_ = oracle.q8_quantize(hn.astype(np.float32))
+                ref = oracle.q8_dequantize(c_, s_).astype(np.float64).reshape(B, -1, 32)
             step = np.broadcast_to(np.abs(ref).max(axis=2, keepdims=True) / 127, ref.shape)
             diff = np.abs(got - ref)
             flip = diff > 0.5 * step
-            # same code: only the scale differs, by the few ulps its amax (fp32 norm
-            # vs fp64 norm) can differ: |code| * dscale <= 127 * 3 * 2^-23 * scale
-            assert np.all(diff[~flip] <= 127 * 3 * 2.0 ** -23 * step[~flip])
+            # same code: only the scale differs, by the ulps its amax (fp32 norm vs
+            # fp64 norm) can differ: 3 for the final product, quotient and root,
+            # plus the fp32 sum of squares' rounding, which grows with the row
+            # length (a tree and a sequential part over D terms: log2(D) ulps
+            # bound it here): |code| * dscale <= 127 * (3 + log2 D) * 2^-23 * scale
+            ulps = 3 + math.log2(w.dim)
+            bad = diff[~flip] > 127 * ulps * 2.0 ** -23 * step[~flip]
+            assert not bad.any(), (f"{key}: {bad.sum()} values off by up to "
+                                   f"{(diff[~flip] / step[~flip]).max():.3e} steps")
             assert np.all(np.abs(diff[flip] / step[flip] - 1) < 1e-3)
             assert flip.mean() < 1e-2, f"{key}: {flip.sum()} codes flipped"
     e_h = rel_l2(g["h"].astype(np.float64) - x, o["h"] - x)
@@ -147,11 +162,14 @@ def test_micro_gqa_ragged_batch(hd):
     check_layer(w, d)
 
 
-@pytest.mark.parametrize("quant", [synth.Q_NONE, synth.Q_WEIGHTS])
+@pytest.mark.parametrize("quant", [synth.Q_NONE, synth.Q_WEIGHTS,
+                                   synth.Q_WEIGHTS | synth.Q_INPUTS | synth.Q_PARTIALS])
 def test_splitk_folded_norm_ragged_batch(quant):
     """Batch 7 at dim 4096: both up-projections take the split-K kernels with
     the RMSNorm folded in (QKV with one 16-row tile per wave, W1/W3 with
-    two), and operand rows 7..15 are zero; bf16 and int8 weights. Checked
+    two), and operand rows 7..15 are zero; bf16 and int8 weights (with int8
+    inputs the norm kernel runs and the split-K kernels read its fragments,
+    their weight loads then counted behind the fragment loads). Checked
     against the oracle (with taps, where a RMSNorm kernel also runs for the xn
     tap alone), then the output without taps must be bitwise the same."""
     w = synth.small_llama(name=f"splitk_norm_b7_q{quant}", dim=4096, n_heads=8, n_kv_heads=2, head_dim=128,
