@@ -36,17 +36,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMaxWk = 16;
 
 // Eight int8 codes -> the bf16 MFMA operand (exact: |code| <= 127 has at
-// most 7 significant bits).
+// most 7 significant bits): one sign-extending byte conversion to fp32 per
+// code, one packed fp32 -> bf16 conversion per two.
 __device__ __forceinline__ bf16x8 i8x8_to_bf16(u32x2 v)
 {
-    uint32_t o[4];
+    bf16x8 o;
 #pragma unroll
-    for (int h = 0; h < 4; h++) {
-        const uint32_t u = (h < 2 ? v.x : v.y) >> (16 * (h & 1));
-        const float f0 = (float)(int8_t)(u & 0xffu), f1 = (float)(int8_t)((u >> 8) & 0xffu);
-        o[h] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-    }
-    return __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+    for (int e = 0; e < 8; e++)
+        o[e] = (__bf16)(float)(int8_t)(((e < 4 ? v.x : v.y) >> (8 * (e & 3))) & 0xffu);
+    return o;
 }
 
 // T = 16-row weight tiles per wave sharing each activation fragment (1 or
