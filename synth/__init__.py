@@ -116,6 +116,11 @@ L70B_W8 = _add(dataclasses.replace(L70B, name="llama2_70b_tp8_b16_w8", quant=Q_W
 # PaLM-540B FFN block of an 8x8 2D weight-stationary grid: E=18432/8, F=73728/8
 PALM_DEC = _add(Ffn2D("palm540b_ffn2d_b512", e_blk=2304, f_blk=9216, batch=512, seed=1005))
 PALM_PRE = _add(Ffn2D("palm540b_ffn2d_prefill8192", e_blk=2304, f_blk=9216, batch=8192, seed=1005))
+# weight-gathered prefill on the same 64 chips: with the weights all-gathered over
+# N chips each chip holds an E x (F N / n) block and takes BL / N tokens; at
+# BL = F N^2 / n = 294,912 tokens the optimal N = sqrt(BL n / F) is 16, so one
+# chip's share is E = 18432, F' = 18432, 18432 tokens
+PALM_GATHERED = _add(Ffn2D("palm540b_ffn2d_gathered", e_blk=18432, f_blk=18432, batch=18432, seed=1008))
 
 
 def get(name: str):

@@ -92,6 +92,12 @@ def test_palm_ffn2d_prefill_8192_sampled_rows():
     _sampled_rows_check(synth.PALM_PRE, [0, 4095, 8191])
 
 
+def test_palm_ffn2d_weight_gathered_sampled_rows():
+    """The weight-gathered prefill share (E = F' = 18432, 18432 tokens): the
+    same kernels at a 37.6 TFLOP shape; rows at 256-row tile edges."""
+    _sampled_rows_check(synth.PALM_GATHERED, [0, 255, 256, 18431])
+
+
 @pytest.mark.parametrize("B,tile", [(2100, 128), (4100, 256)])
 def test_ffn2d_large_batch_tiles_and_ragged_tail(B, tile):
     """Large batches: 2100 rows on the 128-row tiles with 32 K values per
