@@ -97,6 +97,10 @@ def _declare(L):
     L.orc_llama_layer.argtypes = [_P, _P, _P, _P, _P, _P, _P]
     L.orc_llama_layer.restype = ctypes.c_int
     L.orc_ffn2d.argtypes = [_I64, _I64, _P, _P, _P, _P, _I64, _I64, _P]
+    L.orc_logits_shard.argtypes = [_I64, _I64, _I64, _I32, _I32, _P, ctypes.c_int, _P, _D, _P, _P,
+                                   _P]
+    L.orc_logits_shard.restype = ctypes.c_int
+    L.orc_merge_logits.argtypes = [_I64, _I64, _I32, _P, _P]
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -324,3 +328,70 @@ def ffn2d(x, w_gate, w_in, w_out, row0: int = 0, nrows: Optional[int] = None) ->
     y = np.empty((nrows, E), dtype=np.float64)
     lib().orc_ffn2d(E, F, _ptr(x), _ptr(w_gate), _ptr(w_in), _ptr(w_out), row0, nrows, _ptr(y))
     return y
+
+
+# ---------------------------------------------------------------- final stage
+
+def logits_shard(w_cls, g, x, tp: int, s: int, eps: float = 1e-5, dtype="bf16",
+                 w8: bool = False) -> Dict[str, np.ndarray]:
+    """Final RMSNorm + shard s's vocabulary slice of the logits.
+    w_cls [V][D] in dtype (f32 array or bf16 bit patterns), g fp32 [D],
+    x [B][D]. With w8 the classifier goes through the int8 weight codec
+    first (q8_weights). -> {"xn": [B][D], "z": [B][V/tp]} fp64."""
+    dt = _dt(dtype)
+    W = _typed(w_cls, dt)
+    if w8:
+        W, dt = np.ascontiguousarray(q8_weights(W, dtype)[2]), F32
+    V, D = W.shape
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    x = np.ascontiguousarray(x, dtype=np.float64).reshape(-1, D)
+    B = x.shape[0]
+    assert V % tp == 0
+    out = {"xn": np.empty((B, D)), "z": np.empty((B, V // tp))}
+    rc = lib().orc_logits_shard(B, D, V, tp, s, _ptr(W), dt, _ptr(g), eps, _ptr(x), _ptr(out["xn"]),
+                                _ptr(out["z"]))
+    if rc:
+        raise ValueError(f"orc_logits_shard rejected the input ({rc})")
+    return out
+
+
+def merge_logits(slices) -> np.ndarray:
+    """slices [T][B][Vs] (dequantised wires in shard order) -> [B][T*Vs]."""
+    d = np.ascontiguousarray(slices, dtype=np.float64)
+    T, B, Vs = d.shape
+    out = np.empty((B, T * Vs))
+    lib().orc_merge_logits(B, Vs, T, _ptr(d), _ptr(out))
+    return out
+
+
+def logits(w_cls, g, x, tp: int, quant: int = 0, eps: float = 1e-5, dtype="bf16",
+           w8: bool = False) -> Dict[str, np.ndarray]:
+    """Every shard's logits stage in turn, its wire (int8 with Q_PARTIALS)
+    and the merge into full rows. -> {"xn", "z" [T][B][Vs] (before the wire),
+    "codes" / "scales" [T][B][...] (None without Q_PARTIALS), "out" [B][V]}."""
+    zs, ds, cs, ss, xn = [], [], [], [], None
+    for s in range(tp):
+        o = logits_shard(w_cls, g, x, tp, s, eps, dtype, w8)
+        xn = o["xn"]
+        d, c, sc = wire(o["z"], quant)
+        zs.append(o["z"]), ds.append(d), cs.append(c), ss.append(sc)
+    q = bool(quant & Q_PARTIALS)
+    return {"xn": xn, "z": np.stack(zs), "codes": np.stack(cs) if q else None,
+            "scales": np.stack(ss) if q else None, "out": merge_logits(np.stack(ds))}
+
+
+def llama_decode(layers, w_cls, g_final, x, lens, kcaches, vcaches, quant_logits: int = 0,
+                 eps: float = 1e-5, cls_dtype="bf16", cls_w8: bool = False) -> Dict[str, np.ndarray]:
+    """One decode step of a whole model ([DL] buildLlama2Arch: the layer task
+    list once per layer, llamaNextBlock passing each layer's merged output to
+    the next, then the final norm, logits and their merge). layers: a list of
+    (block description, weights) pairs; kcaches / vcaches: one cache pair per
+    layer, updated in place. -> {"h": [L][B][D] layer outputs, "out": [B][V]}."""
+    hs = []
+    h = np.ascontiguousarray(x, dtype=np.float64)
+    for (w, weights), kc, vc in zip(layers, kcaches, vcaches):
+        h = llama_layer(w, weights, h, lens, kc, vc)["out"]
+        hs.append(h)
+    tp = layers[0][0].tp
+    lo = logits(w_cls, g_final, h, tp, quant_logits, eps, cls_dtype, cls_w8)
+    return {"h": np.stack(hs), "out": lo["out"], "z": lo["z"]}

@@ -510,3 +510,47 @@ void orc_ffn2d(int64_t E, int64_t F, const uint16_t *X, const uint16_t *Wgate,
     free(x);
     free(hgt);
 }
+
+/* ---------------------------------------------------------------- final stage */
+
+/* Logits of shard s of T ([DL] root tasks llamaRmsFinal, llamaRmsFinalNorm,
+ * llamaLogits; a worker runs llamaLogits): RMSNorm of the last layer's
+ * merged output with the final gain g, then the shard's rows
+ * [s*V/T, (s+1)*V/T) of the classifier W_cls [V][D] (stored type dt) times
+ * the normalised row. The pages split the vocabulary between the nodes (the
+ * workers compute logits too) but give no split rule; the column split of
+ * [TP] 核心概念 item 1 over the vocabulary is the plain reading: each shard
+ * owns whole logits. The page lists no quantise / sync task between the
+ * final norm and the logits, so the normalised row is used unquantised.
+ *  x [B][D]; xn_out [B][D] (may be NULL); z [B][V/T]. */
+int orc_logits_shard(int64_t B, int64_t D, int64_t V, int32_t T, int32_t s, const void *Wcls,
+                     int dt, const float *g, double eps, const double *x, double *xn_out,
+                     double *z)
+{
+    if (T < 1 || V % T || s < 0 || s >= T)
+        return -1;
+    const int64_t Vs = V / T;
+    const int64_t esz = dt == ORC_F32 ? 4 : 2;
+    double *xn = (double *)malloc(sizeof(double) * (size_t)D);
+    for (int64_t b = 0; b < B; b++) {
+        orc_rmsnorm(D, x + b * D, g, eps, xn);
+        if (xn_out)
+            memcpy(xn_out + b * D, xn, sizeof(double) * (size_t)D);
+        orc_matvec(Vs, D, (const char *)Wcls + s * Vs * D * esz, dt, D, 0, xn, z + b * Vs);
+    }
+    free(xn);
+    return 0;
+}
+
+/* Merge of the shards' logits ([DL] llamaSyncLogits, llamaDequantizeLogits,
+ * llamaMergeLogits): shard i's (dequantised) slice d[i] [B][Vs] becomes
+ * columns [i*Vs, (i+1)*Vs) of the full logits rows, out [B][T*Vs]. With a
+ * vocabulary split the slices are disjoint, so the merge places them and
+ * adds nothing. */
+void orc_merge_logits(int64_t B, int64_t Vs, int32_t T, const double *d, double *out)
+{
+    for (int32_t i = 0; i < T; i++)
+        for (int64_t b = 0; b < B; b++)
+            for (int64_t j = 0; j < Vs; j++)
+                out[b * T * Vs + i * Vs + j] = d[(i * B + b) * Vs + j];
+}

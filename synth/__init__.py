@@ -45,6 +45,7 @@ STREAMS = {
     "wq": 1, "wk": 2, "wv": 3, "wo": 4, "w1": 5, "w3": 6, "w2": 7,
     "g_att": 8, "g_ffn": 9, "x": 10, "lens": 11, "kcache": 12, "vcache": 13,
     "ffn_x": 20, "ffn_win": 21, "ffn_wgate": 22, "ffn_wout": 23,
+    "w_cls": 30, "g_final": 31, "final_x": 32,
 }
 
 
@@ -86,6 +87,22 @@ class Ffn2D:
     kind: str = "ffn2d"
 
 
+@dataclasses.dataclass(frozen=True)
+class LlamaLogits:
+    """The final stage of a Llama-style decode step split over ``tp`` shards:
+    final RMSNorm and the vocabulary slice V/tp of the classifier per shard."""
+    name: str
+    dim: int
+    vocab: int
+    tp: int
+    batch: int
+    w_dtype: str
+    quant: int
+    seed: int
+    norm_eps: float = 1e-5
+    kind: str = "logits"
+
+
 WORKLOADS: Dict[str, object] = {}
 
 
@@ -121,6 +138,15 @@ PALM_PRE = _add(Ffn2D("palm540b_ffn2d_prefill8192", e_blk=2304, f_blk=9216, batc
 # BL = F N^2 / n = 294,912 tokens the optimal N = sqrt(BL n / F) is 16, so one
 # chip's share is E = 18432, F' = 18432, 18432 tokens
 PALM_GATHERED = _add(Ffn2D("palm540b_ffn2d_gathered", e_blk=18432, f_blk=18432, batch=18432, seed=1008))
+
+
+# final norm + logits of Llama-2 (vocabulary 32000) at the two block shapes
+L7B_LOGITS = _add(LlamaLogits("llama2_7b_tp4_logits_b1", dim=4096, vocab=32000, tp=4, batch=1,
+                              w_dtype=BF16, quant=Q_NONE, seed=1009))
+L7B_LOGITS_Q8 = _add(dataclasses.replace(L7B_LOGITS, name="llama2_7b_tp4_logits_b1_q8",
+                                         quant=Q_PARTIALS, seed=1010))
+L70B_LOGITS = _add(LlamaLogits("llama2_70b_tp8_logits_b16", dim=8192, vocab=32000, tp=8, batch=16,
+                               w_dtype=BF16, quant=Q_NONE, seed=1011))
 
 
 def get(name: str):
@@ -229,6 +255,17 @@ def llama_inputs(w: LlamaBlock) -> Dict[str, np.ndarray]:
     d["kcache"] = llama_kv_cache(w, lens, "kcache")
     d["vcache"] = llama_kv_cache(w, lens, "vcache")
     return d
+
+
+def logits_inputs(w: LlamaLogits, batch: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Full classifier W_cls [V][D] (N(0, 0.02), w_dtype), final gain g
+    (N(1, 0.02)) and the last layer's merged output x [B][D] (N(0, 1))."""
+    B = w.batch if batch is None else batch
+    return {
+        "w_cls": weight(w, "w_cls", (w.vocab, w.dim)),
+        "g_final": normal_f32(w.seed, STREAMS["g_final"], (w.dim,), 0.02, 1.0),
+        "x": normal_f32(w.seed, STREAMS["final_x"], (B, w.dim), 1.0),
+    }
 
 
 # ---------------------------------------------------------------- 2D FFN block inputs

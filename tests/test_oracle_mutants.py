@@ -30,6 +30,10 @@ MUTANTS = {
     "append_slot": ("* C + L) * hd;", "* C + L - 1) * hd;"),
     "w2_column_offset": ("w->w2, c->w_dtype, F, s * Fs,", "w->w2, c->w_dtype, F, 0,"),
     "ffn2d_gate_in_swapped": ("hgt[f] = orc_silu(g) * u;", "hgt[f] = orc_silu(u) * g;"),
+    "logits_row_offset": ("(const char *)Wcls + s * Vs * D * esz", "(const char *)Wcls"),
+    "logits_no_final_norm": ("orc_rmsnorm(D, x + b * D, g, eps, xn);",
+                             "memcpy(xn, x + b * D, sizeof(double) * (size_t)D);"),
+    "merge_logits_order": ("out[b * T * Vs + i * Vs + j]", "out[b * T * Vs + (T - 1 - i) * Vs + j]"),
 }
 
 

@@ -483,3 +483,112 @@ def test_ffn2d_matches_float64_matmul_and_row_subsets(orc):
     y = orc.ffn2d(X, Wg, Wi, Wo)
     assert rel_l2(y, ref.numpy()) < 1e-13
     assert np.array_equal(orc.ffn2d(X, Wg, Wi, Wo, row0=2, nrows=2), y[2:4])
+
+
+# ---------------------------------------------------------------- final stage
+
+def test_logits_identity_classifier_closed_form(orc):
+    """W_cls = I (V = D): the merged logits are the final-normalised row,
+    g * x / sqrt(mean x^2 + eps), whatever the number of shards."""
+    D, eps = 64, 1e-5
+    x = _rng(40).standard_normal((2, D))
+    g = (1 + 0.1 * _rng(41).standard_normal(D)).astype(np.float32)
+    want = g.astype(np.float64) * x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+    for tp in (1, 2, 4):
+        o = orc.logits(np.eye(D, dtype=np.float32), g, x, tp, eps=eps, dtype="f32")
+        assert rel_l2(o["out"], want) < 1e-15
+
+
+@pytest.mark.parametrize("tp", [1, 4])
+def test_logits_shards_match_float64_matmul(orc, tp):
+    """Shard s's logits are rows [s*V/T, (s+1)*V/T) of W_cls (bf16) times the
+    normalised row, checked against numpy's float64 matmul per shard, and
+    the merge puts them back in vocabulary order."""
+    V, D, B = 96, 64, 3
+    W = synth.f32_to_bf16_bits(_rng(42).standard_normal((V, D)).astype(np.float32))
+    g = (1 + 0.1 * _rng(43).standard_normal(D)).astype(np.float32)
+    x = _rng(44).standard_normal((B, D))
+    xn = g.astype(np.float64) * x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-5)
+    full = xn @ synth.bf16_bits_to_f32(W).astype(np.float64).T
+    Vs = V // tp
+    for s in range(tp):
+        z = orc.logits_shard(W, g, x, tp, s)["z"]
+        assert np.allclose(z, full[:, s * Vs:(s + 1) * Vs], rtol=1e-13, atol=1e-13)
+    assert np.allclose(orc.logits(W, g, x, tp)["out"], full, rtol=1e-13, atol=1e-13)
+
+
+def test_merge_logits_places_each_slice():
+    import oracle as orc
+    T, B, Vs = 3, 2, 5
+    d = np.array([[[i * 1e6 + b * 1e3 + j for j in range(Vs)] for b in range(B)] for i in range(T)])
+    out = orc.merge_logits(d)
+    for b in range(B):
+        for c in range(T * Vs):
+            assert out[b, c] == (c // Vs) * 1e6 + b * 1e3 + c % Vs
+
+
+def test_logits_int8_wire_is_the_codec_of_each_slice(orc):
+    V, D, B, tp = 128, 64, 2, 2
+    W = _rng(45).standard_normal((V, D)).astype(np.float32)
+    g = np.ones(D, np.float32)
+    x = _rng(46).standard_normal((B, D))
+    o = orc.logits(W, g, x, tp, quant=synth.Q_PARTIALS, dtype="f32")
+    for s in range(tp):
+        c, sc = orc.q8_quantize(o["z"][s].astype(np.float32))
+        assert np.array_equal(c, o["codes"][s].reshape(-1))
+        assert np.array_equal(sc, o["scales"][s].reshape(-1))
+        deq = orc.q8_dequantize(c, sc).reshape(B, V // tp)
+        assert np.array_equal(o["out"][:, s * (V // tp):(s + 1) * (V // tp)], deq)
+
+
+def test_decode_loop_with_zero_output_projections_is_logits_of_x(orc):
+    """With W_O = W2 = 0 every layer adds nothing to the residual stream, so
+    the decode step's logits are the final stage applied to x itself (the
+    layers still append their K/V)."""
+    D, L = 32, 3
+    layers, kcs, vcs = [], [], []
+    for i in range(L):
+        w = synth.small_llama(dim=D, n_heads=2, n_kv_heads=2, head_dim=16, ffn_hidden=64, tp=2,
+                              past=(2, 2), seed=50 + i)
+        wts = synth.llama_weights(w)
+        wts["wo"] = np.zeros_like(wts["wo"])
+        wts["w2"] = np.zeros_like(wts["w2"])
+        layers.append((w, wts))
+        kcs.append(synth.llama_kv_cache(w, synth.llama_lens(w), "kcache"))
+        vcs.append(synth.llama_kv_cache(w, synth.llama_lens(w), "vcache"))
+    x = synth.llama_x(layers[0][0])
+    W = _rng(47).standard_normal((64, D)).astype(np.float32)
+    g = (1 + 0.1 * _rng(48).standard_normal(D)).astype(np.float32)
+    o = orc.llama_decode(layers, W, g, x, synth.llama_lens(layers[0][0]), kcs, vcs, cls_dtype="f32")
+    assert np.array_equal(o["h"][-1], np.asarray(x, np.float64).reshape(o["h"][-1].shape))
+    assert np.array_equal(o["out"], orc.logits(W, g, x, 2, dtype="f32")["out"])
+
+
+def test_decode_loop_feeds_each_layer_the_previous_output(orc):
+    """Layer i + 1 sees layer i's merged output: the loop equals the layers
+    run by hand in order, and differs from feeding every layer x."""
+    D = 32
+    layers, caches = [], []
+    for i in range(2):
+        w = synth.small_llama(dim=D, n_heads=2, n_kv_heads=2, head_dim=16, ffn_hidden=64, tp=2,
+                              past=(2, 2), seed=60 + i)
+        layers.append((w, synth.llama_weights(w)))
+    lens = synth.llama_lens(layers[0][0])
+
+    def fresh():
+        return ([synth.llama_kv_cache(w, lens, "kcache") for w, _ in layers],
+                [synth.llama_kv_cache(w, lens, "vcache") for w, _ in layers])
+
+    W = _rng(49).standard_normal((64, D)).astype(np.float32)
+    g = np.ones(D, np.float32)
+    x = synth.llama_x(layers[0][0])
+    kc, vc = fresh()
+    o = orc.llama_decode(layers, W, g, x, lens, kc, vc, cls_dtype="f32")
+    kc, vc = fresh()
+    h1 = orc.llama_layer(*layers[0], x, lens, kc[0], vc[0])["out"]
+    h2 = orc.llama_layer(*layers[1], h1, lens, kc[1], vc[1])["out"]
+    assert np.array_equal(o["h"][1], h2)
+    assert np.array_equal(o["out"], orc.logits(W, g, h2, 2, dtype="f32")["out"])
+    kc, vc = fresh()
+    h2x = orc.llama_layer(*layers[1], x, lens, kc[1], vc[1])["out"]
+    assert rel_l2(h2x, h2) > 1e-3
