@@ -396,6 +396,138 @@ def run_ffn2d(args, w):
     return res
 
 
+def logits_config(tp, w, rank):
+    dt = {synth.F32: tp.TP_F32, synth.BF16: tp.TP_BF16}
+    return tp.make_config(kind=tp.TP_LOGITS, dim=w.dim, ffn_hidden=w.vocab, tp_size=w.tp,
+                          tp_rank=rank, max_batch=w.batch, w_dtype=dt[w.w_dtype], quant=w.quant,
+                          quant_block=32, norm_eps=w.norm_eps)
+
+
+def run_logits(args, w):
+    """The final stage of rank 0: final RMSNorm + its V/T logits (+ int8 wire),
+    then the merge of all T slices into full rows (the other ranks' wires
+    computed once beforehand, standing in for what would arrive). R copies of
+    rank 0's classifier slice in rotation, as for the layer step."""
+    import torch
+    import tensor_tp_shard_amd as tp
+    T, B, D, Vs = w.tp, w.batch, w.dim, w.vocab // w.tp
+    t_gen = time.time()
+    d = synth.logits_inputs(w)
+    log(f"generated inputs of {w.name} in {time.time() - t_gen:.1f}s")
+    W = {"w1": dev(d["w_cls"]), "g_att": dev(d["g_final"])}
+
+    def shard(rank):
+        sh = tp.Shard(logits_config(tp, w, rank), caches=False)
+        sh.load(W)
+        return sh
+
+    x = dev(d["x"])
+    others = [shard(r) for r in range(1, T)]
+    other_w = [sh.new_wire() for sh in others]
+    for sh, wr in zip(others, other_w):
+        sh.step(tp.TP_STAGE_LOGITS, x, None, B, wr)
+    torch.cuda.synchronize()
+    del others
+    e = 1.125 if w.quant & synth.Q_WEIGHTS else 2 if w.w_dtype == synth.BF16 else 4
+    cls_bytes = int(Vs * D * e)
+    R = args.copies or max(2, int(np.ceil(3 * 256e6 / cls_bytes)))
+    copies = [shard(0) for _ in range(R)]
+    del W
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    wires = [c.new_wire() for c in copies]
+    outs = [torch.empty((B, w.vocab), dtype=torch.float32, device="cuda") for _ in range(R)]
+
+    def one_pass():
+        for r, c in enumerate(copies):
+            c.step(tp.TP_STAGE_LOGITS, x, None, B, wires[r])
+            c.merge_logits([wires[r]] + other_w, outs[r], B)
+
+    passes = max(1, args.steps // R)
+    steps = passes * R
+    wpasses = max(1, args.warmup // R)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = None
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            one_pass()
+        if args.mode == "graph":
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                one_pass()
+        run = graph.replay if graph is not None else one_pass
+        for _ in range(wpasses):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(passes):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        assert torch.isfinite(outs[0]).all().item(), "non-finite logits"
+        kid = tp.kernel_names().index("gemv_logits")
+        for c in copies:
+            tp.kernel_timing_arm(c.handle, kid)
+        for _ in range(passes):
+            one_pass()
+        torch.cuda.synchronize()
+        tot, n = 0.0, 0
+        for c in copies:
+            t_, n_ = tp.kernel_timing_read(c.handle)
+            tot += t_
+            n += n_
+            tp.kernel_timing_arm(c.handle, -1)
+    ms_step = ms / steps
+    k_ms = tot / max(n, 1)
+    achieved = cls_bytes / (k_ms * 1e-3) / 1e9
+    res = {
+        "metric": "final-stage steps/s of one TP shard (final RMSNorm, vocabulary-split logits, "
+                  "wire, merge of all slices)",
+        "value": round(1e3 / ms_step, 1),
+        "unit": "logits-steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": wpasses * R,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if w.quant & synth.Q_WEIGHTS else "bf16" if w.w_dtype == synth.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "shard": f"rank 0 of TP={T}", "batch": B, "vocab": w.vocab,
+                   "quant": w.quant, "copies": R, "launch": args.mode, "step_bytes": cls_bytes},
+        "achieved_GBps": round(cls_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_frac": round(cls_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"kernel": "gemv_logits", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(
+                         f"traffic_gemv_logits_{w.name}.md",
+                         GEMV_MFMA_SOURCES if w.w_dtype == synth.BF16 and B > 4 else GEMV_SOURCES),
+                     "bytes_per_launch": cls_bytes,
+                     "avg_launch_us": round(k_ms * 1e3, 3), "launches": n},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n, t0 = 0, time.perf_counter()
+        while True:
+            z = oracle.logits_shard(d["w_cls"], d["g_final"], d["x"], T, 0, w.norm_eps, w.w_dtype)["z"]
+            dz, _, _ = oracle.wire(z, w.quant)
+            oracle.merge_logits(np.concatenate([dz[None], np.zeros((T - 1, B, Vs))]))
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {
+            "value": round(n / el, 3), "unit": "logits-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} rank-0 final-stage steps of {w.name} (final norm, logits slice, wire, "
+                      f"merge) by the single-threaded fp64 C oracle in {el:.1f} s"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -424,7 +556,8 @@ def main():
         calib_copy(args.calib_copy_mib)
         return
     w = synth.get(args.workload)
-    res = run_ffn2d(args, w) if w.kind == "ffn2d" else run_llama(args, w)
+    runs = {"ffn2d": run_ffn2d, "logits": run_logits, "llama": run_llama}
+    res = runs[w.kind](args, w)
     print(json.dumps(res), flush=True)
 
 

@@ -14,6 +14,12 @@
  *                    SwiGLU -> row-split W2 -> partial -> [int8]
  *   merge            residual + sum of partials -> layer output
  *
+ * and the final stage of the decode step, split over the vocabulary:
+ *
+ *   logits stage     final RMSNorm -> the shard's rows of the classifier
+ *                    -> [int8 block quantisation of the logits slice]
+ *   merge            the shards' (dequantised) slices placed side by side
+ *
  * Sources: distributed-llama issue "[Feature Suggest] Tensor Parallellism for
  * Accelerating LLM" (buildLlama2Arch: the root/worker task list of one layer,
  * llamaRmsAttNorm .. llamaMergeFfn2, with quantise / sync / dequantise /
@@ -49,8 +55,8 @@ extern "C" {
 typedef struct tp_shard tp_shard; /* opaque host-side handle; owns no device memory */
 
 enum { TP_F32 = 0, TP_BF16 = 1 };                         /* element types */
-enum { TP_LLAMA_BLOCK = 0, TP_FFN_2D = 1 };                /* tp_config.kind */
-enum { TP_STAGE_ATTN = 0, TP_STAGE_FFN = 1 };              /* decode_step / merge_partials stage */
+enum { TP_LLAMA_BLOCK = 0, TP_FFN_2D = 1, TP_LOGITS = 2 };          /* tp_config.kind */
+enum { TP_STAGE_ATTN = 0, TP_STAGE_FFN = 1, TP_STAGE_LOGITS = 2 };   /* decode_step / merge_partials stage */
 /* tp_config.quant bit mask. TP_Q_PARTIALS / TP_Q_INPUTS: the block-32 int8
  * round trip of the exchanged partials / the normalised stage inputs
  * (distributed-llama issue, buildLlama2Arch: the quantise / sync / dequantise
@@ -95,6 +101,17 @@ enum { TP_DERR_LEN = 1 }; /* some lens[b] was < 0 or >= max_ctx; that sequence w
  *   block's F slice), w_dtype TP_BF16, tp_size 1, heads ignored, quant 0;
  *   E a multiple of 576, 2F of 288 and F of 64; any max_batch >= 1. The
  *   decode step is Y = (silu(X W_gate^T) * (X W_in^T)) W_out^T.
+ * kind == TP_LOGITS: the final stage (distributed-llama issue,
+ *   buildLlama2Arch: llamaRmsFinal, llamaRmsFinalNorm, llamaLogits,
+ *   llamaQuantizeLogits, llamaSyncLogits, llamaDequantizeLogits,
+ *   llamaMergeLogits). dim = D, ffn_hidden = V (the vocabulary); the shard
+ *   owns the logits [r*V/T, (r+1)*V/T) (column split of the classifier over
+ *   the vocabulary); w_dtype TP_F32 or TP_BF16; heads, head_dim, max_ctx
+ *   and kv_dtype ignored; quant may hold TP_Q_PARTIALS (int8 wire of the
+ *   logits slice) and TP_Q_WEIGHTS (int8 classifier), not TP_Q_INPUTS (the
+ *   page lists no quantisation of the final norm's output); requires V % T
+ *   == 0, max_batch <= 16, D a multiple of 8 (32 with int8 weights), V/T a
+ *   multiple of 8 (32 with TP_Q_PARTIALS).
  */
 typedef struct {
     int32_t kind;
@@ -119,7 +136,9 @@ typedef struct {
  * w_dtype: wq [Hq*hd][D], wk/wv [Hkv*hd][D], wo [D][Hq*hd], w1/w3 [F][D],
  * w2 [D][F]; g_att/g_ffn fp32 [D] RMSNorm gains.
  * For TP_FFN_2D: w1 = W_gate [F][E], w3 = W_in [F][E], w2 = W_out [E][F]
- * (bf16); the others are ignored and may be NULL. */
+ * (bf16); the others are ignored and may be NULL.
+ * For TP_LOGITS: w1 = W_cls [V][D] (w_dtype), g_att = fp32 [D] final RMSNorm
+ * gain; the others are ignored and may be NULL. */
 typedef struct {
     const void *wq, *wk, *wv, *wo, *w1, *w3, *w2;
     const float *g_att, *g_ffn;
@@ -153,7 +172,7 @@ int32_t init_shard(const tp_config *cfg, tp_shard **out, tp_sizes *sizes);
  * `full` alive until the stream reaches this point.
  * k_cache / v_cache hold [max_batch][Hkv_s][max_ctx][hd] kv_dtype each (the
  * caller fills the cached past positions; the library appends); they are
- * unused (may be NULL) for TP_FFN_2D.
+ * unused (may be NULL) for TP_FFN_2D and TP_LOGITS.
  * Errors: TP_EINVAL, TP_EALIGN, TP_ENODEV, TP_EHIP.
  */
 int32_t load_weights(tp_shard *s, const tp_layer_weights *full, void *packed, void *k_cache,
@@ -171,6 +190,11 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *full, void *packed, vo
  *    lens unused (may be NULL).
  *  For TP_FFN_2D only TP_STAGE_FFN is valid: x = bf16 [batch][E], and
  *    wire_out receives Y fp32 [batch][E] (batch <= max_batch, any size).
+ *  For TP_LOGITS only TP_STAGE_LOGITS is valid: x = fp32 [batch][D] (the
+ *    last layer's merged output); wire_out receives the shard's logits
+ *    [batch][V/T] in the wire format below (row length V/T instead of D);
+ *    the taps xn (final-normalised rows) and p_pre (fp32 logits slice) are
+ *    written, the others ignored.
  *  wire_out: the partial this shard exchanges. With TP_Q_PARTIALS: int8
  *    codes [batch][D] at offset 0, then fp32 scales [batch][D/32] at the
  *    offset tp_wire_scales_offset(cfg, batch) (one scale per 32 consecutive
@@ -215,16 +239,33 @@ int32_t decode_merge_step(tp_shard *s, int32_t stage, const void *x, const int32
                           int32_t batch, void *wire_out, const void *const *wires,
                           int32_t n_wires, float *x_out, const tp_taps *taps, void *hip_stream);
 
+/*
+ * merge_logits: the full logits rows from every shard's logits wire
+ * (distributed-llama issue, buildLlama2Arch: llamaSyncLogits,
+ * llamaDequantizeLogits, llamaMergeLogits): out fp32 [batch][V], columns
+ * [i*V/T, (i+1)*V/T) = dequant(wires[i]) ((float)code * scale per element,
+ * or the fp32 values as they are). `wires` is a HOST array of n_wires = T
+ * device pointers in shard order, each a wire decode_step wrote for `batch`
+ * rows with a TP_LOGITS handle of the same configuration. out must not
+ * overlap a wire. TP_LOGITS only.
+ * Errors: TP_EINVAL (wrong kind, n_wires != T, null pointers, out equal to a
+ * wire), TP_EALIGN, TP_EHIP.
+ */
+int32_t merge_logits(const tp_shard *s, const void *const *wires, int32_t n_wires, float *out,
+                     int32_t batch, void *hip_stream);
+
 /* Byte offset of the fp32 scales inside a quantised wire of `batch` rows
- * (16-byte aligned, right after the int8 codes). */
+ * (16-byte aligned, right after the int8 codes; rows of D elements, of V/T
+ * for TP_LOGITS). */
 uint64_t tp_wire_scales_offset(const tp_config *cfg, int32_t batch);
 
 /* TP_Q_WEIGHTS: where projection `proj` (0 = Wqkv, 1 = Wo, 2 = W13 with the
  * W1_f / W3_f rows interleaved, 3 = W2) sits inside the packed weights: its
  * int8 codes [rows][cols] at byte *codes_off, its fp32 scales
  * [rows][cols / 32] at byte *scales_off, both row-major (scale j of a row
- * covers codes 32 j .. 32 j + 31). TP_EINVAL for a handle without int8
- * weights, an unknown proj or a null output. */
+ * covers codes 32 j .. 32 j + 31). For TP_LOGITS, proj 0 is the shard's
+ * classifier rows [V/T][D]. TP_EINVAL for a handle without int8 weights, an
+ * unknown proj or a null output. */
 int32_t tp_packed_int8_view(const tp_shard *s, int32_t proj, uint64_t *codes_off,
                             uint64_t *scales_off, int32_t *rows, int32_t *cols);
 

@@ -4,7 +4,7 @@ Argument marshalling only: every step of the shard's decode step runs in the
 library's HIP kernels. PyTorch supplies device memory (``torch.empty``) and
 the stream (``torch.cuda.current_stream()``). The names mirror the C ABI:
 ``init_shard``, ``load_weights``, ``decode_step``, ``merge_partials``,
-``decode_merge_step``, ``destroy_shard``; ``Shard`` bundles a handle with torch-allocated buffers.
+``decode_merge_step``, ``merge_logits``, ``destroy_shard``; ``Shard`` bundles a handle with torch-allocated buffers.
 
 There is no fallback: if ``libtpshard.so`` is missing or fails to load,
 every call raises.
@@ -19,15 +19,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtpshard.so")
 
 TP_F32, TP_BF16 = 0, 1
-TP_LLAMA_BLOCK, TP_FFN_2D = 0, 1
-TP_STAGE_ATTN, TP_STAGE_FFN = 0, 1
+TP_LLAMA_BLOCK, TP_FFN_2D, TP_LOGITS = 0, 1, 2
+TP_STAGE_ATTN, TP_STAGE_FFN, TP_STAGE_LOGITS = 0, 1, 2
 TP_Q_NONE, TP_Q_PARTIALS, TP_Q_INPUTS, TP_Q_WEIGHTS = 0, 1, 2, 4
 TP_OK, TP_EINVAL, TP_EALIGN, TP_ESTATE, TP_ENODEV, TP_EHIP, TP_ENOTIMPL = 0, -1, -2, -3, -4, -5, -6
 TP_DERR_LEN = 1
 
 # every symbol include/tpshard.h declares
 EXPORTS = ("init_shard", "load_weights", "decode_step", "merge_partials", "decode_merge_step",
-           "tp_wire_scales_offset",
+           "merge_logits", "tp_wire_scales_offset",
            "tp_packed_int8_view",
            "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
            "tp_kernel_name", "destroy_shard", "tp_status_str", "tp_last_error")
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.decode_step.argtypes = [P, I32, P, P, I32, P, P, P]
         L.merge_partials.argtypes = [P, I32, P, I32, P, P, I32, P]
         L.decode_merge_step.argtypes = [P, I32, P, P, I32, P, P, I32, P, P, P]
+        L.merge_logits.argtypes = [P, P, I32, P, I32, P]
         L.tp_wire_scales_offset.argtypes = [P, I32]
         L.tp_wire_scales_offset.restype = U64
         L.tp_read_error_word.argtypes = [P, P, I32, P]
@@ -90,7 +91,7 @@ def lib() -> ctypes.CDLL:
         L.tp_status_str.restype = ctypes.c_char_p
         L.tp_last_error.restype = ctypes.c_char_p
         for f in ("init_shard", "load_weights", "decode_step", "merge_partials",
-                  "decode_merge_step", "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
+                  "decode_merge_step", "merge_logits", "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
                   "tp_packed_int8_view"):
             getattr(L, f).restype = I32
         _lib = L
@@ -170,6 +171,12 @@ def decode_merge_step(handle, stage: int, x, lens, batch: int, wire_out, wires: 
                                    len(wires), _ptr(x_out),
                                    ctypes.byref(t) if t is not None else None, _stream(stream)),
            "decode_merge_step")
+
+
+def merge_logits(handle, wires: Sequence, out, batch: int, stream=None):
+    arr = (ctypes.c_void_p * len(wires))(*[_ptr(w) for w in wires])
+    _check(lib().merge_logits(handle, arr, len(wires), _ptr(out), batch, _stream(stream)),
+           "merge_logits")
 
 
 def wire_scales_offset(cfg: TpConfig, batch: int) -> int:
@@ -256,6 +263,9 @@ class Shard:
 
     def merge(self, stage, wires, residual, out, batch, stream=None):
         merge_partials(self.handle, stage, wires, residual, out, batch, stream)
+
+    def merge_logits(self, wires, out, batch, stream=None):
+        merge_logits(self.handle, wires, out, batch, stream)
 
     def step_merge(self, stage, x, lens, batch, wire_out, wires, x_out, taps=None, stream=None):
         decode_merge_step(self.handle, stage, x, lens, batch, wire_out, wires, x_out, taps, stream)

@@ -62,21 +62,26 @@ enum KernelId {
     KID_FFN2D_UP,
     KID_FFN2D_DOWN,
     KID_ROPE_TABLE,
+    KID_GEMV_LOGITS,
+    KID_MERGE_LOGITS,
     KID_COUNT
 };
 
 const char *const kKernelNames[KID_COUNT] = {
     "rmsnorm",    "gemv_qkv", "attention", "gemv_wo",  "q8_wire",    "gemv_w13_swiglu",
-    "gemv_w2",    "merge",    "ffn2d_up",  "ffn2d_down", "rope_table"};
+    "gemv_w2",    "merge",    "ffn2d_up",  "ffn2d_down", "rope_table", "gemv_logits",
+    "merge_logits"};
 
 } // namespace
 
 struct tp_shard {
     tp_config cfg;
     // derived shape
+    // (TP_LOGITS: F = vocabulary, Fs = the shard's V/T logits)
     int T, r, D, hd, Hq, Hkv, G, Hq_s, Hkv_s, F, Fs, n_qkv, esz, kv_esz;
     bool w8; // TP_Q_WEIGHTS: packed projections are int8 codes + fp32 scales per 32 k
     // packed layout (byte offsets)
+    // (TP_LOGITS: the classifier rows at o_w13 / o_sw13, the final gain at o_gatt)
     uint64_t o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn, o_rope, packed_bytes;
     uint64_t o_sqkv, o_swo, o_sw13, o_sw2; // w8: scale arrays [N][K/32]
     // workspace layout (byte offsets)
@@ -96,9 +101,65 @@ struct tp_shard {
 
 namespace {
 
+// The final stage: the shard's V/T classifier rows (column split over the
+// vocabulary) and the final gain; workspace for the normalised rows, their
+// MFMA fragments, split-K partials and the fp32 logits before quantisation.
+int32_t plan_logits(const tp_config &c, tp_shard &s)
+{
+    const int T = c.tp_size;
+    if (T < 1 || c.tp_rank < 0 || c.tp_rank >= T)
+        return fail(TP_EINVAL, "tp_rank %d outside [0, tp_size=%d)", c.tp_rank, T);
+    if (c.ffn_hidden % T)
+        return fail(TP_EINVAL, "tp_size must divide the vocabulary (ffn_hidden)");
+    if (c.max_batch > 16)
+        return fail(TP_EINVAL, "decode batch is at most 16");
+    if (c.quant & TP_Q_INPUTS)
+        return fail(TP_EINVAL, "TP_LOGITS has no int8 round trip of the normalised input");
+    if (!(c.norm_eps >= 0.f))
+        return fail(TP_EINVAL, "norm_eps must be >= 0");
+    s.T = T;
+    s.r = c.tp_rank;
+    s.Fs = s.F / T;
+    s.esz = c.w_dtype == TP_BF16 ? 2 : 4;
+    s.w8 = (c.quant & TP_Q_WEIGHTS) != 0;
+    const bool qpart = c.quant & TP_Q_PARTIALS;
+    const int vec = 16 / s.esz;
+    if (s.D % 8 || s.Fs % 8 || s.Fs % vec)
+        return fail(TP_EINVAL, "dim and vocab/tp_size must be multiples of 8");
+    if ((s.w8 && s.D % kQBlock) || (qpart && s.Fs % kQBlock))
+        return fail(TP_EINVAL, "int8 weights need dim, an int8 wire vocab/tp_size, multiples of 32");
+    const uint64_t D = s.D, B = c.max_batch, Vs = s.Fs, e = s.w8 ? 1 : s.esz;
+    uint64_t o = 0;
+    s.o_wqkv = s.o_wo = s.o_w2 = s.o_gffn = s.o_rope = 0;
+    s.o_sqkv = s.o_swo = s.o_sw13 = s.o_sw2 = 0;
+    s.o_w13 = o; o = align_up(o + Vs * D * e, 256);
+    if (s.w8) {
+        s.o_sw13 = o; o = align_up(o + Vs * (D / kQBlock) * 4, 256);
+    }
+    s.o_gatt = o; o = align_up(o + D * 4, 256);
+    s.packed_bytes = o;
+    s.mfma_ok = (c.w_dtype == TP_BF16 || s.w8) && c.max_batch > 4 && gemv_mfma_ok(16, s.Fs, s.D, 1);
+    o = 0;
+    s.w_err = o;  o = 256;
+    s.w_xfx = s.w_xfatt = s.w_xfa = s.w_skp = 0;
+    if (s.mfma_ok) {
+        s.w_xfx = o; o = align_up(o + xf_elems(s.D) * 2, 256);
+        const size_t skp = gemv_sk_part_floats(s.Fs, s.D, c.max_batch);
+        s.w_skp = skp ? o : 0;
+        o = align_up(o + skp * 4, 256);
+    }
+    s.w_xn = o; o = align_up(o + B * D * 4, 256);
+    s.w_p = o;  o = align_up(o + B * Vs * 4, 256);
+    s.w_qkv = s.w_part = s.w_att = s.w_a = 0;
+    s.ws_bytes = o;
+    s.kv_bytes = 0;
+    s.wire_bytes = qpart ? align_up(B * Vs, 16) + B * (Vs / kQBlock) * 4 : B * Vs * 4;
+    return TP_OK;
+}
+
 int32_t plan(const tp_config &c, tp_shard &s)
 {
-    if (c.kind != TP_LLAMA_BLOCK && c.kind != TP_FFN_2D)
+    if (c.kind != TP_LLAMA_BLOCK && c.kind != TP_FFN_2D && c.kind != TP_LOGITS)
         return fail(TP_EINVAL, "unknown kind %d", c.kind);
     if (c.w_dtype != TP_F32 && c.w_dtype != TP_BF16)
         return fail(TP_EINVAL, "unknown w_dtype %d", c.w_dtype);
@@ -141,6 +202,8 @@ int32_t plan(const tp_config &c, tp_shard &s)
         s.wire_bytes = (uint64_t)c.max_batch * s.D * 4;
         return TP_OK;
     }
+    if (c.kind == TP_LOGITS)
+        return plan_logits(c, s);
     if (c.kv_dtype != TP_F32 && c.kv_dtype != TP_BF16)
         return fail(TP_EINVAL, "unknown kv_dtype %d", c.kv_dtype);
     const int T = c.tp_size;
@@ -324,7 +387,47 @@ uint64_t tp_wire_scales_offset(const tp_config *cfg, int32_t batch)
 {
     if (!cfg || batch < 0)
         return 0;
-    return align_up((uint64_t)batch * cfg->dim, 16);
+    const uint64_t row = cfg->kind == TP_LOGITS ? (cfg->tp_size > 0 ? cfg->ffn_hidden / cfg->tp_size : 0)
+                                                : (uint64_t)cfg->dim;
+    return align_up((uint64_t)batch * row, 16);
+}
+
+// TP_LOGITS: the classifier rows [r*V/T, (r+1)*V/T) are one contiguous block
+// of W_cls (copied, or cut into int8 blocks of 32 along k) and the final gain.
+static int32_t load_logits(tp_shard *s, const tp_layer_weights *w, void *packed, void *workspace,
+                           hipStream_t st)
+{
+    if (!w->w1 || !w->g_att)
+        return fail(TP_EINVAL, "load_weights: null classifier or final gain");
+    const void *ptrs[] = {packed, workspace, w->w1, w->g_att};
+    for (const void *p : ptrs)
+        if (!aligned16(p))
+            return fail(TP_EALIGN, "load_weights: device buffer not 16-byte aligned");
+    const int32_t dv = check_device();
+    if (dv != TP_OK)
+        return dv;
+    char *P = (char *)packed;
+    const size_t D = s->D, Vs = s->Fs, e = s->esz;
+    const char *src = (const char *)w->w1 + (size_t)s->r * Vs * D * e;
+    hipError_t err;
+    if (s->w8) {
+        const QuantRowsArgs qa{src, s->cfg.w_dtype == TP_BF16, D, (int)Vs, (int)D, (int8_t *)(P + s->o_w13),
+                               D, (float *)(P + s->o_sw13), D / kQBlock};
+        err = launch_quant_rows(qa, st);
+    } else {
+        err = hipMemcpyAsync(P + s->o_w13, src, Vs * D * e, hipMemcpyDeviceToDevice, st);
+    }
+    if (!err)
+        err = hipMemcpyAsync(P + s->o_gatt, w->g_att, D * 4, hipMemcpyDeviceToDevice, st);
+    if (!err)
+        err = launch_clear_u32((unsigned *)((char *)workspace + s->w_err), 1, st);
+    if (err)
+        return hip_fail(err, "load_weights: classifier packing");
+    s->packed = P;
+    s->ws = (char *)workspace;
+    s->kc = s->vc = nullptr;
+    s->loaded = true;
+    return TP_OK;
 }
 
 int32_t load_weights(tp_shard *s, const tp_layer_weights *w, void *packed, void *k_cache,
@@ -333,6 +436,8 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *w, void *packed, void 
     if (!s || !w || !packed || !workspace)
         return fail(TP_EINVAL, "load_weights: null argument");
     const bool llama = s->cfg.kind == TP_LLAMA_BLOCK;
+    if (s->cfg.kind == TP_LOGITS)
+        return load_logits(s, w, packed, workspace, (hipStream_t)hip_stream);
     if (!w->w1 || !w->w3 || !w->w2 ||
         (llama && (!w->wq || !w->wk || !w->wv || !w->wo || !w->g_att || !w->g_ffn || !k_cache ||
                    !v_cache)))
@@ -464,6 +569,62 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *w, void *packed, void 
     return TP_OK;
 }
 
+// The final stage of shard r (distributed-llama issue, buildLlama2Arch:
+// llamaRmsFinal + llamaRmsFinalNorm, llamaLogits, llamaQuantizeLogits): the
+// final RMSNorm of x and the shard's V/T classifier rows times it, with the
+// projection kernels and norm placement of the block's up-projections (norm
+// fused into the GEMV prologue below batch 5, folded into a split-K MFMA GEMV
+// where that applies, else a kernel of its own), then the int8 wire.
+static int32_t logits_step(tp_shard *s, const float *x, int B, void *wire_out, const tp_taps &tp,
+                           hipStream_t st)
+{
+    const int wt = s->w8 ? WT_I8 : s->cfg.w_dtype == TP_BF16 ? WT_BF16 : WT_F32;
+    const bool qpart = s->cfg.quant & TP_Q_PARTIALS;
+    const float *gain = (const float *)(s->packed + s->o_gatt);
+    float *p = qpart ? (float *)(s->ws + s->w_p) : (float *)wire_out;
+    const bool mfma = s->mfma_ok && B > 4;
+    const bool sk_norm = mfma && s->w_skp && gemv_sk_used(s->Fs, s->D);
+    const bool fuse_norm = !mfma && gemv_fused_ok(B, s->D);
+    uint16_t *xfx = mfma ? (uint16_t *)(s->ws + s->w_xfx) : nullptr;
+    GemvArgs g{};
+    g.W = s->packed + s->o_w13;
+    g.ws = s->w8 ? (const float *)(s->packed + s->o_sw13) : nullptr;
+    g.x = x;
+    g.ldx = s->D;
+    g.K = s->D;
+    g.B = B;
+    g.y = p;
+    g.tap = tp.p_pre;
+    g.N = s->Fs;
+    g.ldy = s->Fs;
+    int32_t rc;
+    if (fuse_norm) {
+        g.g = gain;
+        g.eps = s->cfg.norm_eps;
+        g.xn_tap = tp.xn;
+    } else if (!sk_norm || tp.xn) {
+        float *xn = (float *)(s->ws + s->w_xn);
+        NormArgs na{x, gain, xn, tp.xn, xfx, B, s->D, s->cfg.norm_eps, 0};
+        rc = timed(s, KID_RMSNORM, st, "rmsnorm", [&] { return launch_rmsnorm(na, st); });
+        if (rc)
+            return rc;
+        g.x = xn;
+    }
+    rc = timed(s, KID_GEMV_LOGITS, st, "gemv logits", [&] {
+        if (!mfma)
+            return launch_gemv(g, wt, EPI_STORE, st);
+        MfmaGemvArgs m{(const uint16_t *)g.W, xfx, g.y, g.tap, nullptr, g.N, g.K, g.B, g.ldy, 1, g.mo,
+                       s->w_skp ? (float *)(s->ws + s->w_skp) : nullptr, 0, 0,
+                       sk_norm ? x : nullptr, sk_norm ? gain : nullptr, s->cfg.norm_eps, g.ws};
+        return launch_gemv_mfma(m, EPI_STORE, st);
+    });
+    if (rc || !qpart)
+        return rc;
+    WireArgs wa{p, (int8_t *)wire_out,
+                (float *)((char *)wire_out + tp_wire_scales_offset(&s->cfg, B)), B, s->Fs, {}};
+    return timed(s, KID_WIRE, st, "q8 wire", [&] { return launch_wire(wa, st); });
+}
+
 // One stage of the shard step on input x. With mo (llama blocks only) the
 // stage's partials are also merged, mo->x_out = x + sum of mo's wires, by the
 // kernel that writes this shard's own partial (wire mo->own = wire_out).
@@ -475,8 +636,12 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         return fail(TP_EINVAL, "decode_step: null handle");
     if (!s->loaded)
         return fail(TP_ESTATE, "decode_step before load_weights");
-    if (stage != TP_STAGE_ATTN && stage != TP_STAGE_FFN)
+    if (stage != TP_STAGE_ATTN && stage != TP_STAGE_FFN && stage != TP_STAGE_LOGITS)
         return fail(TP_EINVAL, "unknown stage %d", stage);
+    if ((stage == TP_STAGE_LOGITS) != (s->cfg.kind == TP_LOGITS))
+        return fail(TP_EINVAL, "TP_STAGE_LOGITS goes with (and only with) a TP_LOGITS handle");
+    if (mo && s->cfg.kind != TP_LLAMA_BLOCK)
+        return fail(TP_EINVAL, "decode_merge_step applies to TP_LLAMA_BLOCK shards");
     if (batch < 1 || batch > s->cfg.max_batch)
         return fail(TP_EINVAL, "batch %d outside [1, max_batch=%d]", batch, s->cfg.max_batch);
     if (!x || !wire_out)
@@ -514,6 +679,9 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
             return rc;
         return timed(s, KID_FFN2D_DOWN, st, "ffn2d down", [&] { return launch_ffn2d(fa, st, 1); });
     }
+
+    if (s->cfg.kind == TP_LOGITS)
+        return logits_step(s, (const float *)x, batch, wire_out, tp, st);
 
     const bool wbf = s->cfg.w_dtype == TP_BF16;
     const int wt = s->w8 ? WT_I8 : wbf ? WT_BF16 : WT_F32;
@@ -738,6 +906,44 @@ int32_t merge_partials(const tp_shard *s, int32_t stage, const void *const *wire
                  [&] { return launch_merge(m, st); });
 }
 
+int32_t merge_logits(const tp_shard *s, const void *const *wires, int32_t n_wires, float *out,
+                     int32_t batch, void *hip_stream)
+{
+    if (!s)
+        return fail(TP_EINVAL, "merge_logits: null handle");
+    if (s->cfg.kind != TP_LOGITS)
+        return fail(TP_EINVAL, "merge_logits applies to TP_LOGITS shards");
+    if (!wires || n_wires != s->T)
+        return fail(TP_EINVAL, "merge_logits: n_wires %d, the handle has %d shards", n_wires, s->T);
+    if (batch < 1 || batch > s->cfg.max_batch)
+        return fail(TP_EINVAL, "batch %d outside [1, max_batch=%d]", batch, s->cfg.max_batch);
+    if (!out)
+        return fail(TP_EINVAL, "merge_logits: null out");
+    if (!aligned16(out))
+        return fail(TP_EALIGN, "merge_logits: out not 16-byte aligned");
+    LogitsMergeArgs a{};
+    for (int i = 0; i < n_wires; i++) {
+        if (!wires[i])
+            return fail(TP_EINVAL, "merge_logits: wire %d is null", i);
+        if (!aligned16(wires[i]))
+            return fail(TP_EALIGN, "merge_logits: wire %d not 16-byte aligned", i);
+        if (wires[i] == (const void *)out)
+            return fail(TP_EINVAL, "merge_logits: out aliases wire %d", i);
+        a.m.wires[i] = wires[i];
+    }
+    a.m.n_wires = n_wires;
+    a.m.quant = (s->cfg.quant & TP_Q_PARTIALS) ? 1 : 0;
+    a.m.own = -1;
+    a.m.scales_off = tp_wire_scales_offset(&s->cfg, batch);
+    a.out = out;
+    a.B = batch;
+    a.Vs = s->Fs;
+    a.V = s->F;
+    hipStream_t st = (hipStream_t)hip_stream;
+    return timed(const_cast<tp_shard *>(s), KID_MERGE_LOGITS, st, "merge logits",
+                 [&] { return launch_merge_logits(a, n_wires, st); });
+}
+
 int32_t tp_packed_int8_view(const tp_shard *s, int32_t proj, uint64_t *codes_off,
                             uint64_t *scales_off, int32_t *rows, int32_t *cols)
 {
@@ -745,6 +951,15 @@ int32_t tp_packed_int8_view(const tp_shard *s, int32_t proj, uint64_t *codes_off
         return fail(TP_EINVAL, "tp_packed_int8_view: null argument");
     if (!s->w8)
         return fail(TP_EINVAL, "tp_packed_int8_view: the shard has no int8 weights");
+    if (s->cfg.kind == TP_LOGITS) {
+        if (proj != 0)
+            return fail(TP_EINVAL, "tp_packed_int8_view: a TP_LOGITS shard has only projection 0");
+        *codes_off = s->o_w13;
+        *scales_off = s->o_sw13;
+        *rows = s->Fs;
+        *cols = s->D;
+        return TP_OK;
+    }
     switch (proj) {
     case 0: *codes_off = s->o_wqkv; *scales_off = s->o_sqkv; *rows = s->n_qkv; *cols = s->D; break;
     case 1: *codes_off = s->o_wo; *scales_off = s->o_swo; *rows = s->D; *cols = s->Hq_s * s->hd; break;

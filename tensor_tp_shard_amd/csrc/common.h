@@ -337,6 +337,14 @@ struct MergeArgs {
     int B, D;
 };
 
+// Logits merge: wire s's rows [B][Vs] (dequantised) into columns
+// [s*Vs, (s+1)*Vs) of out [B][V]; m.wires / quant / scales_off as in a merge.
+struct LogitsMergeArgs {
+    MergeIn m;
+    float *out;          // [B][V]
+    int B, Vs, V;
+};
+
 // int8 weight packing: rows x cols (cols % 32 == 0) of src -> codes / scales
 struct QuantRowsArgs {
     const void *src;
@@ -380,6 +388,7 @@ size_t gemv_lds_bytes(int B, int K);
 bool gemv_fused_ok(int B, int K);
 hipError_t launch_wire(const WireArgs &a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
+hipError_t launch_merge_logits(const LogitsMergeArgs &a, int T, hipStream_t st);
 hipError_t launch_rope_table(const RopeArgs &a, hipStream_t st);
 hipError_t launch_quant_rows(const QuantRowsArgs &a, hipStream_t st);
 hipError_t launch_clear_u32(unsigned *p, int n, hipStream_t st);

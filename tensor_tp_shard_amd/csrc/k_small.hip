@@ -235,6 +235,32 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a)
     *(float4 *)(m.x_out + i) = acc;
 }
 
+// Logits merge: 4 elements of shard blockIdx.y's slice per thread, read from
+// its wire (int8 codes + block scale, or fp32) and stored at their place in
+// the full row. The shard index is uniform over the workgroup, so the wire's
+// address comes from the kernel arguments with a scalar load.
+__global__ __launch_bounds__(256) void k_merge_logits(LogitsMergeArgs a)
+{
+    const int s = blockIdx.y;
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= (size_t)a.B * a.Vs)
+        return;
+    const size_t b = i / a.Vs, j = i % a.Vs;
+    const u32x4 r = wire_load(a.m, s, i);
+    float4 v;
+    if (a.m.quant) {
+        const float sc = __uint_as_float(r.y);
+        v.x = q8_dequant((int)(int8_t)(r.x & 0xffu), sc);
+        v.y = q8_dequant((int)(int8_t)((r.x >> 8) & 0xffu), sc);
+        v.z = q8_dequant((int)(int8_t)((r.x >> 16) & 0xffu), sc);
+        v.w = q8_dequant((int)(int8_t)(r.x >> 24), sc);
+    } else {
+        v = make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z),
+                        __uint_as_float(r.w));
+    }
+    *(float4 *)(a.out + b * a.V + (size_t)s * a.Vs + j) = v;
+}
+
 // cos / sin of p * theta^(-2i/hd) in fp64, stored fp32: [max_ctx][hd/2].
 __global__ __launch_bounds__(256) void k_rope_table(RopeArgs a)
 {
@@ -273,6 +299,17 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t st)
     if (n4 == 0)
         return hipSuccess;
     hipLaunchKernelGGL(k_merge, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// Host-checked: Vs % 4 == 0, V = T * Vs, out and the wires 16-byte aligned.
+hipError_t launch_merge_logits(const LogitsMergeArgs &a, int T, hipStream_t st)
+{
+    const size_t n4 = (size_t)a.B * a.Vs / 4;
+    if (n4 == 0 || T < 1)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_merge_logits, dim3((unsigned)((n4 + 255) / 256), (unsigned)T), dim3(256), 0,
+                       st, a);
     return hipGetLastError();
 }
 

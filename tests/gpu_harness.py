@@ -138,3 +138,55 @@ def fp32_wire(w, wire: np.ndarray, B: int) -> np.ndarray:
 
 def with_batch(w, B: int):
     return dataclasses.replace(w, batch=B)
+
+
+def logits_config(w, rank: int = 0, max_batch: Optional[int] = None) -> tp.TpConfig:
+    dt = {synth.F32: tp.TP_F32, synth.BF16: tp.TP_BF16}
+    return tp.make_config(kind=tp.TP_LOGITS, dim=w.dim, ffn_hidden=w.vocab, tp_size=w.tp,
+                          tp_rank=rank, max_batch=max_batch or w.batch, w_dtype=dt[w.w_dtype],
+                          quant=w.quant, quant_block=32, norm_eps=w.norm_eps)
+
+
+class Logits:
+    """All T shards of the final stage (final norm + vocabulary-split logits)."""
+
+    def __init__(self, w, d: Dict[str, np.ndarray], max_batch: Optional[int] = None):
+        self.w = w
+        self.dw = {"w1": dev_tensor(d["w_cls"]), "g_att": dev_tensor(d["g_final"])}
+        self.shards = [tp.Shard(logits_config(w, r, max_batch), caches=False) for r in range(w.tp)]
+        for sh in self.shards:
+            sh.load(self.dw)
+        torch().cuda.synchronize()
+
+    def run(self, x_np: np.ndarray, with_taps: bool = True):
+        """Every shard's logits stage, then the merge: wires, taps and the
+        full logits rows as numpy arrays."""
+        t = torch()
+        w = self.w
+        B, Vs = x_np.shape[0], w.vocab // w.tp
+        x = dev_tensor(np.ascontiguousarray(x_np, dtype=np.float32))
+        wires, taps = [], []
+        for sh in self.shards:
+            wires.append(sh.new_wire())
+            tap = None
+            if with_taps:
+                tap = {"xn": t.full((B, w.dim), float("nan"), device="cuda"),
+                       "p_pre": t.full((B, Vs), float("nan"), device="cuda")}
+            taps.append(tap)
+            sh.step(tp.TP_STAGE_LOGITS, x, None, B, wires[-1], tap)
+        out = t.full((B, w.vocab), float("nan"), device="cuda")
+        self.shards[0].merge_logits(wires, out, B)
+        t.cuda.synchronize()
+        res = {"out": to_np(out), "wires": [to_np(v) for v in wires]}
+        if with_taps:
+            res["taps"] = [{k: to_np(v) for k, v in tap.items()} for tap in taps]
+        return res
+
+
+def split_logits_wire(w, wire: np.ndarray, B: int):
+    """(codes int8 [B][V/T], scales fp32 [B][V/T/32]) of a quantised logits wire."""
+    Vs = w.vocab // w.tp
+    off = tp.wire_scales_offset(logits_config(w), B)
+    codes = wire[:B * Vs].view(np.int8).reshape(B, Vs)
+    scales = wire[off:off + B * (Vs // 32) * 4].view(np.float32).reshape(B, Vs // 32)
+    return codes, scales

@@ -167,3 +167,75 @@ def test_null_arguments_and_status_strings():
     names = tp.kernel_names()
     assert "gemv_w13_swiglu" in names and len(names) == len(set(names))
     L.destroy_shard(None)
+
+
+def cfg_logits(**kw):
+    base = dict(kind=tp.TP_LOGITS, dim=4096, ffn_hidden=32000, tp_size=4, tp_rank=1, max_batch=16,
+                w_dtype=tp.TP_BF16, quant=0, quant_block=32)
+    base.update(kw)
+    return tp.make_config(**base)
+
+
+def test_logits_shard_sizes_and_wire_layout():
+    h, s = tp.init_shard(cfg_logits())
+    assert s.kv_cache_each == 0
+    assert s.packed_weights >= 8000 * 4096 * 2 + 4096 * 4
+    assert s.wire == 16 * 8000 * 4
+    tp.destroy_shard(h)
+    c = cfg_logits(quant=tp.TP_Q_PARTIALS)
+    h, s = tp.init_shard(c)
+    assert tp.wire_scales_offset(c, 3) == 3 * 8000  # rows of V/T codes, 16-byte aligned
+    assert tp.wire_scales_offset(c, 1) == 8000
+    assert s.wire == 16 * 8000 + 16 * 250 * 4
+    tp.destroy_shard(h)
+    h, s = tp.init_shard(cfg_logits(quant=tp.TP_Q_WEIGHTS))
+    co, so, r, cols = tp.packed_int8_view(h, 0)
+    assert (r, cols) == (8000, 4096) and co + r * cols <= so and so + r * cols // 8 <= s.packed_weights
+    with pytest.raises(tp.TpError):
+        tp.packed_int8_view(h, 1)
+    tp.destroy_shard(h)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(tp_size=3),                        # T does not divide the vocabulary
+    dict(tp_rank=4),
+    dict(max_batch=17),
+    dict(quant=tp.TP_Q_INPUTS),             # no round trip of the final norm's output
+    dict(dim=4100),                         # not a multiple of 8
+    dict(ffn_hidden=4 * 8004),              # V/T not a multiple of 8
+    dict(ffn_hidden=4 * 8008, quant=tp.TP_Q_PARTIALS),   # V/T not a multiple of 32
+    dict(dim=4104, quant=tp.TP_Q_WEIGHTS),  # int8 weights need dim % 32
+])
+def test_logits_init_rejects_bad_config(kw):
+    with pytest.raises(tp.TpError) as e:
+        tp.init_shard(cfg_logits(**kw))
+    assert e.value.status == tp.TP_EINVAL
+
+
+def test_logits_stage_and_merge_host_errors():
+    h, s = tp.init_shard(cfg_logits(max_batch=2))
+    fake = 0x10000  # never dereferenced: every call below fails on the host
+    with pytest.raises(tp.TpError) as e:
+        tp.decode_step(h, tp.TP_STAGE_LOGITS, fake, None, 1, fake, stream=0)
+    assert e.value.status == tp.TP_ESTATE
+    with pytest.raises(tp.TpError) as e:
+        tp.load_weights(h, {"w1": fake, "g_att": None}, fake, None, None, fake, stream=0)
+    assert e.value.status == tp.TP_EINVAL
+    with pytest.raises(tp.TpError) as e:
+        tp.load_weights(h, {"w1": fake + 8, "g_att": fake}, fake, None, None, fake, stream=0)
+    assert e.value.status == tp.TP_EALIGN
+    for wires, out, B, st in (([fake] * 3, fake + 4096, 1, tp.TP_EINVAL),   # n_wires != T
+                              ([fake] * 4, fake + 4096, 3, tp.TP_EINVAL),   # batch > max_batch
+                              ([fake] * 4, fake + 4, 1, tp.TP_EALIGN),
+                              ([fake, fake, fake, fake + 4096], fake + 4096, 1, tp.TP_EINVAL),
+                              ([fake, None, fake, fake], fake + 4096, 1, tp.TP_EINVAL)):
+        with pytest.raises(tp.TpError) as e:
+            tp.merge_logits(h, wires, out, B, stream=0)
+        assert e.value.status == st
+    # the logits stage belongs to TP_LOGITS handles only, and they have no other
+    hb, _ = tp.init_shard(cfg7b())
+    with pytest.raises(tp.TpError) as e:
+        tp.merge_logits(hb, [fake] * 4, fake + 4096, 1, stream=0)
+    assert e.value.status == tp.TP_EINVAL
+    tp.destroy_shard(hb)
+    tp.destroy_shard(h)
