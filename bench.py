@@ -125,7 +125,10 @@ def llama_bytes(w, lens):
     return weights, kv, w13
 
 
-def run_llama(args, w):
+def llama_rank0(w):
+    """Rank 0's layer of workload w and the other ranks' partials for its
+    input (what rank 0 would receive): -> (inputs, shard builder, x, lens,
+    attention wires, FFN wires of ranks 1..T-1)."""
     import torch
     import tensor_tp_shard_amd as tp
     T, B = w.tp, w.batch
@@ -155,14 +158,19 @@ def run_llama(args, w):
     for sh, wr in zip([s0] + others, wf):
         sh.step(tp.TP_STAGE_FFN, h0, None, B, wr)
     torch.cuda.synchronize()
-    other_att, other_ffn = wa[1:], wf[1:]
-    del others
+    return d, shard, s0, x0, lens, wa[1:], wf[1:]
+
+
+def run_llama(args, w):
+    import torch
+    import tensor_tp_shard_amd as tp
+    T, B = w.tp, w.batch
+    d, shard, s0, x0, lens, other_att, other_ffn = llama_rank0(w)
     # R copies of rank 0's layer
     wbytes, kvbytes, w13bytes = llama_bytes(w, d["lens"])
     step_bytes = wbytes + kvbytes
     R = args.copies or max(2, int(np.ceil(3 * 256e6 / step_bytes)))
     copies = [s0] + [shard(0) for _ in range(R - 1)]
-    del W
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     wires_a = [c.new_wire() for c in copies]
@@ -528,6 +536,146 @@ def run_logits(args, w):
     return res
 
 
+def run_decode(args, wd):
+    """One token through rank 0's shard of the whole model: n_layers layer
+    steps (distinct packed weights and KV caches per layer, each merge done by
+    the kernel producing rank 0's partial) feeding each other, then the final
+    stage (final norm, logits slice, wire, merge of all T slices). The other
+    ranks' partials are computed once for the first layer's input and stand
+    in for what every layer would receive."""
+    import torch
+    import tensor_tp_shard_amd as tp
+    w, wl, L = wd.block, wd.logits, wd.n_layers
+    T, B = w.tp, w.batch
+    d, shard, s0, x0, lens, other_att, other_ffn = llama_rank0(w)
+    layers = [s0] + [shard(0) for _ in range(L - 1)]
+    dl = synth.logits_inputs(wl)
+    WL = {"w1": dev(dl["w_cls"]), "g_att": dev(dl["g_final"])}
+    lsh = []
+    for r in range(T):
+        sh = tp.Shard(logits_config(tp, wl, r), caches=False)
+        sh.load(WL)
+        lsh.append(sh)
+    xl = dev(dl["x"][:B])
+    other_lw = [sh.new_wire() for sh in lsh[1:]]
+    for sh, wr in zip(lsh[1:], other_lw):
+        sh.step(tp.TP_STAGE_LOGITS, xl, None, B, wr)
+    torch.cuda.synchronize()
+    l0 = lsh[0]
+    del lsh, WL
+    torch.cuda.empty_cache()
+    wires_a = [c.new_wire() for c in layers]
+    wires_f = [c.new_wire() for c in layers]
+    xs = [torch.empty_like(x0) for _ in range(L + 1)]
+    hs_ = [torch.empty_like(x0) for _ in range(L)]
+    xs[0].copy_(x0)
+    lwire = l0.new_wire()
+    logits = torch.empty((B, wl.vocab), dtype=torch.float32, device="cuda")
+
+    def one_token():
+        for i, c in enumerate(layers):
+            c.step_merge(tp.TP_STAGE_ATTN, xs[i], lens, B, wires_a[i], [wires_a[i]] + other_att, hs_[i])
+            c.step_merge(tp.TP_STAGE_FFN, hs_[i], None, B, wires_f[i], [wires_f[i]] + other_ffn,
+                         xs[i + 1])
+        l0.step(tp.TP_STAGE_LOGITS, xs[L], None, B, lwire)
+        l0.merge_logits([lwire] + other_lw, logits, B)
+
+    tokens = max(1, args.steps // L)
+    wtok = max(1, args.warmup // L)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = None
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            one_token()
+        if args.mode == "graph":
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                one_token()
+        run = graph.replay if graph is not None else one_token
+        for _ in range(wtok):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(tokens):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        assert torch.isfinite(logits).all().item(), "non-finite logits"
+        kid = tp.kernel_names().index("gemv_w13_swiglu")
+        for c in layers:
+            tp.kernel_timing_arm(c.handle, kid)
+        for _ in range(tokens):
+            one_token()
+        torch.cuda.synchronize()
+        tot, n = 0.0, 0
+        for c in layers:
+            t_, n_ = tp.kernel_timing_read(c.handle)
+            tot += t_
+            n += n_
+            tp.kernel_timing_arm(c.handle, -1)
+    ms_tok = ms / tokens
+    wbytes, kvbytes, w13bytes = llama_bytes(w, d["lens"])
+    ecls = 1.125 if wl.quant & synth.Q_WEIGHTS else 2 if wl.w_dtype == synth.BF16 else 4
+    tok_bytes = L * (wbytes + kvbytes) + int(wl.vocab // T * wl.dim * ecls)
+    k_ms = tot / max(n, 1)
+    achieved = w13bytes / (k_ms * 1e-3) / 1e9
+    res = {
+        "metric": "decode tokens/s of one TP shard through the whole model (all layers + final stage)",
+        "value": round(1e3 / ms_tok * B, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": tokens,
+        "warmup": wtok,
+        "ms_per_step": round(ms_tok, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if w.quant & synth.Q_WEIGHTS else "bf16" if w.w_dtype == synth.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wd.name, "shard": f"rank 0 of TP={T}", "batch": B, "layers": L,
+                   "vocab": wl.vocab, "kv_positions": [int(d["lens"].min()), int(d["lens"].max())],
+                   "launch": args.mode, "token_bytes": int(tok_bytes)},
+        "achieved_GBps": round(tok_bytes / (ms_tok * 1e-3) / 1e9, 1),
+        "hbm_frac": round(tok_bytes / (ms_tok * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"kernel": "gemv_w13_swiglu", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(
+                         f"traffic_gemv_w13_swiglu_{w.name}.md",
+                         GEMV_MFMA_SOURCES if w.w_dtype == synth.BF16 and B > 4 else GEMV_SOURCES),
+                     "bytes_per_launch": int(w13bytes),
+                     "avg_launch_us": round(k_ms * 1e3, 3), "launches": n},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        # bounded sample: whole layer steps and final stages of rank 0 timed
+        # separately, the token rate derived as 1 / (L * t_layer + t_final)
+        half = args.cpu_seconds / 2
+        t_layer = cpu_baseline_llama(w, d, half)
+        t_layer_s = 1.0 / t_layer["value"]
+        n, t0 = 0, time.perf_counter()
+        Vs = wl.vocab // T
+        while True:
+            z = oracle.logits_shard(dl["w_cls"], dl["g_final"], dl["x"][:B], T, 0, wl.norm_eps,
+                                    wl.w_dtype)["z"]
+            dz, _, _ = oracle.wire(z, wl.quant)
+            oracle.merge_logits(np.concatenate([dz[None], np.zeros((T - 1, B, Vs))]))
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= half:
+                break
+        t_final = el / n
+        res["cpu_baseline"] = {
+            "value": round(B / (L * t_layer_s + t_final), 5), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{t_layer['sample']}; {n} final stages in {el:.1f} s; tokens/s = B / "
+                      f"({L} x layer step + final stage)"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -536,6 +684,7 @@ def main():
     ap.add_argument("--workload", default="llama2_7b_tp4_b1", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--copies", type=int, default=0, help="layer copies in rotation (0 = auto)")
+    # a decode workload (whole model) times --steps layer steps, i.e. steps / n_layers tokens
     ap.add_argument("--merge", default="fused", choices=["fused", "separate"],
                     help="merge of a stage's partials by the kernel that produces rank 0's own "
                          "partial (decode_merge_step) or as a kernel of its own (merge_partials)")
@@ -556,7 +705,7 @@ def main():
         calib_copy(args.calib_copy_mib)
         return
     w = synth.get(args.workload)
-    runs = {"ffn2d": run_ffn2d, "logits": run_logits, "llama": run_llama}
+    runs = {"ffn2d": run_ffn2d, "logits": run_logits, "llama": run_llama, "decode": run_decode}
     res = runs[w.kind](args, w)
     print(json.dumps(res), flush=True)
 

@@ -103,6 +103,18 @@ class LlamaLogits:
     kind: str = "logits"
 
 
+@dataclasses.dataclass(frozen=True)
+class LlamaDecode:
+    """A whole decode step of one TP shard: ``n_layers`` blocks of shape
+    ``block`` (each with its own weights and KV cache), then the final stage
+    ``logits``."""
+    name: str
+    block: "LlamaBlock"
+    logits: "LlamaLogits"
+    n_layers: int
+    kind: str = "decode"
+
+
 WORKLOADS: Dict[str, object] = {}
 
 
@@ -147,6 +159,11 @@ L7B_LOGITS_Q8 = _add(dataclasses.replace(L7B_LOGITS, name="llama2_7b_tp4_logits_
                                          quant=Q_PARTIALS, seed=1010))
 L70B_LOGITS = _add(LlamaLogits("llama2_70b_tp8_logits_b16", dim=8192, vocab=32000, tp=8, batch=16,
                                w_dtype=BF16, quant=Q_NONE, seed=1011))
+
+
+# whole decode steps: Llama-2 7B (32 layers) and 70B (80 layers)
+L7B_DECODE = _add(LlamaDecode("llama2_7b_tp4_decode_b1", L7B, L7B_LOGITS, 32))
+L70B_DECODE = _add(LlamaDecode("llama2_70b_tp8_decode_b16", L70B, L70B_LOGITS, 80))
 
 
 def get(name: str):

@@ -303,14 +303,19 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
     // (W8: codes K bytes a row, the lane's 8 bytes of a step at 32 s + 8 q;
     // scales K / 32 floats a row, the block's four at 16 bytes)
     constexpr uint32_t eb = W8 ? 1 : 2; // bytes per weight
+    // A tile past N (the last tile column of an N that is not a multiple of
+    // its width) gets an empty resource: its loads return zeros, and it
+    // stores nothing, while its wave still takes part in the barriers.
     __amdgpu_buffer_rsrc_t Wr[T], Sr[T];
 #pragma unroll
     for (int t = 0; t < T; t++) {
-        Wr[t] = buf_rsrc((const char *)a.W + ((size_t)(n0u + 16 * t) * a.K + (size_t)jb * 128) * eb,
-                         (uint32_t)(16 * a.K - jb * 128) * eb);
+        const bool live = n0u + 16 * t < a.N;
+        Wr[t] = buf_rsrc(live ? (const char *)a.W + ((size_t)(n0u + 16 * t) * a.K + (size_t)jb * 128) * eb
+                              : (const char *)a.W,
+                         live ? (uint32_t)(16 * a.K - jb * 128) * eb : 0u);
         if constexpr (W8)
-            Sr[t] = buf_rsrc(a.ws + (size_t)(n0u + 16 * t) * (a.K / 32) + (size_t)jb * 4,
-                             (uint32_t)(16 * (a.K / 32) - jb * 4) * 4);
+            Sr[t] = buf_rsrc(live ? a.ws + (size_t)(n0u + 16 * t) * (a.K / 32) + (size_t)jb * 4 : a.ws,
+                             live ? (uint32_t)(16 * (a.K / 32) - jb * 4) * 4 : 0u);
     }
     const uint32_t lofs = W8 ? (uint32_t)r * a.K + 8 * q : (uint32_t)r * a.K * 2 + 16 * q;
     const uint32_t sofs = (uint32_t)r * (a.K / 32) * 4;
@@ -424,13 +429,14 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
         for (int t = 0; t < T; t++)
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                if (4 * q + i < a.B)
+                if (4 * q + i < a.B && n0 + 16 * t < a.N)
                     a.part[((size_t)ks * a.B + 4 * q + i) * a.N + n0 + 16 * t + r] = acc[t][i];
     } else if (r < a.B) {
         // lane (q, b = r) holds rows n0 + 16 t + 4q + i (i < 4) of batch column b
 #pragma unroll
         for (int t = 0; t < T; t++)
-            *(f32x4 *)(a.part + ((size_t)ks * a.B + r) * a.N + n0 + 16 * t + 4 * q) = acc[t];
+            if (n0 + 16 * t < a.N)
+                *(f32x4 *)(a.part + ((size_t)ks * a.B + r) * a.N + n0 + 16 * t + 4 * q) = acc[t];
     }
 }
 
@@ -542,11 +548,11 @@ static SkShape sk_shape(int N, int K)
         return sh;
     if (N % 256 == 0 && N / 256 >= 16)
         sh.T = 2;
-    else if (N % 128 == 0)
+    else if (N % 16 == 0) // a ragged last tile column: its tiles past N are idle
         sh.T = 1;
     else
         return sh;
-    sh.R = N / (128 * sh.T);
+    sh.R = (N + 128 * sh.T - 1) / (128 * sh.T);
     // at most 256 workgroups: the folded-RMSNorm kernel holds one 8-wave
     // workgroup per CU, so a 257th would run in a second round (70B
     // up-projection: 280 -> 224 workgroups, 34.8 -> 33.5 us)

@@ -182,6 +182,18 @@ def test_splitk_folded_norm_ragged_batch(quant):
     assert np.array_equal(r["out"].view(np.uint32), g["out"].view(np.uint32))
 
 
+@pytest.mark.parametrize("quant", [synth.Q_NONE, synth.Q_WEIGHTS])
+def test_splitk_ragged_tile_column(quant):
+    """Batch 9 at dim 4096 with Wqkv of 192 rows: the split-K up-projection's
+    second tile column holds 64 rows, so 4 of its 8 waves are past N (empty
+    weight resource, no partial stores) while still taking part in the
+    workgroup's barriers; bf16 and int8 weights."""
+    w = synth.small_llama(name=f"splitk_ragged_q{quant}", dim=4096, n_heads=8, n_kv_heads=2, head_dim=32,
+                          ffn_hidden=4096, tp=2, batch=9, past=(1, 50), w_dtype=synth.BF16,
+                          kv_dtype=synth.BF16, quant=quant, seed=81)
+    check_layer(w)
+
+
 def test_mfma_gemv_one_tile_sixteen_waves():
     """Batch 12, dim 1024, FFN slice 3968: W2 (N 1024, K 3968 < 4096) takes the
     per-tile MFMA kernel with one 16-row tile per wave and 16 waves splitting
