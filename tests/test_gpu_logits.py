@@ -36,11 +36,11 @@ def _tol(w):
     return 1e-4 if w.w_dtype == synth.F32 and not w.quant & synth.Q_WEIGHTS else 1e-3
 
 
-def check_logits(w, B=None, d=None):
+def check_logits(w, B=None, d=None, max_batch=None):
     B = w.batch if B is None else B
     d = d or synth.logits_inputs(w, B)
-    say(f"{w.name} D={w.dim} V={w.vocab} T={w.tp} B={B} quant={w.quant}")
-    g = Logits(w, d, max_batch=B).run(d["x"])
+    say(f"{w.name} D={w.dim} V={w.vocab} T={w.tp} B={B} max_batch={max_batch or B} quant={w.quant}")
+    g = Logits(w, d, max_batch=max_batch or B).run(d["x"])
     o = oracle.logits(d["w_cls"], d["g_final"], d["x"], w.tp, w.quant, w.norm_eps, w.w_dtype,
                       bool(w.quant & synth.Q_WEIGHTS))
     tol, Vs = _tol(w), w.vocab // w.tp
@@ -86,10 +86,20 @@ def _small(name, dim, vocab, tp_, batch, w_dtype=synth.BF16, quant=0, seed=2001)
     (4096, 8192, 4, 16, synth.BF16, 0),         # split-K, folded norm
     (256, 1024, 2, 2, synth.BF16, synth.Q_WEIGHTS),
     (256, 1024, 2, 16, synth.BF16, synth.Q_WEIGHTS | synth.Q_PARTIALS),
+    (256, 512, 1, 3, synth.BF16, synth.Q_PARTIALS),   # one shard: the merge is a dequantised copy
 ], ids=lambda c: f"D{c[0]}_V{c[1]}_T{c[2]}_B{c[3]}_{c[4]}_q{c[5]}")
 def test_logits_shapes(case):
     D, V, T, B, dt, q = case
     check_logits(_small(f"logits_D{D}_V{V}", D, V, T, B, dt, q))
+
+
+@pytest.mark.parametrize("B", [1, 5, 13])
+def test_logits_batch_below_max_batch(B):
+    """A handle planned for batch 16 run at a smaller batch: the int8 wire's
+    scales sit right after that batch's codes (tp_wire_scales_offset of the
+    batch run), in the step and in the merge alike."""
+    check_logits(_small("logits_maxb16", 256, 2048, 4, B, synth.BF16, synth.Q_PARTIALS, seed=2002),
+                 max_batch=16)
 
 
 def test_llama7b_logits_b1():
