@@ -101,6 +101,11 @@ def _declare(L):
                                    _P]
     L.orc_logits_shard.restype = ctypes.c_int
     L.orc_merge_logits.argtypes = [_I64, _I64, _I32, _P, _P]
+    L.orc_attn_batch_shard.argtypes = [_I64, _I64, _I64, _I64, _I64, _D, ctypes.c_int, _P, _P, _P, _P,
+                                       _P]
+    L.orc_attn_batch_shard.restype = ctypes.c_int
+    L.orc_a2a_heads_to_batch.argtypes = [_I64, _I32, _I32, _I64, _P, _P]
+    L.orc_a2a_batch_to_heads.argtypes = [_I64, _I32, _I32, _I64, _P, _P]
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -395,3 +400,44 @@ def llama_decode(layers, w_cls, g_final, x, lens, kcaches, vcaches, quant_logits
     tp = layers[0][0].tp
     lo = logits(w_cls, g_final, h, tp, quant_logits, eps, cls_dtype, cls_w8)
     return {"h": np.stack(hs), "out": lo["out"], "z": lo["z"]}
+
+
+# ---------------------------------------------------------------- batch-sharded attention
+
+def attn_batch_shard(qkv, lens, kcache, vcache, n_heads: int, n_kv_heads: int, head_dim: int,
+                     kv_dtype="bf16", rope_theta: float = 10000.0) -> np.ndarray:
+    """One batch shard's attention: qkv [nb][(Hq + 2 Hkv) hd] raw rows of its
+    sequences, caches [nb][Hkv][max_ctx][hd] (updated in place at slot
+    lens[b]). -> att [nb][Hq hd] fp64."""
+    dt = _dt(kv_dtype)
+    kcache, vcache = _typed(kcache, dt), _typed(vcache, dt)
+    nb, Hkv, C, hd = kcache.shape
+    assert Hkv == n_kv_heads and hd == head_dim and vcache.shape == kcache.shape
+    qkv = np.ascontiguousarray(qkv, dtype=np.float64).reshape(nb, (n_heads + 2 * Hkv) * hd)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    att = np.empty((nb, n_heads * hd))
+    rc = lib().orc_attn_batch_shard(nb, n_heads, Hkv, hd, C, rope_theta, dt, _ptr(qkv), _ptr(lens),
+                                    _ptr(kcache), _ptr(vcache), _ptr(att))
+    if rc:
+        raise ValueError(f"orc_attn_batch_shard rejected the input ({rc})")
+    return att
+
+
+def a2a_heads_to_batch(src, r: int) -> np.ndarray:
+    """src [T][B][C] head-sharded rows of every shard -> shard r's [B/T][T C]."""
+    src = np.ascontiguousarray(src, dtype=np.float64)
+    T, B, C = src.shape
+    assert B % T == 0
+    dst = np.empty((B // T, T * C))
+    lib().orc_a2a_heads_to_batch(B, T, r, C, _ptr(src), _ptr(dst))
+    return dst
+
+
+def a2a_batch_to_heads(src, r: int) -> np.ndarray:
+    """src [T][B/T][T C] batch-sharded rows of every shard -> shard r's [B][C]."""
+    src = np.ascontiguousarray(src, dtype=np.float64)
+    T, nb, TC = src.shape
+    assert TC % T == 0
+    dst = np.empty((T * nb, TC // T))
+    lib().orc_a2a_batch_to_heads(T * nb, T, r, TC // T, _ptr(src), _ptr(dst))
+    return dst

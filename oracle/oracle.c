@@ -554,3 +554,84 @@ void orc_merge_logits(int64_t B, int64_t Vs, int32_t T, const double *d, double 
             for (int64_t j = 0; j < Vs; j++)
                 out[b * T * Vs + i * Vs + j] = d[(i * B + b) * Vs + j];
 }
+
+/* ---------------------------------------------------------------- batch-sharded attention */
+
+/* Batch-sharded attention ([POPE] demo 3 observations: with fewer KV heads
+ * than shards, sharding attention by head would store a KV head on several
+ * chips; sharding by sequence stores each sequence's KV once, on the shard
+ * that owns the sequence with every head local, and the queries and outputs
+ * cross an all-to-all instead). One batch shard: for each of its nb
+ * sequences (rows of qkv: the raw q of every q head, then the raw k and v of
+ * every kv head), RoPE at position lens[b] on q and k, the new k / v
+ * appended at slot lens[b] of the shard's caches, then every q head attends
+ * over its kv head's lens[b] + 1 positions, exactly as in the head-sharded
+ * stage (same rotation, append, scale and kv-head map).
+ *  qkv [nb][(Hq + 2 Hkv) hd]; kc, vc [nb][Hkv][C][hd] (cache dtype kv_dt);
+ *  att [nb][Hq hd]. Returns -2 (nothing written) if a length is outside
+ *  [0, C). */
+int orc_attn_batch_shard(int64_t nb, int64_t Hq, int64_t Hkv, int64_t hd, int64_t C, double theta,
+                         int kv_dt, const double *qkv, const int32_t *lens, void *kc, void *vc,
+                         double *att)
+{
+    if (Hq % Hkv || hd % 2)
+        return -1;
+    for (int64_t b = 0; b < nb; b++)
+        if (lens[b] < 0 || lens[b] >= C)
+            return -2;
+    const int64_t G = Hq / Hkv, ld = (Hq + 2 * Hkv) * hd;
+    const int64_t esz = kv_dt == ORC_F32 ? 4 : 2;
+    double *u = (double *)malloc(sizeof(double) * (size_t)hd);
+    for (int64_t b = 0; b < nb; b++) {
+        const int64_t L = lens[b];
+        const double *row = qkv + b * ld;
+        for (int64_t hk = 0; hk < Hkv; hk++) {
+            const int64_t slot = ((b * Hkv + hk) * C + L) * hd;
+            memcpy(u, row + (Hq + hk) * hd, sizeof(double) * (size_t)hd);
+            orc_rope(hd, L, theta, u);
+            for (int64_t e = 0; e < hd; e++)
+                st(kc, kv_dt, slot + e, u[e]);
+            for (int64_t e = 0; e < hd; e++)
+                st(vc, kv_dt, slot + e, row[(Hq + Hkv + hk) * hd + e]);
+        }
+        for (int64_t h = 0; h < Hq; h++) {
+            const int64_t base = (b * Hkv + h / G) * C * hd;
+            memcpy(u, row + h * hd, sizeof(double) * (size_t)hd);
+            orc_rope(hd, L, theta, u);
+            orc_attend(hd, L + 1, u, (const char *)kc + base * esz, (const char *)vc + base * esz,
+                       kv_dt, hd, att + (b * Hq + h) * hd);
+        }
+    }
+    free(u);
+    return 0;
+}
+
+/* The two all-to-alls around batch-sharded attention, seen from shard r of
+ * T with B sequences in all (nb = B / T per shard) and C = (Hq / T) hd
+ * columns of one head shard:
+ *  heads -> batch: src [T][B][C] (shard i's head-sharded rows: its q heads
+ *    [i Hq/T, (i+1) Hq/T) for every sequence) -> dst [nb][T C]: shard r's
+ *    sequences [r nb, (r+1) nb) with every head, head shard i's columns at
+ *    [i C, (i+1) C);
+ *  batch -> heads: src [T][nb][T C] (shard i's batch-sharded rows) -> dst
+ *    [B][C]: every sequence b (from shard b / nb, row b % nb) with shard r's
+ *    heads, columns [r C, (r+1) C) of that row.
+ * Pure placement: every value is copied unchanged. */
+void orc_a2a_heads_to_batch(int64_t B, int32_t T, int32_t r, int64_t C, const double *src,
+                            double *dst)
+{
+    const int64_t nb = B / T;
+    for (int64_t b = 0; b < nb; b++)
+        for (int32_t i = 0; i < T; i++)
+            for (int64_t c = 0; c < C; c++)
+                dst[b * T * C + i * C + c] = src[((int64_t)i * B + r * nb + b) * C + c];
+}
+
+void orc_a2a_batch_to_heads(int64_t B, int32_t T, int32_t r, int64_t C, const double *src,
+                            double *dst)
+{
+    const int64_t nb = B / T;
+    for (int64_t b = 0; b < B; b++)
+        for (int64_t c = 0; c < C; c++)
+            dst[b * C + c] = src[((b / nb) * nb + b % nb) * T * C + r * C + c];
+}

@@ -33,6 +33,9 @@ MUTANTS = {
     "logits_row_offset": ("(const char *)Wcls + s * Vs * D * esz", "(const char *)Wcls"),
     "logits_no_final_norm": ("orc_rmsnorm(D, x + b * D, g, eps, xn);",
                              "memcpy(xn, x + b * D, sizeof(double) * (size_t)D);"),
+    "batch_attn_kv_map": ("const int64_t base = (b * Hkv + h / G) * C * hd;",
+                          "const int64_t base = (b * Hkv + h % Hkv) * C * hd;"),
+    "a2a_source_row": ("src[((int64_t)i * B + r * nb + b) * C + c]", "src[((int64_t)i * B + b) * C + c]"),
     "merge_logits_order": ("out[b * T * Vs + i * Vs + j]", "out[b * T * Vs + (T - 1 - i) * Vs + j]"),
 }
 

@@ -592,3 +592,62 @@ def test_decode_loop_feeds_each_layer_the_previous_output(orc):
     kc, vc = fresh()
     h2x = orc.llama_layer(*layers[1], x, lens, kc[1], vc[1])["out"]
     assert rel_l2(h2x, h2) > 1e-3
+
+
+# ---------------------------------------------------------------- batch-sharded attention
+
+def test_a2a_placement_and_round_trip():
+    import oracle as orc
+    T, B, C = 4, 8, 6
+    nb = B // T
+    src = np.array([[[i * 1e6 + b * 1e3 + c for c in range(C)] for b in range(B)] for i in range(T)])
+    got = [orc.a2a_heads_to_batch(src, r) for r in range(T)]
+    for r in range(T):
+        for b in range(nb):
+            for i in range(T):
+                assert np.array_equal(got[r][b, i * C:(i + 1) * C], src[i, r * nb + b])
+    back = np.stack(got)  # [T][nb][T C]: every shard's batch-sharded rows
+    for r in range(T):
+        assert np.array_equal(orc.a2a_batch_to_heads(back, r), src[r])
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16"])
+def test_batch_sharded_attention_equals_head_sharded(orc, kv_dtype):
+    """The same attention split two ways: T = 2 head shards (each with its q
+    and kv heads, every sequence) and T = 2 batch shards (each with its
+    sequences, every head) give the same outputs and append the same cache
+    entries. The batch shards' raw q / k / v rows come from the oracle's
+    matvec of the normalised input."""
+    w = synth.small_llama(dim=64, n_heads=8, n_kv_heads=2, head_dim=16, ffn_hidden=64, tp=2, batch=4,
+                          past=(0, 9), kv_dtype=kv_dtype, seed=90)
+    d = synth.llama_inputs(w)
+    lens = d["lens"]
+    B, Hq, Hkv, hd, T = w.batch, w.n_heads, w.n_kv_heads, w.head_dim, w.tp
+    kc_h, vc_h = d["kcache"].copy(), d["vcache"].copy()
+    heads = [orc.attn_shard(w, d, s, d["x"], lens, kc_h, vc_h) for s in range(T)]
+    xn = heads[0]["xn"]
+    raw = np.stack([np.concatenate([orc.matvec(d[k], xn[b]) for k in ("wq", "wk", "wv")])
+                    for b in range(B)])
+    nb, Hq_s = B // T, Hq // T
+    for r in range(T):
+        rows = slice(r * nb, (r + 1) * nb)
+        kc, vc = d["kcache"][rows].copy(), d["vcache"][rows].copy()
+        att = orc.attn_batch_shard(raw[rows], lens[rows], kc, vc, Hq, Hkv, hd, kv_dtype)
+        for h in range(Hq):
+            want = heads[h // Hq_s]["att"][rows, (h % Hq_s) * hd:(h % Hq_s + 1) * hd]
+            assert np.allclose(att[:, h * hd:(h + 1) * hd], want, rtol=1e-13, atol=1e-15)
+        assert np.array_equal(kc.view(np.uint8), kc_h[rows].view(np.uint8))
+        assert np.array_equal(vc.view(np.uint8), vc_h[rows].view(np.uint8))
+
+
+def test_batch_sharded_attention_single_position_returns_v(orc):
+    """No cached past: the only position is the new one, so each q head's
+    output is its kv head's v (as stored, fp32 cache)."""
+    Hq, Hkv, hd, C = 4, 2, 8, 3
+    qkv = _rng(91).standard_normal((2, (Hq + 2 * Hkv) * hd)).astype(np.float32)
+    kc = np.full((2, Hkv, C, hd), np.nan, np.float32)
+    vc = kc.copy()
+    att = orc.attn_batch_shard(qkv, np.zeros(2, np.int32), kc, vc, Hq, Hkv, hd, "f32")
+    for h in range(Hq):
+        v = qkv[:, (Hq + Hkv + h // 2) * hd:(Hq + Hkv + h // 2 + 1) * hd]
+        assert np.array_equal(att[:, h * hd:(h + 1) * hd], v.astype(np.float64))
