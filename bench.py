@@ -536,6 +536,144 @@ def run_logits(args, w):
     return res
 
 
+def attn_batch_config(tp, w, rank):
+    dt = {synth.F32: tp.TP_F32, synth.BF16: tp.TP_BF16}
+    return tp.make_config(kind=tp.TP_ATTN_BATCH, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads,
+                          head_dim=w.head_dim, tp_size=w.tp, tp_rank=rank, max_batch=w.batch,
+                          max_ctx=w.max_ctx, kv_dtype=dt[w.kv_dtype], rope_theta=w.rope_theta)
+
+
+def run_attn_batch(args, w):
+    """Rank 0's batch-sharded attention step: the all-to-all of the queries
+    from the T head shards into its attention input rows, attention of every
+    head over its sequences' caches, and the all-to-all of the outputs back
+    into head shard 0's rows (the other batch shards' outputs computed once).
+    R copies of rank 0's caches in rotation."""
+    import torch
+    import tensor_tp_shard_amd as tp
+    T, B, hd, Hq, Hkv = w.tp, w.batch, w.head_dim, w.n_heads, w.n_kv_heads
+    nb, C = B // T, Hq // T * hd
+    d = synth.attn_batch_inputs(w)
+    kve = 2 if w.kv_dtype == synth.BF16 else 4
+
+    def shard(rank):
+        rows = slice(rank * nb, (rank + 1) * nb)
+        sh = tp.Shard(attn_batch_config(tp, w, rank), caches=False)
+        sh.load({}, k_cache=dev(np.ascontiguousarray(d["kcache"][rows])).reshape(-1),
+                v_cache=dev(np.ascontiguousarray(d["vcache"][rows])).reshape(-1))
+        return sh
+
+    qh = [dev(np.ascontiguousarray(d["qkv"][:, i * C:(i + 1) * C])) for i in range(T)]
+    ld_q = (Hq + 2 * Hkv) * hd
+    outs = []
+    for r in range(1, T):   # the other batch shards' outputs for head shard 0
+        sh = shard(r)
+        x = dev(np.ascontiguousarray(d["qkv"][r * nb:(r + 1) * nb]))
+        att = torch.empty((nb, Hq * hd), device="cuda")
+        sh.step(tp.TP_STAGE_ATTN, x, dev(d["lens"][r * nb:(r + 1) * nb]), nb, att)
+        outs.append(att)
+    torch.cuda.synchronize()
+    kv_bytes = int(np.sum(d["lens"][:nb]) + nb) * Hkv * hd * 2 * kve
+    R = args.copies or max(2, int(np.ceil(3 * 256e6 / max(kv_bytes, 1))))
+    R = min(R, 64)
+    copies = [shard(0) for _ in range(R)]
+    lens0 = dev(d["lens"][:nb])
+    xs = [dev(np.ascontiguousarray(d["qkv"][:nb])) for _ in range(R)]
+    atts = [torch.empty((nb, Hq * hd), device="cuda") for _ in range(R)]
+    backs = [torch.empty((B, C), device="cuda") for _ in range(R)]
+    torch.cuda.synchronize()
+
+    def one_pass():
+        for r, c in enumerate(copies):
+            tp.all_to_all(c.handle, tp.TP_A2A_HEADS_TO_BATCH, qh, C, xs[r], ld_q)
+            c.step(tp.TP_STAGE_ATTN, xs[r], lens0, nb, atts[r])
+            tp.all_to_all(c.handle, tp.TP_A2A_BATCH_TO_HEADS, [atts[r]] + outs, Hq * hd, backs[r], C)
+
+    passes = max(1, args.steps // R)
+    steps = passes * R
+    wpasses = max(1, args.warmup // R)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = None
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            one_pass()
+        if args.mode == "graph":
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                one_pass()
+        run = graph.replay if graph is not None else one_pass
+        for _ in range(wpasses):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(passes):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        assert torch.isfinite(backs[0]).all().item(), "non-finite attention output"
+        kid = tp.kernel_names().index("attention")
+        for c in copies:
+            tp.kernel_timing_arm(c.handle, kid)
+        for _ in range(passes):
+            one_pass()
+        torch.cuda.synchronize()
+        tot, n = 0.0, 0
+        for c in copies:
+            t_, n_ = tp.kernel_timing_read(c.handle)
+            tot += t_
+            n += n_
+            tp.kernel_timing_arm(c.handle, -1)
+    ms_step = ms / steps
+    k_ms = tot / max(n, 1)
+    achieved = kv_bytes / (k_ms * 1e-3) / 1e9
+    res = {
+        "metric": "batch-sharded attention steps/s of one shard (all-to-all in, RoPE + KV append + "
+                  "GQA attention over every head of its sequences, all-to-all out)",
+        "value": round(1e3 / ms_step, 1),
+        "unit": "attention-steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": wpasses * R,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.kv_dtype == synth.F32 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "shard": f"rank 0 of TP={T}", "sequences": nb,
+                   "heads": [Hq, Hkv], "kv_positions": [int(x) for x in d["lens"][:nb]],
+                   "copies": R, "launch": args.mode, "step_bytes": kv_bytes},
+        "roofline": {"kernel": "attention (+ combine)", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": kv_bytes,
+                     "avg_launch_us": round(k_ms * 1e3, 3), "launches": n},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n, t0 = 0, time.perf_counter()
+        kc, vc = d["kcache"][:nb].copy(), d["vcache"][:nb].copy()
+        heads = np.stack([d["qkv"][:, i * C:(i + 1) * C] for i in range(T)])
+        while True:
+            q = oracle.a2a_heads_to_batch(heads, 0)
+            rows = d["qkv"][:nb].astype(np.float64)
+            rows[:, :Hq * hd] = q
+            att = oracle.attn_batch_shard(rows, d["lens"][:nb], kc, vc, Hq, Hkv, hd, w.kv_dtype)
+            oracle.a2a_batch_to_heads(np.concatenate([att[None], np.zeros((T - 1, nb, Hq * hd))]), 0)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {
+            "value": round(n / el, 3), "unit": "attention-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} rank-0 batch-sharded attention steps of {w.name} (all-to-all, attention, "
+                      f"all-to-all) by the single-threaded fp64 C oracle in {el:.1f} s"}
+    return res
+
+
 def run_decode(args, wd):
     """One token through rank 0's shard of the whole model: n_layers layer
     steps (distinct packed weights and KV caches per layer, each merge done by
@@ -705,7 +843,8 @@ def main():
         calib_copy(args.calib_copy_mib)
         return
     w = synth.get(args.workload)
-    runs = {"ffn2d": run_ffn2d, "logits": run_logits, "llama": run_llama, "decode": run_decode}
+    runs = {"ffn2d": run_ffn2d, "logits": run_logits, "llama": run_llama, "decode": run_decode,
+            "attn_batch": run_attn_batch}
     res = runs[w.kind](args, w)
     print(json.dumps(res), flush=True)
 

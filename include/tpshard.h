@@ -55,7 +55,8 @@ extern "C" {
 typedef struct tp_shard tp_shard; /* opaque host-side handle; owns no device memory */
 
 enum { TP_F32 = 0, TP_BF16 = 1 };                         /* element types */
-enum { TP_LLAMA_BLOCK = 0, TP_FFN_2D = 1, TP_LOGITS = 2 };          /* tp_config.kind */
+enum { TP_LLAMA_BLOCK = 0, TP_FFN_2D = 1, TP_LOGITS = 2, TP_ATTN_BATCH = 3 }; /* tp_config.kind */
+enum { TP_A2A_HEADS_TO_BATCH = 0, TP_A2A_BATCH_TO_HEADS = 1 };       /* tp_all_to_all direction */
 enum { TP_STAGE_ATTN = 0, TP_STAGE_FFN = 1, TP_STAGE_LOGITS = 2 };   /* decode_step / merge_partials stage */
 /* tp_config.quant bit mask. TP_Q_PARTIALS / TP_Q_INPUTS: the block-32 int8
  * round trip of the exchanged partials / the normalised stage inputs
@@ -112,6 +113,18 @@ enum { TP_DERR_LEN = 1 }; /* some lens[b] was < 0 or >= max_ctx; that sequence w
  *   page lists no quantisation of the final norm's output); requires V % T
  *   == 0, max_batch <= 16, D a multiple of 8 (32 with int8 weights), V/T a
  *   multiple of 8 (32 with TP_Q_PARTIALS).
+ * kind == TP_ATTN_BATCH: batch-sharded attention (CS349E lecture 4,
+ *   03_pope_partitioning.py, demo 3 observations: with fewer KV heads than
+ *   shards, head sharding would keep a KV head on several shards; sharding
+ *   by sequence keeps each sequence's KV once, with every head local, and
+ *   the queries and outputs cross an all-to-all). max_batch = B, the batch of
+ *   the whole layer; shard r owns sequences [r*B/T, (r+1)*B/T) with all
+ *   n_heads q and n_kv_heads kv heads; n_heads, n_kv_heads, head_dim,
+ *   max_ctx, kv_dtype and rope_theta as for TP_LLAMA_BLOCK; dim, ffn_hidden,
+ *   w_dtype and norm_eps ignored; quant 0. Requires B % T == 0, Hq % Hkv
+ *   == 0, Hq % T == 0 (the head shards on the other side of the all-to-all),
+ *   the head_dim, q-heads-per-kv-head and LDS rules of TP_LLAMA_BLOCK, and
+ *   B <= 16 * T.
  */
 typedef struct {
     int32_t kind;
@@ -172,7 +185,9 @@ int32_t init_shard(const tp_config *cfg, tp_shard **out, tp_sizes *sizes);
  * `full` alive until the stream reaches this point.
  * k_cache / v_cache hold [max_batch][Hkv_s][max_ctx][hd] kv_dtype each (the
  * caller fills the cached past positions; the library appends); they are
- * unused (may be NULL) for TP_FFN_2D and TP_LOGITS.
+ * unused (may be NULL) for TP_FFN_2D and TP_LOGITS. For TP_ATTN_BATCH no
+ * weight is read (all of `full`'s pointers may be NULL) and the caches hold
+ * [B/T][Hkv][max_ctx][hd] kv_dtype each.
  * Errors: TP_EINVAL, TP_EALIGN, TP_ENODEV, TP_EHIP.
  */
 int32_t load_weights(tp_shard *s, const tp_layer_weights *full, void *packed, void *k_cache,
@@ -195,6 +210,13 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *full, void *packed, vo
  *    [batch][V/T] in the wire format below (row length V/T instead of D);
  *    the taps xn (final-normalised rows) and p_pre (fp32 logits slice) are
  *    written, the others ignored.
+ *  For TP_ATTN_BATCH only TP_STAGE_ATTN is valid: x = fp32
+ *    [batch][(Hq + 2*Hkv)*hd] rows of the shard's sequences (batch <= B/T):
+ *    the raw (unrotated) q of every q head, then k and v of every kv head
+ *    (what the all-to-all of the queries and the shard's own K/V projection
+ *    deliver); lens = device int32 [batch] as for the attention stage above
+ *    (slot lens[b] of cache row b); wire_out receives the attention outputs
+ *    fp32 [batch][Hq*hd]; the taps q, k, v (rotated) and att are written.
  *  wire_out: the partial this shard exchanges. With TP_Q_PARTIALS: int8
  *    codes [batch][D] at offset 0, then fp32 scales [batch][D/32] at the
  *    offset tp_wire_scales_offset(cfg, batch) (one scale per 32 consecutive
@@ -253,6 +275,28 @@ int32_t decode_merge_step(tp_shard *s, int32_t stage, const void *x, const int32
  */
 int32_t merge_logits(const tp_shard *s, const void *const *wires, int32_t n_wires, float *out,
                      int32_t batch, void *hip_stream);
+
+/*
+ * tp_all_to_all: the two re-shardings around batch-sharded attention, seen
+ * from shard r of a TP_ATTN_BATCH handle (same passage as TP_ATTN_BATCH),
+ * for the whole batch B = max_batch, with nb = B/T and C = (Hq/T)*hd:
+ *  TP_A2A_HEADS_TO_BATCH: srcs[i] = head shard i's rows [B] (row stride
+ *    ld_src >= C elements; its q heads [i*Hq/T, (i+1)*Hq/T) in columns
+ *    [0, C)) -> dst [nb] rows (stride ld_dst >= T*C): row b gets sequence
+ *    r*nb + b of every head, head shard i's columns at [i*C, (i+1)*C).
+ *  TP_A2A_BATCH_TO_HEADS: srcs[i] = batch shard i's rows [nb] (stride
+ *    ld_src >= T*C; every head) -> dst [B] rows (stride ld_dst >= C): row b
+ *    gets columns [r*C, (r+1)*C) of row b % nb of srcs[b / nb].
+ *  Every value is copied unchanged. `srcs` is a HOST array of n_srcs = T
+ *  device pointers; ld_src and ld_dst are multiples of 4, buffers 16-byte
+ *  aligned; dst must not overlap a source. Other columns of dst are left as
+ *  they are (so the queries can land in the first columns of the attention
+ *  input rows).
+ * Errors: TP_EINVAL (wrong kind or direction, n_srcs != T, strides too
+ * small or not multiples of 4, null pointers), TP_EALIGN, TP_EHIP.
+ */
+int32_t tp_all_to_all(const tp_shard *s, int32_t dir, const void *const *srcs, int32_t n_srcs,
+                      int64_t ld_src, float *dst, int64_t ld_dst, void *hip_stream);
 
 /* Byte offset of the fp32 scales inside a quantised wire of `batch` rows
  * (16-byte aligned, right after the int8 codes; rows of D elements, of V/T

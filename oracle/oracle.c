@@ -586,7 +586,7 @@ int orc_attn_batch_shard(int64_t nb, int64_t Hq, int64_t Hkv, int64_t hd, int64_
         const int64_t L = lens[b];
         const double *row = qkv + b * ld;
         for (int64_t hk = 0; hk < Hkv; hk++) {
-            const int64_t slot = ((b * Hkv + hk) * C + L) * hd;
+            const int64_t slot = (b * Hkv + hk) * C * hd + L * hd; /* row L of the head's cache */
             memcpy(u, row + (Hq + hk) * hd, sizeof(double) * (size_t)hd);
             orc_rope(hd, L, theta, u);
             for (int64_t e = 0; e < hd; e++)
@@ -598,7 +598,8 @@ int orc_attn_batch_shard(int64_t nb, int64_t Hq, int64_t Hkv, int64_t hd, int64_
             const int64_t base = (b * Hkv + h / G) * C * hd;
             memcpy(u, row + h * hd, sizeof(double) * (size_t)hd);
             orc_rope(hd, L, theta, u);
-            orc_attend(hd, L + 1, u, (const char *)kc + base * esz, (const char *)vc + base * esz,
+            const int64_t n_pos = L + 1; /* the cached positions and the new one */
+            orc_attend(hd, n_pos, u, (const char *)kc + base * esz, (const char *)vc + base * esz,
                        kv_dt, hd, att + (b * Hq + h) * hd);
         }
     }

@@ -46,6 +46,7 @@ STREAMS = {
     "g_att": 8, "g_ffn": 9, "x": 10, "lens": 11, "kcache": 12, "vcache": 13,
     "ffn_x": 20, "ffn_win": 21, "ffn_wgate": 22, "ffn_wout": 23,
     "w_cls": 30, "g_final": 31, "final_x": 32,
+    "attn_qkv": 40,
 }
 
 
@@ -101,6 +102,27 @@ class LlamaLogits:
     seed: int
     norm_eps: float = 1e-5
     kind: str = "logits"
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnBatch:
+    """Attention of one decoder layer sharded by sequence over ``tp`` shards
+    (each shard: batch / tp sequences, every head)."""
+    name: str
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    tp: int
+    batch: int
+    past: Tuple[int, int]
+    kv_dtype: str
+    seed: int
+    rope_theta: float = 10000.0
+    kind: str = "attn_batch"
+
+    @property
+    def max_ctx(self) -> int:
+        return self.past[1] + 1
 
 
 @dataclasses.dataclass(frozen=True)
@@ -160,6 +182,12 @@ L7B_LOGITS_Q8 = _add(dataclasses.replace(L7B_LOGITS, name="llama2_7b_tp4_logits_
 L70B_LOGITS = _add(LlamaLogits("llama2_70b_tp8_logits_b16", dim=8192, vocab=32000, tp=8, batch=16,
                                w_dtype=BF16, quant=Q_NONE, seed=1011))
 
+
+# Llama-2-70B attention at TP = 16 (more shards than its 8 kv heads), sharded
+# by sequence: one sequence of the batch of 16 per shard, all 64 / 8 heads
+L70B_ATTN_BATCH = _add(AttnBatch("llama2_70b_tp16_attn_batch_b16", n_heads=64, n_kv_heads=8,
+                                 head_dim=128, tp=16, batch=16, past=(1024, 4096), kv_dtype=BF16,
+                                 seed=1012))
 
 # whole decode steps: Llama-2 7B (32 layers) and 70B (80 layers)
 L7B_DECODE = _add(LlamaDecode("llama2_7b_tp4_decode_b1", L7B, L7B_LOGITS, 32))
@@ -283,6 +311,16 @@ def logits_inputs(w: LlamaLogits, batch: Optional[int] = None) -> Dict[str, np.n
         "g_final": normal_f32(w.seed, STREAMS["g_final"], (w.dim,), 0.02, 1.0),
         "x": normal_f32(w.seed, STREAMS["final_x"], (B, w.dim), 1.0),
     }
+
+
+def attn_batch_inputs(w: AttnBatch) -> Dict[str, np.ndarray]:
+    """Raw q / k / v rows [B][(Hq + 2 Hkv) hd] of every sequence (N(0, 1)),
+    lens and full caches [B][Hkv][max_ctx][hd] as for a Llama block."""
+    lens = llama_lens(w)
+    return {"qkv": normal_f32(w.seed, STREAMS["attn_qkv"],
+                              (w.batch, (w.n_heads + 2 * w.n_kv_heads) * w.head_dim), 1.0),
+            "lens": lens, "kcache": llama_kv_cache(w, lens, "kcache"),
+            "vcache": llama_kv_cache(w, lens, "vcache")}
 
 
 # ---------------------------------------------------------------- 2D FFN block inputs

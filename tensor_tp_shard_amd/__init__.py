@@ -19,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtpshard.so")
 
 TP_F32, TP_BF16 = 0, 1
-TP_LLAMA_BLOCK, TP_FFN_2D, TP_LOGITS = 0, 1, 2
+TP_LLAMA_BLOCK, TP_FFN_2D, TP_LOGITS, TP_ATTN_BATCH = 0, 1, 2, 3
+TP_A2A_HEADS_TO_BATCH, TP_A2A_BATCH_TO_HEADS = 0, 1
 TP_STAGE_ATTN, TP_STAGE_FFN, TP_STAGE_LOGITS = 0, 1, 2
 TP_Q_NONE, TP_Q_PARTIALS, TP_Q_INPUTS, TP_Q_WEIGHTS = 0, 1, 2, 4
 TP_OK, TP_EINVAL, TP_EALIGN, TP_ESTATE, TP_ENODEV, TP_EHIP, TP_ENOTIMPL = 0, -1, -2, -3, -4, -5, -6
@@ -27,7 +28,7 @@ TP_DERR_LEN = 1
 
 # every symbol include/tpshard.h declares
 EXPORTS = ("init_shard", "load_weights", "decode_step", "merge_partials", "decode_merge_step",
-           "merge_logits", "tp_wire_scales_offset",
+           "merge_logits", "tp_all_to_all", "tp_wire_scales_offset",
            "tp_packed_int8_view",
            "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
            "tp_kernel_name", "destroy_shard", "tp_status_str", "tp_last_error")
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
         L.merge_partials.argtypes = [P, I32, P, I32, P, P, I32, P]
         L.decode_merge_step.argtypes = [P, I32, P, P, I32, P, P, I32, P, P, P]
         L.merge_logits.argtypes = [P, P, I32, P, I32, P]
+        L.tp_all_to_all.argtypes = [P, I32, P, I32, ctypes.c_int64, P, ctypes.c_int64, P]
         L.tp_wire_scales_offset.argtypes = [P, I32]
         L.tp_wire_scales_offset.restype = U64
         L.tp_read_error_word.argtypes = [P, P, I32, P]
@@ -91,7 +93,7 @@ def lib() -> ctypes.CDLL:
         L.tp_status_str.restype = ctypes.c_char_p
         L.tp_last_error.restype = ctypes.c_char_p
         for f in ("init_shard", "load_weights", "decode_step", "merge_partials",
-                  "decode_merge_step", "merge_logits", "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
+                  "decode_merge_step", "merge_logits", "tp_all_to_all", "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
                   "tp_packed_int8_view"):
             getattr(L, f).restype = I32
         _lib = L
@@ -177,6 +179,12 @@ def merge_logits(handle, wires: Sequence, out, batch: int, stream=None):
     arr = (ctypes.c_void_p * len(wires))(*[_ptr(w) for w in wires])
     _check(lib().merge_logits(handle, arr, len(wires), _ptr(out), batch, _stream(stream)),
            "merge_logits")
+
+
+def all_to_all(handle, direction: int, srcs: Sequence, ld_src: int, dst, ld_dst: int, stream=None):
+    arr = (ctypes.c_void_p * len(srcs))(*[_ptr(w) for w in srcs])
+    _check(lib().tp_all_to_all(handle, direction, arr, len(srcs), ld_src, _ptr(dst), ld_dst,
+                               _stream(stream)), "tp_all_to_all")
 
 
 def wire_scales_offset(cfg: TpConfig, batch: int) -> int:

@@ -64,13 +64,14 @@ enum KernelId {
     KID_ROPE_TABLE,
     KID_GEMV_LOGITS,
     KID_MERGE_LOGITS,
+    KID_A2A,
     KID_COUNT
 };
 
 const char *const kKernelNames[KID_COUNT] = {
     "rmsnorm",    "gemv_qkv", "attention", "gemv_wo",  "q8_wire",    "gemv_w13_swiglu",
     "gemv_w2",    "merge",    "ffn2d_up",  "ffn2d_down", "rope_table", "gemv_logits",
-    "merge_logits"};
+    "merge_logits", "all_to_all"};
 
 } // namespace
 
@@ -80,6 +81,7 @@ struct tp_shard {
     // (TP_LOGITS: F = vocabulary, Fs = the shard's V/T logits)
     int T, r, D, hd, Hq, Hkv, G, Hq_s, Hkv_s, F, Fs, n_qkv, esz, kv_esz;
     bool w8; // TP_Q_WEIGHTS: packed projections are int8 codes + fp32 scales per 32 k
+    int nb = 0; // TP_ATTN_BATCH: sequences per shard (Hq_s, Hkv_s then hold every head)
     // packed layout (byte offsets)
     // (TP_LOGITS: the classifier rows at o_w13 / o_sw13, the final gain at o_gatt)
     uint64_t o_wqkv, o_wo, o_w13, o_w2, o_gatt, o_gffn, o_rope, packed_bytes;
@@ -157,17 +159,70 @@ int32_t plan_logits(const tp_config &c, tp_shard &s)
     return TP_OK;
 }
 
+// Batch-sharded attention: the shard's nb = B/T sequences with every head;
+// packed holds only the RoPE table; workspace the chunk records.
+int32_t plan_attn_batch(const tp_config &c, tp_shard &s)
+{
+    const int T = c.tp_size;
+    if (c.kv_dtype != TP_F32 && c.kv_dtype != TP_BF16)
+        return fail(TP_EINVAL, "unknown kv_dtype %d", c.kv_dtype);
+    if (T < 1 || c.tp_rank < 0 || c.tp_rank >= T)
+        return fail(TP_EINVAL, "tp_rank %d outside [0, tp_size=%d)", c.tp_rank, T);
+    if (c.max_batch % T || c.max_batch > 16 * T)
+        return fail(TP_EINVAL, "TP_ATTN_BATCH: tp_size must divide max_batch, at most 16 sequences a shard");
+    if (c.quant)
+        return fail(TP_EINVAL, "TP_ATTN_BATCH has no int8 exchange");
+    if (c.n_heads < 1 || c.n_kv_heads < 1 || c.max_ctx < 1)
+        return fail(TP_EINVAL, "heads and max_ctx must be positive");
+    if (c.n_heads % c.n_kv_heads || c.n_heads % T)
+        return fail(TP_EINVAL, "n_kv_heads and tp_size must divide n_heads");
+    if (!attn_hd_supported(c.head_dim))
+        return fail(TP_EINVAL, "head_dim must be 16, 32, 48, 64 or 128");
+    if (c.n_heads / c.n_kv_heads > 8)
+        return fail(TP_EINVAL, "at most 8 q heads per kv head");
+    if (!(c.rope_theta > 0.f))
+        return fail(TP_EINVAL, "rope_theta must be > 0");
+    s.T = T;
+    s.r = c.tp_rank;
+    s.nb = c.max_batch / T;
+    s.hd = c.head_dim;
+    s.Hq = s.Hq_s = c.n_heads;
+    s.Hkv = s.Hkv_s = c.n_kv_heads;
+    s.G = s.Hq / s.Hkv;
+    s.n_qkv = (s.Hq + 2 * s.Hkv) * s.hd;
+    s.kv_esz = c.kv_dtype == TP_BF16 ? 2 : 4;
+    s.esz = 4;
+    s.w8 = false;
+    s.n_chunks = (c.max_ctx + 63) / 64;
+    if (attn_lds_bytes(s.G, s.hd, c.kv_dtype == TP_BF16, s.n_chunks) > 64 * 1024)
+        return fail(TP_EINVAL, "attention workgroup would need more than 64 KiB of LDS");
+    const uint64_t nb = s.nb;
+    s.o_wqkv = s.o_wo = s.o_w13 = s.o_w2 = s.o_gatt = s.o_gffn = 0;
+    s.o_sqkv = s.o_swo = s.o_sw13 = s.o_sw2 = 0;
+    s.o_rope = 0;
+    s.packed_bytes = align_up((uint64_t)c.max_ctx * (s.hd / 2) * 8, 256);
+    s.mfma_ok = false;
+    s.w_xfx = s.w_xfatt = s.w_xfa = s.w_skp = s.w_xn = s.w_qkv = s.w_att = s.w_a = s.w_p = 0;
+    s.w_err = 0;
+    s.w_part = 256;
+    s.ws_bytes = align_up(s.w_part + nb * s.Hq * (uint64_t)s.n_chunks * (s.hd + 4) * 4, 256);
+    s.kv_bytes = nb * s.Hkv * (uint64_t)c.max_ctx * s.hd * s.kv_esz;
+    s.wire_bytes = nb * s.Hq * s.hd * 4;
+    return TP_OK;
+}
+
 int32_t plan(const tp_config &c, tp_shard &s)
 {
-    if (c.kind != TP_LLAMA_BLOCK && c.kind != TP_FFN_2D && c.kind != TP_LOGITS)
+    if (c.kind != TP_LLAMA_BLOCK && c.kind != TP_FFN_2D && c.kind != TP_LOGITS && c.kind != TP_ATTN_BATCH)
         return fail(TP_EINVAL, "unknown kind %d", c.kind);
-    if (c.w_dtype != TP_F32 && c.w_dtype != TP_BF16)
+    const bool weights = c.kind != TP_ATTN_BATCH; // batch-sharded attention has none
+    if (weights && c.w_dtype != TP_F32 && c.w_dtype != TP_BF16)
         return fail(TP_EINVAL, "unknown w_dtype %d", c.w_dtype);
     if (c.quant & ~(TP_Q_PARTIALS | TP_Q_INPUTS | TP_Q_WEIGHTS))
         return fail(TP_EINVAL, "unknown quant bits 0x%x", c.quant);
     if (c.quant && c.quant_block != kQBlock)
         return fail(TP_EINVAL, "quant_block must be 32 (got %d)", c.quant_block);
-    if (c.max_batch < 1 || c.max_batch > (1 << 20) || c.dim < 1 || c.ffn_hidden < 1)
+    if (c.max_batch < 1 || c.max_batch > (1 << 20) || (weights && (c.dim < 1 || c.ffn_hidden < 1)))
         return fail(TP_EINVAL, "dim, ffn_hidden and max_batch must be positive");
     s.cfg = c;
     s.D = c.dim;
@@ -204,6 +259,8 @@ int32_t plan(const tp_config &c, tp_shard &s)
     }
     if (c.kind == TP_LOGITS)
         return plan_logits(c, s);
+    if (c.kind == TP_ATTN_BATCH)
+        return plan_attn_batch(c, s);
     if (c.kv_dtype != TP_F32 && c.kv_dtype != TP_BF16)
         return fail(TP_EINVAL, "unknown kv_dtype %d", c.kv_dtype);
     const int T = c.tp_size;
@@ -430,6 +487,35 @@ static int32_t load_logits(tp_shard *s, const tp_layer_weights *w, void *packed,
     return TP_OK;
 }
 
+// TP_ATTN_BATCH: no weights; the RoPE table, the error word and the caches.
+static int32_t load_attn_batch(tp_shard *s, void *packed, void *k_cache, void *v_cache,
+                               void *workspace, hipStream_t st)
+{
+    if (!k_cache || !v_cache)
+        return fail(TP_EINVAL, "load_weights: null cache pointer");
+    const void *ptrs[] = {packed, workspace, k_cache, v_cache};
+    for (const void *p : ptrs)
+        if (!aligned16(p))
+            return fail(TP_EALIGN, "load_weights: device buffer not 16-byte aligned");
+    const int32_t dv = check_device();
+    if (dv != TP_OK)
+        return dv;
+    char *P = (char *)packed;
+    RopeArgs ra{(float2 *)(P + s->o_rope), s->cfg.max_ctx, s->hd, (double)s->cfg.rope_theta};
+    int32_t rc = timed(s, KID_ROPE_TABLE, st, "rope table", [&] { return launch_rope_table(ra, st); });
+    if (rc)
+        return rc;
+    const hipError_t ce = launch_clear_u32((unsigned *)((char *)workspace + s->w_err), 1, st);
+    if (ce)
+        return hip_fail(ce, "load_weights: clear error word");
+    s->packed = P;
+    s->ws = (char *)workspace;
+    s->kc = k_cache;
+    s->vc = v_cache;
+    s->loaded = true;
+    return TP_OK;
+}
+
 int32_t load_weights(tp_shard *s, const tp_layer_weights *w, void *packed, void *k_cache,
                      void *v_cache, void *workspace, void *hip_stream)
 {
@@ -438,6 +524,8 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *w, void *packed, void 
     const bool llama = s->cfg.kind == TP_LLAMA_BLOCK;
     if (s->cfg.kind == TP_LOGITS)
         return load_logits(s, w, packed, workspace, (hipStream_t)hip_stream);
+    if (s->cfg.kind == TP_ATTN_BATCH)
+        return load_attn_batch(s, packed, k_cache, v_cache, workspace, (hipStream_t)hip_stream);
     if (!w->w1 || !w->w3 || !w->w2 ||
         (llama && (!w->wq || !w->wk || !w->wv || !w->wo || !w->g_att || !w->g_ffn || !k_cache ||
                    !v_cache)))
@@ -625,6 +713,40 @@ static int32_t logits_step(tp_shard *s, const float *x, int B, void *wire_out, c
     return timed(s, KID_WIRE, st, "q8 wire", [&] { return launch_wire(wa, st); });
 }
 
+// Batch-sharded attention of the shard's sequences (CS349E lecture 4, demo 3
+// observations): the attention kernels of the head-sharded stage run over
+// every head of nb sequences; x holds their raw q / k / v rows.
+static int32_t attn_batch_step(tp_shard *s, const float *x, const int32_t *lens, int B, float *out,
+                               const tp_taps &tp, hipStream_t st)
+{
+    if (!lens)
+        return fail(TP_EINVAL, "decode_step: attention stage needs lens");
+    AttnArgs aa{};
+    aa.qkv = x;
+    aa.lens = lens;
+    aa.kc = s->kc;
+    aa.vc = s->vc;
+    aa.rope = (const float2 *)(s->packed + s->o_rope);
+    aa.part = (float *)(s->ws + s->w_part);
+    aa.err = (unsigned *)(s->ws + s->w_err);
+    aa.att = out;
+    aa.tap_q = tp.q;
+    aa.tap_k = tp.k;
+    aa.tap_v = tp.v;
+    aa.tap_att = tp.att;
+    aa.att_xf = nullptr;
+    aa.ld_qkv = s->n_qkv;
+    aa.max_ctx = s->cfg.max_ctx;
+    aa.Hq_s = s->Hq;
+    aa.Hkv_s = s->Hkv;
+    aa.G = s->G;
+    aa.hd = s->hd;
+    aa.n_chunks = s->n_chunks;
+    aa.scale = (float)(1.0 / std::sqrt((double)s->hd));
+    return timed(s, KID_ATTN, st, "attention",
+                 [&] { return launch_attn(aa, s->cfg.kv_dtype == TP_BF16, B, st); });
+}
+
 // One stage of the shard step on input x. With mo (llama blocks only) the
 // stage's partials are also merged, mo->x_out = x + sum of mo's wires, by the
 // kernel that writes this shard's own partial (wire mo->own = wire_out).
@@ -640,10 +762,13 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         return fail(TP_EINVAL, "unknown stage %d", stage);
     if ((stage == TP_STAGE_LOGITS) != (s->cfg.kind == TP_LOGITS))
         return fail(TP_EINVAL, "TP_STAGE_LOGITS goes with (and only with) a TP_LOGITS handle");
+    if (s->cfg.kind == TP_ATTN_BATCH && stage != TP_STAGE_ATTN)
+        return fail(TP_EINVAL, "TP_ATTN_BATCH has only the attention stage");
+    const int max_rows = s->cfg.kind == TP_ATTN_BATCH ? s->nb : s->cfg.max_batch;
+    if (batch < 1 || batch > max_rows)
+        return fail(TP_EINVAL, "batch %d outside [1, %d]", batch, max_rows);
     if (mo && s->cfg.kind != TP_LLAMA_BLOCK)
         return fail(TP_EINVAL, "decode_merge_step applies to TP_LLAMA_BLOCK shards");
-    if (batch < 1 || batch > s->cfg.max_batch)
-        return fail(TP_EINVAL, "batch %d outside [1, max_batch=%d]", batch, s->cfg.max_batch);
     if (!x || !wire_out)
         return fail(TP_EINVAL, "decode_step: null x or wire_out");
     if (!aligned16(x) || !aligned16(wire_out))
@@ -682,6 +807,8 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
 
     if (s->cfg.kind == TP_LOGITS)
         return logits_step(s, (const float *)x, batch, wire_out, tp, st);
+    if (s->cfg.kind == TP_ATTN_BATCH)
+        return attn_batch_step(s, (const float *)x, lens, batch, (float *)wire_out, tp, st);
 
     const bool wbf = s->cfg.w_dtype == TP_BF16;
     const int wt = s->w8 ? WT_I8 : wbf ? WT_BF16 : WT_F32;
@@ -942,6 +1069,49 @@ int32_t merge_logits(const tp_shard *s, const void *const *wires, int32_t n_wire
     hipStream_t st = (hipStream_t)hip_stream;
     return timed(const_cast<tp_shard *>(s), KID_MERGE_LOGITS, st, "merge logits",
                  [&] { return launch_merge_logits(a, n_wires, st); });
+}
+
+int32_t tp_all_to_all(const tp_shard *s, int32_t dir, const void *const *srcs, int32_t n_srcs,
+                      int64_t ld_src, float *dst, int64_t ld_dst, void *hip_stream)
+{
+    if (!s)
+        return fail(TP_EINVAL, "tp_all_to_all: null handle");
+    if (s->cfg.kind != TP_ATTN_BATCH)
+        return fail(TP_EINVAL, "tp_all_to_all applies to TP_ATTN_BATCH shards");
+    if (dir != TP_A2A_HEADS_TO_BATCH && dir != TP_A2A_BATCH_TO_HEADS)
+        return fail(TP_EINVAL, "tp_all_to_all: unknown direction %d", dir);
+    if (!srcs || n_srcs != s->T)
+        return fail(TP_EINVAL, "tp_all_to_all: n_srcs %d, the handle has %d shards", n_srcs, s->T);
+    if (!dst)
+        return fail(TP_EINVAL, "tp_all_to_all: null dst");
+    const int64_t C = (int64_t)(s->Hq / s->T) * s->hd;
+    const int64_t need_src = dir == TP_A2A_HEADS_TO_BATCH ? C : s->T * C;
+    const int64_t need_dst = dir == TP_A2A_HEADS_TO_BATCH ? s->T * C : C;
+    if (ld_src < need_src || ld_dst < need_dst || ld_src % 4 || ld_dst % 4)
+        return fail(TP_EINVAL, "tp_all_to_all: row strides %lld / %lld (need >= %lld / %lld, multiples of 4)",
+                    (long long)ld_src, (long long)ld_dst, (long long)need_src, (long long)need_dst);
+    if (!aligned16(dst))
+        return fail(TP_EALIGN, "tp_all_to_all: dst not 16-byte aligned");
+    A2aArgs a{};
+    for (int i = 0; i < n_srcs; i++) {
+        if (!srcs[i])
+            return fail(TP_EINVAL, "tp_all_to_all: source %d is null", i);
+        if (!aligned16(srcs[i]))
+            return fail(TP_EALIGN, "tp_all_to_all: source %d not 16-byte aligned", i);
+        if (srcs[i] == (const void *)dst)
+            return fail(TP_EINVAL, "tp_all_to_all: dst aliases source %d", i);
+        a.src[i] = (const float *)srcs[i];
+    }
+    a.dst = dst;
+    a.ld_src = ld_src;
+    a.ld_dst = ld_dst;
+    a.nb = s->nb;
+    a.C = (int)C;
+    a.r = s->r;
+    a.T = s->T;
+    a.dir = dir;
+    hipStream_t st = (hipStream_t)hip_stream;
+    return timed(const_cast<tp_shard *>(s), KID_A2A, st, "all-to-all", [&] { return launch_a2a(a, st); });
 }
 
 int32_t tp_packed_int8_view(const tp_shard *s, int32_t proj, uint64_t *codes_off,

@@ -337,6 +337,18 @@ struct MergeArgs {
     int B, D;
 };
 
+// All-to-all around batch-sharded attention, shard r of T: nb rows x C
+// columns from each source i (grid.y) to its place in dst. dir 0 (heads to
+// batch): source row r*nb + b, columns [0, C) -> dst row b, columns
+// [i*C, (i+1)*C); dir 1 (batch to heads): source row b, columns
+// [r*C, (r+1)*C) -> dst row i*nb + b, columns [0, C).
+struct A2aArgs {
+    const float *src[kMaxWires];
+    float *dst;
+    int64_t ld_src, ld_dst; // row strides in elements
+    int nb, C, r, T, dir;
+};
+
 // Logits merge: wire s's rows [B][Vs] (dequantised) into columns
 // [s*Vs, (s+1)*Vs) of out [B][V]; m.wires / quant / scales_off as in a merge.
 struct LogitsMergeArgs {
@@ -389,6 +401,7 @@ bool gemv_fused_ok(int B, int K);
 hipError_t launch_wire(const WireArgs &a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
 hipError_t launch_merge_logits(const LogitsMergeArgs &a, int T, hipStream_t st);
+hipError_t launch_a2a(const A2aArgs &a, hipStream_t st);
 hipError_t launch_rope_table(const RopeArgs &a, hipStream_t st);
 hipError_t launch_quant_rows(const QuantRowsArgs &a, hipStream_t st);
 hipError_t launch_clear_u32(unsigned *p, int n, hipStream_t st);

@@ -261,6 +261,27 @@ __global__ __launch_bounds__(256) void k_merge_logits(LogitsMergeArgs a)
     *(float4 *)(a.out + b * a.V + (size_t)s * a.Vs + j) = v;
 }
 
+// All-to-all: 4 consecutive columns of one row of source blockIdx.y per
+// thread (the source index is uniform over the workgroup: a scalar load of
+// its address from the kernel arguments).
+__global__ __launch_bounds__(256) void k_a2a(A2aArgs a)
+{
+    const int i = blockIdx.y, c4 = a.C / 4;
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= a.nb * c4)
+        return;
+    const int b = t / c4, c = (t % c4) * 4;
+    size_t so, dof;
+    if (a.dir == 0) {
+        so = (size_t)(a.r * a.nb + b) * a.ld_src + c;
+        dof = (size_t)b * a.ld_dst + (size_t)i * a.C + c;
+    } else {
+        so = (size_t)b * a.ld_src + (size_t)a.r * a.C + c;
+        dof = (size_t)(i * a.nb + b) * a.ld_dst + c;
+    }
+    *(float4 *)(a.dst + dof) = *(const float4 *)(a.src[i] + so);
+}
+
 // cos / sin of p * theta^(-2i/hd) in fp64, stored fp32: [max_ctx][hd/2].
 __global__ __launch_bounds__(256) void k_rope_table(RopeArgs a)
 {
@@ -310,6 +331,17 @@ hipError_t launch_merge_logits(const LogitsMergeArgs &a, int T, hipStream_t st)
         return hipSuccess;
     hipLaunchKernelGGL(k_merge_logits, dim3((unsigned)((n4 + 255) / 256), (unsigned)T), dim3(256), 0,
                        st, a);
+    return hipGetLastError();
+}
+
+// Host-checked: C, ld_src, ld_dst multiples of 4, buffers 16-byte aligned,
+// every source holding the rows and columns the direction reads.
+hipError_t launch_a2a(const A2aArgs &a, hipStream_t st)
+{
+    const long n = (long)a.nb * (a.C / 4);
+    if (n == 0 || a.T < 1)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_a2a, dim3((unsigned)((n + 255) / 256), (unsigned)a.T), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -190,3 +190,45 @@ def split_logits_wire(w, wire: np.ndarray, B: int):
     codes = wire[:B * Vs].view(np.int8).reshape(B, Vs)
     scales = wire[off:off + B * (Vs // 32) * 4].view(np.float32).reshape(B, Vs // 32)
     return codes, scales
+
+
+def attn_batch_config(w, rank: int = 0) -> tp.TpConfig:
+    dt = {synth.F32: tp.TP_F32, synth.BF16: tp.TP_BF16}
+    return tp.make_config(kind=tp.TP_ATTN_BATCH, n_heads=w.n_heads, n_kv_heads=w.n_kv_heads,
+                          head_dim=w.head_dim, tp_size=w.tp, tp_rank=rank, max_batch=w.batch,
+                          max_ctx=w.max_ctx, kv_dtype=dt[w.kv_dtype], rope_theta=w.rope_theta)
+
+
+class AttnBatchShard:
+    """One batch shard of sequence-sharded attention with its caches (rows
+    [r*B/T, (r+1)*B/T) of the full caches)."""
+
+    def __init__(self, w, d: Dict[str, np.ndarray], rank: int):
+        self.w, self.r = w, rank
+        self.nb = w.batch // w.tp
+        rows = slice(rank * self.nb, (rank + 1) * self.nb)
+        self.sh = tp.Shard(attn_batch_config(w, rank), caches=False)
+        kc = dev_tensor(np.ascontiguousarray(d["kcache"][rows])).reshape(-1)
+        vc = dev_tensor(np.ascontiguousarray(d["vcache"][rows])).reshape(-1)
+        self.sh.load({}, k_cache=kc, v_cache=vc)
+        self.lens = dev_tensor(np.ascontiguousarray(d["lens"][rows], dtype=np.int32))
+        torch().cuda.synchronize()
+
+    def run(self, qkv, batch: Optional[int] = None, taps: bool = True):
+        """qkv: device fp32 [nb][(Hq + 2 Hkv) hd] -> (att [batch][Hq hd], taps)."""
+        t = torch()
+        w = self.w
+        B = self.nb if batch is None else batch
+        att = t.full((B, w.n_heads * w.head_dim), float("nan"), device="cuda")
+        tap = None
+        if taps:
+            f = lambda *s: t.full(s, float("nan"), device="cuda")  # noqa: E731
+            tap = {"q": f(B, w.n_heads * w.head_dim), "k": f(B, w.n_kv_heads * w.head_dim),
+                   "v": f(B, w.n_kv_heads * w.head_dim), "att": f(B, w.n_heads * w.head_dim)}
+        self.sh.step(tp.TP_STAGE_ATTN, qkv, self.lens, B, att, tap)
+        return att, tap
+
+    def cache(self):
+        w = self.w
+        shape = (self.nb, w.n_kv_heads, w.max_ctx, w.head_dim)
+        return to_np(self.sh.k_cache).reshape(shape), to_np(self.sh.v_cache).reshape(shape)

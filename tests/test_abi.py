@@ -239,3 +239,69 @@ def test_logits_stage_and_merge_host_errors():
     assert e.value.status == tp.TP_EINVAL
     tp.destroy_shard(hb)
     tp.destroy_shard(h)
+
+
+def cfg_attn_batch(**kw):
+    base = dict(kind=tp.TP_ATTN_BATCH, n_heads=64, n_kv_heads=8, head_dim=128, tp_size=16, tp_rank=3,
+                max_batch=16, max_ctx=4097, kv_dtype=tp.TP_BF16)
+    base.update(kw)
+    return tp.make_config(**base)
+
+
+def test_attn_batch_shard_sizes():
+    h, s = tp.init_shard(cfg_attn_batch())
+    assert s.kv_cache_each == 1 * 8 * 4097 * 128 * 2   # one sequence, every kv head
+    assert s.wire == 1 * 64 * 128 * 4
+    assert s.packed_weights >= 4097 * 64 * 8           # the RoPE table only
+    tp.destroy_shard(h)
+    h, s = tp.init_shard(cfg_attn_batch(tp_size=4, max_batch=16))
+    assert s.kv_cache_each == 4 * 8 * 4097 * 128 * 2
+    assert s.wire == 4 * 64 * 128 * 4
+    tp.destroy_shard(h)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(max_batch=24),                    # T does not divide the batch
+    dict(tp_size=4, max_batch=68),         # more than 16 sequences a shard
+    dict(tp_size=128, max_batch=128),      # T does not divide the q heads
+    dict(n_heads=60),                      # n_kv_heads does not divide n_heads
+    dict(n_kv_heads=4),                    # 16 q heads per kv head
+    dict(head_dim=96),
+    dict(quant=tp.TP_Q_PARTIALS),
+    dict(kv_dtype=7),
+])
+def test_attn_batch_init_rejects_bad_config(kw):
+    with pytest.raises(tp.TpError) as e:
+        tp.init_shard(cfg_attn_batch(**kw))
+    assert e.value.status == tp.TP_EINVAL
+
+
+def test_attn_batch_host_errors():
+    h, _ = tp.init_shard(cfg_attn_batch(tp_size=2, tp_rank=1, max_batch=4, n_heads=8, n_kv_heads=2, head_dim=64,
+                                        max_ctx=65))
+    fake = 0x10000  # never dereferenced: every call below fails on the host
+    with pytest.raises(tp.TpError) as e:
+        tp.decode_step(h, tp.TP_STAGE_ATTN, fake, fake, 1, fake, stream=0)
+    assert e.value.status == tp.TP_ESTATE
+    with pytest.raises(tp.TpError) as e:
+        tp.load_weights(h, {}, fake, None, fake, fake, stream=0)
+    assert e.value.status == tp.TP_EINVAL
+    C = 4 * 64  # Hq / T * hd
+    for d, srcs, ld_s, dst, ld_d, st in (
+            (2, [fake] * 2, C, fake + 4096, 2 * C, tp.TP_EINVAL),                      # direction
+            (tp.TP_A2A_HEADS_TO_BATCH, [fake] * 3, C, fake + 4096, 2 * C, tp.TP_EINVAL),  # n_srcs != T
+            (tp.TP_A2A_HEADS_TO_BATCH, [fake] * 2, C - 4, fake + 4096, 2 * C, tp.TP_EINVAL),
+            (tp.TP_A2A_HEADS_TO_BATCH, [fake] * 2, C, fake + 4096, C, tp.TP_EINVAL),   # dst too narrow
+            (tp.TP_A2A_BATCH_TO_HEADS, [fake] * 2, C, fake + 4096, C, tp.TP_EINVAL),   # src too narrow
+            (tp.TP_A2A_HEADS_TO_BATCH, [fake] * 2, C + 2, fake + 4096, 2 * C, tp.TP_EINVAL),
+            (tp.TP_A2A_HEADS_TO_BATCH, [fake] * 2, C, fake + 4100, 2 * C, tp.TP_EALIGN),
+            (tp.TP_A2A_HEADS_TO_BATCH, [fake, fake + 4096], C, fake + 4096, 2 * C, tp.TP_EINVAL)):
+        with pytest.raises(tp.TpError) as e:
+            tp.all_to_all(h, d, srcs, ld_s, dst, ld_d, stream=0)
+        assert e.value.status == st
+    hl, _ = tp.init_shard(cfg_logits())
+    with pytest.raises(tp.TpError) as e:
+        tp.all_to_all(hl, tp.TP_A2A_HEADS_TO_BATCH, [fake] * 4, 4096, fake + 4096, 4096, stream=0)
+    assert e.value.status == tp.TP_EINVAL
+    tp.destroy_shard(hl)
+    tp.destroy_shard(h)

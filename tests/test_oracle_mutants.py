@@ -35,6 +35,7 @@ MUTANTS = {
                              "memcpy(xn, x + b * D, sizeof(double) * (size_t)D);"),
     "batch_attn_kv_map": ("const int64_t base = (b * Hkv + h / G) * C * hd;",
                           "const int64_t base = (b * Hkv + h % Hkv) * C * hd;"),
+    "batch_attn_positions": ("const int64_t n_pos = L + 1;", "const int64_t n_pos = L;"),
     "a2a_source_row": ("src[((int64_t)i * B + r * nb + b) * C + c]", "src[((int64_t)i * B + b) * C + c]"),
     "merge_logits_order": ("out[b * T * Vs + i * Vs + j]", "out[b * T * Vs + (T - 1 - i) * Vs + j]"),
 }
