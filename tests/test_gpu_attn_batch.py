@@ -163,3 +163,59 @@ def test_heads_to_batch_attention_and_back():
         e = rel_l2(back[r], want)
         say(f"re-sharded attention, head shard {r}: rel-L2 {e:.3e}")
         assert e <= 1e-3
+
+
+def test_bad_length_sets_error_word_and_skips_sequence():
+    w = _small(synth.BF16, T=2, B=4, seed=2205)
+    d = synth.attn_batch_inputs(w)
+    say("batch-sharded attention: error word")
+    d["lens"] = d["lens"].copy()
+    d["lens"][3] = w.max_ctx          # shard 1's second sequence
+    sh = AttnBatchShard(w, d, 1)
+    att, _ = sh.run(dev_tensor(np.ascontiguousarray(d["qkv"][2:4])), taps=False)
+    torch.cuda.synchronize()
+    assert tp.read_error_word(sh.sh.handle) == tp.TP_DERR_LEN
+    got = to_np(att)
+    assert np.all(got[1] == 0)
+    kc = d["kcache"][2:3].copy()
+    vc = d["vcache"][2:3].copy()
+    ref = oracle.attn_batch_shard(d["qkv"][2:3], d["lens"][2:3], kc, vc, w.n_heads, w.n_kv_heads,
+                                  w.head_dim, w.kv_dtype)
+    assert rel_l2(got[0], ref[0]) <= 1e-3
+    assert tp.read_error_word(sh.sh.handle) == 0   # read clears
+
+
+def test_graph_replay_of_the_resharded_attention():
+    """All-to-all in, attention, all-to-all out captured in a HIP graph:
+    every replay (with eager work between them) is bitwise the eager result."""
+    w = _small(synth.BF16, T=2, B=4, seed=2206)
+    d = synth.attn_batch_inputs(w)
+    T, nb, hd = w.tp, w.batch // w.tp, w.head_dim
+    C, Hq, Hkv = w.n_heads // T * hd, w.n_heads, w.n_kv_heads
+    say("batch-sharded attention: graph replay")
+    qh = [dev_tensor(np.ascontiguousarray(d["qkv"][:, i * C:(i + 1) * C])) for i in range(T)]
+    shards = [AttnBatchShard(w, d, r) for r in range(T)]
+    xs = [dev_tensor(np.ascontiguousarray(d["qkv"][r * nb:(r + 1) * nb])) for r in range(T)]
+    atts = [torch.empty((nb, Hq * hd), device="cuda") for _ in range(T)]
+    back = torch.empty((w.batch, C), device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+
+    def step():
+        for r, sh in enumerate(shards):
+            tp.all_to_all(sh.sh.handle, tp.TP_A2A_HEADS_TO_BATCH, qh, C, xs[r], (Hq + 2 * Hkv) * hd)
+            sh.sh.step(tp.TP_STAGE_ATTN, xs[r], sh.lens, nb, atts[r])
+        tp.all_to_all(shards[0].sh.handle, tp.TP_A2A_BATCH_TO_HEADS, atts, Hq * hd, back, C)
+
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    eager = to_np(back).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(back).view(np.uint32), eager.view(np.uint32))
+        torch.zeros(1000, device="cuda").sum().item()  # eager work between replays

@@ -151,3 +151,38 @@ def test_decode_step_two_layers_then_logits():
     # oracle's logits up to the tolerance (exact ties may pick either)
     top = o["out"][np.arange(lw.batch), np.argmax(g["out"], axis=1)]
     assert np.all(top >= o["out"].max(axis=1) - 1e-3 * np.abs(o["out"]).max())
+
+
+def test_graph_replay_of_the_final_stage():
+    """Every shard's final stage and the merge captured in a HIP graph (int8
+    wire, batch 16: split-K with the folded norm): every replay, with eager
+    work between them, is bitwise the eager result."""
+    w = _small("logits_graph", 4096, 8192, 4, 16, synth.BF16, synth.Q_PARTIALS, seed=2003)
+    d = synth.logits_inputs(w)
+    say("final stage: graph replay")
+    L = Logits(w, d)
+    from gpu_harness import dev_tensor, to_np
+    import tensor_tp_shard_amd as tp
+    x = dev_tensor(d["x"])
+    wires = [sh.new_wire() for sh in L.shards]
+    out = torch.empty((w.batch, w.vocab), device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+
+    def step():
+        for sh, wr in zip(L.shards, wires):
+            sh.step(tp.TP_STAGE_LOGITS, x, None, w.batch, wr)
+        L.shards[0].merge_logits(wires, out, w.batch)
+
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    eager = to_np(out).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(out).view(np.uint32), eager.view(np.uint32))
+        torch.zeros(1000, device="cuda").sum().item()  # eager work between replays
