@@ -95,6 +95,18 @@ def test_llama70b_tp16_batch_shards():
         check_shard(w, d, r)
 
 
+@pytest.mark.parametrize("kv", [synth.BF16])   # an fp32 K/V chunk of hd 128 exceeds the LDS rule
+def test_llama7b_mha_batch_shard(kv):
+    """Llama-2-7B attention (MHA: one q head per kv head, the vector-FMA
+    attention kernel) sharded by sequence at TP = 4: one sequence per shard
+    with all 32 heads, 2048 cached positions."""
+    w = synth.AttnBatch(f"llama2_7b_tp4_attn_batch_b4_{kv}", n_heads=32, n_kv_heads=32, head_dim=128,
+                        tp=4, batch=4, past=(2048, 2048), kv_dtype=kv, seed=2207)
+    d = synth.attn_batch_inputs(w)
+    for r in (0, 3):
+        check_shard(w, d, r)
+
+
 @pytest.mark.parametrize("T", [2, 4])
 def test_all_to_all_both_directions(T):
     """Heads -> batch into the first columns of wider rows (the attention

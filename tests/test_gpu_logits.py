@@ -118,6 +118,48 @@ def test_llama70b_logits_b16():
     check_logits(synth.L70B_LOGITS)
 
 
+def test_llama7b_logits_b1_int8_classifier():
+    check_logits(dataclasses.replace(synth.L7B_LOGITS, name="llama2_7b_tp4_logits_b1_w8",
+                                     quant=synth.Q_WEIGHTS))
+
+
+def test_llama70b_logits_b16_int8_wire():
+    check_logits(dataclasses.replace(synth.L70B_LOGITS, name="llama2_70b_tp8_logits_b16_q8",
+                                     quant=synth.Q_PARTIALS))
+
+
+def test_decode_step_int8_wires_then_logits():
+    """The two-layer decode step with int8 wires in the layers and on the
+    logits: the layer deltas and the logits within the int8 bound, every
+    wire's codes checked against the codec of the GPU's own partial by the
+    layer and logits checks."""
+    layers = []
+    for i in range(2):
+        w = synth.small_llama(name=f"decode_q8_l{i}", dim=256, n_heads=8, n_kv_heads=4, head_dim=32,
+                              ffn_hidden=512, tp=2, batch=2, past=(3, 40), w_dtype=synth.BF16,
+                              kv_dtype=synth.BF16, quant=synth.Q_PARTIALS, seed=2120 + i)
+        layers.append((w, synth.llama_weights(w)))
+    w0 = layers[0][0]
+    lens = synth.llama_lens(w0)
+    kcs = [synth.llama_kv_cache(w, lens, "kcache") for w, _ in layers]
+    vcs = [synth.llama_kv_cache(w, lens, "vcache") for w, _ in layers]
+    lw = _small("decode_q8_logits", 256, 2048, 2, 2, quant=synth.Q_PARTIALS, seed=2130)
+    ld = synth.logits_inputs(lw)
+    x = synth.llama_x(w0)
+    say(f"decode step with int8 wires: 2 layers x T=2, B=2, lens={lens.tolist()}")
+    h = x
+    for (w, wts), kc, vc in zip(layers, kcs, vcs):
+        h = Layer(w, dict(wts, kcache=kc, vcache=vc)).run(h, lens, with_taps=False)["out"]
+    g = Logits(lw, ld).run(h, with_taps=False)
+    o = oracle.llama_decode(layers, ld["w_cls"], ld["g_final"], x, lens, [k.copy() for k in kcs],
+                            [v.copy() for v in vcs], quant_logits=synth.Q_PARTIALS,
+                            cls_dtype=lw.w_dtype)
+    e_h = rel_l2(h.astype(np.float64) - x, o["h"][-1] - x)
+    e = rel_l2(g["out"], o["out"])
+    say(f"decode step with int8 wires: last layer delta rel-L2 {e_h:.3e}, logits rel-L2 {e:.3e}")
+    assert e_h <= 2e-2 and e <= 2e-2
+
+
 def test_decode_step_two_layers_then_logits():
     """A whole decode step: two layers of every shard in turn, each fed the
     previous layer's merged output, then the final stage, against the
