@@ -72,15 +72,20 @@ __device__ __forceinline__ float dot_chunk(const u32x4 &w, const float4 *xp, flo
     return acc;
 }
 
-// sum over the 256 threads of a block, in a fixed order
-__device__ __forceinline__ float block_sum(float v, float *red4)
+// sum over the NW waves of a block, in a fixed order (pairwise)
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float *red)
 {
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     v = group_sum<64>(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0)
-        red4[threadIdx.x >> 6] = v;
+        red[threadIdx.x >> 6] = v;
     __syncthreads();
-    return (red4[0] + red4[1]) + (red4[2] + red4[3]);
+    const float s4 = (red[0] + red[1]) + (red[2] + red[3]);
+    if constexpr (NW == 8)
+        return s4 + ((red[4] + red[5]) + (red[6] + red[7]));
+    return s4;
 }
 
 // Staging of the activation rows x[b][0..K) (b < B) into LDS as fp32; with
@@ -89,18 +94,19 @@ __device__ __forceinline__ float block_sum(float v, float *red4)
 // float4 = 8 lanes). Row 0 and the gains are loaded by stage_x_issue BEFORE
 // the weight loads are issued, so they return first (vector loads return in
 // order) and the norm is computed while the weights are still in flight.
-constexpr int kXV = 4; // float4 of a row per thread (K <= 4096)
+constexpr int kXV = 4; // float4 of a row per thread (K <= 4096 with 256 or more threads)
 
 struct XRegs {
     float4 x[kXV], g[kXV];
 };
 
+template <int NT>
 __device__ __forceinline__ void stage_x_issue(const GemvArgs &a, XRegs &r)
 {
     const int n4 = a.K / 4;
 #pragma unroll
     for (int i = 0; i < kXV; i++) {
-        const int e = threadIdx.x + 256 * i;
+        const int e = threadIdx.x + NT * i;
         if (e < n4) {
             r.x[i] = ((const float4 *)a.x)[e];
             if (a.g)
@@ -109,6 +115,7 @@ __device__ __forceinline__ void stage_x_issue(const GemvArgs &a, XRegs &r)
     }
 }
 
+template <int NT>
 __device__ void stage_x_finish(const GemvArgs &a, XRegs &r, float *xs, float *red4)
 {
     const int n4 = a.K / 4;
@@ -118,7 +125,7 @@ __device__ void stage_x_finish(const GemvArgs &a, XRegs &r, float *xs, float *re
             const float4 *src = (const float4 *)(a.x + (size_t)b * a.ldx);
 #pragma unroll
             for (int i = 0; i < kXV; i++) {
-                const int e = threadIdx.x + 256 * i;
+                const int e = threadIdx.x + NT * i;
                 if (e < n4)
                     r.x[i] = src[e];
             }
@@ -126,7 +133,7 @@ __device__ void stage_x_finish(const GemvArgs &a, XRegs &r, float *xs, float *re
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < kXV; i++) {
-            const int e = threadIdx.x + 256 * i;
+            const int e = threadIdx.x + NT * i;
             if (e < n4) {
                 const float4 v = r.x[i];
                 ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
@@ -135,19 +142,19 @@ __device__ void stage_x_finish(const GemvArgs &a, XRegs &r, float *xs, float *re
         if (!a.g) {
 #pragma unroll
             for (int i = 0; i < kXV; i++) {
-                const int e = threadIdx.x + 256 * i;
+                const int e = threadIdx.x + NT * i;
                 if (e < n4)
                     dst[e] = r.x[i];
             }
             continue;
         }
-        ss = block_sum(ss, red4);
+        ss = block_sum<NT / 64>(ss, red4);
         const float rr = 1.0f / sqrtf(ss / (float)a.K + a.eps);
         float4 *tap = (a.xn_tap && blockIdx.x == 0) ? (float4 *)(a.xn_tap + (size_t)b * a.K) : nullptr;
 #pragma unroll
         for (int i = 0; i < kXV; i++) {
-            const int e = threadIdx.x + 256 * i;
-            if (256 * i >= n4)
+            const int e = threadIdx.x + NT * i;
+            if (NT * i >= n4)
                 break; // uniform: no lane of this pass holds an element
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             if (e < n4) {
@@ -171,21 +178,22 @@ __device__ void stage_x_finish(const GemvArgs &a, XRegs &r, float *xs, float *re
     }
 }
 
-template <int WT, int NB, int RPW, int EPI, bool MO>
-__global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
+// NW waves per workgroup, one (RPW rows) per wave
+template <int WT, int NB, int RPW, int EPI, bool MO, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemv_lds(GemvArgs a)
 {
     constexpr int V = wt_per_chunk(WT); // elements per 16-byte chunk
     constexpr int KC = 8;           // chunk iterations per lane kept in flight
     extern __shared__ float xs[];   // [B][K]
-    __shared__ float red4[4];
+    __shared__ float red4[NW];
     const int tid = threadIdx.x, lane = tid & 63;
     // the wave index twice: uniform for the weight buffers, and as a lane
     // value for the merge's element index (proven uniform, that address
     // would turn the merge preloads into scalar loads the wave waits on
     // before it can issue its weights)
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int row0 = (blockIdx.x * 4 + wv) * RPW;
-    const int row0v = (blockIdx.x * 4 + (tid >> 6)) * RPW;
+    const int row0 = (blockIdx.x * NW + wv) * RPW;
+    const int row0v = (blockIdx.x * NW + (tid >> 6)) * RPW;
     const bool active = row0 < a.N;
     const int nchunk = a.K / V;
     // one buffer per weight row (an inactive wave's covers nothing)
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
     }
 
     XRegs xr;
-    stage_x_issue(a, xr);
+    stage_x_issue<64 * NW>(a, xr);
     __builtin_amdgcn_sched_barrier(0); // the activation loads stay ahead of the weights
     u32x4 w[RPW][KC];
     float sc[RPW][KC];
@@ -228,7 +236,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a)
         }
     };
     load_w(0);
-    stage_x_finish(a, xr, xs, red4);
+    stage_x_finish<64 * NW>(a, xr, xs, red4);
     __syncthreads();
 
     float acc[RPW][NB];
@@ -392,21 +400,28 @@ bool gemv_fused_ok(int B, int K) { return B <= 4 && K <= 4 * 256 * kXV && gemv_l
 // One row per wave for the plain-store projections (QKV, W_O, W2): twice the
 // waves of two rows per wave, each with a whole row of loads in flight
 // (7B shard step 42.2 -> 41.1 us); the SwiGLU projection pairs W1_f / W3_f
-// rows in one wave.
+// rows in one wave. Four waves a workgroup; eight for a plain store of at
+// least 6144 rows (the 7B shard's 8000 classifier rows: 14.5 -> 14.1 us, the
+// activations staged by half as many workgroups), where the grid still has
+// three workgroups a CU: with eight waves the W1/W3 projection (344
+// workgroups) went 11.2 -> 11.9 us and the QKV one 8.0 -> 8.1 us; two waves
+// were slower everywhere (W1/W3 15.6 us).
 template <int WT, int NB>
 static hipError_t launch_lds(const GemvArgs &a, int epi, hipStream_t st)
 {
     const size_t sm = gemv_lds_bytes(a.B, a.K);
-    const dim3 block(256);
     if (epi == EPI_SWIGLU) {
         const dim3 grid((a.N + 4 * kRPW - 1) / (4 * kRPW));
-        hipLaunchKernelGGL((k_gemv_lds<WT, NB, kRPW, EPI_SWIGLU, false>), grid, block, sm, st, a);
+        hipLaunchKernelGGL((k_gemv_lds<WT, NB, kRPW, EPI_SWIGLU, false, 4>), grid, dim3(256), sm, st, a);
+    } else if (a.mo.n_wires) {
+        hipLaunchKernelGGL((k_gemv_lds<WT, NB, 1, EPI_STORE, true, 4>), dim3((a.N + 3) / 4), dim3(256), sm,
+                           st, a);
+    } else if (a.N >= 6144) {
+        hipLaunchKernelGGL((k_gemv_lds<WT, NB, 1, EPI_STORE, false, 8>), dim3((a.N + 7) / 8), dim3(512), sm,
+                           st, a);
     } else {
-        const dim3 grid((a.N + 3) / 4);
-        if (a.mo.n_wires)
-            hipLaunchKernelGGL((k_gemv_lds<WT, NB, 1, EPI_STORE, true>), grid, block, sm, st, a);
-        else
-            hipLaunchKernelGGL((k_gemv_lds<WT, NB, 1, EPI_STORE, false>), grid, block, sm, st, a);
+        hipLaunchKernelGGL((k_gemv_lds<WT, NB, 1, EPI_STORE, false, 4>), dim3((a.N + 3) / 4), dim3(256), sm,
+                           st, a);
     }
     return hipGetLastError();
 }
