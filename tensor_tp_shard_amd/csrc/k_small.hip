@@ -153,9 +153,9 @@ __global__ __launch_bounds__(kNormThreads) void k_rmsnorm(NormArgs a)
 // x_out = residual + sum of the wires in order, its own wire's value being
 // the dequantised code it just wrote (the other wires' elements are requested
 // together with p). The wires of a quantised exchange are all int8.
-__global__ __launch_bounds__(256) void k_wire(WireArgs a)
+__global__ __launch_bounds__(64) void k_wire(WireArgs a)
 {
-    const int blk = blockIdx.x * 8 + (threadIdx.x >> 5);
+    const int blk = blockIdx.x * 2 + (threadIdx.x >> 5);
     const int nblk = a.B * (a.D / kQBlock);
     const int lane = threadIdx.x & 31;
     const bool ok = blk < nblk;
@@ -309,8 +309,10 @@ hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st)
 
 hipError_t launch_wire(const WireArgs &a, hipStream_t st)
 {
+    // two 32-element blocks (one wave) a workgroup: the 128 blocks of a 7B
+    // row spread over 64 CUs rather than 16
     const int nblk = a.B * (a.D / kQBlock);
-    hipLaunchKernelGGL(k_wire, dim3((nblk + 7) / 8), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_wire, dim3((nblk + 1) / 2), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 
