@@ -7,13 +7,24 @@ the T-1 wires the other ranks produced, standing in for what would arrive
 over xGMI) -> FFN stage (RMSNorm, W1/W3 + SwiGLU, W2) -> merge. By default
 each merge is done by the kernel that produces rank 0's own partial
 (decode_merge_step); --merge separate runs it as a kernel of its own
-(merge_partials). The output of a step is the next step's input. R layer copies (distinct weights, caches
-and workspaces in HBM, R x step bytes > 2 x the 256 MB Infinity Cache) are
-used in rotation so no step reads what the previous one left in the cache.
+(merge_partials). The output of a step is the next step's input. R layer
+copies (distinct weights, caches and workspaces in HBM, R x step bytes > 3 x
+the 256 MB Infinity Cache) are used in rotation, step i on copy i mod R, so
+no step reads what the previous one left in the cache.
 
-Prints ONE JSON line (rank 0). Inputs are seeded synthetic tensors of the
-workload's shapes (no trained weights exist here), resident in HBM before the
-timed region starts.
+Timing: one pass over the R copies is captured as a HIP graph (and the first
+k mod R steps as another), so exactly --steps steps run per timed repeat,
+after exactly --warmup untimed steps; each repeat is bracketed by a device
+synchronisation and HIP events on the launch stream, and `value` is the
+median of --repeats repeats (min and median both reported). Per-kernel
+durations come from the library's HIP event pairs around each launch in an
+eager pass that starts behind a device-side sleep, so the host's launch
+calls never leave the GPU idle inside a pair.
+
+Prints ONE JSON line: the primary workload (the 7B shard by default) with
+the other configurations of the same metric as sub-results under "configs".
+Inputs are seeded synthetic tensors of the workloads' shapes (no trained
+weights exist here), resident in HBM before the timed region starts.
 """
 from __future__ import annotations
 
@@ -21,9 +32,10 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
-from typing import Optional
+from typing import Callable, Dict, List, Optional
 
 import numpy as np
 
@@ -35,7 +47,9 @@ import synth  # noqa: E402
 METRIC = "decode layer-steps/s per TP shard + achieved HBM GB/s (% peak), 7B/70B shapes"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-
+# the other configurations of the metric, reported next to the primary one
+SUB_CONFIGS = ("tiny_llama_tp2_b1", "llama2_7b_tp4_b1_q8", "llama2_70b_tp8_b16",
+               "palm540b_ffn2d_b512", "palm540b_ffn2d_prefill8192")
 
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -101,6 +115,222 @@ def dev(a):
     return torch.from_numpy(a).cuda()
 
 
+# ---------------------------------------------------------------- timing
+
+class Stepper:
+    """Runs k steps of a workload whose step i uses copy i mod R: each full
+    pass over the R copies replays one captured graph, the k mod R steps
+    left replay a graph of the first k mod R steps (eager mode: plain
+    calls). Graphs are captured on first use, outside any timed region."""
+
+    def __init__(self, step: Callable[[int], None], R: int, mode: str, stream):
+        self.step, self.R, self.mode, self.stream = step, R, mode, stream
+        self.graphs = {}
+
+    def prepare(self, *counts):
+        import torch
+        with torch.cuda.stream(self.stream):
+            for i in range(self.R):  # one eager pass before any capture
+                self.step(i)
+        torch.cuda.synchronize()
+        if self.mode == "graph":
+            for k in counts:
+                for n in {self.R if k >= self.R else 0, k % self.R} - {0}:
+                    self._graph(n)
+
+    def _graph(self, n: int):
+        import torch
+        if n not in self.graphs:
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=self.stream):
+                for i in range(n):
+                    self.step(i)
+            torch.cuda.synchronize()
+            self.graphs[n] = g
+        return self.graphs[n]
+
+    def run(self, k: int):
+        import torch
+        with torch.cuda.stream(self.stream):
+            if self.mode == "eager":
+                for i in range(k):
+                    self.step(i % self.R)
+                return
+            full, rem = divmod(k, self.R)
+            if full:
+                g = self._graph(self.R)
+                for _ in range(full):
+                    g.replay()
+            if rem:
+                self._graph(rem).replay()
+
+
+def time_steps(st: Stepper, steps: int, warmup: int, repeats: int) -> List[float]:
+    """Milliseconds of `steps` steps, `repeats` times, after `warmup` steps."""
+    import torch
+    st.prepare(steps, warmup)
+    st.run(warmup)
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st.stream)
+        st.run(steps)
+        e1.record(st.stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    return out
+
+
+_SLEEP_CYCLES_PER_MS = None
+
+
+def _sleep_cycles_per_ms() -> float:
+    """Calibrates torch.cuda._sleep (a device-side spin) in cycles per ms."""
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        import torch
+        n = 2_000_000
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(n)  # first call loads the kernel
+        torch.cuda.synchronize()
+        e0.record()
+        torch.cuda._sleep(n)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = n / max(e0.elapsed_time(e1), 1e-3)
+    return _SLEEP_CYCLES_PER_MS
+
+
+def kernel_times(handles, st: Stepper, steps: int, names) -> Dict[str, float]:
+    """Average duration (us) of each named kernel over an eager pass of
+    `steps` steps, from the library's event pairs on the launch stream. The
+    pass is enqueued behind a device-side sleep longer than the host needs to
+    enqueue it, so the kernels run back to back as in the graph."""
+    import torch
+    import tensor_tp_shard_amd as tp
+    ids = tp.kernel_names()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(st.stream):
+        for i in range(steps):
+            st.step(i % st.R)
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - t0) * 1e3
+    out = {}
+    for name in names:
+        kid = ids.index(name)
+        for h in handles:
+            tp.kernel_timing_arm(h, kid)
+        with torch.cuda.stream(st.stream):
+            torch.cuda._sleep(int(_sleep_cycles_per_ms() * (3 * host_ms + 2)))
+            for i in range(steps):
+                st.step(i % st.R)
+        torch.cuda.synchronize()
+        tot, n = 0.0, 0
+        for h in handles:
+            t_, n_ = tp.kernel_timing_read(h)
+            tot += t_
+            n += n_
+            tp.kernel_timing_arm(h, -1)
+        if n:
+            out[name] = round(tot / n * 1e3, 3)
+    return out
+
+
+def measured_peaks() -> Dict[str, float]:
+    """The denominators measured on this GPU with library code: a 2 GiB
+    read stream (the best of torch's sum / amax reductions) and a large bf16
+    GEMM (hipBLASLt through torch.matmul, 8192^3)."""
+    import torch
+    x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")  # 2 GiB
+    best = 0.0
+    for op in (torch.sum, torch.amax):
+        for _ in range(2):
+            op(x)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            op(x)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 5 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    tf = 10 * 2 * 8192 ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBps": round(best, 1), "bf16_gemm_TFLOPs": round(tf, 1),
+            "how": "2 GiB fp32 read by torch.sum / torch.amax (best); bf16 8192^3 torch.matmul"}
+
+
+def summarize(ms: List[float], steps: int, unit_per_step: float = 1.0) -> dict:
+    med, mn = statistics.median(ms), min(ms)
+    return {"value": round(unit_per_step * steps / (med * 1e-3), 2),
+            "ms_per_step": round(med / steps, 6), "ms_per_step_min": round(mn / steps, 6),
+            "ms_per_step_median": round(med / steps, 6), "repeats": len(ms)}
+
+
+# ---------------------------------------------------------------- oracle baseline
+
+def cpu_info() -> dict:
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+def cpu_baseline(one_step: Callable[[], None], seconds: float, unit: str, per_step: float,
+                 what: str) -> dict:
+    """The oracle as it stands, timed on this host: the OpenMP build (the
+    same source, independent rows on every thread; `value`) and the plain
+    single-threaded build, each repeating one step of `what` for about
+    `seconds` (at least once). per_step scales steps to the unit."""
+    import oracle
+
+    def run(omp: bool):
+        threads = oracle.use_threads(omp)
+        n, t0 = 0, time.perf_counter()
+        while True:
+            one_step()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        return n, el, threads
+
+    n1, el1, _ = run(False)
+    nm, elm, threads = run(True)
+    oracle.use_threads(False)
+    return {"value": round(per_step * nm / elm, 6), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{nm} {what} by the fp64 C oracle built with OpenMP ({threads} threads) "
+                      f"in {elm:.1f} s",
+            "single_thread": {"value": round(per_step * n1 / el1, 6), "cores": 1,
+                              "sample": f"{n1} {what} by the plain single-threaded build in "
+                                        f"{el1:.1f} s"},
+            **cpu_info()}
+
+
+# ---------------------------------------------------------------- Llama shard layer step
+
 def llama_config(tp, w, rank):
     dt = {synth.F32: tp.TP_F32, synth.BF16: tp.TP_BF16}
     return tp.make_config(kind=tp.TP_LLAMA_BLOCK, dim=w.dim, n_heads=w.n_heads,
@@ -161,15 +391,19 @@ def llama_rank0(w):
     return d, shard, s0, x0, lens, wa[1:], wf[1:]
 
 
-def run_llama(args, w):
+def wdtype(w):
+    return "int8" if w.quant & synth.Q_WEIGHTS else "bf16" if w.w_dtype == synth.BF16 else "f32"
+
+
+def run_llama(args, w, with_cpu=True):
     import torch
     import tensor_tp_shard_amd as tp
     T, B = w.tp, w.batch
     d, shard, s0, x0, lens, other_att, other_ffn = llama_rank0(w)
-    # R copies of rank 0's layer
     wbytes, kvbytes, w13bytes = llama_bytes(w, d["lens"])
     step_bytes = wbytes + kvbytes
-    R = args.copies or max(2, int(np.ceil(3 * 256e6 / step_bytes)))
+    # (at most 64: the 2 MB tiny block is latency-bound, its copies stay cached)
+    R = args.copies or min(64, max(2, int(np.ceil(3 * 256e6 / step_bytes))))
     copies = [s0] + [shard(0) for _ in range(R - 1)]
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -179,82 +413,36 @@ def run_llama(args, w):
     hs_ = [torch.empty_like(x0) for _ in range(R)]
     xs[0].copy_(x0)
 
-    def one_pass_fused():
+    def step_fused(r):
         # layer copy r reads xs[r] and writes xs[r+1]; each merge is done by
         # the kernel that produces rank 0's own partial of that stage
-        for r, c in enumerate(copies):
-            xin, xout = xs[r], xs[(r + 1) % R]
-            c.step_merge(tp.TP_STAGE_ATTN, xin, lens, B, wires_a[r], [wires_a[r]] + other_att,
-                         hs_[r])
-            c.step_merge(tp.TP_STAGE_FFN, hs_[r], None, B, wires_f[r], [wires_f[r]] + other_ffn,
-                         xout)
+        c, xin, xout = copies[r], xs[r], xs[(r + 1) % R]
+        c.step_merge(tp.TP_STAGE_ATTN, xin, lens, B, wires_a[r], [wires_a[r]] + other_att, hs_[r])
+        c.step_merge(tp.TP_STAGE_FFN, hs_[r], None, B, wires_f[r], [wires_f[r]] + other_ffn, xout)
 
-    def one_pass_separate():
-        # layer copy r reads xs[r] and writes xs[r+1]; the pass ends where it began
-        for r, c in enumerate(copies):
-            xin, xout = xs[r], xs[(r + 1) % R]
-            c.step(tp.TP_STAGE_ATTN, xin, lens, B, wires_a[r])
-            c.merge(tp.TP_STAGE_ATTN, [wires_a[r]] + other_att, xin, hs_[r], B)
-            c.step(tp.TP_STAGE_FFN, hs_[r], None, B, wires_f[r])
-            c.merge(tp.TP_STAGE_FFN, [wires_f[r]] + other_ffn, hs_[r], xout, B)
+    def step_separate(r):
+        c, xin, xout = copies[r], xs[r], xs[(r + 1) % R]
+        c.step(tp.TP_STAGE_ATTN, xin, lens, B, wires_a[r])
+        c.merge(tp.TP_STAGE_ATTN, [wires_a[r]] + other_att, xin, hs_[r], B)
+        c.step(tp.TP_STAGE_FFN, hs_[r], None, B, wires_f[r])
+        c.merge(tp.TP_STAGE_FFN, [wires_f[r]] + other_ffn, hs_[r], xout, B)
 
-    one_pass = one_pass_fused if args.merge == "fused" else one_pass_separate
-
-    passes = max(1, args.steps // R)
-    steps = passes * R
-    wpasses = max(1, args.warmup // R)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
-    graph = None
-    with torch.cuda.stream(stream):
-        for _ in range(2):
-            one_pass()
-        if args.mode == "graph":
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=stream):
-                one_pass()
-        run = graph.replay if graph is not None else one_pass
-        for _ in range(wpasses):
-            run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(passes):
-            run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        assert torch.isfinite(xs[0]).all().item(), "non-finite layer output"
-        # dominant-kernel timing: library-recorded HIP events around each launch of the
-        # up-projection kernel, on the stream it is launched on, over the same number of steps
-        kid = tp.kernel_names().index("gemv_w13_swiglu")
-        for c in copies:
-            tp.kernel_timing_arm(c.handle, kid)
-        for _ in range(passes):
-            one_pass()
-        torch.cuda.synchronize()
-        tot, n = 0.0, 0
-        for c in copies:
-            t_, n_ = tp.kernel_timing_read(c.handle)
-            tot += t_
-            n += n_
-            tp.kernel_timing_arm(c.handle, -1)
-    ms_step = ms / steps
-    k_ms = tot / max(n, 1)
-    achieved = w13bytes / (k_ms * 1e-3) / 1e9
+    st = Stepper(step_fused if args.merge == "fused" else step_separate, R, args.mode, stream)
+    ms = time_steps(st, args.steps, args.warmup, args.repeats)
+    assert torch.isfinite(xs[0]).all().item(), "non-finite layer output"
+    names = ["rmsnorm", "gemv_qkv", "attention", "gemv_wo", "q8_wire", "gemv_w13_swiglu", "gemv_w2",
+             "merge"]
+    kt = kernel_times([c.handle for c in copies], st, max(args.steps, R), names)
+    s = summarize(ms, args.steps)
+    ms_step = s["ms_per_step"]
+    k_us = kt["gemv_w13_swiglu"]
+    achieved = w13bytes / (k_us * 1e-6) / 1e9
     res = {
-        "metric": METRIC,
-        "value": round(1e3 / ms_step, 1),
-        "unit": "layer-steps/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": wpasses * R,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int8" if w.quant & synth.Q_WEIGHTS else "bf16" if w.w_dtype == synth.BF16 else "f32",
+        "metric": METRIC, "value": s["value"], "unit": "layer-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wdtype(w),
         "data": "synthetic",
         "config": {"workload": w.name, "shard": f"rank 0 of TP={T}", "batch": B,
                    "kv_positions": [int(d["lens"].min()), int(d["lens"].max())],
@@ -262,23 +450,26 @@ def run_llama(args, w):
                    "merge": ("fused into the producer of rank 0's partial" if args.merge == "fused"
                              else "kernel of its own"),
                    "step_bytes": int(step_bytes)},
+        "ms_per_step_min": s["ms_per_step_min"], "ms_per_step_median": s["ms_per_step_median"],
+        "repeats": s["repeats"],
         "achieved_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "kernels_us": kt,
         "roofline": {"kernel": "gemv_w13_swiglu", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(
                          f"traffic_gemv_w13_swiglu_{w.name}.md",
                          GEMV_MFMA_SOURCES if w.w_dtype == synth.BF16 and B > 4 else GEMV_SOURCES),
-                     "bytes_per_launch": int(w13bytes),
-                     "avg_launch_us": round(k_ms * 1e3, 3), "launches": n},
+                     "bytes_per_launch": int(w13bytes), "avg_launch_us": k_us},
     }
-    if not args.no_cpu_baseline:
+    if with_cpu and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_llama(w, d, args.cpu_seconds)
     return res
 
 
-def cpu_baseline_llama(w, d, seconds):
-    """The fp64 oracle, as it stands, doing rank 0's layer step on the host."""
+def llama_oracle_step(w, d):
+    """One rank-0 layer step of the oracle (attention stage, wire, merge, FFN
+    stage, wire, merge; the other ranks' partials taken as zeros)."""
     import dataclasses
     import oracle
     x = d["x"].astype(np.float64)
@@ -291,24 +482,26 @@ def cpu_baseline_llama(w, d, seconds):
             d[k] = oracle.q8_weights(d[k], w.w_dtype)[2]
         w = dataclasses.replace(w, w_dtype=synth.F32, quant=w.quant & ~synth.Q_WEIGHTS)
     zeros = np.zeros((w.tp - 1, w.batch, w.dim))
-    n, t0 = 0, time.perf_counter()
-    while True:
+
+    def one():
         a = oracle.attn_shard(w, d, 0, x, d["lens"], kc, vc)
         da, _, _ = oracle.wire(a["p"], w.quant)
         h = oracle.merge(x, np.concatenate([da[None], zeros]))
         f = oracle.ffn_shard(w, d, 0, h)
         df, _, _ = oracle.wire(f["p"], w.quant)
         oracle.merge(h, np.concatenate([df[None], zeros]))
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": round(n / el, 3), "unit": "layer-steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} rank-0 shard layer steps of {w.name} (attention stage, wire, merge, "
-                      f"FFN stage, wire, merge) by the single-threaded fp64 C oracle in {el:.1f} s"}
+    return one
 
 
-def run_ffn2d(args, w):
+def cpu_baseline_llama(w, d, seconds):
+    return cpu_baseline(llama_oracle_step(w, d), seconds, "layer-steps/s", 1.0,
+                        f"rank-0 shard layer steps of {w.name} (attention stage, wire, merge, "
+                        f"FFN stage, wire, merge)")
+
+
+# ---------------------------------------------------------------- PaLM 2D FFN block
+
+def run_ffn2d(args, w, with_cpu=True):
     """One step = the block's up-projection + SwiGLU and down-projection for
     the workload's token count, over R rotating weight copies."""
     import torch
@@ -331,78 +524,50 @@ def run_ffn2d(args, w):
     flops = 2.0 * B * E * F * 3
     up_flops = 2.0 * B * E * 2 * F
 
-    def one_pass():
-        for r, c in enumerate(copies):
-            c.step(tp.TP_STAGE_FFN, x, None, B, ys[r])
+    def step(r):
+        copies[r].step(tp.TP_STAGE_FFN, x, None, B, ys[r])
 
-    passes = max(1, args.steps // R)
-    wpasses = max(1, args.warmup // R)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
-        one_pass()
-        graph = None
-        if args.mode == "graph":
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=stream):
-                one_pass()
-        run = graph.replay if graph is not None else one_pass
-        for _ in range(wpasses):
-            run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(passes):
-            run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        kid = tp.kernel_names().index("ffn2d_up")
-        for c in copies:
-            tp.kernel_timing_arm(c.handle, kid)
-        for _ in range(passes):
-            one_pass()
-        torch.cuda.synchronize()
-        tot, n = 0.0, 0
-        for c in copies:
-            t_, n_ = tp.kernel_timing_read(c.handle)
-            tot += t_
-            n += n_
-            tp.kernel_timing_arm(c.handle, -1)
-    steps = passes * R
-    ms_step = ms / steps
-    k_ms = tot / max(n, 1)
-    ach = up_flops / (k_ms * 1e-3) / 1e12
+    st = Stepper(step, R, args.mode, stream)
+    ms = time_steps(st, args.steps, args.warmup, args.repeats)
+    kt = kernel_times([c.handle for c in copies], st, max(args.steps, R), ["ffn2d_up", "ffn2d_down"])
+    s = summarize(ms, args.steps)
+    ms_step = s["ms_per_step"]
+    ach = up_flops / (kt["ffn2d_up"] * 1e-6) / 1e12
     res = {
-        "metric": METRIC, "value": round(1e3 / ms_step, 2), "unit": "ffn-block-steps/s",
-        "n_gpus": 1, "steps": steps, "warmup": wpasses * R, "ms_per_step": round(ms_step, 5),
+        "metric": METRIC, "value": s["value"], "unit": "ffn-block-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": B, "E_block": E, "F_block": F, "layer_copies": R,
                    "launch": args.mode},
+        "ms_per_step_min": s["ms_per_step_min"], "ms_per_step_median": s["ms_per_step_median"],
+        "repeats": s["repeats"],
         "achieved_TFLOPs": round(flops / (ms_step * 1e-3) / 1e12, 1),
         "mfma_frac": round(flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "kernels_us": kt,
         "roofline": {"kernel": "ffn2d_up", "bound": "mfma", "achieved": round(ach, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(f"traffic_ffn2d_up_{w.name}.md", FFN2D_SOURCES),
-                     "flops_per_launch": up_flops, "avg_launch_us": round(k_ms * 1e3, 3),
-                     "launches": n},
+                     "flops_per_launch": up_flops, "avg_launch_us": kt["ffn2d_up"]},
     }
-    if not args.no_cpu_baseline:
+    if with_cpu and not args.no_cpu_baseline:
         import oracle
-        rows, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < args.cpu_seconds:
-            oracle.ffn2d(d["x"], d["w_gate"], d["w_in"], d["w_out"], row0=rows % B, nrows=1)
-            rows += 1
-        el = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": round(rows / el / B, 6), "unit": "ffn-block-steps/s",
-                               "cores": 1, "kind": "oracle",
-                               "sample": f"{rows} token rows of {w.name} by the single-threaded "
-                                         f"fp64 C oracle in {el:.1f} s, scaled to {B} rows"}
+        rows = [0]
+        nr = 16
+
+        def one():  # a few token rows of the block (rows are independent)
+            oracle.ffn2d(d["x"], d["w_gate"], d["w_in"], d["w_out"], row0=rows[0] % B, nrows=nr)
+            rows[0] += nr
+        res["cpu_baseline"] = cpu_baseline(one, args.cpu_seconds, "ffn-block-steps/s", nr / B,
+                                           f"groups of {nr} token rows of {w.name}, scaled to "
+                                           f"{B} rows,")
     return res
 
+
+# ---------------------------------------------------------------- final stage
 
 def logits_config(tp, w, rank):
     dt = {synth.F32: tp.TP_F32, synth.BF16: tp.TP_BF16}
@@ -411,7 +576,7 @@ def logits_config(tp, w, rank):
                           quant_block=32, norm_eps=w.norm_eps)
 
 
-def run_logits(args, w):
+def run_logits(args, w, with_cpu=True):
     """The final stage of rank 0: final RMSNorm + its V/T logits (+ int8 wire),
     then the merge of all T slices into full rows (the other ranks' wires
     computed once beforehand, standing in for what would arrive). R copies of
@@ -446,95 +611,54 @@ def run_logits(args, w):
     wires = [c.new_wire() for c in copies]
     outs = [torch.empty((B, w.vocab), dtype=torch.float32, device="cuda") for _ in range(R)]
 
-    def one_pass():
-        for r, c in enumerate(copies):
-            c.step(tp.TP_STAGE_LOGITS, x, None, B, wires[r])
-            c.merge_logits([wires[r]] + other_w, outs[r], B)
+    def step(r):
+        copies[r].step(tp.TP_STAGE_LOGITS, x, None, B, wires[r])
+        copies[r].merge_logits([wires[r]] + other_w, outs[r], B)
 
-    passes = max(1, args.steps // R)
-    steps = passes * R
-    wpasses = max(1, args.warmup // R)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
-    graph = None
-    with torch.cuda.stream(stream):
-        for _ in range(2):
-            one_pass()
-        if args.mode == "graph":
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=stream):
-                one_pass()
-        run = graph.replay if graph is not None else one_pass
-        for _ in range(wpasses):
-            run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(passes):
-            run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        assert torch.isfinite(outs[0]).all().item(), "non-finite logits"
-        kid = tp.kernel_names().index("gemv_logits")
-        for c in copies:
-            tp.kernel_timing_arm(c.handle, kid)
-        for _ in range(passes):
-            one_pass()
-        torch.cuda.synchronize()
-        tot, n = 0.0, 0
-        for c in copies:
-            t_, n_ = tp.kernel_timing_read(c.handle)
-            tot += t_
-            n += n_
-            tp.kernel_timing_arm(c.handle, -1)
-    ms_step = ms / steps
-    k_ms = tot / max(n, 1)
-    achieved = cls_bytes / (k_ms * 1e-3) / 1e9
+    st = Stepper(step, R, args.mode, stream)
+    ms = time_steps(st, args.steps, args.warmup, args.repeats)
+    assert torch.isfinite(outs[0]).all().item(), "non-finite logits"
+    kt = kernel_times([c.handle for c in copies], st, max(args.steps, R),
+                      ["rmsnorm", "gemv_logits", "q8_wire", "merge_logits"])
+    s = summarize(ms, args.steps)
+    ms_step = s["ms_per_step"]
+    achieved = cls_bytes / (kt["gemv_logits"] * 1e-6) / 1e9
     res = {
         "metric": "final-stage steps/s of one TP shard (final RMSNorm, vocabulary-split logits, "
                   "wire, merge of all slices)",
-        "value": round(1e3 / ms_step, 1),
-        "unit": "logits-steps/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": wpasses * R,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int8" if w.quant & synth.Q_WEIGHTS else "bf16" if w.w_dtype == synth.BF16 else "f32",
-        "data": "synthetic",
+        "value": s["value"], "unit": "logits-steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wdtype(w), "data": "synthetic",
         "config": {"workload": w.name, "shard": f"rank 0 of TP={T}", "batch": B, "vocab": w.vocab,
                    "quant": w.quant, "copies": R, "launch": args.mode, "step_bytes": cls_bytes},
+        "ms_per_step_min": s["ms_per_step_min"], "ms_per_step_median": s["ms_per_step_median"],
+        "repeats": s["repeats"],
         "achieved_GBps": round(cls_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(cls_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "kernels_us": kt,
         "roofline": {"kernel": "gemv_logits", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(
                          f"traffic_gemv_logits_{w.name}.md",
                          GEMV_MFMA_SOURCES if w.w_dtype == synth.BF16 and B > 4 else GEMV_SOURCES),
-                     "bytes_per_launch": cls_bytes,
-                     "avg_launch_us": round(k_ms * 1e3, 3), "launches": n},
+                     "bytes_per_launch": cls_bytes, "avg_launch_us": kt["gemv_logits"]},
     }
-    if not args.no_cpu_baseline:
+    if with_cpu and not args.no_cpu_baseline:
         import oracle
-        n, t0 = 0, time.perf_counter()
-        while True:
+
+        def one():
             z = oracle.logits_shard(d["w_cls"], d["g_final"], d["x"], T, 0, w.norm_eps, w.w_dtype)["z"]
             dz, _, _ = oracle.wire(z, w.quant)
             oracle.merge_logits(np.concatenate([dz[None], np.zeros((T - 1, B, Vs))]))
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
-        res["cpu_baseline"] = {
-            "value": round(n / el, 3), "unit": "logits-steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} rank-0 final-stage steps of {w.name} (final norm, logits slice, wire, "
-                      f"merge) by the single-threaded fp64 C oracle in {el:.1f} s"}
+        res["cpu_baseline"] = cpu_baseline(one, args.cpu_seconds, "logits-steps/s", 1.0,
+                                           f"rank-0 final-stage steps of {w.name} (final norm, "
+                                           f"logits slice, wire, merge)")
     return res
 
+
+# ---------------------------------------------------------------- batch-sharded attention
 
 def attn_batch_config(tp, w, rank):
     dt = {synth.F32: tp.TP_F32, synth.BF16: tp.TP_BF16}
@@ -543,7 +667,7 @@ def attn_batch_config(tp, w, rank):
                           max_ctx=w.max_ctx, kv_dtype=dt[w.kv_dtype], rope_theta=w.rope_theta)
 
 
-def run_attn_batch(args, w):
+def run_attn_batch(args, w, with_cpu=True):
     """Rank 0's batch-sharded attention step: the all-to-all of the queries
     from the T head shards into its attention input rows, attention of every
     head over its sequences' caches, and the all-to-all of the outputs back
@@ -583,104 +707,63 @@ def run_attn_batch(args, w):
     backs = [torch.empty((B, C), device="cuda") for _ in range(R)]
     torch.cuda.synchronize()
 
-    def one_pass():
-        for r, c in enumerate(copies):
-            tp.all_to_all(c.handle, tp.TP_A2A_HEADS_TO_BATCH, qh, C, xs[r], ld_q)
-            c.step(tp.TP_STAGE_ATTN, xs[r], lens0, nb, atts[r])
-            tp.all_to_all(c.handle, tp.TP_A2A_BATCH_TO_HEADS, [atts[r]] + outs, Hq * hd, backs[r], C)
+    def step(r):
+        c = copies[r]
+        tp.all_to_all(c.handle, tp.TP_A2A_HEADS_TO_BATCH, qh, C, xs[r], ld_q)
+        c.step(tp.TP_STAGE_ATTN, xs[r], lens0, nb, atts[r])
+        tp.all_to_all(c.handle, tp.TP_A2A_BATCH_TO_HEADS, [atts[r]] + outs, Hq * hd, backs[r], C)
 
-    passes = max(1, args.steps // R)
-    steps = passes * R
-    wpasses = max(1, args.warmup // R)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
-    graph = None
-    with torch.cuda.stream(stream):
-        for _ in range(2):
-            one_pass()
-        if args.mode == "graph":
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=stream):
-                one_pass()
-        run = graph.replay if graph is not None else one_pass
-        for _ in range(wpasses):
-            run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(passes):
-            run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        assert torch.isfinite(backs[0]).all().item(), "non-finite attention output"
-        kid = tp.kernel_names().index("attention")
-        for c in copies:
-            tp.kernel_timing_arm(c.handle, kid)
-        for _ in range(passes):
-            one_pass()
-        torch.cuda.synchronize()
-        tot, n = 0.0, 0
-        for c in copies:
-            t_, n_ = tp.kernel_timing_read(c.handle)
-            tot += t_
-            n += n_
-            tp.kernel_timing_arm(c.handle, -1)
-    ms_step = ms / steps
-    k_ms = tot / max(n, 1)
-    achieved = kv_bytes / (k_ms * 1e-3) / 1e9
+    st = Stepper(step, R, args.mode, stream)
+    ms = time_steps(st, args.steps, args.warmup, args.repeats)
+    assert torch.isfinite(backs[0]).all().item(), "non-finite attention output"
+    kt = kernel_times([c.handle for c in copies], st, max(args.steps, R), ["attention", "all_to_all"])
+    s = summarize(ms, args.steps)
+    ms_step = s["ms_per_step"]
+    achieved = kv_bytes / (kt["attention"] * 1e-6) / 1e9
     res = {
         "metric": "batch-sharded attention steps/s of one shard (all-to-all in, RoPE + KV append + "
                   "GQA attention over every head of its sequences, all-to-all out)",
-        "value": round(1e3 / ms_step, 1),
-        "unit": "attention-steps/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": wpasses * R,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32" if w.kv_dtype == synth.F32 else "bf16",
+        "value": s["value"], "unit": "attention-steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if w.kv_dtype == synth.F32 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "shard": f"rank 0 of TP={T}", "sequences": nb,
                    "heads": [Hq, Hkv], "kv_positions": [int(x) for x in d["lens"][:nb]],
                    "copies": R, "launch": args.mode, "step_bytes": kv_bytes},
+        "ms_per_step_min": s["ms_per_step_min"], "ms_per_step_median": s["ms_per_step_median"],
+        "repeats": s["repeats"], "kernels_us": kt,
         "roofline": {"kernel": "attention (+ combine)", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": kv_bytes,
-                     "avg_launch_us": round(k_ms * 1e3, 3), "launches": n},
+                     "traffic": None, "bytes_per_launch": kv_bytes, "avg_launch_us": kt["attention"]},
     }
-    if not args.no_cpu_baseline:
+    if with_cpu and not args.no_cpu_baseline:
         import oracle
-        n, t0 = 0, time.perf_counter()
         kc, vc = d["kcache"][:nb].copy(), d["vcache"][:nb].copy()
         heads = np.stack([d["qkv"][:, i * C:(i + 1) * C] for i in range(T)])
-        while True:
+
+        def one():
             q = oracle.a2a_heads_to_batch(heads, 0)
             rows = d["qkv"][:nb].astype(np.float64)
             rows[:, :Hq * hd] = q
             att = oracle.attn_batch_shard(rows, d["lens"][:nb], kc, vc, Hq, Hkv, hd, w.kv_dtype)
             oracle.a2a_batch_to_heads(np.concatenate([att[None], np.zeros((T - 1, nb, Hq * hd))]), 0)
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
-        res["cpu_baseline"] = {
-            "value": round(n / el, 3), "unit": "attention-steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} rank-0 batch-sharded attention steps of {w.name} (all-to-all, attention, "
-                      f"all-to-all) by the single-threaded fp64 C oracle in {el:.1f} s"}
+        res["cpu_baseline"] = cpu_baseline(one, args.cpu_seconds, "attention-steps/s", 1.0,
+                                           f"rank-0 batch-sharded attention steps of {w.name} "
+                                           f"(all-to-all, attention, all-to-all)")
     return res
 
 
-def run_decode(args, wd):
+# ---------------------------------------------------------------- whole decode step
+
+def run_decode(args, wd, with_cpu=True):
     """One token through rank 0's shard of the whole model: n_layers layer
     steps (distinct packed weights and KV caches per layer, each merge done by
     the kernel producing rank 0's partial) feeding each other, then the final
     stage (final norm, logits slice, wire, merge of all T slices). The other
     ranks' partials are computed once for the first layer's input and stand
-    in for what every layer would receive."""
+    in for what every layer would receive. A step is one token."""
     import torch
     import tensor_tp_shard_amd as tp
     w, wl, L = wd.block, wd.logits, wd.n_layers
@@ -710,7 +793,7 @@ def run_decode(args, wd):
     lwire = l0.new_wire()
     logits = torch.empty((B, wl.vocab), dtype=torch.float32, device="cuda")
 
-    def one_token():
+    def one_token(_r):
         for i, c in enumerate(layers):
             c.step_merge(tp.TP_STAGE_ATTN, xs[i], lens, B, wires_a[i], [wires_a[i]] + other_att, hs_[i])
             c.step_merge(tp.TP_STAGE_FFN, hs_[i], None, B, wires_f[i], [wires_f[i]] + other_ffn,
@@ -718,65 +801,28 @@ def run_decode(args, wd):
         l0.step(tp.TP_STAGE_LOGITS, xs[L], None, B, lwire)
         l0.merge_logits([lwire] + other_lw, logits, B)
 
-    tokens = max(1, args.steps // L)
-    wtok = max(1, args.warmup // L)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
-    graph = None
-    with torch.cuda.stream(stream):
-        for _ in range(2):
-            one_token()
-        if args.mode == "graph":
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=stream):
-                one_token()
-        run = graph.replay if graph is not None else one_token
-        for _ in range(wtok):
-            run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(tokens):
-            run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        assert torch.isfinite(logits).all().item(), "non-finite logits"
-        kid = tp.kernel_names().index("gemv_w13_swiglu")
-        for c in layers:
-            tp.kernel_timing_arm(c.handle, kid)
-        for _ in range(tokens):
-            one_token()
-        torch.cuda.synchronize()
-        tot, n = 0.0, 0
-        for c in layers:
-            t_, n_ = tp.kernel_timing_read(c.handle)
-            tot += t_
-            n += n_
-            tp.kernel_timing_arm(c.handle, -1)
-    ms_tok = ms / tokens
+    st = Stepper(one_token, 1, args.mode, stream)
+    ms = time_steps(st, args.steps, args.warmup, args.repeats)
+    assert torch.isfinite(logits).all().item(), "non-finite logits"
+    kt = kernel_times([c.handle for c in layers], st, 1, ["gemv_w13_swiglu"])
+    s = summarize(ms, args.steps)
+    ms_tok = s["ms_per_step"]
     wbytes, kvbytes, w13bytes = llama_bytes(w, d["lens"])
     ecls = 1.125 if wl.quant & synth.Q_WEIGHTS else 2 if wl.w_dtype == synth.BF16 else 4
     tok_bytes = L * (wbytes + kvbytes) + int(wl.vocab // T * wl.dim * ecls)
-    k_ms = tot / max(n, 1)
-    achieved = w13bytes / (k_ms * 1e-3) / 1e9
+    achieved = w13bytes / (kt["gemv_w13_swiglu"] * 1e-6) / 1e9
     res = {
         "metric": "decode tokens/s of one TP shard through the whole model (all layers + final stage)",
-        "value": round(1e3 / ms_tok * B, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": tokens,
-        "warmup": wtok,
-        "ms_per_step": round(ms_tok, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int8" if w.quant & synth.Q_WEIGHTS else "bf16" if w.w_dtype == synth.BF16 else "f32",
-        "data": "synthetic",
+        "value": round(1e3 / ms_tok * B, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_tok, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wdtype(w), "data": "synthetic",
         "config": {"workload": wd.name, "shard": f"rank 0 of TP={T}", "batch": B, "layers": L,
                    "vocab": wl.vocab, "kv_positions": [int(d["lens"].min()), int(d["lens"].max())],
                    "launch": args.mode, "token_bytes": int(tok_bytes)},
+        "ms_per_step_min": s["ms_per_step_min"], "ms_per_step_median": s["ms_per_step_median"],
+        "repeats": s["repeats"],
         "achieved_GBps": round(tok_bytes / (ms_tok * 1e-3) / 1e9, 1),
         "hbm_frac": round(tok_bytes / (ms_tok * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {"kernel": "gemv_w13_swiglu", "bound": "hbm", "achieved": round(achieved, 1),
@@ -784,56 +830,89 @@ def run_decode(args, wd):
                      "traffic": measured_traffic(
                          f"traffic_gemv_w13_swiglu_{w.name}.md",
                          GEMV_MFMA_SOURCES if w.w_dtype == synth.BF16 and B > 4 else GEMV_SOURCES),
-                     "bytes_per_launch": int(w13bytes),
-                     "avg_launch_us": round(k_ms * 1e3, 3), "launches": n},
+                     "bytes_per_launch": int(w13bytes), "avg_launch_us": kt["gemv_w13_swiglu"]},
     }
-    if not args.no_cpu_baseline:
+    if with_cpu and not args.no_cpu_baseline:
         import oracle
-        # bounded sample: whole layer steps and final stages of rank 0 timed
-        # separately, the token rate derived as 1 / (L * t_layer + t_final)
-        half = args.cpu_seconds / 2
-        t_layer = cpu_baseline_llama(w, d, half)
-        t_layer_s = 1.0 / t_layer["value"]
-        n, t0 = 0, time.perf_counter()
+        layer = llama_oracle_step(w, d)
         Vs = wl.vocab // T
-        while True:
+
+        def final():
             z = oracle.logits_shard(dl["w_cls"], dl["g_final"], dl["x"][:B], T, 0, wl.norm_eps,
                                     wl.w_dtype)["z"]
             dz, _, _ = oracle.wire(z, wl.quant)
             oracle.merge_logits(np.concatenate([dz[None], np.zeros((T - 1, B, Vs))]))
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= half:
-                break
-        t_final = el / n
+        tl = cpu_baseline(layer, args.cpu_seconds / 2, "layer-steps/s", 1.0, "layer steps")
+        tf = cpu_baseline(final, args.cpu_seconds / 2, "final-steps/s", 1.0, "final stages")
         res["cpu_baseline"] = {
-            "value": round(B / (L * t_layer_s + t_final), 5), "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{t_layer['sample']}; {n} final stages in {el:.1f} s; tokens/s = B / "
-                      f"({L} x layer step + final stage)"}
+            "value": round(B / (L / tl["value"] + 1 / tf["value"]), 6), "unit": "tokens/s",
+            "cores": tl["cores"], "kind": "oracle",
+            "sample": f"{tl['sample']}; {tf['sample']}; tokens/s = B / ({L} x layer step + "
+                      f"final stage)",
+            "single_thread": {"value": round(B / (L / tl["single_thread"]["value"]
+                                                  + 1 / tf["single_thread"]["value"]), 6),
+                              "cores": 1},
+            **cpu_info()}
     return res
+
+
+RUNS = {"ffn2d": run_ffn2d, "logits": run_logits, "llama": run_llama, "decode": run_decode,
+        "attn_batch": run_attn_batch}
+
+
+def sub_result(res: dict, peaks: dict) -> dict:
+    """The figures of one configuration kept under the primary line's "configs"."""
+    keep = ("value", "unit", "ms_per_step", "ms_per_step_min", "ms_per_step_median", "repeats",
+            "dtype", "achieved_GBps", "hbm_frac", "achieved_TFLOPs", "mfma_frac", "kernels_us",
+            "roofline", "cpu_baseline")
+    out = {k: res[k] for k in keep if k in res}
+    out["config"] = res["config"]
+    add_measured_fracs(out, peaks)
+    return out
+
+
+def add_measured_fracs(res: dict, peaks: dict):
+    """Fractions of the measured peaks next to those of the spec peaks."""
+    if not peaks:
+        return
+    if "achieved_GBps" in res:
+        res["hbm_frac_of_measured"] = round(res["achieved_GBps"] / peaks["hbm_read_GBps"], 4)
+    if "achieved_TFLOPs" in res:
+        res["mfma_frac_of_measured"] = round(res["achieved_TFLOPs"] / peaks["bf16_gemm_TFLOPs"], 4)
+    rf = res.get("roofline")
+    if rf:
+        den = peaks["hbm_read_GBps"] if rf["unit"] == "GB/s" else peaks["bf16_gemm_TFLOPs"]
+        rf["frac_of_measured"] = round(rf["achieved"] / den, 4)
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4000)
-    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=400, help="timed steps per repeat")
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps before the first repeat")
+    ap.add_argument("--repeats", type=int, default=5, help="timed repeats (value = median)")
     ap.add_argument("--workload", default="llama2_7b_tp4_b1", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--configs", default="auto",
+                    help="sub-configurations to add under 'configs': 'all' (the other configurations "
+                         "of the metric), 'none', or a comma list of workloads; 'auto' = all for the "
+                         "default workload, none otherwise")
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--copies", type=int, default=0, help="layer copies in rotation (0 = auto)")
-    # a decode workload (whole model) times --steps layer steps, i.e. steps / n_layers tokens
     ap.add_argument("--merge", default="fused", choices=["fused", "separate"],
                     help="merge of a stage's partials by the kernel that produces rank 0's own "
                          "partial (decode_merge_step) or as a kernel of its own (merge_partials)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a device copy of this many MiB (counter calibration) and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the shard step runs every shard in turn on one device "
               "and uses no collectives; --gpus above 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.repeats < 1:
+        print("--steps and --repeats must be >= 1, --warmup >= 0", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
@@ -843,9 +922,28 @@ def main():
         calib_copy(args.calib_copy_mib)
         return
     w = synth.get(args.workload)
-    runs = {"ffn2d": run_ffn2d, "logits": run_logits, "llama": run_llama, "decode": run_decode,
-            "attn_batch": run_attn_batch}
-    res = runs[w.kind](args, w)
+    res = RUNS[w.kind](args, w)
+    peaks = {} if args.no_peaks else measured_peaks()
+    if peaks:
+        res["measured_peaks"] = peaks
+        add_measured_fracs(res, peaks)
+    subs = args.configs
+    if subs == "auto":
+        subs = "all" if args.workload == "llama2_7b_tp4_b1" else "none"
+    names = [] if subs == "none" else list(SUB_CONFIGS) if subs == "all" else subs.split(",")
+    configs = {}
+    for name in names:
+        if name == args.workload:
+            continue
+        log(f"sub-configuration {name}")
+        ws = synth.get(name)
+        sargs = argparse.Namespace(**vars(args))
+        sargs.cpu_seconds = min(args.cpu_seconds, 3.0)
+        configs[name] = sub_result(RUNS[ws.kind](sargs, ws), peaks)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    if configs:
+        res["configs"] = configs
     print(json.dumps(res), flush=True)
 
 

@@ -164,9 +164,12 @@ typedef struct {
  *  k, v [B][Hkv_s*hd]   rotated keys, values        (attention stage)
  *  att  [B][Hq_s*hd]    attention outputs           (attention stage)
  *  a    [B][F_s]        SwiGLU activations          (FFN stage)
- *  p_pre [B][D]         the stage's fp32 partial before quantisation */
+ *  p_pre [B][D]         the stage's fp32 partial before quantisation
+ *  xq   [B][D]          normalised stage input BEFORE the int8 round trip
+ *                       (the fp32 row the quantiser of TP_Q_INPUTS codes;
+ *                       equal to xn when that bit is off) */
 typedef struct {
-    float *xn, *q, *k, *v, *att, *a, *p_pre;
+    float *xn, *q, *k, *v, *att, *a, *p_pre, *xq;
 } tp_taps;
 
 /*

@@ -35,16 +35,31 @@ F32, BF16 = 0, 1
 Q_PARTIALS, Q_INPUTS, Q_WEIGHTS = 1, 2, 4
 QBLOCK = 32
 
+# The same source built with -fopenmp: independent output rows, features and
+# heads spread over the host's threads, every sum in the same order (same bits).
+LIB_OMP = os.path.join(HERE, "liboracle_omp.so")
+
 _lib = None
+_loaded: Dict[str, ctypes.CDLL] = {}
 
 
-def build(force: bool = False) -> str:
-    """Compile oracle.c into liboracle.so with gcc (always when force)."""
-    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-        tmp = LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"])
-        os.replace(tmp, LIB)
-    return LIB
+def build(force: bool = False, omp: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (liboracle_omp.so with omp) with gcc
+    (always when force)."""
+    out = LIB_OMP if omp else LIB
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(SRC):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, *(["-fopenmp"] if omp else []), "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, out)
+    return out
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if path not in _loaded:
+        L = ctypes.CDLL(path)
+        _declare(L)
+        _loaded[path] = L
+    return _loaded[path]
 
 
 def lib() -> ctypes.CDLL:
@@ -52,9 +67,20 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB):
             build()
-        _lib = ctypes.CDLL(LIB)
-        _declare(_lib)
+        _lib = _load(LIB)
     return _lib
+
+
+def use_threads(omp: bool) -> int:
+    """Route the functions below to the OpenMP build (omp) or the plain one;
+    returns the number of threads the chosen build uses."""
+    global _lib
+    if omp:
+        build(omp=True)
+    elif not os.path.exists(LIB):
+        build()
+    _lib = _load(LIB_OMP if omp else LIB)
+    return int(_lib.orc_threads())
 
 
 _P = ctypes.c_void_p

@@ -9,7 +9,10 @@
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
  * (no FMA contraction, no fast-math: every fp32 step of the int8 codec is one
- * IEEE operation, and fp64 sums are plain left-to-right loops).
+ * IEEE operation, and fp64 sums are plain left-to-right loops). The same
+ * source built with -fopenmp spreads independent output rows, features and
+ * heads over the host's threads (the omp pragmas below); every sum keeps its
+ * order, so both builds return the same bits. The plain build ignores them.
  *
  * Pages followed (cited by title and the part of the page):
  *  [DL]  distributed-llama issue "[Feature Suggest] Tensor Parallellism for
@@ -35,10 +38,23 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 enum { ORC_Q_PARTIALS = 1, ORC_Q_INPUTS = 2 };
 #define ORC_QBLOCK 32
+
+/* Threads an OpenMP build uses for its parallel loops (1 for the plain build). */
+int orc_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------- storage */
 
@@ -138,6 +154,7 @@ void orc_q8_dequantize(int64_t n, const int8_t *codes, const float *scales, floa
 void orc_matvec(int64_t N, int64_t K, const void *W, int dt, int64_t ldw, int64_t col0,
                 const double *x, double *y)
 {
+#pragma omp parallel for if (N >= 64) schedule(static)
     for (int64_t n = 0; n < N; n++) {
         double acc = 0.0;
         for (int64_t k = 0; k < K; k++)
@@ -147,7 +164,7 @@ void orc_matvec(int64_t N, int64_t K, const void *W, int dt, int64_t ldw, int64_
 }
 
 /* Rotary position encoding of one head vector at position pos ([DL]
- * llamaMultiheadAtt: "add RoPE encoding"). The pages name RoPE only; the
+ * llamaMultiheadAtt, whose description names RoPE). The pages name RoPE only; the
  * Llama form is taken: adjacent pairs (u_2i, u_2i+1) rotated by
  * pos * theta^(-2i/hd). */
 void orc_rope(int64_t hd, int64_t pos, double theta, double *u)
@@ -178,7 +195,7 @@ void orc_softmax(int64_t n, const double *s, double *w)
 }
 
 /* One query head attending over n_pos cached positions ([DL]
- * llamaMultiheadAtt: "compute a part of multi-head attention locally"):
+ * llamaMultiheadAtt: each node attends with its own heads over its own cache):
  * o = sum_t softmax_t(q . K[t] / sqrt(hd)) V[t]. K and V point at n_pos rows
  * of hd stored elements each, ld_kv elements apart. The pages fix no scale or
  * mask; the usual 1/sqrt(hd) is taken, and decode attends to every cached
@@ -311,7 +328,7 @@ int orc_attn_shard(const orc_llama_cfg *c, const orc_llama_weights *w, int32_t s
             orc_rope(hd, L, c->rope_theta, kv);
             if (k_out)
                 memcpy(k_out + (b * Hkv_s + g) * hd, kv, sizeof(double) * (size_t)hd);
-            for (int64_t e = 0; e < hd; e++) /* append ([DL]: "merge kv-cache") */
+            for (int64_t e = 0; e < hd; e++) /* append to the cache ([DL] llamaMultiheadAtt) */
                 st(kc, c->kv_dtype, slot + e, kv[e]);
             orc_matvec(hd, D, (const char *)w->wv + hk * hd * D * esz, c->w_dtype, D, 0, xn, kv);
             if (v_out)
@@ -320,6 +337,7 @@ int orc_attn_shard(const orc_llama_cfg *c, const orc_llama_weights *w, int32_t s
                 st(vc, c->kv_dtype, slot + e, kv[e]);
         }
         /* attention of each local q head over its kv head's L + 1 positions */
+#pragma omp parallel for if (Hq_s > 1) schedule(static)
         for (int64_t h = 0; h < Hq_s; h++) {
             const int64_t hk = (s * Hq_s + h) / G;
             const int64_t esz = c->kv_dtype == ORC_F32 ? 4 : 2;
@@ -342,7 +360,7 @@ int orc_attn_shard(const orc_llama_cfg *c, const orc_llama_weights *w, int32_t s
 }
 
 /* FFN stage of shard s ([DL] llamaRmfFfn, llamaRmfFfnNorm,
- * llamaQuantizeRmfFfn, llamaFfn "SwiGLU", llamaFfn2; [TP] 運作原理):
+ * llamaQuantizeRmfFfn, llamaFfn (SwiGLU), llamaFfn2; [TP] 運作原理):
  *  h   [B][D]      stage input (residual after the attention merge)
  * outputs (any may be NULL except p):
  *  hn  [B][D]      normalised input (after the optional Q8 round trip)
@@ -359,15 +377,16 @@ int orc_ffn_shard(const orc_llama_cfg *c, const orc_llama_weights *w, int32_t s,
         return -1;
     double *hn = (double *)malloc(sizeof(double) * (size_t)D);
     double *a = (double *)malloc(sizeof(double) * (size_t)Fs);
-    double g1, g3;
     for (int64_t b = 0; b < B; b++) {
         orc_rmsnorm(D, h + b * D, w->g_ffn, c->norm_eps, hn);
         if (c->quant & ORC_Q_INPUTS)
             q8_round_trip(D, hn, NULL, NULL);
         if (hn_out)
             memcpy(hn_out + b * D, hn, sizeof(double) * (size_t)D);
+#pragma omp parallel for schedule(static)
         for (int64_t f = 0; f < Fs; f++) {
             const int64_t row = s * Fs + f;
+            double g1, g3;
             orc_matvec(1, D, (const char *)w->w1 + row * D * esz, c->w_dtype, D, 0, hn, &g1);
             orc_matvec(1, D, (const char *)w->w3 + row * D * esz, c->w_dtype, D, 0, hn, &g3);
             a[f] = orc_silu(g1) * g3;
@@ -496,11 +515,12 @@ void orc_ffn2d(int64_t E, int64_t F, const uint16_t *X, const uint16_t *Wgate,
 {
     double *x = (double *)malloc(sizeof(double) * (size_t)E);
     double *hgt = (double *)malloc(sizeof(double) * (size_t)F);
-    double g, u;
     for (int64_t r = 0; r < nrows; r++) {
         for (int64_t e = 0; e < E; e++)
             x[e] = ld(X, ORC_BF16, (row0 + r) * E + e);
+#pragma omp parallel for schedule(static)
         for (int64_t f = 0; f < F; f++) {
+            double g, u;
             orc_matvec(1, E, Wgate + f * E, ORC_BF16, E, 0, x, &g);
             orc_matvec(1, E, Win + f * E, ORC_BF16, E, 0, x, &u);
             hgt[f] = orc_silu(g) * u;

@@ -58,7 +58,7 @@ class TpLayerWeights(ctypes.Structure):
 
 
 class TpTaps(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("xn", "q", "k", "v", "att", "a", "p_pre")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("xn", "q", "k", "v", "att", "a", "p_pre", "xq")]
 
 
 _lib = None

@@ -690,9 +690,10 @@ static int32_t logits_step(tp_shard *s, const float *x, int B, void *wire_out, c
         g.g = gain;
         g.eps = s->cfg.norm_eps;
         g.xn_tap = tp.xn;
-    } else if (!sk_norm || tp.xn) {
+        g.xq_tap = tp.xq;
+    } else if (!sk_norm || tp.xn || tp.xq) {
         float *xn = (float *)(s->ws + s->w_xn);
-        NormArgs na{x, gain, xn, tp.xn, xfx, B, s->D, s->cfg.norm_eps, 0};
+        NormArgs na{x, gain, xn, tp.xn, xfx, B, s->D, s->cfg.norm_eps, 0, tp.xq};
         rc = timed(s, KID_RMSNORM, st, "rmsnorm", [&] { return launch_rmsnorm(na, st); });
         if (rc)
             return rc;
@@ -758,6 +759,8 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         return fail(TP_EINVAL, "decode_step: null handle");
     if (!s->loaded)
         return fail(TP_ESTATE, "decode_step before load_weights");
+    char *ws = s->ws;
+    unsigned *err_word = (unsigned *)(ws + s->w_err);
     if (stage != TP_STAGE_ATTN && stage != TP_STAGE_FFN && stage != TP_STAGE_LOGITS)
         return fail(TP_EINVAL, "unknown stage %d", stage);
     if ((stage == TP_STAGE_LOGITS) != (s->cfg.kind == TP_LOGITS))
@@ -775,7 +778,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         return fail(TP_EALIGN, "decode_step: x / wire_out not 16-byte aligned");
     const tp_taps nt{};
     const tp_taps &tp = taps ? *taps : nt;
-    const float *tp_ptrs[] = {tp.xn, tp.q, tp.k, tp.v, tp.att, tp.a, tp.p_pre};
+    const float *tp_ptrs[] = {tp.xn, tp.q, tp.k, tp.v, tp.att, tp.a, tp.p_pre, tp.xq};
     for (const float *p : tp_ptrs)
         if (p && !aligned16(p))
             return fail(TP_EALIGN, "decode_step: tap not 16-byte aligned");
@@ -793,8 +796,8 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         Ffn2dArgs fa{(const uint16_t *)x,
                      (const uint16_t *)(s->packed + s->o_w13),
                      (const uint16_t *)(s->packed + s->o_w2),
-                     (uint16_t *)(s->ws + s->w_a),
-                     (float *)(s->ws + s->w_p),
+                     (uint16_t *)(ws + s->w_a),
+                     (float *)(ws + s->w_p),
                      (float *)wire_out,
                      B,
                      s->D,
@@ -817,7 +820,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
     const bool qin = s->cfg.quant & TP_Q_INPUTS, qpart = s->cfg.quant & TP_Q_PARTIALS;
     const float *gain = (const float *)(s->packed + (stage == TP_STAGE_ATTN ? s->o_gatt : s->o_gffn));
     // the partial goes straight into the wire unless it is quantised
-    float *p = qpart ? (float *)(s->ws + s->w_p) : (float *)wire_out;
+    float *p = qpart ? (float *)(ws + s->w_p) : (float *)wire_out;
     int8_t *codes = qpart ? (int8_t *)wire_out : nullptr;
     float *scales = qpart ? (float *)((char *)wire_out + tp_wire_scales_offset(&s->cfg, B)) : nullptr;
     int32_t rc;
@@ -833,9 +836,9 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
     // batch's rows fit in LDS, else a kernel of its own writing xn
     const bool fuse_norm = !mfma && gemv_fused_ok(B, s->D);
     const float *in = (const float *)x;
-    uint16_t *xfx = mfma ? (uint16_t *)(s->ws + s->w_xfx) : nullptr;
-    uint16_t *xfatt = mfma ? (uint16_t *)(s->ws + s->w_xfatt) : nullptr;
-    uint16_t *xfa = mfma ? (uint16_t *)(s->ws + s->w_xfa) : nullptr;
+    uint16_t *xfx = mfma ? (uint16_t *)(ws + s->w_xfx) : nullptr;
+    uint16_t *xfatt = mfma ? (uint16_t *)(ws + s->w_xfatt) : nullptr;
+    uint16_t *xfa = mfma ? (uint16_t *)(ws + s->w_xfa) : nullptr;
     GemvArgs up{};
     up.x = in;
     up.ldx = s->D;
@@ -846,9 +849,10 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         up.eps = s->cfg.norm_eps;
         up.qin = qin ? 1 : 0;
         up.xn_tap = tp.xn;
-    } else if (!sk_norm || tp.xn) { // with sk_norm only for the xn tap
-        float *xn = (float *)(s->ws + s->w_xn);
-        NormArgs na{in, gain, xn, tp.xn, xfx, B, s->D, s->cfg.norm_eps, qin ? 1 : 0};
+        up.xq_tap = tp.xq;
+    } else if (!sk_norm || tp.xn || tp.xq) { // with sk_norm only for the xn / xq taps
+        float *xn = (float *)(ws + s->w_xn);
+        NormArgs na{in, gain, xn, tp.xn, xfx, B, s->D, s->cfg.norm_eps, qin ? 1 : 0, tp.xq};
         rc = timed(s, KID_RMSNORM, st, "rmsnorm", [&] { return launch_rmsnorm(na, st); });
         if (rc)
             return rc;
@@ -868,7 +872,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         if (!mfma)
             return launch_gemv(g, wt, epi, st);
         MfmaGemvArgs m{(const uint16_t *)g.W, xf, g.y, g.tap, yf, g.N, g.K, g.B, g.ldy, 1, g.mo,
-                       s->w_skp ? (float *)(s->ws + s->w_skp) : nullptr, 0, 0,
+                       s->w_skp ? (float *)(ws + s->w_skp) : nullptr, 0, 0,
                        norm ? in : nullptr, norm ? gain : nullptr, s->cfg.norm_eps, g.ws};
         return launch_gemv_mfma(m, epi, st);
     };
@@ -876,7 +880,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
     if (stage == TP_STAGE_ATTN) {
         if (!lens)
             return fail(TP_EINVAL, "decode_step: attention stage needs lens");
-        float *qkv = (float *)(s->ws + s->w_qkv);
+        float *qkv = (float *)(ws + s->w_qkv);
         up.W = s->packed + s->o_wqkv;
         up.ws = wscales(s->o_sqkv);
         up.y = qkv;
@@ -885,15 +889,15 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         rc = timed(s, KID_GEMV_QKV, st, "gemv qkv", [&] { return run_gemv(up, xfx, nullptr, EPI_STORE, sk_norm); });
         if (rc)
             return rc;
-        float *att = (float *)(s->ws + s->w_att);
+        float *att = (float *)(ws + s->w_att);
         AttnArgs aa{};
         aa.qkv = qkv;
         aa.lens = lens;
         aa.kc = s->kc;
         aa.vc = s->vc;
         aa.rope = (const float2 *)(s->packed + s->o_rope);
-        aa.part = (float *)(s->ws + s->w_part);
-        aa.err = (unsigned *)(s->ws + s->w_err);
+        aa.part = (float *)(ws + s->w_part);
+        aa.err = err_word;
         aa.att = att;
         aa.tap_q = tp.q;
         aa.tap_k = tp.k;
@@ -921,7 +925,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         if (rc)
             return rc;
     } else {
-        float *a = (float *)(s->ws + s->w_a);
+        float *a = (float *)(ws + s->w_a);
         up.W = s->packed + s->o_w13;
         up.ws = wscales(s->o_sw13);
         up.y = a;

@@ -236,6 +236,7 @@ struct NormArgs {
     int B, D;
     float eps;
     int quant;           // int8 round trip of the normalised row
+    float *tap_pre;      // optional [B][D]: the normalised row before that round trip
 };
 
 // ---------------------------------------------------------------- MFMA fragment layout
@@ -304,6 +305,7 @@ struct GemvArgs {
     float eps;
     int qin;
     float *xn_tap;       // [B][K]: the normalised rows, written by block 0
+    float *xq_tap;       // [B][K]: the same before the int8 round trip, block 0
     // EPI_STORE, fp32 wires: merge of the stage's partials (this kernel's
     // output y is wire mo.own), written to mo.x_out [B][ldy]
     MergeIn mo;

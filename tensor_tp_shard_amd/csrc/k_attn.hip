@@ -2,8 +2,8 @@
 // attention over one shard's cache, with the chunk combine fused in.
 //
 // Pages: distributed-llama issue "[Feature Suggest] Tensor Parallellism for
-// Accelerating LLM", buildLlama2Arch task llamaMultiheadAtt ("merge kv-cache,
-// add RoPE encoding, compute a part of multi-head attention locally");
+// Accelerating LLM", buildLlama2Arch task llamaMultiheadAtt (RoPE, the append
+// of the new key and value to the cache, and this node's share of the heads);
 // tt-metal issue "Llama-2 (meta) TT implementation" (GQA vs MHA matters for
 // Llama-2); CS349E lecture 4 03_pope_partitioning.py, demo 3 observations
 // (with 8 KV groups, head sharding at TP <= 8 keeps each KV head on exactly

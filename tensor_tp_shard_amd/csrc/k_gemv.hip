@@ -9,7 +9,7 @@
 // Accelerating LLM", buildLlama2Arch tasks llamaRmsAttNorm / llamaRmfFfnNorm
 // (fused here as the prologue of the projection that consumes the normalised
 // row), llamaQuantizeRmsAtt / llamaQuantizeRmfFfn (int8 round trip of that
-// row), llamaQkv, llamaAttOutput, llamaFfn ("Compute SwiGLU activation"),
+// row), llamaQkv, llamaAttOutput, llamaFfn (the SwiGLU activation),
 // llamaFfn2.
 //
 // Design (HBM-bound: every weight byte is read once and used B times):
@@ -151,6 +151,7 @@ __device__ void stage_x_finish(const GemvArgs &a, XRegs &r, float *xs, float *re
         ss = block_sum<NT / 64>(ss, red4);
         const float rr = 1.0f / sqrtf(ss / (float)a.K + a.eps);
         float4 *tap = (a.xn_tap && blockIdx.x == 0) ? (float4 *)(a.xn_tap + (size_t)b * a.K) : nullptr;
+        float4 *tapq = (a.xq_tap && blockIdx.x == 0) ? (float4 *)(a.xq_tap + (size_t)b * a.K) : nullptr;
 #pragma unroll
         for (int i = 0; i < kXV; i++) {
             const int e = threadIdx.x + NT * i;
@@ -160,6 +161,8 @@ __device__ void stage_x_finish(const GemvArgs &a, XRegs &r, float *xs, float *re
             if (e < n4) {
                 const float4 x = r.x[i], g = r.g[i];
                 v = make_float4(g.x * x.x * rr, g.y * x.y * rr, g.z * x.z * rr, g.w * x.w * rr);
+                if (tapq)
+                    tapq[e] = v;
             }
             if (a.qin) { // every lane takes part; lanes past the row hold 0
                 const float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));

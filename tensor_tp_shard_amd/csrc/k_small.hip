@@ -131,6 +131,11 @@ __global__ __launch_bounds__(kNormThreads) void k_rmsnorm(NormArgs a)
                 for (int t = 0; t < 8; t++)
                     e[t] = 0.f;
             }
+            if (a.tap_pre && run < nruns) { // the row the quantiser sees
+                float4 *tp = (float4 *)(a.tap_pre + (size_t)b * a.D);
+                tp[2 * run] = make_float4(e[0], e[1], e[2], e[3]);
+                tp[2 * run + 1] = make_float4(e[4], e[5], e[6], e[7]);
+            }
             if (a.quant) { // every lane takes part; 4 consecutive threads hold a block of 32
                 float m = 0.f;
 #pragma unroll

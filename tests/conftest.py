@@ -27,3 +27,31 @@ def orc():
     import oracle
     oracle.lib()
     return oracle
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _num(s):
+    return float.fromhex(s) if "0x" in s else float(s)
+
+
+def golden_q8_blocks():
+    """The hand-worked int8 blocks of tests/golden/q8_blocks.txt: a list of
+    {"name", "scale", "x" (32 floats), "codes" (32 ints)}."""
+    blocks, cur = [], None
+    with open(os.path.join(GOLDEN, "q8_blocks.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("block"):
+                cur = {"name": line.split()[1], "x": [], "codes": []}
+                blocks.append(cur)
+            elif line.startswith("scale"):
+                cur["scale"] = _num(line.split()[1])
+            else:
+                a, b = line.split("->")
+                cur["x"].append(_num(a.strip()))
+                cur["codes"].append(int(b))
+    return blocks

@@ -73,10 +73,11 @@ class Layer:
         hd, T = w.head_dim, w.tp
         f = lambda *s: t.full(s, float("nan"), dtype=t.float32, device="cuda")  # noqa: E731
         if stage == tp.TP_STAGE_ATTN:
-            return {"xn": f(B, w.dim), "q": f(B, w.n_heads // T * hd), "k": f(B, w.n_kv_heads // T * hd),
-                    "v": f(B, w.n_kv_heads // T * hd), "att": f(B, w.n_heads // T * hd),
-                    "p_pre": f(B, w.dim)}
-        return {"xn": f(B, w.dim), "a": f(B, w.ffn_hidden // T), "p_pre": f(B, w.dim)}
+            return {"xn": f(B, w.dim), "xq": f(B, w.dim), "q": f(B, w.n_heads // T * hd),
+                    "k": f(B, w.n_kv_heads // T * hd), "v": f(B, w.n_kv_heads // T * hd),
+                    "att": f(B, w.n_heads // T * hd), "p_pre": f(B, w.dim)}
+        return {"xn": f(B, w.dim), "xq": f(B, w.dim), "a": f(B, w.ffn_hidden // T),
+                "p_pre": f(B, w.dim)}
 
     def stage(self, stage: int, x, lens, B: int, with_taps: bool = True):
         """Runs `stage` on every rank; returns (wires, taps) per rank."""
@@ -232,3 +233,23 @@ class AttnBatchShard:
         w = self.w
         shape = (self.nb, w.n_kv_heads, w.max_ctx, w.head_dim)
         return to_np(self.sh.k_cache).reshape(shape), to_np(self.sh.v_cache).reshape(shape)
+
+
+def wire_values(w, wire: np.ndarray, B: int) -> np.ndarray:
+    """The values a merge adds for one wire, float32 [B][D]: the fp32 partial,
+    or float32(code) * scale per element of an int8 wire (one float32
+    multiply, numpy's IEEE rounding)."""
+    if not w.quant & synth.Q_PARTIALS:
+        return fp32_wire(w, wire, B)
+    codes, scales = split_wire(w, wire, B)
+    c = codes.reshape(B, -1, 32).astype(np.float32)
+    return (c * scales[:, :, None]).reshape(B, w.dim)
+
+
+def host_merge(residual: np.ndarray, parts) -> np.ndarray:
+    """residual + parts[0] + parts[1] + ... in float32, one add per part in
+    order: what the merge is defined to produce, bit for bit."""
+    acc = np.ascontiguousarray(residual, dtype=np.float32).copy()
+    for p in parts:
+        acc = acc + np.asarray(p, dtype=np.float32)
+    return acc

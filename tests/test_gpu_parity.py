@@ -19,7 +19,7 @@ import oracle
 import synth
 import tensor_tp_shard_amd as tp
 from conftest import rel_l2
-from gpu_harness import Layer, fp32_wire, split_wire
+from gpu_harness import Layer, fp32_wire, host_merge, split_wire, wire_values
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,18 @@ def _kv_widen(w, a):
     return synth.bf16_bits_to_f32(a) if w.kv_dtype == synth.BF16 else a
 
 
+def _row_errs(got, ref):
+    """(max over rows of the per-row relative L2, max-abs error) in float64."""
+    got = np.asarray(got, dtype=np.float64).reshape(ref.shape[0], -1)
+    ref = np.asarray(ref, dtype=np.float64).reshape(ref.shape[0], -1)
+    rows = [rel_l2(got[b], ref[b]) for b in range(ref.shape[0])]
+    return max(rows), float(np.max(np.abs(got - ref)))
+
+
+def _bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
 def check_layer(w, d=None, ranks=None):
     d = d or synth.llama_inputs(w)
     say(f"{w.name} B={w.batch} T={w.tp} quant={w.quant} lens={d['lens'][:4].tolist()}")
@@ -55,22 +67,77 @@ def check_layer(w, d=None, ranks=None):
     tol = _tol(w)
     B, D = w.batch, w.dim
     x = d["x"].astype(np.float64)
-    errs = {}
+    errs, maxabs = {}, {}
+    # every row alone is held to the contract's bar (1e-4 fp32, 2e-2 bf16);
+    # whole tensors to the stricter internal gate `tol` (a code flipped at a
+    # tie in an int8 input can move one short-context row's attention by a
+    # few 1e-3 while the tensor stays near 1e-5)
+    row_bar = 1e-4 if w.w_dtype == synth.F32 else 2e-2
+
+    def cmp(name, got, ref, bar):
+        assert np.all(np.isfinite(got)), f"{name} not finite"
+        e = rel_l2(got, ref)
+        e_row, ma = _row_errs(got, np.asarray(ref))
+        errs[name], maxabs[name] = e, ma
+        assert e <= bar, f"{w.name}: {name} rel-L2 {e:.3e} > {bar}"
+        assert e_row <= max(bar, row_bar), f"{w.name}: {name} worst row rel-L2 {e_row:.3e}"
+
+    T, hd = w.tp, w.head_dim
+    Hq_s, G = w.n_heads // T, w.n_heads // w.n_kv_heads
+    w8 = bool(w.quant & synth.Q_WEIGHTS)
+    wo_ref = oracle.q8_weights(d["wo"], w.w_dtype)[2] if w8 else d["wo"]
     for r in (ranks or range(w.tp)):
         ta, tf = g["taps_att"][r], g["taps_ffn"][r]
-        pairs = [("xn", ta["xn"], o["xn"][r]), ("q", ta["q"], o["q"][r]), ("k", ta["k"], o["k"][r]),
-                 ("v", ta["v"], o["v"][r]), ("att", ta["att"], o["att"][r]),
-                 ("p_att", ta["p_pre"], o["p_att"][r]), ("hn", tf["xn"], o["hn"][r]),
-                 ("a", tf["a"], o["a"][r]), ("p_ffn", tf["p_pre"], o["p_ffn"][r])]
-        for name, got, ref in pairs:
+        # end to end against the oracle's layer: the steps before the KV append
+        # at the internal gate, those after it at the contract's bar (the new
+        # token's k and v, larger than the cached entries by the input's scale,
+        # can dominate the softmax, and their bf16 rounding may differ by one
+        # ulp between an fp32 and an fp64 projection: a rounding decision like
+        # an int8 code at a tie, which each stage-local check below takes from
+        # the GPU's own values)
+        pairs = [("xn", ta["xn"], o["xn"][r], tol), ("q", ta["q"], o["q"][r], tol),
+                 ("k", ta["k"], o["k"][r], tol), ("v", ta["v"], o["v"][r], tol),
+                 ("att", ta["att"], o["att"][r], row_bar), ("p_att", ta["p_pre"], o["p_att"][r], row_bar),
+                 ("hn", tf["xn"], o["hn"][r], row_bar), ("a", tf["a"], o["a"][r], row_bar),
+                 ("p_ffn", tf["p_pre"], o["p_ffn"][r], row_bar)]
+        for name, got, ref, bar in pairs:
             if w.quant & synth.Q_INPUTS and name in ("xn", "hn"):
                 continue  # checked on the int8 grid below
-            e = rel_l2(got, ref)
-            errs[f"{name}[{r}]"] = e
-            assert np.all(np.isfinite(got)), f"{name}[{r}] not finite"
-            assert e <= tol, f"{w.name}: {name}[{r}] rel-L2 {e:.3e} > {tol}"
-        # KV append: slot lens[b] matches the oracle's, every other slot is bitwise unchanged
+            cmp(f"{name}[{r}]", got, ref, bar)
+        # stage by stage at the internal gate, each oracle step fed the GPU's own
+        # inputs: attention of the oracle's queries over the GPU's cache after
+        # the append; W_O of the GPU's attention output; the FFN stage of the
+        # GPU's merged h
         gk, gv = L.cache(r)
+        att_ref = np.empty((B, Hq_s * hd))
+        for b in range(B):
+            n = int(d["lens"][b]) + 1
+            for h in range(Hq_s):
+                att_ref[b, h * hd:(h + 1) * hd] = oracle.attend(
+                    o["q"][r][b, h * hd:(h + 1) * hd], gk[b, h // G, :n], gv[b, h // G, :n], w.kv_dtype)
+        cmp(f"att_stage[{r}]", ta["att"], att_ref, tol)
+        p_ref = np.stack([oracle.matvec(wo_ref, ta["att"][b], "f32" if w8 else w.w_dtype,
+                                        col0=r * Hq_s * hd, K=Hq_s * hd) for b in range(B)])
+        cmp(f"p_att_stage[{r}]", ta["p_pre"], p_ref, tol)
+        of = oracle.ffn_shard(w, d, r, g["h"])
+        for name, key in (("hn", "xn"), ("a", "a"), ("p_ffn", "p_pre")):
+            if w.quant & synth.Q_INPUTS and name == "hn":
+                continue
+            cmp(f"{name}_stage[{r}]", tf[key], of[name if name != "p_ffn" else "p"], tol)
+        # the normalised rows before the int8 round trip: against the oracle's
+        # norm of the same stage input (for the FFN stage, the GPU's own merged h)
+        for stage, tap, xin, gain in (("att", ta, d["x"], d["g_att"]), ("ffn", tf, g["h"], d["g_ffn"])):
+            ref = np.stack([oracle.rmsnorm(xin[b], gain, w.norm_eps) for b in range(B)])
+            cmp(f"xq_{stage}[{r}]", tap["xq"], ref, tol)
+            if w.quant & synth.Q_INPUTS:
+                # the round trip itself is integer work: bit for bit the oracle
+                # codec of the GPU's own fp32 row (codes, scales and products)
+                c_, s_ = oracle.q8_quantize(tap["xq"])
+                assert np.array_equal(_bits(tap["xn"]).reshape(-1), _bits(oracle.q8_dequantize(c_, s_))), \
+                    f"{w.name}: int8 round trip of the {stage} input, shard {r}"
+            else:
+                assert np.array_equal(_bits(tap["xn"]), _bits(tap["xq"]))
+        # KV append: slot lens[b] matches the oracle's, every other slot is bitwise unchanged
         hs = w.n_kv_heads // w.tp
         for got, ref, init in ((gk, kc, d["kcache"]), (gv, vc, d["vcache"])):
             ref_s, init_s = ref[:, r * hs:(r + 1) * hs], init[:, r * hs:(r + 1) * hs]
@@ -88,18 +155,24 @@ def check_layer(w, d=None, ranks=None):
                 assert np.array_equal(scales.reshape(-1).view(np.uint32), os_.view(np.uint32))
         else:
             assert np.array_equal(fp32_wire(w, g["wire_att"][r], B), ta["p_pre"])
+    # the merges, bit for bit: residual + each wire's values (float32(code) * scale
+    # for an int8 wire) in wire order, one float32 add each, from the GPU's own wires
+    ranks_all = range(w.tp)
+    h_ref = host_merge(d["x"], [wire_values(w, g["wire_att"][r], B) for r in ranks_all])
+    o_ref = host_merge(g["h"], [wire_values(w, g["wire_ffn"][r], B) for r in ranks_all])
+    assert np.array_equal(_bits(g["h"]), _bits(h_ref)), f"{w.name}: attention merge not exact"
+    assert np.array_equal(_bits(g["out"]), _bits(o_ref)), f"{w.name}: FFN merge not exact"
     if w.quant & synth.Q_INPUTS:
-        # the normalised inputs went through the int8 round trip: they match the
-        # oracle's except where fp32-vs-fp64 rounding flips a code at a tie,
-        # and then by exactly one step of that block's scale
+        # end to end the normalised inputs match the oracle's except where fp32-vs-fp64
+        # rounding flips a code at a tie, and then by exactly one step of that
+        # block's scale (the bit-exact check above is the contract; this reports)
         for key, tk in (("xn", "taps_att"), ("hn", "taps_ffn")):
             got = g[tk][0]["xn"].astype(np.float64).reshape(B, -1, 32)
             ref = o[key][0].reshape(B, -1, 32)
             if key == "hn" and w.quant & synth.Q_PARTIALS:
                 # the FFN input is the merge of int8 wires, whose codes may flip at a
-                # tie between the GPU's fp32 and the oracle's fp64 partials (the
-                # wires are checked against the codec of the GPU's own partial): so
-                # is hn, against the oracle's norm + round trip of the GPU's own h
+                # tie between the GPU's fp32 and the oracle's fp64 partials: so is
+                # hn, against the oracle's norm + round trip of the GPU's own h
                 hn = np.stack([oracle.rmsnorm(g["h"][b], d["g_ffn"], w.norm_eps) for b in range(B)])
                 c_, s_ = oracle.q8_quantize(hn.astype(np.float32))
                 ref = oracle.q8_dequantize(c_, s_).astype(np.float64).reshape(B, -1, 32)
@@ -117,12 +190,13 @@ def check_layer(w, d=None, ranks=None):
                                    f"{(diff[~flip] / step[~flip]).max():.3e} steps")
             assert np.all(np.abs(diff[flip] / step[flip] - 1) < 1e-3)
             assert flip.mean() < 1e-2, f"{key}: {flip.sum()} codes flipped"
-    e_h = rel_l2(g["h"].astype(np.float64) - x, o["h"] - x)
-    e_o = rel_l2(g["out"].astype(np.float64) - g["h"], o["out"] - o["h"])
-    errs["h-x"], errs["out-h"] = e_h, e_o
+            say(f"{w.name} {key}: {int(flip.sum())} of {flip.size} codes one step off the oracle's")
     tq = tol if not w.quant & synth.Q_PARTIALS else 2e-2
-    assert e_h <= tq and e_o <= tq, f"merge deltas {e_h:.3e} {e_o:.3e}"
-    say(f"{w.name} max rel-L2 {max(errs.values()):.3e}")
+    cmp("h-x", g["h"].astype(np.float64) - x, o["h"] - x, tq)
+    cmp("out-h", g["out"].astype(np.float64) - g["h"], o["out"] - o["h"], tq)
+    worst = max(errs, key=errs.get)
+    say(f"{w.name} max rel-L2 {errs[worst]:.3e} ({worst}); max-abs "
+        + " ".join(f"{k}={v:.2e}" for k, v in maxabs.items() if "[" not in k or k.endswith("[0]")))
     return L, g, o
 
 
@@ -276,36 +350,18 @@ def test_determinism_and_batch_rows():
         assert rel_l2(r1["out"][0] - r1["h"][0], a["out"][row] - a["h"][row]) < 1e-5
 
 
-def test_llama70b_tp8_b16_shards():
-    """Full 70B-shaped layer: shards 0 and 7 (attention stage on the seeded
-    input, FFN stage on a seeded stand-in for the merged residual), each
-    against the oracle's stage for that shard."""
-    w = synth.L70B
-    d = synth.llama_inputs(w)
-    say(f"{w.name} lens={d['lens'].tolist()}")
-    import torch
-    from gpu_harness import dev_tensor
-    ranks = [0, 7]
-    L = Layer(w, d, ranks=ranks)
-    x = dev_tensor(d["x"])
-    lens = dev_tensor(d["lens"])
-    h_np = synth.llama_x(w, stream_offset=1)
-    h = dev_tensor(h_np)
-    wa, ta = L.stage(tp.TP_STAGE_ATTN, x, lens, w.batch)
-    wf, tf = L.stage(tp.TP_STAGE_FFN, h, None, w.batch)
-    torch.cuda.synchronize()
-    kc, vc = d["kcache"].copy(), d["vcache"].copy()
-    for r in ranks:
-        say(f"{w.name} oracle shard {r}")
-        oa = oracle.attn_shard(w, d, r, d["x"], d["lens"], kc, vc)
-        of = oracle.ffn_shard(w, d, r, h_np)
-        for name, key, ref in (("q", "q", oa["q"]), ("k", "k", oa["k"]), ("v", "v", oa["v"]),
-                               ("att", "att", oa["att"]), ("p_att", "p_pre", oa["p"])):
-            e = rel_l2(ta[r][key].cpu().numpy(), ref)
-            assert e <= 1e-3, f"{name}[{r}] rel-L2 {e:.3e}"
-        for name, key, ref in (("hn", "xn", of["hn"]), ("a", "a", of["a"]), ("p_ffn", "p_pre", of["p"])):
-            e = rel_l2(tf[r][key].cpu().numpy(), ref)
-            assert e <= 1e-3, f"{name}[{r}] rel-L2 {e:.3e}"
+@pytest.mark.timeout(600)
+def test_llama70b_tp8_b16_all_shards_and_merges():
+    """The full 70B-shaped layer (TP = 8, batch 16, lengths in [1024, 4096]):
+    all 8 shards, their KV appends and both merges against the oracle's
+    layer, and the merges bit for bit against the host float32 sum of the
+    GPU's own wires. The oracle runs its OpenMP build here (the same bits as
+    the plain build, pinned on the CPU)."""
+    oracle.use_threads(True)
+    try:
+        check_layer(synth.L70B)
+    finally:
+        oracle.use_threads(False)
 
 
 def test_bad_length_sets_error_word_and_skips_row():

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import synth
-from conftest import rel_l2
+from conftest import golden_q8_blocks, rel_l2
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -159,26 +159,7 @@ def test_silu(orc):
 # ---------------------------------------------------------------- int8 codec
 
 def _golden_blocks():
-    blocks, cur = [], None
-    with open(os.path.join(GOLDEN, "q8_blocks.txt")) as f:
-        for line in f:
-            line = line.strip()
-            if not line or line.startswith("#"):
-                continue
-            if line.startswith("block"):
-                cur = {"name": line.split()[1], "x": [], "codes": []}
-                blocks.append(cur)
-            elif line.startswith("scale"):
-                cur["scale"] = _num(line.split()[1])
-            else:
-                a, b = line.split("->")
-                cur["x"].append(_num(a.strip()))
-                cur["codes"].append(int(b))
-    return blocks
-
-
-def _num(s):
-    return float.fromhex(s) if "0x" in s else float(s)
+    return golden_q8_blocks()
 
 
 @pytest.mark.parametrize("blk", _golden_blocks(), ids=lambda b: b["name"])
@@ -651,3 +632,29 @@ def test_batch_sharded_attention_single_position_returns_v(orc):
     for h in range(Hq):
         v = qkv[:, (Hq + Hkv + h // 2) * hd:(Hq + Hkv + h // 2 + 1) * hd]
         assert np.array_equal(att[:, h * hd:(h + 1) * hd], v.astype(np.float64))
+
+
+def test_openmp_build_returns_the_same_bits():
+    """The OpenMP build (independent rows, features and heads on several
+    threads, every sum in its order) equals the plain build bit for bit, on
+    a whole quantised GQA layer and the 2D FFN block."""
+    import oracle
+    w = synth.small_llama(name="omp_pin", dim=256, n_heads=8, n_kv_heads=2, head_dim=32,
+                          ffn_hidden=512, tp=2, batch=3, past=(5, 90), w_dtype=synth.BF16,
+                          kv_dtype=synth.BF16, quant=synth.Q_PARTIALS | synth.Q_INPUTS, seed=91)
+    d = synth.llama_inputs(w)
+    f2 = synth.ffn2d_inputs(synth.Ffn2D("omp_pin_2d", e_blk=64, f_blk=96, batch=4, seed=92))
+    outs = []
+    try:
+        for omp in (False, True):
+            oracle.use_threads(omp)
+            o = oracle.llama_layer(w, d, d["x"], d["lens"], d["kcache"].copy(), d["vcache"].copy())
+            y = oracle.ffn2d(f2["x"], f2["w_gate"], f2["w_in"], f2["w_out"])
+            outs.append((o, y))
+    finally:
+        oracle.use_threads(False)
+    (a, ya), (b, yb) = outs
+    for k, v in a.items():
+        if v is not None:
+            assert np.array_equal(np.asarray(v).view(np.uint8), np.asarray(b[k]).view(np.uint8)), k
+    assert np.array_equal(ya.view(np.uint8), yb.view(np.uint8))
