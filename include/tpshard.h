@@ -233,6 +233,31 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
                     int32_t batch, void *wire_out, const tp_taps *taps, void *hip_stream);
 
 /*
+ * decode_step_noalloc: decode_step for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same kernels, arguments and results as decode_step, but
+ * the per-step buffers (the workspace's regions) live in one static device
+ * array of the library, 16 MiB per GPU, held until the process ends; the
+ * handle's workspace, if any, is not used, and a TP_LLAMA_BLOCK handle may be
+ * loaded with workspace = NULL (its other stage calls then return
+ * TP_ESTATE). The array's address on each device is looked up when a handle
+ * is loaded on it. Nothing is allocated, freed or created by this call.
+ *  err_out: NULL or a device uint32 (4-byte aligned) into which the TP_DERR_*
+ *    bits of this call are ORed (the library never clears it).
+ *  Every call on one GPU uses that GPU's array: calls that overlap on one GPU
+ *  (concurrent streams, or host threads) race and must be serialised by the
+ *  caller. Each call writes every buffer region before reading it, so no state
+ *  carries over between calls.
+ *  The kernel-timing probe is not used by this call.
+ * Errors: those of decode_step; TP_EINVAL for a kind other than
+ * TP_LLAMA_BLOCK or a shard whose workspace (tp_sizes.workspace) exceeds the
+ * 16 MiB array; TP_EALIGN for a misaligned err_out.
+ */
+int32_t decode_step_noalloc(tp_shard *s, int32_t stage, const void *x, const int32_t *lens,
+                            int32_t batch, void *wire_out, const tp_taps *taps, uint32_t *err_out,
+                            void *hip_stream);
+
+/*
  * merge_partials: out = residual + sum_{i < n_wires} dequant(wires[i]) in the
  * order of the array (shard order), per element, in fp32; `wires` is a HOST
  * array of n_wires device pointers in this shard's wire format. out may

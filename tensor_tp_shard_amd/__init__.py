@@ -27,7 +27,8 @@ TP_OK, TP_EINVAL, TP_EALIGN, TP_ESTATE, TP_ENODEV, TP_EHIP, TP_ENOTIMPL = 0, -1,
 TP_DERR_LEN = 1
 
 # every symbol include/tpshard.h declares
-EXPORTS = ("init_shard", "load_weights", "decode_step", "merge_partials", "decode_merge_step",
+EXPORTS = ("init_shard", "load_weights", "decode_step", "decode_step_noalloc", "merge_partials",
+           "decode_merge_step",
            "merge_logits", "tp_all_to_all", "tp_wire_scales_offset",
            "tp_packed_int8_view",
            "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
@@ -75,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.init_shard.argtypes = [P, P, P]
         L.load_weights.argtypes = [P, P, P, P, P, P, P]
         L.decode_step.argtypes = [P, I32, P, P, I32, P, P, P]
+        L.decode_step_noalloc.argtypes = [P, I32, P, P, I32, P, P, P, P]
         L.merge_partials.argtypes = [P, I32, P, I32, P, P, I32, P]
         L.decode_merge_step.argtypes = [P, I32, P, P, I32, P, P, I32, P, P, P]
         L.merge_logits.argtypes = [P, P, I32, P, I32, P]
@@ -92,7 +94,7 @@ def lib() -> ctypes.CDLL:
         L.tp_status_str.argtypes = [I32]
         L.tp_status_str.restype = ctypes.c_char_p
         L.tp_last_error.restype = ctypes.c_char_p
-        for f in ("init_shard", "load_weights", "decode_step", "merge_partials",
+        for f in ("init_shard", "load_weights", "decode_step", "decode_step_noalloc", "merge_partials",
                   "decode_merge_step", "merge_logits", "tp_all_to_all", "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
                   "tp_packed_int8_view"):
             getattr(L, f).restype = I32
@@ -155,6 +157,16 @@ def decode_step(handle, stage: int, x, lens, batch: int, wire_out, taps: Optiona
     _check(lib().decode_step(handle, stage, _ptr(x), _ptr(lens), batch, _ptr(wire_out),
                              ctypes.byref(t) if t is not None else None, _stream(stream)),
            "decode_step")
+
+
+def decode_step_noalloc(handle, stage: int, x, lens, batch: int, wire_out,
+                        taps: Optional[dict] = None, err_out=None, stream=None):
+    t = None
+    if taps:
+        t = TpTaps(**{k: _ptr(v) for k, v in taps.items()})
+    _check(lib().decode_step_noalloc(handle, stage, _ptr(x), _ptr(lens), batch, _ptr(wire_out),
+                                     ctypes.byref(t) if t is not None else None, _ptr(err_out),
+                                     _stream(stream)), "decode_step_noalloc")
 
 
 def merge_partials(handle, stage: int, wires: Sequence, residual, out, batch: int, stream=None):
@@ -242,13 +254,15 @@ class Shard:
     """A shard handle plus torch-allocated device buffers of the sizes
     init_shard asks for (packed weights, K/V caches, workspace)."""
 
-    def __init__(self, cfg: TpConfig, device="cuda", caches: bool = True):
+    def __init__(self, cfg: TpConfig, device="cuda", caches: bool = True, workspace: bool = True):
         import torch
         self.cfg = cfg
         self.handle, self.sizes = init_shard(cfg)
         dev = torch.device(device)
         self.packed = torch.empty(self.sizes.packed_weights, dtype=torch.uint8, device=dev)
-        self.workspace = torch.empty(self.sizes.workspace, dtype=torch.uint8, device=dev)
+        # no workspace: the stages run only through decode_step_noalloc
+        self.workspace = (torch.empty(self.sizes.workspace, dtype=torch.uint8, device=dev)
+                          if workspace else None)
         kvt = torch.bfloat16 if cfg.kv_dtype == TP_BF16 else torch.float32
         self.k_cache = self.v_cache = None
         if caches and self.sizes.kv_cache_each:
@@ -268,6 +282,9 @@ class Shard:
 
     def step(self, stage, x, lens, batch, wire_out, taps=None, stream=None):
         decode_step(self.handle, stage, x, lens, batch, wire_out, taps, stream)
+
+    def step_noalloc(self, stage, x, lens, batch, wire_out, taps=None, err_out=None, stream=None):
+        decode_step_noalloc(self.handle, stage, x, lens, batch, wire_out, taps, err_out, stream)
 
     def merge(self, stage, wires, residual, out, batch, stream=None):
         merge_partials(self.handle, stage, wires, residual, out, batch, stream)

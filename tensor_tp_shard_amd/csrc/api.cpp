@@ -519,9 +519,11 @@ static int32_t load_attn_batch(tp_shard *s, void *packed, void *k_cache, void *v
 int32_t load_weights(tp_shard *s, const tp_layer_weights *w, void *packed, void *k_cache,
                      void *v_cache, void *workspace, void *hip_stream)
 {
-    if (!s || !w || !packed || !workspace)
+    const bool llama = s && s->cfg.kind == TP_LLAMA_BLOCK;
+    // a Llama block may be loaded without a workspace: its stages then run only
+    // through decode_step_noalloc, on the library's static scratch
+    if (!s || !w || !packed || (!workspace && !llama))
         return fail(TP_EINVAL, "load_weights: null argument");
-    const bool llama = s->cfg.kind == TP_LLAMA_BLOCK;
     if (s->cfg.kind == TP_LOGITS)
         return load_logits(s, w, packed, workspace, (hipStream_t)hip_stream);
     if (s->cfg.kind == TP_ATTN_BATCH)
@@ -650,9 +652,17 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *w, void *packed, void 
     s->ws = (char *)workspace;
     s->kc = k_cache;
     s->vc = v_cache;
-    const hipError_t ce = launch_clear_u32((unsigned *)(s->ws + s->w_err), 1, st);
-    if (ce)
-        return hip_fail(ce, "load_weights: clear error word");
+    if (llama) { // set-up of decode_step_noalloc: this device's scratch address, once per device
+        void *sp = nullptr;
+        const hipError_t se = scratch_address(&sp);
+        if (se)
+            return hip_fail(se, "load_weights: scratch address");
+    }
+    if (s->ws) {
+        const hipError_t ce = launch_clear_u32((unsigned *)(s->ws + s->w_err), 1, st);
+        if (ce)
+            return hip_fail(ce, "load_weights: clear error word");
+    }
     s->loaded = true;
     return TP_OK;
 }
@@ -753,14 +763,19 @@ static int32_t attn_batch_step(tp_shard *s, const float *x, const int32_t *lens,
 // kernel that writes this shard's own partial (wire mo->own = wire_out).
 static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeIn *mo,
                          const int32_t *lens, int32_t batch, void *wire_out, const tp_taps *taps,
-                         void *hip_stream)
+                         void *hip_stream, char *ws = nullptr, unsigned *err_word = nullptr)
 {
     if (!s)
         return fail(TP_EINVAL, "decode_step: null handle");
     if (!s->loaded)
         return fail(TP_ESTATE, "decode_step before load_weights");
-    char *ws = s->ws;
-    unsigned *err_word = (unsigned *)(ws + s->w_err);
+    // the workspace: the handle's, or (decode_step_noalloc) the static scratch
+    if (!ws)
+        ws = s->ws;
+    if (!ws)
+        return fail(TP_ESTATE, "no workspace was bound at load_weights: use decode_step_noalloc");
+    if (!err_word)
+        err_word = (unsigned *)(ws + s->w_err);
     if (stage != TP_STAGE_ATTN && stage != TP_STAGE_FFN && stage != TP_STAGE_LOGITS)
         return fail(TP_EINVAL, "unknown stage %d", stage);
     if ((stage == TP_STAGE_LOGITS) != (s->cfg.kind == TP_LOGITS))
@@ -960,6 +975,43 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
     return step_impl(s, stage, x, nullptr, lens, batch, wire_out, taps, hip_stream);
 }
 
+// decode_step on the static scratch (scratch.hip) instead of the handle's
+// workspace: the same kernels and arguments, the workspace regions at the
+// same offsets inside the scratch. Allocates nothing: the scratch address was
+// looked up when the handle was loaded; the kernel-timing probe is bypassed
+// (it would create events). No region of the workspace carries anything from
+// one call to the next (every kernel writes what a later one reads), and
+// device errors go to the caller's err_out (or to an unread word of the
+// scratch), so nothing in the scratch needs clearing.
+int32_t decode_step_noalloc(tp_shard *s, int32_t stage, const void *x, const int32_t *lens,
+                            int32_t batch, void *wire_out, const tp_taps *taps, uint32_t *err_out,
+                            void *hip_stream)
+{
+    if (!s)
+        return fail(TP_EINVAL, "decode_step_noalloc: null handle");
+    if (s->cfg.kind != TP_LLAMA_BLOCK)
+        return fail(TP_EINVAL, "decode_step_noalloc applies to TP_LLAMA_BLOCK shards");
+    if (!s->loaded)
+        return fail(TP_ESTATE, "decode_step_noalloc before load_weights");
+    if (s->ws_bytes > kScratchBytes)
+        return fail(TP_EINVAL,
+                    "decode_step_noalloc: this shard needs %llu bytes of workspace, the static "
+                    "scratch holds %llu (use decode_step with a workspace)",
+                    (unsigned long long)s->ws_bytes, (unsigned long long)kScratchBytes);
+    if (err_out && ((uintptr_t)err_out & 3u))
+        return fail(TP_EALIGN, "decode_step_noalloc: err_out not 4-byte aligned");
+    void *sp = nullptr;
+    const hipError_t se = scratch_address(&sp);
+    if (se)
+        return hip_fail(se, "decode_step_noalloc: scratch address");
+    const int armed = s->timing_kernel;
+    s->timing_kernel = -1;
+    const int32_t rc = step_impl(s, stage, x, nullptr, lens, batch, wire_out, taps, hip_stream,
+                                 (char *)sp, (unsigned *)err_out);
+    s->timing_kernel = armed;
+    return rc;
+}
+
 // Validates a merge request and fills mi (x_out = residual + sum of the wires).
 static int32_t merge_request(const tp_shard *s, int32_t stage, const void *const *wires,
                              int32_t n_wires, const float *residual, float *x_out, int32_t batch,
@@ -1150,6 +1202,8 @@ int32_t tp_read_error_word(tp_shard *s, uint32_t *word, int32_t clear, void *hip
         return fail(TP_EINVAL, "tp_read_error_word: null argument");
     if (!s->loaded)
         return fail(TP_ESTATE, "tp_read_error_word before load_weights");
+    if (!s->ws)
+        return fail(TP_ESTATE, "tp_read_error_word: no workspace was bound at load_weights");
     hipStream_t st = (hipStream_t)hip_stream;
     hipError_t e = hipMemcpyAsync(word, s->ws + s->w_err, 4, hipMemcpyDeviceToHost, st);
     if (!e && clear)
