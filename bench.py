@@ -224,7 +224,7 @@ def kernel_times(handles, st: Stepper, steps: int, names) -> Dict[str, float]:
         for h in handles:
             tp.kernel_timing_arm(h, kid)
         with torch.cuda.stream(st.stream):
-            torch.cuda._sleep(int(_sleep_cycles_per_ms() * (3 * host_ms + 2)))
+            torch.cuda._sleep(int(_sleep_cycles_per_ms() * min(3 * host_ms + 2, 250)))
             for i in range(steps):
                 st.step(i % st.R)
         torch.cuda.synchronize()
@@ -240,40 +240,42 @@ def kernel_times(handles, st: Stepper, steps: int, names) -> Dict[str, float]:
 
 
 def measured_peaks() -> Dict[str, float]:
-    """The denominators measured on this GPU with library code: a 2 GiB
-    read stream (the best of torch's sum / amax reductions) and a large bf16
-    GEMM (hipBLASLt through torch.matmul, 8192^3)."""
+    """The denominators measured on this GPU by the library's probes: a read
+    stream over 2 GiB (16-byte nontemporal loads, the best of three grid
+    sizes) and a bf16 MFMA loop with no memory traffic (the best of two
+    occupancies), each the best of 5 timed launches after a warm-up."""
     import torch
-    x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")  # 2 GiB
-    best = 0.0
-    for op in (torch.sum, torch.amax):
-        for _ in range(2):
-            op(x)
+    import tensor_tp_shard_amd as tp
+
+    def best_ms(launch, reps=5):
+        launch()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(5):
-            op(x)
-        e1.record()
-        torch.cuda.synchronize()
-        best = max(best, 5 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-    del x
-    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
-    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
-    for _ in range(3):
-        a @ b
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        a @ b
-    e1.record()
-    torch.cuda.synchronize()
-    tf = 10 * 2 * 8192 ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12
-    del a, b
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return min(out)
+
+    nbytes = 1 << 31
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+    gbps = max(nbytes / (best_ms(lambda: tp.probe_read(buf, nbytes, sink, blocks)) * 1e-3) / 1e9
+               for blocks in (1024, 2048, 4096))
+    del buf
+    iters = 2000
+    fout = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    tflops = max(blocks * 4 * iters * 4 * 32768 /
+                 (best_ms(lambda: tp.probe_mfma(blocks, iters, fout)) * 1e-3) / 1e12
+                 for blocks in (512, 1024))
+    del fout, sink
     torch.cuda.empty_cache()
-    return {"hbm_read_GBps": round(best, 1), "bf16_gemm_TFLOPs": round(tf, 1),
-            "how": "2 GiB fp32 read by torch.sum / torch.amax (best); bf16 8192^3 torch.matmul"}
+    return {"hbm_read_GBps": round(gbps, 1), "bf16_mfma_TFLOPs": round(tflops, 1),
+            "how": "library probes: 2 GiB read with 16-byte nontemporal loads (best of 1024/2048/4096 "
+                   "workgroups); bf16 32x32x16 MFMA loop from registers (best of 2 and 4 waves a SIMD)"}
 
 
 def summarize(ms: List[float], steps: int, unit_per_step: float = 1.0) -> dict:
@@ -878,10 +880,10 @@ def add_measured_fracs(res: dict, peaks: dict):
     if "achieved_GBps" in res:
         res["hbm_frac_of_measured"] = round(res["achieved_GBps"] / peaks["hbm_read_GBps"], 4)
     if "achieved_TFLOPs" in res:
-        res["mfma_frac_of_measured"] = round(res["achieved_TFLOPs"] / peaks["bf16_gemm_TFLOPs"], 4)
+        res["mfma_frac_of_measured"] = round(res["achieved_TFLOPs"] / peaks["bf16_mfma_TFLOPs"], 4)
     rf = res.get("roofline")
     if rf:
-        den = peaks["hbm_read_GBps"] if rf["unit"] == "GB/s" else peaks["bf16_gemm_TFLOPs"]
+        den = peaks["hbm_read_GBps"] if rf["unit"] == "GB/s" else peaks["bf16_mfma_TFLOPs"]
         rf["frac_of_measured"] = round(rf["achieved"] / den, 4)
 
 

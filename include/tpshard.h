@@ -357,6 +357,21 @@ int32_t tp_kernel_timing_arm(tp_shard *s, int32_t kernel_id);
 int32_t tp_kernel_timing_read(tp_shard *s, double *total_ms, int32_t *launches);
 const char *tp_kernel_name(int32_t kernel_id); /* NULL past the last id */
 
+/*
+ * Measured-peak probes: the benchmark's measured denominators, not steps of
+ * the shard. Enqueue only; the caller times them (HIP events).
+ *  tp_probe_read: `blocks` workgroups read [buf, buf + bytes) once, each a
+ *    contiguous span, with 16-byte nontemporal loads, eight per thread in
+ *    flight; out receives one uint32 per workgroup (an XOR of what it read).
+ *  tp_probe_mfma: `blocks` workgroups of 4 waves each run iters x 4
+ *    independent bf16 MFMAs (32 x 32 x 16: 32768 flops each) per wave from
+ *    registers, no memory traffic; out receives blocks * 256 floats.
+ *  Buffers 16-byte aligned; 1 <= blocks <= 2^20, iters >= 1.
+ * Errors: TP_EINVAL, TP_EALIGN, TP_ENODEV, TP_EHIP.
+ */
+int32_t tp_probe_read(const void *buf, uint64_t bytes, uint32_t *out, int32_t blocks, void *hip_stream);
+int32_t tp_probe_mfma(int32_t blocks, int32_t iters, float *out, void *hip_stream);
+
 void destroy_shard(tp_shard *s);
 const char *tp_status_str(int32_t status);
 const char *tp_last_error(void);

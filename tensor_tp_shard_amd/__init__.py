@@ -32,7 +32,8 @@ EXPORTS = ("init_shard", "load_weights", "decode_step", "decode_step_noalloc", "
            "merge_logits", "tp_all_to_all", "tp_wire_scales_offset",
            "tp_packed_int8_view",
            "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
-           "tp_kernel_name", "destroy_shard", "tp_status_str", "tp_last_error")
+           "tp_kernel_name", "tp_probe_read", "tp_probe_mfma", "destroy_shard", "tp_status_str",
+           "tp_last_error")
 
 
 class TpError(RuntimeError):
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.tp_packed_int8_view.argtypes = [P, I32, P, P, P, P]
         L.tp_kernel_timing_arm.argtypes = [P, I32]
         L.tp_kernel_timing_read.argtypes = [P, P, P]
+        L.tp_probe_read.argtypes = [P, U64, P, I32, P]
+        L.tp_probe_mfma.argtypes = [I32, I32, P, P]
         L.tp_kernel_name.argtypes = [I32]
         L.tp_kernel_name.restype = ctypes.c_char_p
         L.destroy_shard.argtypes = [P]
@@ -96,7 +99,7 @@ def lib() -> ctypes.CDLL:
         L.tp_last_error.restype = ctypes.c_char_p
         for f in ("init_shard", "load_weights", "decode_step", "decode_step_noalloc", "merge_partials",
                   "decode_merge_step", "merge_logits", "tp_all_to_all", "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
-                  "tp_packed_int8_view"):
+                  "tp_packed_int8_view", "tp_probe_read", "tp_probe_mfma"):
             getattr(L, f).restype = I32
         _lib = L
     return _lib
@@ -241,6 +244,16 @@ def kernel_names():
             return out
         out.append(n.decode())
         i += 1
+
+
+def probe_read(buf, nbytes: int, out, blocks: int, stream=None):
+    """Enqueues the read-stream probe over nbytes of buf (measurement only)."""
+    _check(lib().tp_probe_read(_ptr(buf), nbytes, _ptr(out), blocks, _stream(stream)), "tp_probe_read")
+
+
+def probe_mfma(blocks: int, iters: int, out, stream=None):
+    """Enqueues the bf16 MFMA-loop probe (measurement only)."""
+    _check(lib().tp_probe_mfma(blocks, iters, _ptr(out), _stream(stream)), "tp_probe_mfma")
 
 
 def destroy_shard(handle):

@@ -1247,6 +1247,32 @@ const char *tp_kernel_name(int32_t kernel_id)
     return (kernel_id >= 0 && kernel_id < KID_COUNT) ? kKernelNames[kernel_id] : nullptr;
 }
 
+int32_t tp_probe_read(const void *buf, uint64_t bytes, uint32_t *out, int32_t blocks, void *hip_stream)
+{
+    if (!buf || !out || bytes == 0 || blocks < 1 || blocks > (1 << 20))
+        return fail(TP_EINVAL, "tp_probe_read: null buffer, no bytes or blocks outside [1, 2^20]");
+    if (!aligned16(buf) || !aligned16(out))
+        return fail(TP_EALIGN, "tp_probe_read: buffers not 16-byte aligned");
+    const int32_t rc = check_device();
+    if (rc)
+        return rc;
+    const hipError_t e = launch_probe_read(buf, bytes, out, blocks, (hipStream_t)hip_stream);
+    return e ? hip_fail(e, "tp_probe_read") : TP_OK;
+}
+
+int32_t tp_probe_mfma(int32_t blocks, int32_t iters, float *out, void *hip_stream)
+{
+    if (!out || blocks < 1 || blocks > (1 << 20) || iters < 1)
+        return fail(TP_EINVAL, "tp_probe_mfma: null out, blocks outside [1, 2^20] or iters < 1");
+    if (!aligned16(out))
+        return fail(TP_EALIGN, "tp_probe_mfma: out not 16-byte aligned");
+    const int32_t rc = check_device();
+    if (rc)
+        return rc;
+    const hipError_t e = launch_probe_mfma(blocks, iters, out, (hipStream_t)hip_stream);
+    return e ? hip_fail(e, "tp_probe_mfma") : TP_OK;
+}
+
 const char *tp_status_str(int32_t st)
 {
     switch (st) {

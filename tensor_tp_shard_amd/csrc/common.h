@@ -410,6 +410,10 @@ hipError_t launch_clear_u32(unsigned *p, int n, hipStream_t st);
 hipError_t launch_ffn2d(const Ffn2dArgs &a, hipStream_t st, int which);
 int ffn2d_splits(int B, int E, int F);
 
+// measured-peak probes (k_probe.hip)
+hipError_t launch_probe_read(const void *buf, uint64_t bytes, uint32_t *out, int blocks, hipStream_t st);
+hipError_t launch_probe_mfma(int blocks, int iters, float *out, hipStream_t st);
+
 // The static device buffer behind decode_step_noalloc (scratch.hip): its size,
 // and its address on the current device (looked up once per device, then cached).
 constexpr size_t kScratchBytes = (size_t)16 << 20;
