@@ -879,10 +879,18 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
     down.tap = tp.p_pre;
     down.N = s->D;
     down.ldy = s->D;
-    if (mo && !qpart) // fp32 wires: the down-projection's store epilogue merges
-        down.mo = *mo;
     down.B = B;
     const int Kd = stage == TP_STAGE_ATTN ? s->Hq_s * s->hd : s->Fs;
+    // int8 wire below batch 5: the down-projection's epilogue quantises its
+    // partial into the wire (and merges the int8 wires), no k_wire launch
+    const bool wire_epi = qpart && !mfma && gemv_fused_ok(B, Kd);
+    if (mo && (!qpart || wire_epi)) // the down-projection's epilogue merges
+        down.mo = *mo;
+    if (wire_epi) {
+        down.codes = codes;
+        down.scales = scales;
+    }
+    const int down_epi = wire_epi ? EPI_Q8 : EPI_STORE;
     auto run_gemv = [&](const GemvArgs &g, const uint16_t *xf, uint16_t *yf, int epi, bool norm) {
         if (!mfma)
             return launch_gemv(g, wt, epi, st);
@@ -936,7 +944,7 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         down.x = att;
         down.K = Kd;
         down.ldx = Kd;
-        rc = timed(s, KID_GEMV_WO, st, "gemv wo", [&] { return run_gemv(down, xfatt, nullptr, EPI_STORE, false); });
+        rc = timed(s, KID_GEMV_WO, st, "gemv wo", [&] { return run_gemv(down, xfatt, nullptr, down_epi, false); });
         if (rc)
             return rc;
     } else {
@@ -955,12 +963,12 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         down.x = a;
         down.K = Kd;
         down.ldx = Kd;
-        rc = timed(s, KID_GEMV_W2, st, "gemv w2", [&] { return run_gemv(down, xfa, nullptr, EPI_STORE, false); });
+        rc = timed(s, KID_GEMV_W2, st, "gemv w2", [&] { return run_gemv(down, xfa, nullptr, down_epi, false); });
         if (rc)
             return rc;
     }
 
-    if (qpart) {
+    if (qpart && !wire_epi) {
         WireArgs wa{p, codes, scales, B, s->D, {}};
         if (mo) // int8 wires: the quantiser merges
             wa.mo = *mo;

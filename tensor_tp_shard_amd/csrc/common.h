@@ -284,7 +284,11 @@ struct MfmaGemvArgs {
     const float *ws;     // int8 weights: W holds the codes, ws the scales [N][K/32]
 };
 
-enum GemvEpi { EPI_STORE = 0, EPI_SWIGLU = 1 };
+// EPI_Q8 (batch <= 4, LDS-staged GEMV only): the row-split projection's
+// partial goes straight into the block-32 int8 wire (codes + scales), each
+// workgroup owning whole 32-row blocks; with a merge request the int8 wires
+// are merged in the same epilogue.
+enum GemvEpi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_Q8 = 2 };
 
 // Weight types of the projections: fp32, bf16, or int8 codes with one fp32
 // scale per 32 consecutive k of a row (the block-32 codec applied to the
@@ -307,8 +311,11 @@ struct GemvArgs {
     float *xn_tap;       // [B][K]: the normalised rows, written by block 0
     float *xq_tap;       // [B][K]: the same before the int8 round trip, block 0
     // EPI_STORE, fp32 wires: merge of the stage's partials (this kernel's
-    // output y is wire mo.own), written to mo.x_out [B][ldy]
+    // output y is wire mo.own), written to mo.x_out [B][ldy]; EPI_Q8: the
+    // same with int8 wires
     MergeIn mo;
+    int8_t *codes;       // EPI_Q8: [B][ldy] int8 codes of the wire
+    float *scales;       // EPI_Q8: [B][ldy/32] block scales
 };
 
 struct AttnArgs {

@@ -213,7 +213,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_lds(GemvArgs a)
     // residual and the other wires' elements before the weights are requested
     float mres = 0.f;
     uint2 mpre[kMO];
-    if constexpr (MO) {
+    // EPI_Q8: thread t < 32 NB quantises (and merges) output row
+    // blockIdx.x * 32 + t % 32 of batch row t / 32
+    const int qb = tid >> 5, qi = tid & 31, qrow = blockIdx.x * 32 + qi;
+    const bool qact = EPI == EPI_Q8 && qb < a.B && qrow < a.N;
+    if constexpr (MO && EPI == EPI_Q8) {
+        if (tid < 32 * NB && qact)
+            merge_preload1<true>(a.mo, (size_t)qb * a.ldy + qrow, mres, mpre);
+    } else if constexpr (MO) {
         const int mr = lane / NB, mb = lane % NB;
         if (active && lane < RPW * NB && mb < a.B)
             merge_preload1<false>(a.mo, (size_t)mb * a.ldy + row0v + mr, mres, mpre);
@@ -273,6 +280,35 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_lds(GemvArgs a)
         for (int b = 0; b < NB; b++)
             acc[r][b] = group_sum<64>(acc[r][b]);
 
+    if constexpr (EPI == EPI_Q8) {
+        static_assert(NW * RPW == 32, "a workgroup owns one 32-row block of the wire");
+        // the block's 32 x NB partials through LDS, then one 32-lane group per
+        // batch row: block max, scale, codes, and the merge of the int8 wires
+        __shared__ float pq[32][NB];
+        if (active && lane == 0)
+#pragma unroll
+            for (int r = 0; r < RPW; r++)
+#pragma unroll
+                for (int b = 0; b < NB; b++)
+                    pq[wv * RPW + r][b] = acc[r][b];
+        __syncthreads();
+        if (tid < 32 * NB) { // whole 32-lane groups: the butterfly below needs every lane
+            const float v = qact ? pq[qi][qb] : 0.f;
+            const float sc = q8_scale(group_max<32>(fabsf(v)));
+            if (qact) {
+                const size_t e = (size_t)qb * a.ldy + qrow;
+                const int code = q8_code(v, sc);
+                a.codes[e] = (int8_t)code;
+                if (qi == 0)
+                    a.scales[(size_t)qb * (a.ldy / kQBlock) + qrow / kQBlock] = sc;
+                if (a.tap)
+                    a.tap[e] = v;
+                if constexpr (MO)
+                    merge_finish1<true>(a.mo, e, q8_dequant(code, sc), mres, mpre);
+            }
+        }
+        return;
+    }
     if (active) {
         if constexpr (EPI == EPI_SWIGLU) {
             static_assert(RPW == 2, "SwiGLU pairs rows (W1_f, W3_f)");
@@ -413,7 +449,15 @@ template <int WT, int NB>
 static hipError_t launch_lds(const GemvArgs &a, int epi, hipStream_t st)
 {
     const size_t sm = gemv_lds_bytes(a.B, a.K);
-    if (epi == EPI_SWIGLU) {
+    if (epi == EPI_Q8) { // 32-row workgroups: eight waves of four rows (sixteen waves of two
+                         // rows were slower: 7B int8-wire step 45.8 -> 49.4 us)
+        if (a.mo.n_wires)
+            hipLaunchKernelGGL((k_gemv_lds<WT, NB, 4, EPI_Q8, true, 8>), dim3((a.N + 31) / 32), dim3(512), sm,
+                               st, a);
+        else
+            hipLaunchKernelGGL((k_gemv_lds<WT, NB, 4, EPI_Q8, false, 8>), dim3((a.N + 31) / 32), dim3(512), sm,
+                               st, a);
+    } else if (epi == EPI_SWIGLU) {
         const dim3 grid((a.N + 4 * kRPW - 1) / (4 * kRPW));
         hipLaunchKernelGGL((k_gemv_lds<WT, NB, kRPW, EPI_SWIGLU, false, 4>), grid, dim3(256), sm, st, a);
     } else if (a.mo.n_wires) {
@@ -453,8 +497,8 @@ static hipError_t launch_t(const GemvArgs &a, int epi, hipStream_t st)
             return launch_lds<WT, 2>(a, epi, st);
         return launch_lds<WT, 4>(a, epi, st);
     }
-    if (a.g)
-        return hipErrorInvalidValue; // the fused norm needs the LDS path
+    if (a.g || epi == EPI_Q8)
+        return hipErrorInvalidValue; // the fused norm and the int8 epilogue need the LDS path
     if (a.B <= 8)
         return launch_gx<WT, 8>(a, epi, st);
     return launch_gx<WT, 16>(a, epi, st);
