@@ -277,11 +277,21 @@ static Ffn2dCfg ffn2d_cfg(int B)
     return {256, 32, 8};
 }
 
+// The down-projection's tiles: 64 rows up to 1024 (twice the output tiles of
+// 128-row tiles, so half the K splits and half the fp32 partials written and
+// read back), else those of the up-projection.
+static Ffn2dCfg ffn2d_cfg_down(int B)
+{
+    if (B <= 1024)
+        return {64, 64, 4};
+    return ffn2d_cfg(B);
+}
+
 // Number of K splits of the down-projection for a batch of B rows: enough
 // workgroups for the 256 CUs when the output has few tiles.
 int ffn2d_splits(int B, int E, int F)
 {
-    const Ffn2dCfg c = ffn2d_cfg(B);
+    const Ffn2dCfg c = ffn2d_cfg_down(B);
     const int tiles = ((B + c.bm - 1) / c.bm) * (E / kBN);
     int s = 256 / (tiles > 0 ? tiles : 1);
     s = s < 1 ? 1 : s > 8 ? 8 : s;
@@ -320,12 +330,14 @@ hipError_t launch_ffn2d(const Ffn2dArgs &f, hipStream_t st, int which)
         launch_gemm_cfg<FFN_UP>(c, g, dim3(2 * f.F / kBN, mt, 1), st);
         return hipGetLastError();
     }
+    const Ffn2dCfg cd = ffn2d_cfg_down(f.B);
+    const int mtd = (f.B + cd.bm - 1) / cd.bm;
     const int S = ffn2d_splits(f.B, f.E, f.F);
-    const int ksteps = f.F / c.kb;
+    const int ksteps = f.F / cd.kb;
     const int per = (ksteps + S - 1) / S;
     const int splits = (ksteps + per - 1) / per;
     GemmArgs g{f.h, f.w2, nullptr, splits > 1 ? f.part : f.y, f.B, f.E, f.F, per};
-    launch_gemm_cfg<FFN_DOWN>(c, g, dim3(f.E / kBN, mt, splits), st);
+    launch_gemm_cfg<FFN_DOWN>(cd, g, dim3(f.E / kBN, mtd, splits), st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1)
         return e;
