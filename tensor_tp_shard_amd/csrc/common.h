@@ -56,6 +56,10 @@ __device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2); // nontemporal
 }
 
+// s_waitcnt vmcnt(0), the other counters unconstrained (gfx9 encoding): no
+// vector memory operation of this wave in flight afterwards
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+
 // ---------------------------------------------------------------- wave reductions
 
 // Rotation right by N lanes inside each 16-lane row (DPP row_ror:N, a VALU

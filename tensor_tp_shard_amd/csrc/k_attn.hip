@@ -590,26 +590,17 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(AttnArgs a)
 {
     extern __shared__ float smem[];
     const int hd = a.hd, h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int L = a.lens[b];
     const size_t ob = (size_t)b * a.Hq_s * hd + (size_t)h * hd;
-    if (L < 0 || L >= a.max_ctx) { // skipped sequence: its attention output is 0
-        for (int i = tid; i < hd; i += kCombThreads) {
-            a.att[ob + i] = 0.f;
-            if (a.tap_att)
-                a.tap_att[ob + i] = 0.f;
-            if (a.att_xf)
-                xf_store(a.att_xf, b, h * hd + i, 0.f);
-        }
-        return;
-    }
-    const int nch = L / kChunk + 1;
     const float *rec = a.part + ((size_t)b * a.Hq_s + h) * (size_t)a.n_chunks * (hd + 4);
     float *wts = smem;                                // [n_chunks] e^(m_c - M)
     float *inv_l = wts + a.n_chunks;                  // [1]
     float *osum = smem + ((a.n_chunks + 4 + 3) & ~3); // [phases][hd]
     const int w = tid >> 6, lane = tid & 63;
+    // the first batch of chunk records (of every chunk the grid has: 528 bytes
+    // each) is requested before the sequence length is read; records of
+    // chunks past the sequence are stale and masked below
     float2 ml0 = make_float2(-INFINITY, 0.f);
-    if (w == 0 && lane < nch)
+    if (w == 0 && lane < a.n_chunks)
         ml0 = *(const float2 *)(rec + (size_t)lane * (hd + 4));
     const int quads = hd / 4;
     const int cph = kCombThreads / quads;             // chunk phases (quads <= 32)
@@ -621,9 +612,24 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(AttnArgs a)
 #pragma unroll
     for (int u = 0; u < kCU; u++) {
         const int cc = cp + u * cph;
-        if (qact && cc < nch)
+        if (qact && cc < a.n_chunks)
             v[u] = *(const float4 *)(rd + (size_t)cc * (hd + 4));
     }
+    const int L = a.lens[b];
+    if (L < 0 || L >= a.max_ctx) { // skipped sequence: its attention output is 0
+        wait_vmcnt0(); // nothing in flight when the wave ends
+        for (int i = tid; i < hd; i += kCombThreads) {
+            a.att[ob + i] = 0.f;
+            if (a.tap_att)
+                a.tap_att[ob + i] = 0.f;
+            if (a.att_xf)
+                xf_store(a.att_xf, b, h * hd + i, 0.f);
+        }
+        return;
+    }
+    const int nch = L / kChunk + 1;
+    if (lane >= nch)
+        ml0 = make_float2(-INFINITY, 0.f);
     if (w == 0) {
         float m = ml0.x;
         for (int cc = lane + 64; cc < nch; cc += 64) // sequences longer than 64 chunks
