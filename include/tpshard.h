@@ -174,14 +174,22 @@ typedef struct {
 
 /*
  * init_shard: validate cfg, plan the shard's slice and return a host handle
- * and the device buffer sizes. Host only: enqueues nothing and needs no GPU.
+ * and the device buffer sizes. The slice follows aiterms.tw "Tensor
+ * Parallelism", 核心概念 items 1 and 2: the shard keeps whole output rows of
+ * the column-split projections (its q / kv heads of Wq, Wk, Wv and its FFN
+ * features of W1, W3) and the matching input columns of the row-split ones
+ * (Wo, W2), whose products are full-size partials to be summed. Host only: enqueues nothing and needs no GPU.
  * Errors: TP_EINVAL (null pointer, unknown enum, shape rule above broken).
  */
 int32_t init_shard(const tp_config *cfg, tp_shard **out, tp_sizes *sizes);
 
 /*
  * load_weights: slice the shard's part out of the FULL layer weights and
- * pack it into `packed` (layout private to the library), compute the RoPE
+ * pack it into `packed` (layout private to the library; the slices are those
+ * of aiterms.tw "Tensor Parallelism", 核心概念 items 1-2, and the KV heads a
+ * shard owns follow CS349E lecture 4, 03_pope_partitioning.py, demo 3
+ * observations: with TP up to the number of KV heads, each KV head lives on
+ * exactly one shard), compute the RoPE
  * cos/sin table (fp64 on the device, stored fp32) into `packed`, clear the
  * device error word in `workspace`, and remember k_cache / v_cache /
  * workspace for later calls. Enqueued on hip_stream; the caller must keep
@@ -197,7 +205,13 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *full, void *packed, vo
                      void *v_cache, void *workspace, void *hip_stream);
 
 /*
- * decode_step: one stage of the shard's decode step for `batch` rows.
+ * decode_step: one stage of the shard's decode step for `batch` rows: the
+ * worker side of one layer of distributed-llama issue "[Feature Suggest]
+ * Tensor Parallellism for Accelerating LLM", buildLlama2Arch (attention
+ * stage: llamaRmsAttNorm, llamaQuantizeRmsAtt, llamaQkv, llamaMultiheadAtt,
+ * llamaAttOutput, llamaQuantizeAtt; FFN stage: llamaRmfFfnNorm,
+ * llamaQuantizeRmfFfn, llamaFfn, llamaFfn2, llamaQuantizeFfn2), with every
+ * shard normalising its own input instead of receiving the root's.
  *  stage TP_STAGE_ATTN: x = fp32 [batch][D] residual input; lens = device
  *    int32 [batch] cached positions per sequence: the new token's K/V are
  *    written at slot lens[b] and attention covers lens[b] + 1 positions.
@@ -258,7 +272,10 @@ int32_t decode_step_noalloc(tp_shard *s, int32_t stage, const void *x, const int
                             void *hip_stream);
 
 /*
- * merge_partials: out = residual + sum_{i < n_wires} dequant(wires[i]) in the
+ * merge_partials (distributed-llama issue, buildLlama2Arch: llamaSyncAtt /
+ * llamaDequantizeAtt / llamaMergeAtt and their FFN counterparts; aiterms.tw
+ * "Tensor Parallelism", 運作原理: the row-split partials' all-reduce):
+ * out = residual + sum_{i < n_wires} dequant(wires[i]) in the
  * order of the array (shard order), per element, in fp32; `wires` is a HOST
  * array of n_wires device pointers in this shard's wire format. out may
  * alias residual. fp32 [batch][D] throughout.

@@ -167,8 +167,12 @@ __global__ __launch_bounds__(64 * NWV, (KB == 32 && NWV == 4) ? 2 : 1) void k_ge
             wait_vmcnt<0>();
         }
         // every wave's stage ks is in LDS and stage ks-1's buffer is free; a bare
-        // barrier (no fence: a fence would also wait for the later stages' loads)
+        // barrier (no fence: a fence would also wait for the later stages' loads),
+        // with compiler-only memory clobbers on both sides so that no LDS read or
+        // load issue can be moved across it
+        asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         if (ks + kStages - 1 < nks)
             issue(ks + kStages - 1);
         const char *As = lds + (ks % kStages) * kStageB, *Bs = As + BM * kRowB;
