@@ -238,7 +238,7 @@ __global__ __launch_bounds__(64 * mfma_max_waves(T, W8)) void k_gemv_mfma(MfmaGe
 // row's sum of squares over their slice, and the reduce scales row b by
 // 1 / sqrt(sum / K + eps). This drops the RMSNorm launch that had to finish
 // before the projection (70B step 97.4 -> 88.9 us with the reduce below).
-constexpr int kSkWaves = 8, kSkMaxNbs = 8;
+constexpr int kSkMaxNbs = 8;
 
 // s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding)
 template <int N>
@@ -253,17 +253,21 @@ __device__ __forceinline__ void wait_vmcnt()
 // consecutive k = 128 (jb + jl) + 32 s + 8 q of row b, where u = ((jl * 4 +
 // s) * 4 + q) * 16 + b is also its 16-byte unit in the fragment layout;
 // the workgroups of tile column 0 add up each row's squares over the slice.
-constexpr int kSkUnits = kSkMaxNbs * 256 / (64 * kSkWaves); // 8-element units per thread
+template <int NW>
+constexpr int sk_units() { return (kSkMaxNbs * 256 + 64 * NW - 1) / (64 * NW); } // 8-element units per thread
 
 // W8: int8 weights as in k_gemv_mfma (each MFMA step one 32-block, operands
 // swapped, the step's product times the row's scale); the lane's partials
 // (row r, batches 4q..4q+3) are stored one by one.
-template <int T, bool NORM, bool W8>
-__global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
+// NW waves a workgroup (8, or 7 where that makes the tile columns times the
+// slices fill the 256 CUs: 70B W1/W3, 224 -> 256 workgroups).
+template <int T, int NW, bool NORM, bool W8>
+__global__ __launch_bounds__(64 * NW) void k_gemv_sk(MfmaGemvArgs a)
 {
+    constexpr int kSkUnits = sk_units<NW>();
     constexpr int P = W8 ? 4 : 2; // 128-wide K blocks in flight per wave (the same bytes)
     __shared__ __attribute__((aligned(1024))) char lds[kSkMaxNbs * 8192];
-    __shared__ float ssr[NORM ? 64 * kSkWaves : 1];
+    __shared__ float ssr[NORM ? 64 * NW : 1];
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
     const int ks = blockIdx.y, jb = ks * a.nbs;
     const int nbl = min(a.nbs, (a.K >> 7) - jb); // blocks in this slice
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
         const __amdgpu_buffer_rsrc_t gr = buf_rsrc(a.g, (uint32_t)a.K * 4);
 #pragma unroll
         for (int i = 0; i < kSkUnits; i++) {
-            const int u = threadIdx.x + 64 * kSkWaves * i;
+            const int u = threadIdx.x + 64 * NW * i;
             const uint32_t k = (uint32_t)(jb << 7) + (u >> 4) * 8;
             const bool in = u < 256 * nbl;
             const uint32_t xo = in && b < a.B ? ((uint32_t)b * a.K + k) * 4 : kOob;
@@ -290,16 +294,16 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
     } else {
         // the slice's fragments: nbl x 8 KiB = 8 nbl wave loads of 1 KiB
         const u32x4 *xf = (const u32x4 *)a.xf + (size_t)jb * 512;
-        for (int seg = wv; seg < 8 * nbl; seg += kSkWaves)
+        for (int seg = wv; seg < 8 * nbl; seg += NW)
             __builtin_amdgcn_global_load_lds((const void *)(xf + (size_t)seg * 64 + lane),
                                              (__attribute__((address_space(3))) void *)(lds + seg * 1024), 16, 0, 0);
     }
-    const int n0 = (blockIdx.x * kSkWaves + wv) * 16 * T;
+    const int n0 = (blockIdx.x * NW + wv) * 16 * T;
     // one resource per 16-row tile from the slice start of its first row (wave
     // uniform, so the descriptor stays in scalar registers); lane (q, r) reads
     // row r at r K + 128 (block) + 32 s + 8 q elements, blocks past the slice
     // at kOob
-    const int n0u = (blockIdx.x * kSkWaves + __builtin_amdgcn_readfirstlane(wv)) * 16 * T;
+    const int n0u = (blockIdx.x * NW + __builtin_amdgcn_readfirstlane(wv)) * 16 * T;
     // (W8: codes K bytes a row, the lane's 8 bytes of a step at 32 s + 8 q;
     // scales K / 32 floats a row, the block's four at 16 bytes)
     constexpr uint32_t eb = W8 ? 1 : 2; // bytes per weight
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
                 float ss = 0.f;
 #pragma unroll
                 for (int i = 0; i < kSkUnits; i++) {
-                    const int u = threadIdx.x + 64 * kSkWaves * i;
+                    const int u = threadIdx.x + 64 * NW * i;
                     if (u < 256 * nbl) {
                         float e[8], f[8];
 #pragma unroll
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemv_sk(MfmaGemvArgs a)
                 if (blockIdx.x == 0 && threadIdx.x < 16) {
                     // row b's squares over the slice, threads b, b + 16, ... in order
                     float t3 = 0.f;
-                    for (int i = 0; i < 4 * kSkWaves; i++)
+                    for (int i = 0; i < 4 * NW; i++)
                         t3 += ssr[threadIdx.x + 16 * i];
                     a.part[(size_t)a.S * a.B * a.N + ks * 16 + threadIdx.x] = t3;
                 }
@@ -537,32 +541,45 @@ __global__ __launch_bounds__(64) void k_gemv_sk_epi(MfmaGemvArgs a)
 // slice and slices, aiming at up to 256 workgroups; T = 0 when the shape
 // does not tile (the per-tile kernel takes it).
 struct SkShape {
-    int T, nbs, S, R;
+    int T, nbs, S, R, NW;
 };
 static SkShape sk_shape(int N, int K)
 {
     const int nb = K / 128;
-    SkShape sh{0, 0, 0, 0};
+    SkShape sh{0, 0, 0, 0, 0};
     // only long K: with K < 4096 the per-tile kernel's activation traffic is
     // small and the reduce launch would cost more than it saves (70B W_O and
     // W2 measured slower split)
     if (K % 128 || K < 4096)
         return sh;
+    int T;
     if (N % 256 == 0 && N / 256 >= 16)
-        sh.T = 2;
+        T = 2;
     else if (N % 16 == 0) // a ragged last tile column: its tiles past N are idle
-        sh.T = 1;
+        T = 1;
     else
         return sh;
-    sh.R = (N + 128 * sh.T - 1) / (128 * sh.T);
-    // at most 256 workgroups: the folded-RMSNorm kernel holds one 8-wave
-    // workgroup per CU, so a 257th would run in a second round (70B
-    // up-projection: 280 -> 224 workgroups, 34.8 -> 33.5 us)
-    const int st = 256 / sh.R > 1 ? 256 / sh.R : 1;
-    int nbs = (nb + st - 1) / st;
-    nbs = nbs < 2 ? 2 : nbs > kSkMaxNbs ? kSkMaxNbs : nbs;
-    sh.nbs = nbs;
-    sh.S = (nb + nbs - 1) / nbs;
+    // at most 256 workgroups: the folded-RMSNorm kernel holds one workgroup
+    // per CU, so a 257th would run in a second round (70B up-projection: 280
+    // -> 224 workgroups, 34.8 -> 33.5 us). Of 8 and 7 waves a workgroup, the
+    // one whose grid keeps more CUs busy with live tiles (a weights-only
+    // probe of the 70B W1/W3 grid: 224 workgroups of 8 waves 23.8 us, 256 of
+    // 7 waves 21.5 us)
+    double best = -1.0;
+    for (const int NW : {8, 7}) {
+        const int tiles = N / 16, R = (tiles + T * NW - 1) / (T * NW);
+        const int st = 256 / R > 1 ? 256 / R : 1;
+        int nbs = (nb + st - 1) / st;
+        nbs = nbs < 2 ? 2 : nbs > kSkMaxNbs ? kSkMaxNbs : nbs;
+        const int S = (nb + nbs - 1) / nbs;
+        if (NW != 8 && R * S > 256)
+            continue;
+        const double busy = (double)R * S * tiles / ((double)R * T * NW);
+        if (busy > best + 1e-9) {
+            best = busy;
+            sh = SkShape{T, nbs, S, R, NW};
+        }
+    }
     return sh;
 }
 
@@ -591,13 +608,17 @@ hipError_t launch_gemv_mfma(const MfmaGemvArgs &a0, int epi, hipStream_t st)
     if (a.part && sh.T) {
         a.nbs = sh.nbs;
         a.S = sh.S;
-        const dim3 grid(sh.R, sh.S), block(64 * kSkWaves);
-#define TPS_SK(NORM, W8)                                                           \
-    do {                                                                           \
-        if (sh.T == 2)                                                             \
-            hipLaunchKernelGGL((k_gemv_sk<2, NORM, W8>), grid, block, 0, st, a);   \
-        else                                                                       \
-            hipLaunchKernelGGL((k_gemv_sk<1, NORM, W8>), grid, block, 0, st, a);   \
+        const dim3 grid(sh.R, sh.S), block(64 * sh.NW);
+#define TPS_SK(NORM, W8)                                                             \
+    do {                                                                             \
+        if (sh.T == 2 && sh.NW == 7)                                                 \
+            hipLaunchKernelGGL((k_gemv_sk<2, 7, NORM, W8>), grid, block, 0, st, a);  \
+        else if (sh.T == 2)                                                          \
+            hipLaunchKernelGGL((k_gemv_sk<2, 8, NORM, W8>), grid, block, 0, st, a);  \
+        else if (sh.NW == 7)                                                         \
+            hipLaunchKernelGGL((k_gemv_sk<1, 7, NORM, W8>), grid, block, 0, st, a);  \
+        else                                                                         \
+            hipLaunchKernelGGL((k_gemv_sk<1, 8, NORM, W8>), grid, block, 0, st, a);  \
     } while (0)
         if (a.xs) {
             if (a.ws)

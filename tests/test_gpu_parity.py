@@ -258,13 +258,26 @@ def test_splitk_folded_norm_ragged_batch(quant):
 
 @pytest.mark.parametrize("quant", [synth.Q_NONE, synth.Q_WEIGHTS])
 def test_splitk_ragged_tile_column(quant):
-    """Batch 9 at dim 4096 with Wqkv of 192 rows: the split-K up-projection's
-    second tile column holds 64 rows, so 4 of its 8 waves are past N (empty
-    weight resource, no partial stores) while still taking part in the
-    workgroup's barriers; bf16 and int8 weights."""
+    """Batch 9 at dim 4096 with Wqkv of 192 rows (12 tiles of 16): the
+    split-K up-projection takes 7-wave workgroups, so its second tile column
+    holds 5 tiles and 2 of its 7 waves are past N (empty weight resource, no
+    partial stores) while still taking part in the workgroup's barriers; bf16
+    and int8 weights."""
     w = synth.small_llama(name=f"splitk_ragged_q{quant}", dim=4096, n_heads=8, n_kv_heads=2, head_dim=32,
                           ffn_hidden=4096, tp=2, batch=9, past=(1, 50), w_dtype=synth.BF16,
                           kv_dtype=synth.BF16, quant=quant, seed=81)
+    check_layer(w)
+
+
+@pytest.mark.parametrize("quant", [synth.Q_NONE, synth.Q_WEIGHTS])
+def test_splitk_seven_wave_two_tile_columns(quant):
+    """Batch 11, dim 4096, FFN slice 3584: W1/W3 (N 7168) takes split-K
+    workgroups of 7 waves with two 16-row tiles each (32 tile columns x 8
+    slices = 256 workgroups, as for the 70B up-projection), with the RMSNorm
+    folded in; bf16 and int8 weights."""
+    w = synth.small_llama(name=f"splitk_nw7_q{quant}", dim=4096, n_heads=8, n_kv_heads=2, head_dim=128,
+                          ffn_hidden=7168, tp=2, batch=11, past=(1, 40), w_dtype=synth.BF16,
+                          kv_dtype=synth.BF16, quant=quant, seed=83)
     check_layer(w)
 
 
