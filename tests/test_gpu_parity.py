@@ -236,6 +236,22 @@ def test_micro_gqa_ragged_batch(hd):
     check_layer(w, d)
 
 
+@pytest.mark.parametrize("kv,hd,n_kv", [(synth.BF16, 128, 8), (synth.BF16, 128, 4), (synth.F32, 64, 2)])
+def test_register_attention_ragged_batch(kv, hd, n_kv):
+    """The register-resident attention (a 256-byte cache row: bf16 at hd 128,
+    fp32 at hd 64) with 1, 2 and 4 q heads per kv head, batch 7, lengths 0,
+    1, 15, 16, 63, 64 and 130: the new token alone, the edges of a wave's 16
+    positions and of a chunk's 64, the owner's row in every wave slot."""
+    w = synth.small_llama(name=f"micro_reg_{kv}_{hd}_{n_kv}", dim=256, n_heads=8, n_kv_heads=n_kv,
+                          head_dim=hd, ffn_hidden=256, tp=2, batch=7, past=(0, 130), w_dtype=synth.BF16,
+                          kv_dtype=kv, seed=85)
+    d = synth.llama_inputs(w)
+    d["lens"] = np.array([0, 1, 15, 16, 63, 64, 130], np.int32)
+    d["kcache"] = synth.llama_kv_cache(w, d["lens"], "kcache")
+    d["vcache"] = synth.llama_kv_cache(w, d["lens"], "vcache")
+    check_layer(w, d)
+
+
 @pytest.mark.parametrize("quant", [synth.Q_NONE, synth.Q_WEIGHTS,
                                    synth.Q_WEIGHTS | synth.Q_INPUTS | synth.Q_PARTIALS])
 def test_splitk_folded_norm_ragged_batch(quant):
@@ -377,8 +393,12 @@ def test_llama70b_tp8_b16_all_shards_and_merges():
         oracle.use_threads(False)
 
 
-def test_bad_length_sets_error_word_and_skips_row():
-    w = synth.small_llama(name="micro_err", dim=128, n_heads=4, n_kv_heads=4, head_dim=32,
+@pytest.mark.parametrize("hd", [32, 128])
+def test_bad_length_sets_error_word_and_skips_row(hd):
+    """An out-of-range length sets the device error word, the row's attention
+    is zero; hd 32 takes the LDS-staged vector attention, hd 128 (bf16 cache,
+    one q head per kv head) the register-resident one."""
+    w = synth.small_llama(name=f"micro_err{hd}", dim=128, n_heads=4, n_kv_heads=4, head_dim=hd,
                           ffn_hidden=256, tp=1, batch=3, past=(5, 9), w_dtype=synth.BF16,
                           kv_dtype=synth.BF16, seed=79)
     d = synth.llama_inputs(w)
