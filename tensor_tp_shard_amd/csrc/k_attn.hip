@@ -568,9 +568,13 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo_elem, float hi_elem)
 }
 
 // LDS: queries and probabilities as bf16 hi / lo parts in 16-row MFMA
-// operand form (rows past G zero), the K chunk row-major with padded rows,
-// V in 8-position groups [t/8][dim][t%8] so that a B fragment (8 consecutive
-// positions of one dim) is one aligned 16-byte read.
+// operand form (rows past G zero), the K and V chunks row-major with padded
+// rows, as loaded. A B fragment of P.V needs 8 consecutive positions of one
+// dim: gfx950's transposing LDS read (ds_read_b64_tr_b16) gives each lane of
+// a 16-lane group 4 rows of its dim from the 4 x 4 pieces the group points at
+// (lane r addresses row r / 4, dims 4 (r % 4) .. +3; measured layout). Staging
+// V as 8-position groups instead took 8 two-byte LDS writes per 16-byte piece
+// (70B: the K / V staging phase 1.16 us of a 9 us launch).
 __host__ __device__ inline size_t attn_mfma_smem_bytes(int G, int hd)
 {
     return (size_t)2 * 16 * (hd + 8) * 2 +    // q hi, lo (rows padded by 16 bytes)
@@ -578,8 +582,10 @@ __host__ __device__ inline size_t attn_mfma_smem_bytes(int G, int hd)
            (size_t)2 * 16 * (kChunk + 8) * 2 + // p hi, lo (rows padded by 16 bytes)
            sizeof(float) * 2 * 16 +            // (m, l)
            (size_t)kChunk * (hd * 2 + 16) +    // K
-           (size_t)kChunk * hd * 2;            // V groups
+           (size_t)kChunk * (hd * 2 + 32);     // V (rows padded by 32 bytes)
 }
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
@@ -649,7 +655,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
     uint16_t *pl_s = ph_s + 16 * pld;              // [16][pld]
     float *ml = (float *)(pl_s + 16 * pld);        // [16][2]
     char *K_s = (char *)(ml + 2 * 16);             // [64][rowb]
-    uint16_t *V_g = (uint16_t *)(K_s + kChunk * rowb); // [8][hd][8]
+    constexpr int rowv = hd * 2 + 32; // padded V row: the 4 rows of a transposed read hit 4 bank groups
+    char *V_s = K_s + kChunk * rowb;  // [64][rowv]
 
     const size_t head_base = ((size_t)b * a.Hkv_s + g) * a.max_ctx * hd;
     const float *qkv = a.qkv + (size_t)b * a.ld_qkv;
@@ -711,21 +718,13 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
         *(uint32_t *)(ph_s + e) = 0u;
         *(uint32_t *)(pl_s + e) = 0u;
     }
-    // K rows as loaded; V into 8-position groups, the element order rotated by
-    // the piece's column so the 16 lanes of a row write 8 different banks
+    // K and V rows as loaded (V is read back transposed by the P.V step)
 #pragma unroll
     for (int i = 0; i < kPieces; i++) {
         const int p = tid + 256 * i;
         const int row = p / ppr, col = p % ppr;
         *(u32x4 *)(K_s + row * rowb + col * 16) = kv[0][i];
-        const u32x4 v = kv[1][i];
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        uint16_t *vb = V_g + (size_t)(row >> 3) * hd * 8 + (row & 7);
-#pragma unroll
-        for (int e0 = 0; e0 < 8; e0++) {
-            const int e = (e0 + col) & 7;
-            vb[(8 * col + e) * 8] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-        }
+        *(u32x4 *)(V_s + row * rowv + col * 16) = kv[1][i];
     }
     __syncthreads();
     if (owner) { // rotate and append the new key / value at slot L (cache and LDS)
@@ -741,9 +740,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
             ((uint16_t *)a.vc)[e] = v0;
             ((uint16_t *)a.vc)[e + 1] = v1;
             *(uint32_t *)(K_s + tl * rowb + 4 * p) = (uint32_t)k0 | ((uint32_t)k1 << 16);
-            uint16_t *vb = V_g + (size_t)(tl >> 3) * hd * 8 + (tl & 7);
-            vb[(2 * p) * 8] = v0;
-            vb[(2 * p + 1) * 8] = v1;
+            *(uint32_t *)(V_s + tl * rowv + 4 * p) = (uint32_t)v0 | ((uint32_t)v1 << 16);
             if (a.tap_k) {
                 float *tk = a.tap_k + (size_t)b * a.Hkv_s * hd + g * hd;
                 float *tv = a.tap_v + (size_t)b * a.Hkv_s * hd + g * hd;
@@ -799,7 +796,15 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
         for (int ks = 0; ks < kChunk / 32; ks++) {
             const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(ph_s + r * pld + 32 * ks + 8 * q));
             const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(pl_s + r * pld + 32 * ks + 8 * q));
-            const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(V_g + ((size_t)(4 * ks + q) * hd + 16 * dt + r) * 8));
+            // B[k][n] = V[32 ks + k][16 dt + n], lane (q, r) holding k = 8q..8q+7 of n = r:
+            // two transposing reads of 4 positions each; lane r of the 16-lane
+            // group supplies the address of row 32 ks + 8q + 4h + r / 4, dims
+            // 16 dt + 4 (r % 4) .. +3, and gets back those 4 rows of dim 16 dt + r
+            const char *vp = V_s + (32 * ks + 8 * q + (r >> 2)) * rowv + (16 * dt + 4 * (r & 3)) * 2;
+            const v4i16_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)vp);
+            const v4i16_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16_t *)(vp + 4 * rowv));
+            const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, acc, 0, 0, 0);
         }

@@ -59,6 +59,17 @@ struct GemmArgs {
     uint16_t *H;       // FFN_UP: [M][N/2] bf16
     float *C;          // FFN_DOWN: [splits][M][N] fp32
     int M, N, K, ksteps_per_split;
+    // Which tiles share an XCD (consecutive linear workgroup ids go to the 8
+    // XCDs in turn, so the tiles with the same id % 8 share one L2).
+    // 0: grid order, x = N-tile fastest: the M-tiles of an N-tile share an XCD
+    //    (the weight tile is fetched into one L2; every XCD fetches all of A).
+    // 1: split-K, S dividing 8: an XCD takes one split's K range and 8/S of
+    //    the N-tiles with every M-tile, so each weight tile is fetched once
+    //    and each A slice by 8/S XCDs instead of all the N-tiles' XCDs.
+    // 2: one split: the XCDs form gm groups of M-tiles x 8/gm groups of
+    //    N-tiles, an XCD taking every tile of its pair of groups (gm = 8: A
+    //    fetched once, the weights by every XCD).
+    int map, gm;
 };
 
 // An LDS row holds the stage's KB values of a matrix row (2 KB bytes); its
@@ -108,9 +119,26 @@ __global__ __launch_bounds__(64 * NWV, (KB == 32 && NWV == 4) ? 2 : 1) void k_ge
     __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageB];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wm = wv >> 1, wn = wv & 1; // wave grid kWM x 2
-    // grid: x = N-tile (fastest, so the M-tiles of one N-tile share id % 8), y = M-tile, z = split
-    const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * BM;
-    const int ks0 = blockIdx.z * a.ksteps_per_split;
+    // grid: x = N-tile, y = M-tile, z = split; the tile this workgroup takes
+    // depends on a.map (see GemmArgs)
+    int tn = blockIdx.x, tm = blockIdx.y, tz = blockIdx.z;
+    if (a.map != 0) {
+        const int NT = gridDim.x, MT = gridDim.y, SZ = gridDim.z;
+        const int L = blockIdx.x + NT * (blockIdx.y + MT * blockIdx.z), x = L & 7, j = L >> 3;
+        if (a.map == 1) {
+            const int g = 8 / SZ, per = NT / g;
+            tz = x / g;
+            tm = j / per;
+            tn = (x % g) * per + j % per;
+        } else {
+            const int gn = 8 / a.gm, mtg = MT / a.gm, ntg = NT / gn;
+            tz = 0;
+            tm = (x / gn) * mtg + j / ntg;
+            tn = (x % gn) * ntg + j % ntg;
+        }
+    }
+    const int n0 = tn * kBN, m0 = tm * BM;
+    const int ks0 = tz * a.ksteps_per_split;
     const int nks = min(a.ksteps_per_split, a.K / kBK - ks0);
 
     f32x4 acc[kMT][kNT];
@@ -231,7 +259,7 @@ __global__ __launch_bounds__(64 * NWV, (KB == 32 && NWV == 4) ? 2 : 1) void k_ge
                     a.H[(size_t)(m + 1) * F + f] = f32_to_bf16(silu_fast(g1) * u1);
             }
     } else {
-        float *C = a.C + (size_t)blockIdx.z * a.M * a.N;
+        float *C = a.C + (size_t)tz * a.M * a.N;
 #pragma unroll
         for (int i = 0; i < kMT; i++)
 #pragma unroll
@@ -330,7 +358,7 @@ hipError_t launch_ffn2d(const Ffn2dArgs &f, hipStream_t st, int which)
     const Ffn2dCfg c = ffn2d_cfg(f.B);
     const int mt = (f.B + c.bm - 1) / c.bm;
     if (which == 0) {
-        GemmArgs g{f.x, f.w13, f.h, nullptr, f.B, 2 * f.F, f.E, f.E / c.kb};
+        GemmArgs g{f.x, f.w13, f.h, nullptr, f.B, 2 * f.F, f.E, f.E / c.kb, 0, 1};
         launch_gemm_cfg<FFN_UP>(c, g, dim3(2 * f.F / kBN, mt, 1), st);
         return hipGetLastError();
     }
@@ -340,8 +368,15 @@ hipError_t launch_ffn2d(const Ffn2dArgs &f, hipStream_t st, int which)
     const int ksteps = f.F / cd.kb;
     const int per = (ksteps + S - 1) / S;
     const int splits = (ksteps + per - 1) / per;
-    GemmArgs g{f.h, f.w2, nullptr, splits > 1 ? f.part : f.y, f.B, f.E, f.F, per};
-    launch_gemm_cfg<FFN_DOWN>(cd, g, dim3(f.E / kBN, mtd, splits), st);
+    GemmArgs g{f.h, f.w2, nullptr, splits > 1 ? f.part : f.y, f.B, f.E, f.F, per, 0, 1};
+    const int ntd = f.E / kBN;
+    if (splits > 1 && 8 % splits == 0 && ntd % (8 / splits) == 0) {
+        g.map = 1;
+    } else if (splits == 1 && mtd % 8 == 0) {
+        g.map = 2;
+        g.gm = 8;
+    }
+    launch_gemm_cfg<FFN_DOWN>(cd, g, dim3(ntd, mtd, splits), st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1)
         return e;
