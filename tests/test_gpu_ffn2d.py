@@ -81,7 +81,11 @@ def _sampled_rows_check(w, rows):
 
 
 def test_palm_ffn2d_decode_512_sampled_rows():
-    y = _sampled_rows_check(synth.PALM_DEC, [0, 1, 127, 128, 300, 511])
+    """512 tokens: the down-projection splits K 4 ways and maps one split and
+    half the N-tiles to each XCD; a row in every 64-row M-tile (each row
+    covers every N-tile and split) plus tile edges."""
+    rows = sorted({0, 1, 63, 64, 127, 128, 300, 511} | {64 * t + 17 for t in range(8)})
+    y = _sampled_rows_check(synth.PALM_DEC, rows)
     # deterministic: a second run is bitwise equal
     d = synth.ffn2d_inputs(synth.PALM_DEC)
     (y2,) = run_ffn2d(d, 512, [512])
@@ -89,7 +93,9 @@ def test_palm_ffn2d_decode_512_sampled_rows():
 
 
 def test_palm_ffn2d_prefill_8192_sampled_rows():
-    _sampled_rows_check(synth.PALM_PRE, [0, 4095, 8191])
+    """8192 tokens: the one-split down-projection gives each XCD 1/8 of the
+    256-row M-tiles with every N-tile; a row in every M-tile."""
+    _sampled_rows_check(synth.PALM_PRE, sorted({0, 4095, 8191} | {256 * t + 101 for t in range(32)}))
 
 
 def test_palm_ffn2d_weight_gathered_sampled_rows():
