@@ -74,12 +74,26 @@ __device__ __forceinline__ float lane_value(float v, int l)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// DPP lane permutations inside 16-lane rows (VALU operand modifiers, no LDS
+// round trip): swap neighbours (lane i ^ 1), swap pairs (i ^ 2), mirror each
+// 8-lane half (i -> 7 - i) and mirror the row (i -> 15 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_perm(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppRowMirror = 0x140;
+
 // Reductions over groups of W consecutive lanes (W a power of two <= 64),
 // result in every lane of the group; all lanes of the wave active. W = 64:
 // rotations by 8, 4, 2, 1 leave each 16-lane row's total in its lanes, then
 // the four row totals (lanes 0, 16, 32, 48) are combined as wave-uniform
-// values, (r0 + r1) + (r2 + r3). Smaller W: xor butterfly through
-// ds_bpermute.
+// values, (r0 + r1) + (r2 + r3). Smaller W: a butterfly, each step adding
+// the partner lane's value: lanes i ^ 1 and i ^ 2 by DPP, then, with every
+// 4- (8-) lane group already uniform, the mirrored lane stands for lane i ^ 4
+// (i ^ 8), also by DPP; the step across 16-lane rows (W = 32) through
+// ds_bpermute. Each lane adds the same two values as in a plain xor
+// butterfly, so the results are those of one.
 template <int W>
 __device__ __forceinline__ float group_sum(float v)
 {
@@ -90,9 +104,16 @@ __device__ __forceinline__ float group_sum(float v)
         v += row_ror<1>(v);
         return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
     } else {
-#pragma unroll
-        for (int o = W / 2; o > 0; o >>= 1)
-            v += __shfl_xor(v, o, kWave);
+        static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32, "group width");
+        v += dpp_perm<kDppXor1>(v);
+        if constexpr (W >= 4)
+            v += dpp_perm<kDppXor2>(v);
+        if constexpr (W >= 8)
+            v += dpp_perm<kDppHalfMirror>(v);
+        if constexpr (W >= 16)
+            v += dpp_perm<kDppRowMirror>(v);
+        if constexpr (W >= 32)
+            v += __shfl_xor(v, 16, kWave);
         return v;
     }
 }
@@ -107,9 +128,16 @@ __device__ __forceinline__ float group_max(float v)
         v = fmaxf(v, row_ror<1>(v));
         return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
     } else {
-#pragma unroll
-        for (int o = W / 2; o > 0; o >>= 1)
-            v = fmaxf(v, __shfl_xor(v, o, kWave));
+        static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32, "group width");
+        v = fmaxf(v, dpp_perm<kDppXor1>(v));
+        if constexpr (W >= 4)
+            v = fmaxf(v, dpp_perm<kDppXor2>(v));
+        if constexpr (W >= 8)
+            v = fmaxf(v, dpp_perm<kDppHalfMirror>(v));
+        if constexpr (W >= 16)
+            v = fmaxf(v, dpp_perm<kDppRowMirror>(v));
+        if constexpr (W >= 32)
+            v = fmaxf(v, __shfl_xor(v, 16, kWave));
         return v;
     }
 }
