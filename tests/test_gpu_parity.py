@@ -252,6 +252,19 @@ def test_register_attention_ragged_batch(kv, hd, n_kv):
     check_layer(w, d)
 
 
+def test_attention_more_than_64_chunks():
+    """A sequence of 4250 positions (67 chunks of 64) next to short ones: the
+    combine reads its chunk records in two rounds of 64."""
+    w = synth.small_llama(name="micro_long", dim=128, n_heads=8, n_kv_heads=8, head_dim=128,
+                          ffn_hidden=256, tp=2, batch=3, past=(1, 4250), w_dtype=synth.BF16,
+                          kv_dtype=synth.BF16, seed=87)
+    d = synth.llama_inputs(w)
+    d["lens"] = np.array([4250, 1, 4095], np.int32)
+    d["kcache"] = synth.llama_kv_cache(w, d["lens"], "kcache")
+    d["vcache"] = synth.llama_kv_cache(w, d["lens"], "vcache")
+    check_layer(w, d)
+
+
 @pytest.mark.parametrize("quant", [synth.Q_NONE, synth.Q_WEIGHTS,
                                    synth.Q_WEIGHTS | synth.Q_INPUTS | synth.Q_PARTIALS])
 def test_splitk_folded_norm_ragged_batch(quant):
