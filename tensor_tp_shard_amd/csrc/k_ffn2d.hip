@@ -20,15 +20,18 @@
 //    operand tile from L2 for half as many partner tiles as 128-row tiles,
 //    and give the 8192-token down-projection exactly one workgroup per CU
 //    (8 N-tiles x 32 M-tiles): 8192-token block 1.133 -> 1.080 ms;
-//  - a 3-stage LDS ring filled by direct global->LDS loads
-//    (global_load_lds_dwordx4), two stages ahead of the MFMAs, one barrier
-//    per stage, waits by vmcnt and no register staging. Up to 1024 rows a
-//    stage holds 64 K values (128 bytes of every row, occupancy 1): each
-//    1 KiB wave load is 8 full 128-byte lines, where 64-byte rows made it 16
-//    half-used lines and the L2 delivered about half the bytes per request
-//    (512 tokens: 124.6 -> 118.4 us per block). Larger M keeps 32 K values
-//    per stage at occupancy 2, which hides more latency there. 16-byte chunks
-//    are XOR-swizzled per row against bank conflicts;
+//  - an LDS ring filled by direct global->LDS loads (global_load_lds_dwordx4),
+//    one barrier per stage, waits by vmcnt and no register staging. Up to
+//    1024 rows: 3 stages (loads two stages ahead) of 64 K values (128 bytes
+//    of every row, occupancy 1): each 1 KiB wave load is 8 full 128-byte
+//    lines, where 64-byte rows made it 16 half-used lines and the L2
+//    delivered about half the bytes per request (512 tokens: 124.6 -> 118.4
+//    us per block). Below 4096 rows: 3 stages of 32 K values at occupancy 2,
+//    which hides more latency there. 256-row tiles: 2 stages (loads one
+//    stage ahead) of 64 K values, so the eight waves meet at half as many
+//    barriers per MFMA (8192-token block 0.944 -> 0.879 ms; 3 stages of 32,
+//    or 4, were level, and a raised wave priority over the MFMAs slower).
+//    16-byte chunks are XOR-swizzled per row against bank conflicts;
 //  - tile order puts the M-tiles of one N-tile on the same XCD (linear
 //    workgroup id % 8), so a weight tile is fetched into one L2 once;
 //  - up-projection epilogue: the packed W_gate/W_in rows interleave in
@@ -95,15 +98,17 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// BM = 64 or 128 rows of A per workgroup; KB = 32 or 64 K values per stage.
-// KB = 64 (occupancy 1) makes every wave load 8 full 128-byte lines and suits
-// decode-sized M, where the L2 delivery of the weights is the limit; KB = 32
-// (64-byte rows, occupancy 2) hides more latency for large, compute-bound M.
-template <int EPI, int BM, int KB, int NWV = 4>
+// BM = 64, 128 or 256 rows of A per workgroup; KB = 32 or 64 K values per
+// stage; NST stages in the LDS ring. KB = 64 (occupancy 1) makes every wave
+// load 8 full 128-byte lines and suits decode-sized M, where the L2 delivery
+// of the weights is the limit; KB = 32 (64-byte rows, occupancy 2) hides more
+// latency for 128-row tiles of a larger M.
+template <int EPI, int BM, int KB, int NWV = 4, int NST = 3>
 __global__ __launch_bounds__(64 * NWV, (KB == 32 && NWV == 4) ? 2 : 1) void k_gemm_nt(GemmArgs a)
 {
     constexpr int kBK = KB;
-    constexpr int kStages = 3;                         // LDS ring of 3 stages
+    constexpr int kStages = NST;                       // LDS ring of NST stages
+    static_assert(NST >= 2, "a stage is loaded while another is read");
     constexpr int kWM = NWV / 2;                       // waves in M (2 in N)
     constexpr int kRowB = KB * 2;                      // bytes of a row per stage
     constexpr int kRowsSeg = 1024 / kRowB;             // rows per 1 KiB wave load
@@ -305,8 +310,9 @@ static Ffn2dCfg ffn2d_cfg(int B)
     if (B < 4096)
         return {128, 32, 4};
     // 256 x 288 tiles, 8 waves of 64 x 144: each operand tile is fetched from
-    // L2 for half as many partner tiles in M as with 128-row tiles
-    return {256, 32, 8};
+    // L2 for half as many partner tiles in M as with 128-row tiles; 64 K
+    // values a stage, two stages
+    return {256, 64, 8};
 }
 
 // The down-projection's tiles: 64 rows up to 1024 (twice the output tiles of
@@ -331,23 +337,23 @@ int ffn2d_splits(int B, int E, int F)
     return s > ksteps ? ksteps : s;
 }
 
-template <int EPI, int BM, int KB, int NWV = 4>
+template <int EPI, int BM, int KB, int NWV = 4, int NST = 3>
 static void launch_gemm(const GemmArgs &g, dim3 grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((k_gemm_nt<EPI, BM, KB, NWV>), grid, dim3(64 * NWV), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_nt<EPI, BM, KB, NWV, NST>), grid, dim3(64 * NWV), 0, st, g);
 }
 
 template <int EPI>
 static void launch_gemm_cfg(const Ffn2dCfg &c, const GemmArgs &g, dim3 grid, hipStream_t st)
 {
-    if (c.bm == 64)
+    if (c.bm == 256)
+        launch_gemm<EPI, 256, 64, 8, 2>(g, grid, st);
+    else if (c.bm == 64)
         launch_gemm<EPI, 64, 64>(g, grid, st);
     else if (c.kb == 64)
         launch_gemm<EPI, 128, 64>(g, grid, st);
-    else if (c.bm == 128)
-        launch_gemm<EPI, 128, 32>(g, grid, st);
     else
-        launch_gemm<EPI, 256, 32, 8>(g, grid, st);
+        launch_gemm<EPI, 128, 32>(g, grid, st);
 }
 
 // which = 0: up-projection + SwiGLU into a.h; which = 1: down-projection
