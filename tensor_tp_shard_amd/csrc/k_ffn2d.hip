@@ -15,7 +15,8 @@
 // (each lane holds 8 consecutive k of one row of A and of one row of B).
 //  - workgroup tile BM x 288 (BM = 64 up to 256 rows, 128 up to 4095, else
 //    256), waves as (BM/64) x 2 (four, or eight for BM = 256), wave tile
-//    64 x 144 (4 x 9 MFMA tiles; BM/2 x 144 for BM = 64); 288 divides the
+//    64 x 144 (4 x 9 MFMA tiles; BM/2 x 144 for BM = 64, where two such
+//    groups of four waves split each stage's K); 288 divides the
 //    PaLM block's 2F = 18432 and E = 2304. The 256-row tiles fetch each
 //    operand tile from L2 for half as many partner tiles as 128-row tiles,
 //    and give the 8192-token down-projection exactly one workgroup per CU
@@ -103,13 +104,23 @@ __device__ __forceinline__ void wait_vmcnt()
 // load 8 full 128-byte lines and suits decode-sized M, where the L2 delivery
 // of the weights is the limit; KB = 32 (64-byte rows, occupancy 2) hides more
 // latency for 128-row tiles of a larger M.
-template <int EPI, int BM, int KB, int NWV = 4, int NST = 3>
+// KS = 2 (64-row tiles): two groups of four waves share the tile and the LDS
+// ring, group g taking MFMA k-step g of every 64-K stage; group 1 hands its
+// sums to group 0 through LDS at the end. Two waves a SIMD then hide each
+// other's LDS and barrier waits (512-token split-K down-projection 45.6 ->
+// 43.4 us). The 128-row tile does not fit two waves a SIMD that way (its 36
+// accumulator tiles a wave spill), and 64-row tiles for the 512-token
+// up-projection were slower (58 -> 71 us: each weight tile fetched for twice
+// as many M-tiles).
+template <int EPI, int BM, int KB, int NWV = 4, int NST = 3, int KS = 1>
 __global__ __launch_bounds__(64 * NWV, (KB == 32 && NWV == 4) ? 2 : 1) void k_gemm_nt(GemmArgs a)
 {
     constexpr int kBK = KB;
     constexpr int kStages = NST;                       // LDS ring of NST stages
     static_assert(NST >= 2, "a stage is loaded while another is read");
-    constexpr int kWM = NWV / 2;                       // waves in M (2 in N)
+    constexpr int kGW = NWV / KS;                      // waves of a k-group
+    constexpr int kWM = kGW / 2;                       // waves in M (2 in N)
+    static_assert(KS == 1 || (KS == 2 && KB == 64), "a k-group takes one MFMA k-step of a 64-K stage");
     constexpr int kRowB = KB * 2;                      // bytes of a row per stage
     constexpr int kRowsSeg = 1024 / kRowB;             // rows per 1 KiB wave load
     constexpr int kChunks = kRowB / 16;                // 16-byte chunks per row
@@ -123,7 +134,8 @@ __global__ __launch_bounds__(64 * NWV, (KB == 32 && NWV == 4) ? 2 : 1) void k_ge
     static_assert(kMaxSegs - kMinSegs <= 1, "waves issue kMaxSegs or kMaxSegs - 1 segments");
     __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageB];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv >> 1, wn = wv & 1; // wave grid kWM x 2
+    const int kg = wv / kGW, wl = wv % kGW; // k-group, wave in the group
+    const int wm = wl >> 1, wn = wl & 1;    // wave grid kWM x 2
     // grid: x = N-tile, y = M-tile, z = split; the tile this workgroup takes
     // depends on a.map (see GemmArgs)
     int tn = blockIdx.x, tm = blockIdx.y, tz = blockIdx.z;
@@ -209,9 +221,11 @@ __global__ __launch_bounds__(64 * NWV, (KB == 32 && NWV == 4) ? 2 : 1) void k_ge
         if (ks + kStages - 1 < nks)
             issue(ks + kStages - 1);
         const char *As = lds + (ks % kStages) * kStageB, *Bs = As + BM * kRowB;
-        // two MFMA k-steps of 32 per stage: lane quarter q takes chunk 4 kk + q
+        // MFMA k-steps of 32 (a k-group takes every KS-th): lane quarter q takes
+        // chunk 4 kk + q
 #pragma unroll
-        for (int kk = 0; kk < kBK / 32; kk++) {
+        for (int k2 = 0; k2 < kBK / 32 / KS; k2++) {
+            const int kk = k2 * KS + kg;
             bf16x8 af[kMT], bfr[kNT];
 #pragma unroll
             for (int i = 0; i < kMT; i++)
@@ -235,6 +249,30 @@ __global__ __launch_bounds__(64 * NWV, (KB == 32 && NWV == 4) ? 2 : 1) void k_ge
                 __builtin_amdgcn_sched_group_barrier(0x008, kMT, 0);
             }
         }
+    }
+
+    if constexpr (KS == 2) {
+        // every wave is past its last LDS read of the ring (and no load is in
+        // flight: the last iteration waited for all), so the ring holds group
+        // 1's sums, lane-major per (wave, tile)
+        static_assert(kGW * kMT * kNT * 64 * 16 <= kStages * kStageB, "the sums fit the ring");
+        f32x4 *red = (f32x4 *)lds;
+        __syncthreads();
+        if (kg == 1) {
+#pragma unroll
+            for (int i = 0; i < kMT; i++)
+#pragma unroll
+                for (int j = 0; j < kNT; j++)
+                    red[((wl * kMT + i) * kNT + j) * 64 + lane] = acc[i][j];
+        }
+        __syncthreads();
+        if (kg == 1)
+            return;
+#pragma unroll
+        for (int i = 0; i < kMT; i++)
+#pragma unroll
+            for (int j = 0; j < kNT; j++)
+                acc[i][j] += red[((wl * kMT + i) * kNT + j) * 64 + lane];
     }
 
     // lane holds C[m0 + wm*BM/kWM + i*16 + 4*(lane/16) + r][n0 + wn*kWN + j*16 + lane%16]
@@ -337,10 +375,10 @@ int ffn2d_splits(int B, int E, int F)
     return s > ksteps ? ksteps : s;
 }
 
-template <int EPI, int BM, int KB, int NWV = 4, int NST = 3>
+template <int EPI, int BM, int KB, int NWV = 4, int NST = 3, int KS = 1>
 static void launch_gemm(const GemmArgs &g, dim3 grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((k_gemm_nt<EPI, BM, KB, NWV, NST>), grid, dim3(64 * NWV), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_nt<EPI, BM, KB, NWV, NST, KS>), grid, dim3(64 * NWV), 0, st, g);
 }
 
 template <int EPI>
@@ -349,7 +387,7 @@ static void launch_gemm_cfg(const Ffn2dCfg &c, const GemmArgs &g, dim3 grid, hip
     if (c.bm == 256)
         launch_gemm<EPI, 256, 64, 8, 2>(g, grid, st);
     else if (c.bm == 64)
-        launch_gemm<EPI, 64, 64>(g, grid, st);
+        launch_gemm<EPI, 64, 64, 8, 3, 2>(g, grid, st);
     else if (c.kb == 64)
         launch_gemm<EPI, 128, 64>(g, grid, st);
     else
