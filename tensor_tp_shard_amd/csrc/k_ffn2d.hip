@@ -14,13 +14,20 @@
 // K-contiguous, which is the operand layout of v_mfma_f32_16x16x32_bf16
 // (each lane holds 8 consecutive k of one row of A and of one row of B).
 //  - workgroup tile BM x 288 (BM = 64 up to 256 rows, 128 up to 4095, else
-//    256), waves as (BM/64) x 2 (four, or eight for BM = 256), wave tile
-//    64 x 144 (4 x 9 MFMA tiles; BM/2 x 144 for BM = 64, where two such
-//    groups of four waves split each stage's K); 288 divides the
-//    PaLM block's 2F = 18432 and E = 2304. The 256-row tiles fetch each
-//    operand tile from L2 for half as many partner tiles as 128-row tiles,
-//    and give the 8192-token down-projection exactly one workgroup per CU
-//    (8 N-tiles x 32 M-tiles): 8192-token block 1.133 -> 1.080 ms;
+//    256); 288 divides the PaLM block's 2F = 18432 and E = 2304. Waves form a
+//    kWM x 2 grid over the tile (wave tile BM/kWM x 144, MFMA tiles of 16 x
+//    16): 16 waves of 32 x 144 for 256 rows, 8 of 32 x 144 for 128 rows with
+//    64-K stages, 4 of 64 x 144 (two waves a SIMD by occupancy) for 128 rows
+//    with 32-K stages, and for 64 rows two k-groups of 8 waves of 16 x 144.
+//    Smaller wave tiles read more LDS bytes per MFMA, but the extra waves
+//    hide each other's LDS, barrier and load waits: measured, 256 rows 8 ->
+//    16 waves 0.849 -> 0.830 ms per 8192-token block, 128 rows 4 -> 8 waves
+//    92.2 -> 86.1 us per 512-token block (16 waves: 87.7), and one wave a
+//    SIMD with 128 x 128 or 112 x 128 wave tiles was slower still. The
+//    256-row tiles fetch each operand tile from L2 for half as many partner
+//    tiles as 128-row tiles, and give the 8192-token down-projection exactly
+//    one workgroup per CU (8 N-tiles x 32 M-tiles): 8192-token block 1.133 ->
+//    1.080 ms;
 //  - an LDS ring filled by direct global->LDS loads (global_load_lds_dwordx4),
 //    one barrier per stage, waits by vmcnt and no register staging. Up to
 //    1024 rows: 3 stages (loads two stages ahead) of 64 K values (128 bytes
@@ -104,14 +111,13 @@ __device__ __forceinline__ void wait_vmcnt()
 // load 8 full 128-byte lines and suits decode-sized M, where the L2 delivery
 // of the weights is the limit; KB = 32 (64-byte rows, occupancy 2) hides more
 // latency for 128-row tiles of a larger M.
-// KS = 2 (64-row tiles): two groups of four waves share the tile and the LDS
-// ring, group g taking MFMA k-step g of every 64-K stage; group 1 hands its
-// sums to group 0 through LDS at the end. Two waves a SIMD then hide each
-// other's LDS and barrier waits (512-token split-K down-projection 45.6 ->
-// 43.4 us). The 128-row tile does not fit two waves a SIMD that way (its 36
-// accumulator tiles a wave spill), and 64-row tiles for the 512-token
-// up-projection were slower (58 -> 71 us: each weight tile fetched for twice
-// as many M-tiles).
+// KS = 2 (64-row tiles): two groups of NWV / 2 waves share the tile and the
+// LDS ring, group g taking MFMA k-step g of every 64-K stage; group 1 hands
+// its sums to group 0 through LDS at the end. The waves then hide each
+// other's LDS and barrier waits (512-token split-K down-projection with two
+// groups of four: 45.6 -> 43.4 us; of eight: 43.9 -> 42.7 us). 64-row tiles
+// for the 512-token up-projection were slower (58 -> 71 us: each weight tile
+// fetched for twice as many M-tiles).
 template <int EPI, int BM, int KB, int NWV = 4, int NST = 3, int KS = 1>
 __global__ __launch_bounds__(64 * NWV, (KB == 32 && NWV == 4) ? 2 : 1) void k_gemm_nt(GemmArgs a)
 {
@@ -335,22 +341,22 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float *P, float *Y, 
     *(float4 *)(Y + i) = acc;
 }
 
-// Tile rows and K values per stage for a batch of B rows (see k_gemm_nt).
+// Tile rows and K values per stage for a batch of B rows (see k_gemm_nt; the
+// wave count and stage count follow from these in launch_gemm_cfg).
 struct Ffn2dCfg {
-    int bm, kb, nwv;
+    int bm, kb;
 };
 static Ffn2dCfg ffn2d_cfg(int B)
 {
     if (B <= 256)
-        return {64, 64, 4};
+        return {64, 64};
     if (B <= 1024)
-        return {128, 64, 4};
+        return {128, 64};
     if (B < 4096)
-        return {128, 32, 4};
-    // 256 x 288 tiles, 8 waves of 64 x 144: each operand tile is fetched from
-    // L2 for half as many partner tiles in M as with 128-row tiles; 64 K
-    // values a stage, two stages
-    return {256, 64, 8};
+        return {128, 32};
+    // 256 x 288 tiles: each operand tile is fetched from L2 for half as many
+    // partner tiles in M as with 128-row tiles; 64 K values a stage, two stages
+    return {256, 64};
 }
 
 // The down-projection's tiles: 64 rows up to 1024 (twice the output tiles of
@@ -359,7 +365,7 @@ static Ffn2dCfg ffn2d_cfg(int B)
 static Ffn2dCfg ffn2d_cfg_down(int B)
 {
     if (B <= 1024)
-        return {64, 64, 4};
+        return {64, 64};
     return ffn2d_cfg(B);
 }
 
@@ -381,15 +387,17 @@ static void launch_gemm(const GemmArgs &g, dim3 grid, hipStream_t st)
     hipLaunchKernelGGL((k_gemm_nt<EPI, BM, KB, NWV, NST, KS>), grid, dim3(64 * NWV), 0, st, g);
 }
 
+// 256 rows: 16 waves, two stages; 64 rows: two k-groups of 8 waves; 128 rows:
+// 8 waves with 64-K stages, 4 (occupancy 2) with 32-K stages.
 template <int EPI>
 static void launch_gemm_cfg(const Ffn2dCfg &c, const GemmArgs &g, dim3 grid, hipStream_t st)
 {
     if (c.bm == 256)
-        launch_gemm<EPI, 256, 64, 8, 2>(g, grid, st);
+        launch_gemm<EPI, 256, 64, 16, 2>(g, grid, st);
     else if (c.bm == 64)
-        launch_gemm<EPI, 64, 64, 8, 3, 2>(g, grid, st);
+        launch_gemm<EPI, 64, 64, 16, 3, 2>(g, grid, st);
     else if (c.kb == 64)
-        launch_gemm<EPI, 128, 64>(g, grid, st);
+        launch_gemm<EPI, 128, 64, 8>(g, grid, st);
     else
         launch_gemm<EPI, 128, 32>(g, grid, st);
 }
