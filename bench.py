@@ -434,7 +434,7 @@ def run_llama(args, w, with_cpu=True):
     st = Stepper(step_fused if args.merge == "fused" else step_separate, R, args.mode, stream)
     ms = time_steps(st, args.steps, args.warmup, args.repeats)
     assert torch.isfinite(xs[0]).all().item(), "non-finite layer output"
-    names = ["rmsnorm", "gemv_qkv", "attention", "gemv_wo", "q8_wire", "gemv_w13_swiglu", "gemv_w2",
+    names = ["rmsnorm", "gemv_qkv", "qkv_attention", "attention", "gemv_wo", "q8_wire", "gemv_w13_swiglu", "gemv_w2",
              "merge"]
     kt = kernel_times([c.handle for c in copies], st, max(args.steps, R), names)
     s = summarize(ms, args.steps)

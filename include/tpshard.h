@@ -82,7 +82,12 @@ enum {
 };
 
 /* Bits of the device error word (first 4 bytes of the workspace). */
-enum { TP_DERR_LEN = 1 }; /* some lens[b] was < 0 or >= max_ctx; that sequence was skipped */
+enum {
+    TP_DERR_LEN = 1,    /* some lens[b] was < 0 or >= max_ctx; that sequence was skipped */
+    TP_DERR_HANDOFF = 2 /* in the one-launch QKV projection + attention (decode_step, batch
+                           <= 4), an attention workgroup waited 0.17 s for its queries and
+                           went on without them: that stage's outputs are invalid */
+};
 
 /*
  * Shard configuration. Sizes are those of the FULL (unsharded) model; the
@@ -141,7 +146,9 @@ typedef struct {
 typedef struct {
     uint64_t packed_weights; /* the shard's packed weights, gains and RoPE table */
     uint64_t kv_cache_each;  /* one of K or V: [max_batch][Hkv_s][max_ctx][hd] kv_dtype */
-    uint64_t workspace;      /* activations between kernels + the device error word */
+    uint64_t workspace;      /* activations between kernels, the device error word and (batch
+                                <= 4 one-launch QKV + attention) a step counter: one workspace
+                                per handle, kept between calls */
     uint64_t wire;           /* one shard's exchanged partial for max_batch rows */
 } tp_sizes;
 
@@ -241,6 +248,10 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *full, void *packed, vo
  *    away from zero, clamped to +-127; an all-zero block has scale 0).
  *    Otherwise fp32 [batch][D].
  *  taps: NULL or optional intermediate outputs (tp_taps).
+ *  At batch <= 4 with a bf16 cache of head dim 128 and at most 2 q heads per
+ *  kv head, the attention stage runs the QKV projection and the chunk
+ *  attention as one launch (the queries handed between its workgroups);
+ *  the results are bitwise those of the separate launches.
  * Errors: TP_EINVAL, TP_EALIGN, TP_ESTATE (no load_weights yet), TP_EHIP.
  */
 int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *lens,
@@ -249,7 +260,8 @@ int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *le
 /*
  * decode_step_noalloc: decode_step for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
- * forbid hipMalloc). Same kernels, arguments and results as decode_step, but
+ * forbid hipMalloc). Same kernels, arguments and results as decode_step
+ * (the QKV projection and the attention always as separate launches), but
  * the per-step buffers (the workspace's regions) live in one static device
  * array of the library, 16 MiB per GPU, held until the process ends; the
  * handle's workspace, if any, is not used, and a TP_LLAMA_BLOCK handle may be

@@ -25,6 +25,7 @@ TP_STAGE_ATTN, TP_STAGE_FFN, TP_STAGE_LOGITS = 0, 1, 2
 TP_Q_NONE, TP_Q_PARTIALS, TP_Q_INPUTS, TP_Q_WEIGHTS = 0, 1, 2, 4
 TP_OK, TP_EINVAL, TP_EALIGN, TP_ESTATE, TP_ENODEV, TP_EHIP, TP_ENOTIMPL = 0, -1, -2, -3, -4, -5, -6
 TP_DERR_LEN = 1
+TP_DERR_HANDOFF = 2
 
 # every symbol include/tpshard.h declares
 EXPORTS = ("init_shard", "load_weights", "decode_step", "decode_step_noalloc", "merge_partials",

@@ -65,13 +65,14 @@ enum KernelId {
     KID_GEMV_LOGITS,
     KID_MERGE_LOGITS,
     KID_A2A,
+    KID_QKV_ATTN,
     KID_COUNT
 };
 
 const char *const kKernelNames[KID_COUNT] = {
     "rmsnorm",    "gemv_qkv", "attention", "gemv_wo",  "q8_wire",    "gemv_w13_swiglu",
     "gemv_w2",    "merge",    "ffn2d_up",  "ffn2d_down", "rope_table", "gemv_logits",
-    "merge_logits", "all_to_all"};
+    "merge_logits", "all_to_all", "qkv_attention"};
 
 } // namespace
 
@@ -88,6 +89,9 @@ struct tp_shard {
     uint64_t o_sqkv, o_swo, o_sw13, o_sw2; // w8: scale arrays [N][K/32]
     // workspace layout (byte offsets)
     uint64_t w_err, w_xfx, w_xfatt, w_xfa, w_skp, w_xn, w_qkv, w_part, w_att, w_a, w_p, ws_bytes;
+    // fused QKV + attention (batch <= 4): the stage's epoch (one word, 256
+    // bytes reserved), then hand-off words [min(max_batch, 4)][n_qkv]; 0: none
+    uint64_t w_hand = 0, hand_bytes = 0;
     int n_chunks;
     bool mfma_ok = false; // the batch 5..16 MFMA path applies to this shape
     uint64_t kv_bytes, wire_bytes, part_rows = 0;
@@ -347,6 +351,15 @@ int32_t plan(const tp_config &c, tp_shard &s)
     s.w_att = o;  o = align_up(o + B * s.Hq_s * s.hd * 4, 256);
     s.w_a = o;    o = align_up(o + B * s.Fs * 4, 256);
     s.w_p = o;    o = align_up(o + B * D * 4, 256);
+    {
+        const int wt = s.w8 ? WT_I8 : c.w_dtype == TP_BF16 ? WT_BF16 : WT_F32;
+        const int hb = c.max_batch < 4 ? c.max_batch : 4;
+        if (qkv_attn_fusable(wt, 1, s.D, s.n_qkv, s.G, s.hd, c.kv_dtype == TP_BF16)) {
+            s.w_hand = o;
+            s.hand_bytes = 256 + (uint64_t)hb * s.n_qkv * 8;
+            o = align_up(o + s.hand_bytes, 256);
+        }
+    }
     s.ws_bytes = o;
     s.kv_bytes = B * s.Hkv_s * (uint64_t)c.max_ctx * s.hd * s.kv_esz;
     const uint64_t wq = align_up(B * D, 16) + B * (D / kQBlock) * 4;
@@ -659,7 +672,9 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *w, void *packed, void 
             return hip_fail(se, "load_weights: scratch address");
     }
     if (s->ws) {
-        const hipError_t ce = launch_clear_u32((unsigned *)(s->ws + s->w_err), 1, st);
+        hipError_t ce = launch_clear_u32((unsigned *)(s->ws + s->w_err), 1, st);
+        if (!ce && s->w_hand) // epoch 0 and no word carrying a tag
+            ce = launch_clear_u32((unsigned *)(s->ws + s->w_hand), (int)(s->hand_bytes / 4), st);
         if (ce)
             return hip_fail(ce, "load_weights: clear error word");
     }
@@ -909,9 +924,17 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         up.y = qkv;
         up.N = s->n_qkv;
         up.ldy = s->n_qkv;
-        rc = timed(s, KID_GEMV_QKV, st, "gemv qkv", [&] { return run_gemv(up, xfx, nullptr, EPI_STORE, sk_norm); });
-        if (rc)
-            return rc;
+        // batch <= 4 on the handle's own workspace (the hand-off words and
+        // the epoch live there): the projection and the chunk attention in
+        // one launch
+        const bool fused_qa = s->w_hand && ws == s->ws && fuse_norm &&
+                              qkv_attn_fusable(wt, B, s->D, s->n_qkv, s->G, s->hd, s->cfg.kv_dtype == TP_BF16);
+        if (!fused_qa) {
+            rc = timed(s, KID_GEMV_QKV, st, "gemv qkv",
+                       [&] { return run_gemv(up, xfx, nullptr, EPI_STORE, sk_norm); });
+            if (rc)
+                return rc;
+        }
         float *att = (float *)(ws + s->w_att);
         AttnArgs aa{};
         aa.qkv = qkv;
@@ -935,8 +958,15 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         aa.hd = s->hd;
         aa.n_chunks = s->n_chunks;
         aa.scale = (float)(1.0 / std::sqrt((double)s->hd));
-        rc = timed(s, KID_ATTN, st, "attention",
-                   [&] { return launch_attn(aa, s->cfg.kv_dtype == TP_BF16, B, st); });
+        if (fused_qa) {
+            char *hb = ws + s->w_hand;
+            rc = timed(s, KID_QKV_ATTN, st, "qkv + attention", [&] {
+                return launch_qkv_attn(up, aa, (uint64_t *)(hb + 256), (uint32_t *)hb, wt, B, st);
+            });
+        } else {
+            rc = timed(s, KID_ATTN, st, "attention",
+                       [&] { return launch_attn(aa, s->cfg.kv_dtype == TP_BF16, B, st); });
+        }
         if (rc)
             return rc;
         down.W = s->packed + s->o_wo;

@@ -60,6 +60,45 @@ __device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_
 // vector memory operation of this wave in flight afterwards
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
 
+// ---------------------------------------------------------------- RoPE
+// The rotation of one pair (x, y) by (c, s) = (cos, sin):
+// (x c - y s, x s + y c), each as one fused multiply-add over the other,
+// rounded, product. Written out so that every kernel rounds it the same way:
+// left to the compiler's contraction, which of the two products was fused
+// differed between kernels, by one ulp of the result.
+__device__ __forceinline__ float2 rope_pair(float x, float y, float c, float s)
+{
+    return make_float2(fmaf(x, c, -(y * s)), fmaf(x, s, y * c));
+}
+
+// ---------------------------------------------------------------- hand-off words
+// A value passed from one workgroup to another inside one launch: the fp32
+// bits in the low half and the launch's tag in the high half of one 8-byte
+// word, written and read by single agent-scope atomic accesses. These keep
+// the word coherent across the XCDs' separate L2 caches, and a reader that
+// sees the tag sees the value stored with it, so no fence is needed. The
+// tag is the stage's epoch + 1, never 0 (the zeroed region matches no tag).
+__device__ __forceinline__ void hand_publish(uint64_t *w, float v, uint32_t tag)
+{
+    __hip_atomic_store(w, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+// Two aligned hand-off words in one 16-byte load with the device-scope cache
+// policy (sc1, the bits the compiler gives an agent-scope atomic load): each
+// 8-byte word arrives whole, as it was stored, so its tag vouches for its
+// value; all of a lane's loads are issued before the first is waited on (a
+// chain of atomic loads would wait for each in turn).
+constexpr int kCpolSc1 = 16;
+__device__ __forceinline__ u32x4 hand_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1);
+}
+// error-word bits (the C header's TP_DERR_*)
+constexpr uint32_t kDerrLen = 1u, kDerrHandoff = 2u;
+// longest wait for hand-off words: 2^24 ticks of the 100 MHz real-time
+// counter (0.17 s), then kDerrHandoff is set and the waiter goes on
+constexpr uint64_t kHandWaitTicks = 1ull << 24;
+
 // ---------------------------------------------------------------- wave reductions
 
 // Rotation right by N lanes inside each 16-lane row (DPP row_ror:N, a VALU
@@ -363,6 +402,7 @@ struct AttnArgs {
     int ld_qkv, max_ctx, Hq_s, Hkv_s, G, hd, n_chunks;
     float scale;
     int B;               // sequences (set by launch_attn)
+    uint32_t *epoch;     // fused QKV + attention: the stage's epoch, advanced by the combine (else null)
 };
 
 struct WireArgs {
@@ -435,6 +475,9 @@ size_t gemv_sk_part_floats(int N, int K, int B);
 bool gemv_sk_used(int N, int K); // the batch-16 N x K projection takes the split-K kernels
 bool gemv_mfma_ok(int B, int N, int K, int w_bf16);
 hipError_t launch_attn(const AttnArgs &a, int kv_bf16, int B, hipStream_t st);
+bool qkv_attn_fusable(int wt, int B, int K, int N, int G, int hd, int kv_bf16);
+hipError_t launch_qkv_attn(const GemvArgs &g, const AttnArgs &a, uint64_t *hand, uint32_t *epoch, int wt,
+                           int B, hipStream_t st);
 size_t attn_lds_bytes(int G, int hd, int kv_bf16, int n_chunks);
 bool attn_hd_supported(int hd);
 size_t gemv_lds_bytes(int B, int K);

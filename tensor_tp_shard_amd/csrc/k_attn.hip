@@ -32,7 +32,7 @@
 //           publishing through agent-scope fences (which on this chip write
 //           back and invalidate a whole XCD L2 per workgroup) or than a last-
 //           arriving chunk workgroup doing it (measured slower).
-#include "common.h"
+#include "gemv_lds.h"
 
 namespace tps {
 
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
     const int L = a.lens[b];
     if (L < 0 || L >= a.max_ctx) { // skipped sequence: flagged here, zeroed by the combine
         if (c == 0 && g == 0 && tid == 0)
-            atomicOr(a.err, 1u);
+            atomicOr(a.err, kDerrLen);
         return;
     }
     const int t0 = c * kChunk;
@@ -154,8 +154,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
         const int i = tid + 256 * u;
         if (i < G * half) {
             const int j = i / half, p = i % half;
-            const float r0 = qp[u].x * cs[u].x - qp[u].y * cs[u].y;
-            const float r1 = qp[u].x * cs[u].y + qp[u].y * cs[u].x;
+            const float2 rr = rope_pair(qp[u].x, qp[u].y, cs[u].x, cs[u].y);
+            const float r0 = rr.x, r1 = rr.y;
             q_s[j * hd + 2 * p] = r0;
             q_s[j * hd + 2 * p + 1] = r1;
             if (c == 0 && a.tap_q) {
@@ -181,7 +181,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
         if (tid < half) {
             const int p = tid;
             const float2 cr = cs[0];
-            const float r0 = nk.x * cr.x - nk.y * cr.y, r1 = nk.x * cr.y + nk.y * cr.x;
+            const float2 rr = rope_pair(nk.x, nk.y, cr.x, cr.y);
+            const float r0 = rr.x, r1 = rr.y;
             const float v0 = nv.x, v1 = nv.y;
             const size_t e = head_base + (size_t)L * hd + 2 * p;
             store_kv<KBF16>(a.kc, e, r0);
@@ -323,8 +324,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
 // With the LDS form's staging, phase barriers and phase sums gone, the work
 // after the K / V loads arrive drops from ~2.4 us to a few hundred ns per
 // workgroup (7B shard: per-workgroup timestamps).
-template <bool KBF16, int GM, int HD>
-__global__ __launch_bounds__(256) void k_attn_reg(AttnArgs a)
+//
+// With HAND (the fused QKV projection + attention launch, k_qkv_attn), the
+// raw q / k / v come as hand-off words from the projection workgroups of the
+// same launch rather than from a.qkv: the K / V loads are issued first, then
+// the first 16 lanes of wave 0 wait for the words of the kv head's G queries
+// (and, in the chunk that owns position L, of the new key and value) until
+// every one carries the launch's tag, and pass them on through LDS; the
+// arithmetic is the same as from a.qkv, so the results are bitwise those of
+// the separate launches.
+template <bool KBF16, int GM, int HD, bool HAND>
+__device__ __forceinline__ void attn_reg_body(const AttnArgs &a, int c, int g, int b, const uint64_t *hand,
+                                              uint32_t tag)
 {
     constexpr int esz = KBF16 ? 2 : 4;
     static_assert(HD * esz == 256, "one 16-byte piece per lane of a 16-lane row");
@@ -333,12 +344,11 @@ __global__ __launch_bounds__(256) void k_attn_reg(AttnArgs a)
     __shared__ __attribute__((aligned(16))) float o_s[GM][4][4][ldo]; // [head][wave][row slot][dim]
     __shared__ float ml_s[GM][4][2];
     const int G = a.G;
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, rs = lane >> 4, col = lane & 15;
     const int L = a.lens[b];
     if (L < 0 || L >= a.max_ctx) { // skipped sequence: flagged here, zeroed by the combine
         if (c == 0 && g == 0 && tid == 0)
-            atomicOr(a.err, 1u);
+            atomicOr(a.err, kDerrLen);
         return;
     }
     const int t0 = c * kChunk;
@@ -350,12 +360,14 @@ __global__ __launch_bounds__(256) void k_attn_reg(AttnArgs a)
     // the query pieces and rotation factors first, then K and V (rows past
     // the sequence are not read: zero, so their values cannot reach o)
     float4 qr[GM][DP / 4];
+    if constexpr (!HAND) {
 #pragma unroll
-    for (int j = 0; j < GM; j++)
-        if (j < G)
+        for (int j = 0; j < GM; j++)
+            if (j < G)
 #pragma unroll
-            for (int e = 0; e < DP / 4; e++)
-                qr[j][e] = *(const float4 *)(qkv + (g * G + j) * HD + col * DP + 4 * e);
+                for (int e = 0; e < DP / 4; e++)
+                    qr[j][e] = *(const float4 *)(qkv + (g * G + j) * HD + col * DP + 4 * e);
+    }
     float4 cs[DP / 4]; // (cos, sin) of pairs col*DP/2 .. +DP/2-1 at position L
     const float4 *rope = (const float4 *)(a.rope + (size_t)L * (HD / 2) + col * (DP / 2));
 #pragma unroll
@@ -376,6 +388,59 @@ __global__ __launch_bounds__(256) void k_attn_reg(AttnArgs a)
             }
         }
     }
+    const int lr = L - t0;
+    // HAND: rows 0..G-1 the raw queries, G (GM) the new key, GM + 1 the new value
+    __shared__ __attribute__((aligned(16))) float hq_s[HAND ? GM + 2 : 1][HD];
+    if constexpr (HAND) {
+        if (wv == 0) {
+            const bool owner = lr < kChunk;
+            // the sequence's words; lane col holds dims col*DP .. +DP-1 of each row
+            const __amdgpu_buffer_rsrc_t hr = buf_rsrc(hand + (size_t)b * a.ld_qkv, (uint32_t)a.ld_qkv * 8u);
+            const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + kHandWaitTicks;
+            for (;;) {
+                asm volatile("" ::: "memory"); // a fresh load every round
+                bool ok = true;
+                if (rs == 0) {
+                    u32x4 hw[GM + 2][DP / 2];
+                    bool use[GM + 2];
+#pragma unroll
+                    for (int j = 0; j < GM + 2; j++) {
+                        const int row = j < GM ? (j < G ? g * G + j : -1)
+                                                : owner ? (j == GM ? a.Hq_s + g : a.Hq_s + a.Hkv_s + g) : -1;
+                        use[j] = row >= 0;
+#pragma unroll
+                        for (int e = 0; e < DP / 2; e++)
+                            hw[j][e] = hand_load16(hr, use[j] ? (uint32_t)(row * HD + col * DP + 2 * e) * 8u : kOob);
+                    }
+#pragma unroll
+                    for (int j = 0; j < GM + 2; j++)
+                        if (use[j])
+#pragma unroll
+                            for (int e = 0; e < DP / 2; e++) {
+                                const u32x4 w = hw[j][e];
+                                ok = ok && w.y == tag && w.w == tag;
+                                hq_s[j][col * DP + 2 * e] = __uint_as_float(w.x);
+                                hq_s[j][col * DP + 2 * e + 1] = __uint_as_float(w.z);
+                            }
+                }
+                if (__builtin_amdgcn_ballot_w64(!ok) == 0)
+                    break;
+                if (__builtin_amdgcn_s_memrealtime() > t_end) {
+                    if (lane == 0)
+                        atomicOr(a.err, kDerrHandoff);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < GM; j++)
+            if (j < G)
+#pragma unroll
+                for (int e = 0; e < DP / 4; e++)
+                    qr[j][e] = *(const float4 *)&hq_s[j][col * DP + 4 * e];
+    }
     // rotated queries (RoPE on adjacent pairs)
     float q[GM][DP];
 #pragma unroll
@@ -384,10 +449,11 @@ __global__ __launch_bounds__(256) void k_attn_reg(AttnArgs a)
 #pragma unroll
             for (int e = 0; e < DP / 4; e++) {
                 const float4 x = qr[j][e], r = cs[e];
-                q[j][4 * e + 0] = x.x * r.x - x.y * r.y;
-                q[j][4 * e + 1] = x.x * r.y + x.y * r.x;
-                q[j][4 * e + 2] = x.z * r.z - x.w * r.w;
-                q[j][4 * e + 3] = x.z * r.w + x.w * r.z;
+                const float2 r0 = rope_pair(x.x, x.y, r.x, r.y), r1 = rope_pair(x.z, x.w, r.z, r.w);
+                q[j][4 * e + 0] = r0.x;
+                q[j][4 * e + 1] = r0.y;
+                q[j][4 * e + 2] = r1.x;
+                q[j][4 * e + 3] = r1.y;
             }
     if (c == 0 && wv == 0 && rs == 0 && a.tap_q)
 #pragma unroll
@@ -399,19 +465,21 @@ __global__ __launch_bounds__(256) void k_attn_reg(AttnArgs a)
     // the owner of position L: its lanes rotate the new key, round key and
     // value to the cache type, append them and use them in place of the
     // loaded (stale) row
-    const int lr = L - t0;
     if (lr < kChunk && wv == lr >> 4 && rs == (lr & 3)) {
         const int i = (lr >> 2) & 3;
         float nk[DP], nv[DP];
 #pragma unroll
         for (int e = 0; e < DP / 4; e++) {
-            const float4 k4 = *(const float4 *)(qkv + (a.Hq_s + g) * HD + col * DP + 4 * e);
-            const float4 v4 = *(const float4 *)(qkv + (a.Hq_s + a.Hkv_s + g) * HD + col * DP + 4 * e);
+            const float4 k4 = HAND ? *(const float4 *)&hq_s[HAND ? GM : 0][col * DP + 4 * e]
+                                   : *(const float4 *)(qkv + (a.Hq_s + g) * HD + col * DP + 4 * e);
+            const float4 v4 = HAND ? *(const float4 *)&hq_s[HAND ? GM + 1 : 0][col * DP + 4 * e]
+                                   : *(const float4 *)(qkv + (a.Hq_s + a.Hkv_s + g) * HD + col * DP + 4 * e);
             const float4 r = cs[e];
-            nk[4 * e + 0] = k4.x * r.x - k4.y * r.y;
-            nk[4 * e + 1] = k4.x * r.y + k4.y * r.x;
-            nk[4 * e + 2] = k4.z * r.z - k4.w * r.w;
-            nk[4 * e + 3] = k4.z * r.w + k4.w * r.z;
+            const float2 r0 = rope_pair(k4.x, k4.y, r.x, r.y), r1 = rope_pair(k4.z, k4.w, r.z, r.w);
+            nk[4 * e + 0] = r0.x;
+            nk[4 * e + 1] = r0.y;
+            nk[4 * e + 2] = r1.x;
+            nk[4 * e + 3] = r1.y;
             nv[4 * e + 0] = v4.x;
             nv[4 * e + 1] = v4.y;
             nv[4 * e + 2] = v4.z;
@@ -547,6 +615,12 @@ __global__ __launch_bounds__(256) void k_attn_reg(AttnArgs a)
     }
 }
 
+template <bool KBF16, int GM, int HD>
+__global__ __launch_bounds__(256) void k_attn_reg(AttnArgs a)
+{
+    attn_reg_body<KBF16, GM, HD, false>(a, blockIdx.x, blockIdx.y, blockIdx.z, nullptr, 0u);
+}
+
 // ---------------------------------------------------------------- GQA on MFMA
 // The same work split and chunk records for a bf16 cache with G >= 4 q heads
 // per kv head, where the VALU version spends its time re-reading the G
@@ -637,7 +711,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
     c = __builtin_amdgcn_readfirstlane(c);
     L = __builtin_amdgcn_readfirstlane(L);
     if (bad && blockIdx.x == 0 && g == 0 && tid == 0)
-        atomicOr(a.err, 1u);
+        atomicOr(a.err, kDerrLen);
     if (b < 0)
         return;
     const int t0 = c * kChunk;
@@ -701,8 +775,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
         const int j = i / half, p = i % half;
         float r0 = 0.f, r1 = 0.f;
         if (j < G) {
-            r0 = qp[u].x * cs[u].x - qp[u].y * cs[u].y;
-            r1 = qp[u].x * cs[u].y + qp[u].y * cs[u].x;
+            const float2 rr = rope_pair(qp[u].x, qp[u].y, cs[u].x, cs[u].y);
+            r0 = rr.x;
+            r1 = rr.y;
             if (c == 0 && a.tap_q) {
                 const int h = g * G + j;
                 a.tap_q[(size_t)b * a.Hq_s * hd + h * hd + 2 * p] = r0;
@@ -731,7 +806,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a)
         if (tid < half) {
             const int p = tid, tl = L - t0;
             const float2 cr = cs[0];
-            const float r0 = nk.x * cr.x - nk.y * cr.y, r1 = nk.x * cr.y + nk.y * cr.x;
+            const float2 rr = rope_pair(nk.x, nk.y, cr.x, cr.y);
+            const float r0 = rr.x, r1 = rr.y;
             const size_t e = head_base + (size_t)L * hd + 2 * p;
             const uint16_t k0 = f32_to_bf16(r0), k1 = f32_to_bf16(r1);
             const uint16_t v0 = f32_to_bf16(nv.x), v1 = f32_to_bf16(nv.y);
@@ -832,6 +908,10 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(AttnArgs a)
 {
     extern __shared__ float smem[];
     const int hd = a.hd, h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    // after a fused QKV + attention launch: the next one's tag (every
+    // workgroup of that launch has read this one's)
+    if (a.epoch && h == 0 && b == 0 && tid == 0)
+        a.epoch[0] = (a.epoch[0] + 1u) & 0x7fffffffu;
     const size_t ob = (size_t)b * a.Hq_s * hd + (size_t)h * hd;
     const float *rec = a.part + ((size_t)b * a.Hq_s + h) * (size_t)a.n_chunks * (hd + 4);
     float *wts = smem;                                // [n_chunks] e^(m_c - M)
@@ -1001,9 +1081,96 @@ hipError_t launch_attn(const AttnArgs &args, int kv_bf16, int B, hipStream_t st)
 {
     AttnArgs a = args;
     a.B = B;
+    a.epoch = nullptr;
     const hipError_t e = kv_bf16 ? launch_attn_t<true>(a, B, st) : launch_attn_t<false>(a, B, st);
     if (e != hipSuccess)
         return e;
+    hipLaunchKernelGGL(k_combine, dim3(a.Hq_s, B), dim3(kCombThreads),
+                       combine_smem_bytes(a.G, a.hd, a.n_chunks), st, a);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------- QKV projection + attention in one launch
+// Below batch 5 with a 256-byte bf16 cache row and at most 2 q heads per kv
+// head (the register-resident attention; the 7B shard), the QKV projection
+// and the chunk attention share one launch: workgroups 0 .. n_proj - 1 run
+// the batch <= 4 GEMV (norm fused, every output also published as a hand-off
+// word), the rest the attention chunks, (chunk, kv head, sequence) with the
+// chunk fastest. An attention workgroup issues its K / V loads at once and
+// waits only for the hand-off words of its own kv head, so the cache stream
+// runs beside the weight stream instead of after it. Workgroups are
+// dispatched in id order, so every projection workgroup is running or done
+// before the first attention workgroup can wait (the projection never
+// waits), and the wait is bounded besides (kDerrHandoff). Then the combine,
+// which also advances the epoch the tags are made from.
+struct QkvAttnArgs {
+    GemvArgs g;
+    AttnArgs a;
+    uint64_t *hand;        // [B][n_qkv] hand-off words
+    const uint32_t *epoch; // the stage's epoch: this launch's tag is epoch + 1
+    int n_proj;            // projection workgroups (4 rows each)
+};
+
+template <int WT, int NB, int GM>
+__global__ __launch_bounds__(256) void k_qkv_attn(QkvAttnArgs q)
+{
+    extern __shared__ float xs[]; // the projection's [B][K] activations
+    const uint32_t tag = q.epoch[0] + 1u;
+    if ((int)blockIdx.x < q.n_proj) {
+        gemv_lds_body<WT, NB, 1, EPI_STORE, false, 4>(q.g, blockIdx.x, xs, q.hand, tag);
+        return;
+    }
+    const int id = (int)blockIdx.x - q.n_proj, nc = q.a.n_chunks;
+    attn_reg_body<true, GM, 128, true>(q.a, id % nc, (id / nc) % q.a.Hkv_s, id / (nc * q.a.Hkv_s), q.hand, tag);
+}
+
+bool qkv_attn_fusable(int wt, int B, int K, int N, int G, int hd, int kv_bf16)
+{
+    return (wt == WT_BF16 || wt == WT_I8) && B >= 1 && B <= 4 && gemv_fused_ok(B, K) && N < 6144 &&
+           kv_bf16 && hd == 128 && G >= 1 && G <= 2;
+}
+
+template <int WT, int NB>
+static void launch_qkv_attn_t(const QkvAttnArgs &q, dim3 grid, size_t sm, hipStream_t st)
+{
+    if (q.a.G <= 1)
+        hipLaunchKernelGGL((k_qkv_attn<WT, NB, 1>), grid, dim3(256), sm, st, q);
+    else
+        hipLaunchKernelGGL((k_qkv_attn<WT, NB, 2>), grid, dim3(256), sm, st, q);
+}
+
+// Host-checked preconditions: qkv_attn_fusable(...), g the QKV projection's
+// arguments (fused norm, EPI_STORE, no merge, y = a.qkv, ldy = a.ld_qkv =
+// N), hand [B][N] words and epoch zeroed before the first launch.
+hipError_t launch_qkv_attn(const GemvArgs &g, const AttnArgs &args, uint64_t *hand, uint32_t *epoch, int wt,
+                           int B, hipStream_t st)
+{
+    QkvAttnArgs q{g, args, hand, epoch, (g.N + 3) / 4};
+    q.a.B = B;
+    q.a.epoch = nullptr;
+    const dim3 grid(q.n_proj + q.a.n_chunks * q.a.Hkv_s * B);
+    const size_t sm = gemv_lds_bytes(B, g.K);
+    if (wt == WT_I8) {
+        if (B <= 1)
+            launch_qkv_attn_t<WT_I8, 1>(q, grid, sm, st);
+        else if (B <= 2)
+            launch_qkv_attn_t<WT_I8, 2>(q, grid, sm, st);
+        else
+            launch_qkv_attn_t<WT_I8, 4>(q, grid, sm, st);
+    } else {
+        if (B <= 1)
+            launch_qkv_attn_t<WT_BF16, 1>(q, grid, sm, st);
+        else if (B <= 2)
+            launch_qkv_attn_t<WT_BF16, 2>(q, grid, sm, st);
+        else
+            launch_qkv_attn_t<WT_BF16, 4>(q, grid, sm, st);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    AttnArgs a = args;
+    a.B = B;
+    a.epoch = epoch;
     hipLaunchKernelGGL(k_combine, dim3(a.Hq_s, B), dim3(kCombThreads),
                        combine_smem_bytes(a.G, a.hd, a.n_chunks), st, a);
     return hipGetLastError();

@@ -252,6 +252,23 @@ def test_register_attention_ragged_batch(kv, hd, n_kv):
     check_layer(w, d)
 
 
+@pytest.mark.parametrize("n_kv,quant", [(8, synth.Q_NONE), (4, synth.Q_WEIGHTS),
+                                         (8, synth.Q_PARTIALS | synth.Q_INPUTS)])
+def test_fused_qkv_attention_ragged_batch(n_kv, quant):
+    """Batch 4 with a bf16 cache of head dim 128 and 1 or 2 q heads per kv
+    head: the QKV projection and the attention in one launch (the queries
+    handed between its workgroups), lengths 0, 15, 64 and 130: the new token
+    alone, a wave's last slot, the first position of a chunk, a third chunk."""
+    w = synth.small_llama(name=f"micro_fused_{n_kv}_{quant}", dim=512, n_heads=8, n_kv_heads=n_kv,
+                          head_dim=128, ffn_hidden=512, tp=2, batch=4, past=(0, 130),
+                          w_dtype=synth.BF16, kv_dtype=synth.BF16, quant=quant, seed=86)
+    d = synth.llama_inputs(w)
+    d["lens"] = np.array([0, 15, 64, 130], np.int32)
+    d["kcache"] = synth.llama_kv_cache(w, d["lens"], "kcache")
+    d["vcache"] = synth.llama_kv_cache(w, d["lens"], "vcache")
+    check_layer(w, d)
+
+
 def test_attention_more_than_64_chunks():
     """A sequence of 4250 positions (67 chunks of 64) next to short ones: the
     combine reads its chunk records in two rounds of 64."""
