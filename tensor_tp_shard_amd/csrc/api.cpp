@@ -89,9 +89,12 @@ struct tp_shard {
     uint64_t o_sqkv, o_swo, o_sw13, o_sw2; // w8: scale arrays [N][K/32]
     // workspace layout (byte offsets)
     uint64_t w_err, w_xfx, w_xfatt, w_xfa, w_skp, w_xn, w_qkv, w_part, w_att, w_a, w_p, ws_bytes;
-    // fused QKV + attention (batch <= 4): the stage's epoch (one word, 256
-    // bytes reserved), then hand-off words [min(max_batch, 4)][n_qkv]; 0: none
-    uint64_t w_hand = 0, hand_bytes = 0;
+    // one-launch QKV + attention (batch <= 4): the stage's epoch (one word,
+    // 256 bytes reserved), then hand-off words [min(max_batch, 4)][n_qkv],
+    // then the chunk records as words [min(max_batch, 4)][Hq_s][n_chunks][hd
+    // + 4] (at w_hand + hand_rec); 0: none
+    uint64_t w_hand = 0, hand_bytes = 0, hand_rec = 0;
+    bool hand_dirty = false; // a stage failed after its fused launch: clear before the next
     int n_chunks;
     bool mfma_ok = false; // the batch 5..16 MFMA path applies to this shape
     uint64_t kv_bytes, wire_bytes, part_rows = 0;
@@ -356,7 +359,8 @@ int32_t plan(const tp_config &c, tp_shard &s)
         const int hb = c.max_batch < 4 ? c.max_batch : 4;
         if (qkv_attn_fusable(wt, 1, s.D, s.n_qkv, s.G, s.hd, c.kv_dtype == TP_BF16)) {
             s.w_hand = o;
-            s.hand_bytes = 256 + (uint64_t)hb * s.n_qkv * 8;
+            s.hand_rec = align_up(256 + (uint64_t)hb * s.n_qkv * 8, 256);
+            s.hand_bytes = s.hand_rec + (uint64_t)hb * s.Hq_s * s.n_chunks * (s.hd + 4) * 8;
             o = align_up(o + s.hand_bytes, 256);
         }
     }
@@ -960,9 +964,18 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         aa.scale = (float)(1.0 / std::sqrt((double)s->hd));
         if (fused_qa) {
             char *hb = ws + s->w_hand;
+            if (s->hand_dirty) { // epoch 0 and no word carrying a tag again
+                const hipError_t ce = launch_clear_u32((unsigned *)hb, (int)(s->hand_bytes / 4), st);
+                if (ce)
+                    return hip_fail(ce, "decode_step: clear hand-off words");
+                s->hand_dirty = false;
+            }
             rc = timed(s, KID_QKV_ATTN, st, "qkv + attention", [&] {
-                return launch_qkv_attn(up, aa, (uint64_t *)(hb + 256), (uint32_t *)hb, wt, B, st);
+                return launch_qkv_attn(up, aa, (uint64_t *)(hb + 256), (uint64_t *)(hb + s->hand_rec),
+                                       (const uint32_t *)hb, wt, B, st);
             });
+            down.epoch = (uint32_t *)hb; // W_O advances the epoch for the next launch
+            s->hand_dirty = rc != TP_OK;
         } else {
             rc = timed(s, KID_ATTN, st, "attention",
                        [&] { return launch_attn(aa, s->cfg.kv_dtype == TP_BF16, B, st); });
@@ -975,8 +988,11 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         down.K = Kd;
         down.ldx = Kd;
         rc = timed(s, KID_GEMV_WO, st, "gemv wo", [&] { return run_gemv(down, xfatt, nullptr, down_epi, false); });
-        if (rc)
+        if (rc) {
+            if (down.epoch)
+                s->hand_dirty = true;
             return rc;
+        }
     } else {
         float *a = (float *)(ws + s->w_a);
         up.W = s->packed + s->o_w13;

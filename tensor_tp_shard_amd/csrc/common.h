@@ -387,6 +387,11 @@ struct GemvArgs {
     MergeIn mo;
     int8_t *codes;       // EPI_Q8: [B][ldy] int8 codes of the wire
     float *scales;       // EPI_Q8: [B][ldy/32] block scales
+    // after a one-launch QKV + attention (the stage's W_O): the epoch whose
+    // + 1 tagged that launch's hand-off words, advanced by thread 0 of
+    // workgroup 0 (this kernel starts after every workgroup of that launch
+    // has read it); null otherwise
+    uint32_t *epoch;
 };
 
 struct AttnArgs {
@@ -402,7 +407,6 @@ struct AttnArgs {
     int ld_qkv, max_ctx, Hq_s, Hkv_s, G, hd, n_chunks;
     float scale;
     int B;               // sequences (set by launch_attn)
-    uint32_t *epoch;     // fused QKV + attention: the stage's epoch, advanced by the combine (else null)
 };
 
 struct WireArgs {
@@ -476,8 +480,8 @@ bool gemv_sk_used(int N, int K); // the batch-16 N x K projection takes the spli
 bool gemv_mfma_ok(int B, int N, int K, int w_bf16);
 hipError_t launch_attn(const AttnArgs &a, int kv_bf16, int B, hipStream_t st);
 bool qkv_attn_fusable(int wt, int B, int K, int N, int G, int hd, int kv_bf16);
-hipError_t launch_qkv_attn(const GemvArgs &g, const AttnArgs &a, uint64_t *hand, uint32_t *epoch, int wt,
-                           int B, hipStream_t st);
+hipError_t launch_qkv_attn(const GemvArgs &g, const AttnArgs &a, uint64_t *hand, uint64_t *recw,
+                           const uint32_t *epoch, int wt, int B, hipStream_t st);
 size_t attn_lds_bytes(int G, int hd, int kv_bf16, int n_chunks);
 bool attn_hd_supported(int hd);
 size_t gemv_lds_bytes(int B, int K);

@@ -177,6 +177,8 @@ __device__ __forceinline__ void gemv_lds_body(const GemvArgs &a, int blk, float 
     constexpr int KC = 8;           // chunk iterations per lane kept in flight
     __shared__ float red4[NW];
     const int tid = threadIdx.x, lane = tid & 63;
+    if (a.epoch && blk == 0 && tid == 0)
+        a.epoch[0] = (a.epoch[0] + 1u) & 0x7fffffffu;
     // the wave index twice: uniform for the weight buffers, and as a lane
     // value for the merge's element index (proven uniform, that address
     // would turn the merge preloads into scalar loads the wave waits on

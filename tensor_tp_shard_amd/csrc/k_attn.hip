@@ -328,14 +328,16 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a)
 // With HAND (the fused QKV projection + attention launch, k_qkv_attn), the
 // raw q / k / v come as hand-off words from the projection workgroups of the
 // same launch rather than from a.qkv: the K / V loads are issued first, then
-// the first 16 lanes of wave 0 wait for the words of the kv head's G queries
-// (and, in the chunk that owns position L, of the new key and value) until
-// every one carries the launch's tag, and pass them on through LDS; the
-// arithmetic is the same as from a.qkv, so the results are bitwise those of
-// the separate launches.
+// wave 0 waits for the words of the kv head's G queries (and, in the chunk
+// that owns position L, of the new key and value), one 16-lane row per row of
+// words, until every one carries the launch's tag, and passes them on
+// through LDS; the chunk
+// record goes out as tagged words (recw, laid out as a.part) to the combine
+// workgroups of the launch. The arithmetic is the same as from a.qkv, so the
+// results are bitwise those of the separate launches.
 template <bool KBF16, int GM, int HD, bool HAND>
 __device__ __forceinline__ void attn_reg_body(const AttnArgs &a, int c, int g, int b, const uint64_t *hand,
-                                              uint32_t tag)
+                                              uint64_t *recw, uint32_t tag)
 {
     constexpr int esz = KBF16 ? 2 : 4;
     static_assert(HD * esz == 256, "one 16-byte piece per lane of a 16-lane row");
@@ -392,36 +394,31 @@ __device__ __forceinline__ void attn_reg_body(const AttnArgs &a, int c, int g, i
     // HAND: rows 0..G-1 the raw queries, G (GM) the new key, GM + 1 the new value
     __shared__ __attribute__((aligned(16))) float hq_s[HAND ? GM + 2 : 1][HD];
     if constexpr (HAND) {
+        static_assert(!HAND || GM + 2 <= 4, "one 16-lane row of wave 0 per hand-off row");
         if (wv == 0) {
             const bool owner = lr < kChunk;
             // the sequence's words; lane col holds dims col*DP .. +DP-1 of each row
             const __amdgpu_buffer_rsrc_t hr = buf_rsrc(hand + (size_t)b * a.ld_qkv, (uint32_t)a.ld_qkv * 8u);
             const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + kHandWaitTicks;
+            // the 16-lane row rs of wave 0 takes hq_s row rs: q heads g G ..
+            // g G + G - 1, then (owner only) the new key and value
+            const int j = rs;
+            const int row = j < GM ? (j < G ? g * G + j : -1)
+                                   : owner ? (j == GM ? a.Hq_s + g : a.Hq_s + a.Hkv_s + g) : -1;
             for (;;) {
                 asm volatile("" ::: "memory"); // a fresh load every round
                 bool ok = true;
-                if (rs == 0) {
-                    u32x4 hw[GM + 2][DP / 2];
-                    bool use[GM + 2];
+                if (j < GM + 2 && row >= 0) {
+                    u32x4 hw[DP / 2];
 #pragma unroll
-                    for (int j = 0; j < GM + 2; j++) {
-                        const int row = j < GM ? (j < G ? g * G + j : -1)
-                                                : owner ? (j == GM ? a.Hq_s + g : a.Hq_s + a.Hkv_s + g) : -1;
-                        use[j] = row >= 0;
+                    for (int e = 0; e < DP / 2; e++)
+                        hw[e] = hand_load16(hr, (uint32_t)(row * HD + col * DP + 2 * e) * 8u);
 #pragma unroll
-                        for (int e = 0; e < DP / 2; e++)
-                            hw[j][e] = hand_load16(hr, use[j] ? (uint32_t)(row * HD + col * DP + 2 * e) * 8u : kOob);
+                    for (int e = 0; e < DP / 2; e++) {
+                        ok = ok && hw[e].y == tag && hw[e].w == tag;
+                        hq_s[j][col * DP + 2 * e] = __uint_as_float(hw[e].x);
+                        hq_s[j][col * DP + 2 * e + 1] = __uint_as_float(hw[e].z);
                     }
-#pragma unroll
-                    for (int j = 0; j < GM + 2; j++)
-                        if (use[j])
-#pragma unroll
-                            for (int e = 0; e < DP / 2; e++) {
-                                const u32x4 w = hw[j][e];
-                                ok = ok && w.y == tag && w.w == tag;
-                                hq_s[j][col * DP + 2 * e] = __uint_as_float(w.x);
-                                hq_s[j][col * DP + 2 * e + 1] = __uint_as_float(w.z);
-                            }
                 }
                 if (__builtin_amdgcn_ballot_w64(!ok) == 0)
                     break;
@@ -606,11 +603,20 @@ __device__ __forceinline__ void attn_reg_body(const AttnArgs &a, int c, int g, i
             o += e * ow;
             l += e * ml_s[j][w][1];
         }
-        float *rec = rec0 + j * rec_stride;
-        rec[4 + d] = o;
-        if (d == 0) {
-            rec[0] = M;
-            rec[1] = l;
+        if (HAND && recw) { // the same record as tagged words, for the combine workgroups
+            uint64_t *rw = recw + ((size_t)b * a.Hq_s + (size_t)g * G + j) * rec_stride + (size_t)c * (HD + 4);
+            hand_publish(rw + 4 + d, o, tag);
+            if (d == 0) {
+                hand_publish(rw, M, tag);
+                hand_publish(rw + 1, l, tag);
+            }
+        } else {
+            float *rec = rec0 + j * rec_stride;
+            rec[4 + d] = o;
+            if (d == 0) {
+                rec[0] = M;
+                rec[1] = l;
+            }
         }
     }
 }
@@ -618,7 +624,7 @@ __device__ __forceinline__ void attn_reg_body(const AttnArgs &a, int c, int g, i
 template <bool KBF16, int GM, int HD>
 __global__ __launch_bounds__(256) void k_attn_reg(AttnArgs a)
 {
-    attn_reg_body<KBF16, GM, HD, false>(a, blockIdx.x, blockIdx.y, blockIdx.z, nullptr, 0u);
+    attn_reg_body<KBF16, GM, HD, false>(a, blockIdx.x, blockIdx.y, blockIdx.z, nullptr, nullptr, 0u);
 }
 
 // ---------------------------------------------------------------- GQA on MFMA
@@ -908,10 +914,6 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(AttnArgs a)
 {
     extern __shared__ float smem[];
     const int hd = a.hd, h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    // after a fused QKV + attention launch: the next one's tag (every
-    // workgroup of that launch has read this one's)
-    if (a.epoch && h == 0 && b == 0 && tid == 0)
-        a.epoch[0] = (a.epoch[0] + 1u) & 0x7fffffffu;
     const size_t ob = (size_t)b * a.Hq_s * hd + (size_t)h * hd;
     const float *rec = a.part + ((size_t)b * a.Hq_s + h) * (size_t)a.n_chunks * (hd + 4);
     float *wts = smem;                                // [n_chunks] e^(m_c - M)
@@ -1012,6 +1014,142 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(AttnArgs a)
     }
 }
 
+// The combine of k_combine as run by one 256-thread workgroup of the fused
+// launch, on the chunk records published there as tagged words (recw): the
+// workgroup loads every word of the sequence's nch records in one round (at
+// most 18 16-byte loads a thread, all issued before the first is checked),
+// keeps the values in LDS, and repeats the round until every word carries
+// the launch's tag (a barrier-wide vote, bounded like the query wait); then
+// it computes from LDS exactly what k_combine's 512 threads compute, each
+// thread standing in for threads tid and tid + 256 of that kernel (the same
+// chunk phases, the same order of every sum), so att is bitwise the separate
+// combine's. hd = 128, n_chunks <= kHandCombChunks.
+constexpr int kHandCombChunks = 64;
+constexpr int kRecF = 128 + 4; // floats (words) of a chunk record at hd 128
+
+// LDS of the combine workgroup: the records, later the [16][128] phase sums
+// in the same place, then the chunk weights and 1 / l
+__host__ __device__ inline size_t hand_comb_region(int n_chunks)
+{
+    const size_t r = (size_t)n_chunks * kRecF, o = (size_t)(kCombThreads / 32) * 128;
+    return r > o ? r : o;
+}
+__host__ __device__ inline size_t hand_comb_smem_bytes(int n_chunks)
+{
+    return (hand_comb_region(n_chunks) + n_chunks + 4) * sizeof(float);
+}
+
+__device__ __forceinline__ void combine_hand_body(const AttnArgs &a, int h, int b, const uint64_t *recw,
+                                                  uint32_t tag, float *smem)
+{
+    constexpr int hd = 128, quads = hd / 4, cph = kCombThreads / quads, VT = kCombThreads / 256;
+    constexpr int rpieces = kRecF / 2;                          // 16-byte pieces of a record
+    constexpr int kBatch = 6, kRounds = 3;                      // 18 pieces a thread
+    static_assert(kBatch * kRounds * 256 >= kHandCombChunks * rpieces, "one round covers 64 records");
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const size_t ob = (size_t)b * a.Hq_s * hd + (size_t)h * hd;
+    float *rec_s = smem;                            // [nch][kRecF] the records; later [cph][hd] sums
+    float *wts = smem + hand_comb_region(a.n_chunks); // [n_chunks] e^(m_c - M)
+    float *inv_l = wts + a.n_chunks;                // [1]
+    const int L = a.lens[b];
+    if (L < 0 || L >= a.max_ctx) { // skipped sequence: its attention output is 0
+        for (int i = tid; i < hd; i += 256) {
+            a.att[ob + i] = 0.f;
+            if (a.tap_att)
+                a.tap_att[ob + i] = 0.f;
+        }
+        return;
+    }
+    const int nch = L / kChunk + 1, np = nch * rpieces;
+    const __amdgpu_buffer_rsrc_t rr =
+        buf_rsrc(recw + ((size_t)b * a.Hq_s + h) * (size_t)a.n_chunks * kRecF, (uint32_t)np * 16u);
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + kHandWaitTicks;
+    for (;;) {
+        asm volatile("" ::: "memory"); // a fresh load every round
+        bool ok = true;
+#pragma unroll
+        for (int r = 0; r < kRounds; r++) {
+            u32x4 v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; u++) {
+                const int pc = tid + 256 * (kBatch * r + u);
+                v[u] = hand_load16(rr, pc < np ? (uint32_t)pc * 16u : kOob);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; u++) {
+                const int pc = tid + 256 * (kBatch * r + u);
+                if (pc < np && pc % rpieces != 1) { // piece 1 of a record is never written
+                    ok = ok && v[u].y == tag && v[u].w == tag;
+                    *(float2 *)(rec_s + 2 * pc) = make_float2(__uint_as_float(v[u].x), __uint_as_float(v[u].z));
+                }
+            }
+        }
+        if (!__syncthreads_or(!ok))
+            break;
+        if (__builtin_amdgcn_s_memrealtime() > t_end) {
+            if (tid == 0)
+                atomicOr(a.err, kDerrHandoff);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    // (__syncthreads_or is a barrier: every record is in LDS)
+    if (w == 0) {
+        const float2 ml0 = lane < nch ? *(const float2 *)(rec_s + (size_t)lane * kRecF) : make_float2(-INFINITY, 0.f);
+        float m = ml0.x;
+        for (int cc = lane + 64; cc < nch; cc += 64)
+            m = fmaxf(m, rec_s[(size_t)cc * kRecF]);
+        const float M = group_max<64>(m);
+        float l = 0.f;
+        if (lane < nch) {
+            const float e = expf(ml0.x - M);
+            wts[lane] = e;
+            l = e * ml0.y;
+        }
+        for (int cc = lane + 64; cc < nch; cc += 64) {
+            const float2 q = *(const float2 *)(rec_s + (size_t)cc * kRecF);
+            const float e = expf(q.x - M);
+            wts[cc] = e;
+            l += e * q.y;
+        }
+        l = group_sum<64>(l);
+        if (lane == 0)
+            inv_l[0] = 1.0f / l;
+    }
+    __syncthreads();
+    float4 o[VT];
+#pragma unroll
+    for (int k = 0; k < VT; k++) {
+        const int vt = tid + 256 * k, cp = vt / quads, d = (vt % quads) * 4;
+        o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int cc = cp; cc < nch; cc += cph) {
+            const float4 v = *(const float4 *)(rec_s + (size_t)cc * kRecF + 4 + d);
+            const float wv = wts[cc];
+            o[k].x += wv * v.x;
+            o[k].y += wv * v.y;
+            o[k].z += wv * v.z;
+            o[k].w += wv * v.w;
+        }
+    }
+    __syncthreads(); // the records are read: their LDS takes the phase sums
+    float *osum = rec_s;
+#pragma unroll
+    for (int k = 0; k < VT; k++) {
+        const int vt = tid + 256 * k, cp = vt / quads, d = (vt % quads) * 4;
+        *(float4 *)(osum + (size_t)cp * hd + d) = o[k];
+    }
+    __syncthreads();
+    for (int i = tid; i < hd; i += 256) {
+        float t = 0.f;
+        for (int p = 0; p < cph; p++)
+            t += osum[(size_t)p * hd + i];
+        const float r = t * inv_l[0];
+        a.att[ob + i] = r;
+        if (a.tap_att)
+            a.tap_att[ob + i] = r;
+    }
+}
+
 static size_t combine_smem_bytes(int G, int hd, int n_chunks)
 {
     (void)G;
@@ -1081,7 +1219,6 @@ hipError_t launch_attn(const AttnArgs &args, int kv_bf16, int B, hipStream_t st)
 {
     AttnArgs a = args;
     a.B = B;
-    a.epoch = nullptr;
     const hipError_t e = kv_bf16 ? launch_attn_t<true>(a, B, st) : launch_attn_t<false>(a, B, st);
     if (e != hipSuccess)
         return e;
@@ -1101,27 +1238,39 @@ hipError_t launch_attn(const AttnArgs &args, int kv_bf16, int B, hipStream_t st)
 // runs beside the weight stream instead of after it. Workgroups are
 // dispatched in id order, so every projection workgroup is running or done
 // before the first attention workgroup can wait (the projection never
-// waits), and the wait is bounded besides (kDerrHandoff). Then the combine,
-// which also advances the epoch the tags are made from.
+// waits), and the wait is bounded besides (kDerrHandoff). Up to 64 chunks a
+// sequence, the last Hq_s x B workgroups combine the chunk records of one
+// (sequence, q head) each, taken as tagged words as soon as they are all
+// published, so the stage needs no combine launch (longer caches: k_combine
+// after the launch); W_O, the stage's next kernel, advances the epoch the
+// tags are made from.
 struct QkvAttnArgs {
     GemvArgs g;
     AttnArgs a;
     uint64_t *hand;        // [B][n_qkv] hand-off words
+    uint64_t *recw;        // [B][Hq_s][n_chunks][hd + 4] chunk records as hand-off words
     const uint32_t *epoch; // the stage's epoch: this launch's tag is epoch + 1
-    int n_proj;            // projection workgroups (4 rows each)
+    int n_proj, n_attn;    // projection workgroups (4 rows each), attention workgroups
+    // (then, with recw, Hq_s x B combine workgroups; without, float records
+    // in a.part for a k_combine launch)
 };
 
 template <int WT, int NB, int GM>
 __global__ __launch_bounds__(256) void k_qkv_attn(QkvAttnArgs q)
 {
-    extern __shared__ float xs[]; // the projection's [B][K] activations
+    extern __shared__ float xs[]; // the projection's [B][K] activations, or the combine's sums
     const uint32_t tag = q.epoch[0] + 1u;
-    if ((int)blockIdx.x < q.n_proj) {
-        gemv_lds_body<WT, NB, 1, EPI_STORE, false, 4>(q.g, blockIdx.x, xs, q.hand, tag);
-        return;
+    const int id = (int)blockIdx.x; // (q.recw: Hq_s x B combine workgroups after the attention)
+    if (id < q.n_proj) {
+        gemv_lds_body<WT, NB, 1, EPI_STORE, false, 4>(q.g, id, xs, q.hand, tag);
+    } else if (id < q.n_proj + q.n_attn) {
+        const int t = id - q.n_proj, nc = q.a.n_chunks;
+        attn_reg_body<true, GM, 128, true>(q.a, t % nc, (t / nc) % q.a.Hkv_s, t / (nc * q.a.Hkv_s), q.hand,
+                                           q.recw, tag);
+    } else {
+        const int t = id - q.n_proj - q.n_attn;
+        combine_hand_body(q.a, t % q.a.Hq_s, t / q.a.Hq_s, q.recw, tag, xs);
     }
-    const int id = (int)blockIdx.x - q.n_proj, nc = q.a.n_chunks;
-    attn_reg_body<true, GM, 128, true>(q.a, id % nc, (id / nc) % q.a.Hkv_s, id / (nc * q.a.Hkv_s), q.hand, tag);
 }
 
 bool qkv_attn_fusable(int wt, int B, int K, int N, int G, int hd, int kv_bf16)
@@ -1141,15 +1290,19 @@ static void launch_qkv_attn_t(const QkvAttnArgs &q, dim3 grid, size_t sm, hipStr
 
 // Host-checked preconditions: qkv_attn_fusable(...), g the QKV projection's
 // arguments (fused norm, EPI_STORE, no merge, y = a.qkv, ldy = a.ld_qkv =
-// N), hand [B][N] words and epoch zeroed before the first launch.
-hipError_t launch_qkv_attn(const GemvArgs &g, const AttnArgs &args, uint64_t *hand, uint32_t *epoch, int wt,
-                           int B, hipStream_t st)
+// N), hand [B][N] and recw [B][Hq_s][n_chunks][hd + 4] words and the epoch
+// zeroed before the first launch, and a later kernel of the stage advancing
+// the epoch after each launch (the W_O projection: GemvArgs::epoch).
+hipError_t launch_qkv_attn(const GemvArgs &g, const AttnArgs &args, uint64_t *hand, uint64_t *recw,
+                           const uint32_t *epoch, int wt, int B, hipStream_t st)
 {
-    QkvAttnArgs q{g, args, hand, epoch, (g.N + 3) / 4};
+    // the combine in the same launch while a sequence's records fit in LDS
+    const bool comb = args.n_chunks <= kHandCombChunks;
+    QkvAttnArgs q{g, args, hand, comb ? recw : nullptr, epoch, (g.N + 3) / 4, args.n_chunks * args.Hkv_s * B};
     q.a.B = B;
-    q.a.epoch = nullptr;
-    const dim3 grid(q.n_proj + q.a.n_chunks * q.a.Hkv_s * B);
-    const size_t sm = gemv_lds_bytes(B, g.K);
+    const dim3 grid(q.n_proj + q.n_attn + (comb ? q.a.Hq_s * B : 0));
+    const size_t sg = gemv_lds_bytes(B, g.K), sc = comb ? hand_comb_smem_bytes(q.a.n_chunks) : 0;
+    const size_t sm = sg > sc ? sg : sc;
     if (wt == WT_I8) {
         if (B <= 1)
             launch_qkv_attn_t<WT_I8, 1>(q, grid, sm, st);
@@ -1166,13 +1319,10 @@ hipError_t launch_qkv_attn(const GemvArgs &g, const AttnArgs &args, uint64_t *ha
             launch_qkv_attn_t<WT_BF16, 4>(q, grid, sm, st);
     }
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
+    if (e != hipSuccess || comb)
         return e;
-    AttnArgs a = args;
-    a.B = B;
-    a.epoch = epoch;
-    hipLaunchKernelGGL(k_combine, dim3(a.Hq_s, B), dim3(kCombThreads),
-                       combine_smem_bytes(a.G, a.hd, a.n_chunks), st, a);
+    hipLaunchKernelGGL(k_combine, dim3(q.a.Hq_s, B), dim3(kCombThreads),
+                       combine_smem_bytes(q.a.G, q.a.hd, q.a.n_chunks), st, q.a);
     return hipGetLastError();
 }
 

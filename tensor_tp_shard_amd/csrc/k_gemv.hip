@@ -53,6 +53,8 @@ __global__ __launch_bounds__(256) void k_gemv_gx(GemvArgs a)
     constexpr int U = 4;
     const int lane = threadIdx.x & 63;
     const int row0 = ((blockIdx.x * 256 + threadIdx.x) >> 6) * RPW;
+    if (a.epoch && blockIdx.x == 0 && threadIdx.x == 0)
+        a.epoch[0] = (a.epoch[0] + 1u) & 0x7fffffffu;
     if (row0 >= a.N)
         return;
     float mres = 0.f;
