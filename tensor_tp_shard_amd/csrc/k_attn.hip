@@ -1258,7 +1258,7 @@ struct QkvAttnArgs {
 template <int WT, int NB, int GM>
 __global__ __launch_bounds__(256) void k_qkv_attn(QkvAttnArgs q)
 {
-    extern __shared__ float xs[]; // the projection's [B][K] activations, or the combine's sums
+    extern __shared__ __attribute__((aligned(16))) float xs[]; // the projection's [B][K] activations, or the combine's sums
     const uint32_t tag = q.epoch[0] + 1u;
     const int id = (int)blockIdx.x; // (q.recw: Hq_s x B combine workgroups after the attention)
     if (id < q.n_proj) {

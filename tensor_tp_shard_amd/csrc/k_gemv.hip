@@ -38,7 +38,7 @@ namespace tps {
 template <int WT, int NB, int RPW, int EPI, bool MO, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gemv_lds(GemvArgs a)
 {
-    extern __shared__ float xs[]; // [B][K]
+    extern __shared__ __attribute__((aligned(16))) float xs[]; // [B][K]
     gemv_lds_body<WT, NB, RPW, EPI, MO, NW>(a, blockIdx.x, xs, nullptr, 0u);
 }
 

@@ -73,6 +73,12 @@ CASES = {
                                          head_dim=128, ffn_hidden=8192, tp=2, batch=16,
                                          past=(1, 40), w_dtype=synth.BF16, kv_dtype=synth.BF16,
                                          seed=306),
+    # QKV, attention, combine and W_O in one launch (bf16 cache of head dim
+    # 128, batch <= 4): W_O's merging store there
+    "fused_qkv_attn_b3": synth.small_llama(name="fused_qa", dim=512, n_heads=8, n_kv_heads=8,
+                                           head_dim=128, ffn_hidden=512, tp=4, batch=3,
+                                           past=(1, 100), w_dtype=synth.BF16, kv_dtype=synth.BF16,
+                                           seed=307),
     # dim > 8192 with int8 wires
     "wide_q8_b2": synth.small_llama(name="wide_q8", dim=8448, n_heads=4, n_kv_heads=4,
                                     head_dim=32, ffn_hidden=256, tp=2, batch=2, past=(2, 40),
