@@ -84,7 +84,8 @@ def sources_sha256(sources) -> str:
     return h.hexdigest()
 
 
-GEMV_SOURCES = ("tensor_tp_shard_amd/csrc/k_gemv.hip", "tensor_tp_shard_amd/csrc/common.h")
+GEMV_SOURCES = ("tensor_tp_shard_amd/csrc/k_gemv.hip", "tensor_tp_shard_amd/csrc/gemv_lds.h",
+                "tensor_tp_shard_amd/csrc/common.h")
 # batch 5..16 with bf16 weights: the MFMA projections
 GEMV_MFMA_SOURCES = ("tensor_tp_shard_amd/csrc/k_gemv_mfma.hip", "tensor_tp_shard_amd/csrc/common.h")
 FFN2D_SOURCES = ("tensor_tp_shard_amd/csrc/k_ffn2d.hip", "tensor_tp_shard_amd/csrc/common.h")
