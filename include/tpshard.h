@@ -387,6 +387,18 @@ int32_t tp_kernel_timing_read(tp_shard *s, double *total_ms, int32_t *launches);
 const char *tp_kernel_name(int32_t kernel_id); /* NULL past the last id */
 
 /*
+ * tp_handoff_test: for tests of the error path of the one-launch QKV +
+ * attention (decode_step, batch <= 4, see TP_DERR_HANDOFF). Sets, for the
+ * handle's later attention stages, the longest wait for another workgroup's
+ * values in ticks of the 100 MHz real-time counter (0: the normal 2^24) and a
+ * mask XORed into the tag the waiting workgroups look for (nonzero: a tag no
+ * word carries, so every wait runs out and TP_DERR_HANDOFF is set; the
+ * stage's outputs are then invalid). tp_handoff_test(s, 0, 0) restores the
+ * normal behaviour. Host only; errors: TP_EINVAL (null handle).
+ */
+int32_t tp_handoff_test(tp_shard *s, uint32_t wait_ticks, uint32_t tag_xor);
+
+/*
  * Measured-peak probes: the benchmark's measured denominators, not steps of
  * the shard. Enqueue only; the caller times them (HIP events).
  *  tp_probe_read: `blocks` workgroups read [buf, buf + bytes) once, each a

@@ -34,7 +34,7 @@ EXPORTS = ("init_shard", "load_weights", "decode_step", "decode_step_noalloc", "
            "tp_packed_int8_view",
            "tp_read_error_word", "tp_kernel_timing_arm", "tp_kernel_timing_read",
            "tp_kernel_name", "tp_probe_read", "tp_probe_mfma", "destroy_shard", "tp_status_str",
-           "tp_last_error")
+           "tp_last_error", "tp_handoff_test")
 
 
 class TpError(RuntimeError):
@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
         L.tp_probe_read.argtypes = [P, U64, P, I32, P]
         L.tp_probe_mfma.argtypes = [I32, I32, P, P]
         L.tp_kernel_name.argtypes = [I32]
+        L.tp_handoff_test.argtypes = [P, ctypes.c_uint32, ctypes.c_uint32]
         L.tp_kernel_name.restype = ctypes.c_char_p
         L.destroy_shard.argtypes = [P]
         L.destroy_shard.restype = None
@@ -235,6 +236,11 @@ def kernel_timing_read(handle):
     _check(lib().tp_kernel_timing_read(handle, ctypes.byref(ms), ctypes.byref(n)),
            "tp_kernel_timing_read")
     return ms.value, n.value
+
+
+def handoff_test(handle, wait_ticks: int, tag_xor: int) -> None:
+    """Test hook of the one-launch attention's bounded waits (tp_handoff_test)."""
+    _check(lib().tp_handoff_test(handle, wait_ticks, tag_xor), "tp_handoff_test")
 
 
 def kernel_names():

@@ -95,6 +95,7 @@ struct tp_shard {
     // + 4] (at w_hand + hand_rec); 0: none
     uint64_t w_hand = 0, hand_bytes = 0, hand_rec = 0;
     bool hand_dirty = false; // a stage failed after its fused launch: clear before the next
+    uint32_t hand_wait_ticks = 0, hand_tag_xor = 0; // tp_handoff_test (0, 0: normal)
     int n_chunks;
     bool mfma_ok = false; // the batch 5..16 MFMA path applies to this shape
     uint64_t kv_bytes, wire_bytes, part_rows = 0;
@@ -962,6 +963,8 @@ static int32_t step_impl(tp_shard *s, int32_t stage, const void *x, const MergeI
         aa.hd = s->hd;
         aa.n_chunks = s->n_chunks;
         aa.scale = (float)(1.0 / std::sqrt((double)s->hd));
+        aa.hand_wait_ticks = s->hand_wait_ticks;
+        aa.hand_tag_xor = s->hand_tag_xor;
         if (fused_qa) {
             char *hb = ws + s->w_hand;
             if (s->hand_dirty) { // epoch 0 and no word carrying a tag again
@@ -1293,6 +1296,15 @@ int32_t tp_kernel_timing_read(tp_shard *s, double *total_ms, int32_t *launches)
     }
     *total_ms = tot;
     *launches = (int32_t)s->ev_used;
+    return TP_OK;
+}
+
+int32_t tp_handoff_test(tp_shard *s, uint32_t wait_ticks, uint32_t tag_xor)
+{
+    if (!s)
+        return fail(TP_EINVAL, "tp_handoff_test: null handle");
+    s->hand_wait_ticks = wait_ticks;
+    s->hand_tag_xor = tag_xor;
     return TP_OK;
 }
 

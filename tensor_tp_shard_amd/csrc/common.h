@@ -407,7 +407,17 @@ struct AttnArgs {
     int ld_qkv, max_ctx, Hq_s, Hkv_s, G, hd, n_chunks;
     float scale;
     int B;               // sequences (set by launch_attn)
+    // one-launch QKV + attention, for the error-path test only (0, 0 otherwise):
+    // the longest wait for hand-off words in ticks (0: kHandWaitTicks) and a
+    // mask applied to the tag the waiting workgroups look for (nonzero: a tag
+    // no word carries, so every wait runs out)
+    uint32_t hand_wait_ticks, hand_tag_xor;
 };
+
+__device__ __forceinline__ uint64_t hand_wait_ticks(const AttnArgs &a)
+{
+    return a.hand_wait_ticks ? (uint64_t)a.hand_wait_ticks : kHandWaitTicks;
+}
 
 struct WireArgs {
     const float *p;      // [B][D]

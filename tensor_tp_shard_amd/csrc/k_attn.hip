@@ -399,7 +399,8 @@ __device__ __forceinline__ void attn_reg_body(const AttnArgs &a, int c, int g, i
             const bool owner = lr < kChunk;
             // the sequence's words; lane col holds dims col*DP .. +DP-1 of each row
             const __amdgpu_buffer_rsrc_t hr = buf_rsrc(hand + (size_t)b * a.ld_qkv, (uint32_t)a.ld_qkv * 8u);
-            const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + kHandWaitTicks;
+            const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + hand_wait_ticks(a);
+            const uint32_t want = tag ^ a.hand_tag_xor; // (a test's never-published tag when set)
             // the 16-lane row rs of wave 0 takes hq_s row rs: q heads g G ..
             // g G + G - 1, then (owner only) the new key and value
             const int j = rs;
@@ -415,7 +416,7 @@ __device__ __forceinline__ void attn_reg_body(const AttnArgs &a, int c, int g, i
                         hw[e] = hand_load16(hr, (uint32_t)(row * HD + col * DP + 2 * e) * 8u);
 #pragma unroll
                     for (int e = 0; e < DP / 2; e++) {
-                        ok = ok && hw[e].y == tag && hw[e].w == tag;
+                        ok = ok && hw[e].y == want && hw[e].w == want;
                         hq_s[j][col * DP + 2 * e] = __uint_as_float(hw[e].x);
                         hq_s[j][col * DP + 2 * e + 1] = __uint_as_float(hw[e].z);
                     }
@@ -1063,7 +1064,8 @@ __device__ __forceinline__ void combine_hand_body(const AttnArgs &a, int h, int 
     const int nch = L / kChunk + 1, np = nch * rpieces;
     const __amdgpu_buffer_rsrc_t rr =
         buf_rsrc(recw + ((size_t)b * a.Hq_s + h) * (size_t)a.n_chunks * kRecF, (uint32_t)np * 16u);
-    const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + kHandWaitTicks;
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + hand_wait_ticks(a);
+    const uint32_t want = tag ^ a.hand_tag_xor; // (a test's never-published tag when set)
     for (;;) {
         asm volatile("" ::: "memory"); // a fresh load every round
         bool ok = true;
@@ -1079,7 +1081,7 @@ __device__ __forceinline__ void combine_hand_body(const AttnArgs &a, int h, int 
             for (int u = 0; u < kBatch; u++) {
                 const int pc = tid + 256 * (kBatch * r + u);
                 if (pc < np && pc % rpieces != 1) { // piece 1 of a record is never written
-                    ok = ok && v[u].y == tag && v[u].w == tag;
+                    ok = ok && v[u].y == want && v[u].w == want;
                     *(float2 *)(rec_s + 2 * pc) = make_float2(__uint_as_float(v[u].x), __uint_as_float(v[u].z));
                 }
             }

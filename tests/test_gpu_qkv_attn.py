@@ -152,3 +152,31 @@ def test_fused_graph_replays_take_each_replays_inputs():
         assert _same(A.k_cache, Z.k_cache) and _same(A.v_cache, Z.v_cache), f"replay {rep}: caches"
         torch.zeros(1000, device="cuda").sum().item()  # eager work between replays
     assert tp.read_error_word(A.handle) == 0
+
+
+def test_handoff_wait_runs_out_sets_the_error_word():
+    """The bounded wait's error path, forced from the host (tp_handoff_test):
+    the waiting workgroups look for a tag no word carries, with a 20 us limit.
+    The launch ends, TP_DERR_HANDOFF is set; with the normal settings back, the
+    next call equals the separate launches again (the same cache slot is
+    written by both shards)."""
+    import torch
+    w, d, _ = _layer("mha_bf16")
+    A, Z = _twins(w, d, 0)
+    B = 2
+    x = dev_tensor(np.random.default_rng(105).standard_normal((B, w.dim)).astype(np.float32))
+    lens = dev_tensor(d["lens"][:B])
+    say("qkv + attention: hand-off waits forced to run out")
+    tp.handoff_test(A.handle, 2000, 0x40000000)
+    A.step(tp.TP_STAGE_ATTN, x, lens, B, A.new_wire())
+    torch.cuda.synchronize()
+    assert tp.read_error_word(A.handle) == tp.TP_DERR_HANDOFF
+    tp.handoff_test(A.handle, 0, 0)
+    wa, wz = A.new_wire(), Z.new_wire()
+    A.step(tp.TP_STAGE_ATTN, x, lens, B, wa)
+    Z.step_noalloc(tp.TP_STAGE_ATTN, x, lens, B, wz)
+    torch.cuda.synchronize()
+    n = _wire_bytes(w, A.cfg, B)
+    assert _same(wa[:n], wz[:n])
+    assert _same(A.k_cache, Z.k_cache) and _same(A.v_cache, Z.v_cache)
+    assert tp.read_error_word(A.handle) == 0
