@@ -558,10 +558,14 @@ __device__ __forceinline__ void attn_reg_body(const AttnArgs &a, int c, int g, i
             break;
         float m = fmaxf(fmaxf(sc[0][j], sc[1][j]), fmaxf(sc[2][j], sc[3][j]));
         m = fmaxf(fmaxf(lane_value(m, 0), lane_value(m, 16)), fmaxf(lane_value(m, 32), lane_value(m, 48)));
+        // the hardware exponential (__expf, a few ulp): each wave's chain of
+        // scores, softmax and values runs alone on its SIMD at this point, and
+        // the libm expf's range reduction made it measurably longer (7B step
+        // 36.9 -> 36.6 us); the exponent is <= 0, the weights within 1e-6
         float p[4], ls = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            p[i] = m == -INFINITY || sc[i][j] == -INFINITY ? 0.f : expf(sc[i][j] - m);
+            p[i] = m == -INFINITY || sc[i][j] == -INFINITY ? 0.f : __expf(sc[i][j] - m);
             ls += p[i];
         }
         const float l = (lane_value(ls, 0) + lane_value(ls, 16)) + (lane_value(ls, 32) + lane_value(ls, 48));
@@ -599,7 +603,7 @@ __device__ __forceinline__ void attn_reg_body(const AttnArgs &a, int c, int g, i
         float o = 0.f, l = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; w++) {
-            const float e = mw[w] == -INFINITY ? 0.f : expf(mw[w] - M);
+            const float e = mw[w] == -INFINITY ? 0.f : __expf(mw[w] - M);
             const float ow = (o_s[j][w][0][d] + o_s[j][w][1][d]) + (o_s[j][w][2][d] + o_s[j][w][3][d]);
             o += e * ow;
             l += e * ml_s[j][w][1];
