@@ -1050,11 +1050,13 @@ int32_t decode_step_noalloc(tp_shard *s, int32_t stage, const void *x, const int
         return fail(TP_EINVAL, "decode_step_noalloc applies to TP_LLAMA_BLOCK shards");
     if (!s->loaded)
         return fail(TP_ESTATE, "decode_step_noalloc before load_weights");
-    if (s->ws_bytes > kScratchBytes)
+    // (the hand-off region, last in the workspace, is not used here)
+    const uint64_t need = s->w_hand ? s->w_hand : s->ws_bytes;
+    if (need > kScratchBytes)
         return fail(TP_EINVAL,
                     "decode_step_noalloc: this shard needs %llu bytes of workspace, the static "
                     "scratch holds %llu (use decode_step with a workspace)",
-                    (unsigned long long)s->ws_bytes, (unsigned long long)kScratchBytes);
+                    (unsigned long long)need, (unsigned long long)kScratchBytes);
     if (err_out && ((uintptr_t)err_out & 3u))
         return fail(TP_EALIGN, "decode_step_noalloc: err_out not 4-byte aligned");
     void *sp = nullptr;

@@ -31,7 +31,11 @@
 //           sum_c l_c e^(m_c - M). A separate launch is cheaper here than
 //           publishing through agent-scope fences (which on this chip write
 //           back and invalidate a whole XCD L2 per workgroup) or than a last-
-//           arriving chunk workgroup doing it (measured slower).
+//           arriving chunk workgroup doing it (measured slower). Only the
+//           one-launch QKV + attention of a batch <= 4 stage (k_qkv_attn,
+//           below) combines in the same launch, its records passed as
+//           tagged 8-byte words that need no fence; for the MFMA attention
+//           at 70B that hand-off cost more than the launch it saves.
 #include "gemv_lds.h"
 
 namespace tps {

@@ -118,8 +118,8 @@ def test_fused_equals_separate_launches(case):
 def test_fused_graph_replays_take_each_replays_inputs():
     """The attention stage captured once and replayed with new inputs copied
     in between: every replay equals the separate launches on those inputs
-    (the combine advances the epoch that each replay's tags come from, so no
-    replay can take the previous one's hand-off words)."""
+    (the stage's W_O kernel advances the epoch that each replay's tags come
+    from, so no replay can take the previous one's hand-off words)."""
     import torch
     w, d, _ = _layer("mha_bf16")
     B = 3
