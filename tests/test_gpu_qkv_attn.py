@@ -180,3 +180,36 @@ def test_handoff_wait_runs_out_sets_the_error_word():
     assert _same(wa[:n], wz[:n])
     assert _same(A.k_cache, Z.k_cache) and _same(A.v_cache, Z.v_cache)
     assert tp.read_error_word(A.handle) == 0
+
+
+def test_fused_at_the_7b_shape_batch4_grid_beyond_residency():
+    """The 7B shard's shape (dim 4096, 8 of 32 heads, 2048 cached positions)
+    at batch 4: the one-launch grid (768 projection, 1056 attention and 32
+    combine workgroups) no longer fits on the GPU at once, so waiting
+    workgroups are resident while later producers wait for slots. Rank 0,
+    three calls in a row, bitwise against the separate launches."""
+    import dataclasses
+    import torch
+    w = dataclasses.replace(synth.L7B, name="qkv_attn_7b_b4", batch=4, past=(1500, 2048), seed=106)
+    d = synth.llama_inputs(w)
+    d["lens"] = np.array([2047, 1500, 1983, 1600], np.int32)
+    d["kcache"] = synth.llama_kv_cache(w, d["lens"] + 1, "kcache")
+    d["vcache"] = synth.llama_kv_cache(w, d["lens"] + 1, "vcache")
+    A, Z = _twins(w, d, 0)
+    rng = np.random.default_rng(107)
+    say("qkv + attention at the 7B shape, batch 4")
+    for call in range(3):
+        B = 4
+        x = dev_tensor(rng.standard_normal((B, w.dim)).astype(np.float32))
+        lens = dev_tensor(np.minimum(d["lens"] + call, w.max_ctx - 1).astype(np.int32))
+        wa, wz = A.new_wire(), Z.new_wire()
+        ta, tz = _taps(w, B), _taps(w, B)
+        A.step(tp.TP_STAGE_ATTN, x, lens, B, wa, ta)
+        Z.step_noalloc(tp.TP_STAGE_ATTN, x, lens, B, wz, tz)
+        torch.cuda.synchronize()
+        n = _wire_bytes(w, A.cfg, B)
+        assert _same(wa[:n], wz[:n]), f"call {call}: wires differ"
+        for k in ta:
+            assert _same(ta[k], tz[k]), f"call {call}: tap {k} differs"
+        assert _same(A.k_cache, Z.k_cache) and _same(A.v_cache, Z.v_cache), f"call {call}: caches"
+    assert tp.read_error_word(A.handle) == 0
