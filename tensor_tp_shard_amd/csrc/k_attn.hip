@@ -1245,10 +1245,13 @@ hipError_t launch_attn(const AttnArgs &args, int kv_bf16, int B, hipStream_t st)
 // word), the rest the attention chunks, (chunk, kv head, sequence) with the
 // chunk fastest. An attention workgroup issues its K / V loads at once and
 // waits only for the hand-off words of its own kv head, so the cache stream
-// runs beside the weight stream instead of after it. Workgroups are
-// dispatched in id order, so every projection workgroup is running or done
-// before the first attention workgroup can wait (the projection never
-// waits), and the wait is bounded besides (kDerrHandoff). Up to 64 chunks a
+// runs beside the weight stream instead of after it. The dispatcher hands
+// out a 1-D grid's workgroups in id order, so every projection workgroup is
+// running or done before the first attention workgroup can wait (the
+// projection never waits; at the 7B shape and batch 1 the whole grid is
+// resident at once anyway), and the wait is bounded besides (kDerrHandoff,
+// set by a workgroup that gives up: that stage's outputs are invalid; a
+// wait never outlives 0.17 s, so the kernel always ends). Up to 64 chunks a
 // sequence, the last Hq_s x B workgroups combine the chunk records of one
 // (sequence, q head) each, taken as tagged words as soon as they are all
 // published, so the stage needs no combine launch (longer caches: k_combine
