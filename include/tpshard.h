@@ -249,9 +249,10 @@ int32_t load_weights(tp_shard *s, const tp_layer_weights *full, void *packed, vo
  *    Otherwise fp32 [batch][D].
  *  taps: NULL or optional intermediate outputs (tp_taps).
  *  At batch <= 4 with a bf16 cache of head dim 128 and at most 2 q heads per
- *  kv head, the attention stage runs the QKV projection and the chunk
- *  attention as one launch (the queries handed between its workgroups);
- *  the results are bitwise those of the separate launches.
+ *  kv head, the attention stage runs the QKV projection, the chunk
+ *  attention and the combine of the chunks as one launch (queries and chunk
+ *  records handed between its workgroups as tagged words); the results are
+ *  bitwise those of the separate launches.
  * Errors: TP_EINVAL, TP_EALIGN, TP_ESTATE (no load_weights yet), TP_EHIP.
  */
 int32_t decode_step(tp_shard *s, int32_t stage, const void *x, const int32_t *lens,
