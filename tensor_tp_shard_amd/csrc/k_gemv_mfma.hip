@@ -35,15 +35,29 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxWk = 16;
 
-// Eight int8 codes -> the bf16 MFMA operand (exact: |code| <= 127 has at
-// most 7 significant bits): one sign-extending byte conversion to fp32 per
-// code, one packed fp32 -> bf16 conversion per two.
-__device__ __forceinline__ bf16x8 i8x8_to_bf16(u32x2 v)
+// Eight int8 codes -> the bf16 MFMA operand, biased: u = code + 128 (the
+// sign bit flipped, one xor per four codes) as exact bf16 integers in
+// [1, 255], one unsigned-byte conversion to fp32 per code and one packed
+// fp32 -> bf16 conversion per two. The product then carries 128 times the
+// block's activation sum too, taken out by starting the accumulator at
+// x . (-128) (kNeg128, an MFMA per activation half shared by the step's tiles).
+__device__ __forceinline__ bf16x8 i8x8_to_bf16_biased(u32x2 v)
+{
+    const uint32_t lo = v.x ^ 0x80808080u, hi = v.y ^ 0x80808080u;
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        o[e] = (__bf16)(float)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xffu);
+    return o;
+}
+
+// -128 in every element of a bf16 MFMA operand
+__device__ __forceinline__ bf16x8 neg128_bf16x8()
 {
     bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; e++)
-        o[e] = (__bf16)(float)(int8_t)(((e < 4 ? v.x : v.y) >> (8 * (e & 3))) & 0xffu);
+        o[e] = (__bf16)(-128.f);
     return o;
 }
 
@@ -52,8 +66,9 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16(u32x2 v)
 // byte; the register cost limits such workgroups to 8 waves.
 // W8: int8 codes with a scale per 32 k of a row. MFMA step s of 128-block j
 // then covers exactly the 32-block 4j + s (lane q holds its codes 8q..8q+7,
-// 8 contiguous bytes), so each step's product goes through a fresh
-// accumulator and is added times the scale. The operands swap roles
+// 8 contiguous bytes), so each step's product goes through an accumulator
+// of its own (started at the step's -128 x correction of the biased codes,
+// shared by the step's tiles) and is added times the scale. The operands swap roles
 // (activations A, weights B): lane (q, r) then holds batches 4q..4q+3 of the
 // single weight row r, whose scale is one value per step; the partial sums
 // go to the reduction buffer in the usual (row 4q + i, batch r) places.
@@ -117,13 +132,20 @@ __global__ __launch_bounds__(64 * mfma_max_waves(T, W8)) void k_gemv_mfma(MfmaGe
             if (j + p < j1)
 #pragma unroll
                 for (int s = 0; s < 4; s++)
+                {
+                    f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if constexpr (W8) {
+                        // c0[i] = -128 x (batch 4q + i) summed over the 32-block
+                        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xh[p][s]), neg128_bf16x8(), c0, 0, 0, 0);
+                        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xl[p][s]), neg128_bf16x8(), c0, 0, 0, 0);
+                    }
 #pragma unroll
                     for (int t = 0; t < T; t++) {
                         if constexpr (W8) {
-                            const bf16x8 wb = i8x8_to_bf16(w8[p][t][s]);
+                            const bf16x8 wb = i8x8_to_bf16_biased(w8[p][t][s]);
                             // d[i] = batch 4q + i of weight row r over 32-block 4 (j + p) + s
                             f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xh[p][s]), wb,
-                                                                              f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                                                                              c0, 0, 0, 0);
                             d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xl[p][s]), wb, d, 0, 0, 0);
                             const float scv = sc[p][t][s];
                             acc[t][0] += scv * d[0];
@@ -136,6 +158,7 @@ __global__ __launch_bounds__(64 * mfma_max_waves(T, W8)) void k_gemv_mfma(MfmaGe
                             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, __builtin_bit_cast(bf16x8, xl[p][s]), acc[t], 0, 0, 0);
                         }
                     }
+                }
     }
     // lane holds rows n0 + 16 t + 4q + i (i < 4) of batch column b = r
     const int b = r;
@@ -407,12 +430,17 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_sk(MfmaGemvArgs a)
                 for (int s = 0; s < 4; s++) {
                     const u32x4 xh = *(const u32x4 *)(lds + (((jl + p) * 2 + 0) * 4 + s) * 1024 + lane * 16);
                     const u32x4 xl = *(const u32x4 *)(lds + (((jl + p) * 2 + 1) * 4 + s) * 1024 + lane * 16);
+                    f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if constexpr (W8) {
+                        // c0[i] = -128 x (batch 4q + i) summed over the 32-block
+                        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xh), neg128_bf16x8(), c0, 0, 0, 0);
+                        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xl), neg128_bf16x8(), c0, 0, 0, 0);
+                    }
 #pragma unroll
                     for (int t = 0; t < T; t++) {
                         if constexpr (W8) {
-                            const bf16x8 wb = i8x8_to_bf16(w8[p][t][s]);
-                            f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xh), wb,
-                                                                              f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                            const bf16x8 wb = i8x8_to_bf16_biased(w8[p][t][s]);
+                            f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xh), wb, c0, 0, 0, 0);
                             d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xl), wb, d, 0, 0, 0);
                             const float scv = sc[p][t][s];
                             acc[t][0] += scv * d[0];
