@@ -113,3 +113,35 @@ def test_ffn2d_large_batch_tiles_and_ragged_tail(B, tile):
     full = B // tile * tile
     rows = sorted({0, 1, tile - 1, tile, 2 * tile - 1, full - tile, full - 1} | set(range(full, B)))
     _sampled_rows_check(w, rows)
+
+
+def test_palm_ffn2d_split_k_across_calls():
+    """The split-K down-projection on one handle over calls of 512, 130, 512
+    and 64 rows (4, 8, 4 and 8 splits sharing the partials buffer), each on
+    new inputs (the token rows rolled): every call's sampled rows against the
+    oracle (a partial left from an earlier call would show), the two 512-row
+    calls on the same inputs bitwise equal."""
+    import torch
+    w = synth.PALM_DEC
+    d = synth.ffn2d_inputs(w)
+    E = d["x"].shape[1]
+    F = d["w_gate"].shape[0]
+    cfg = tp.make_config(kind=tp.TP_FFN_2D, dim=E, ffn_hidden=F, tp_size=1, tp_rank=0,
+                         max_batch=w.batch, w_dtype=tp.TP_BF16)
+    sh = tp.Shard(cfg, caches=False)
+    sh.load({"w1": dev(d["w_gate"]), "w3": dev(d["w_in"]), "w2": dev(d["w_out"])})
+    outs = {}
+    for call, (B, shift) in enumerate([(512, 0), (130, 37), (512, 0), (64, 301)]):
+        xs = np.roll(d["x"], shift, axis=0)[:B]
+        say(f"ffn2d split-K: call {call}, {B} rows, roll {shift}")
+        y = torch.full((B, E), float("nan"), dtype=torch.float32, device="cuda")
+        sh.step(tp.TP_STAGE_FFN, dev(xs), None, B, y)
+        torch.cuda.synchronize()
+        y = y.cpu().numpy()
+        assert np.all(np.isfinite(y))
+        for r in sorted({0, 1, 63, B - 1} | {64 * t + 17 for t in range(B // 64)}):
+            ref = oracle.ffn2d(xs, d["w_gate"], d["w_in"], d["w_out"], row0=r, nrows=1)
+            e = rel_l2(y[r], ref[0])
+            assert e <= TOL, f"call {call} row {r} rel-L2 {e:.3e}"
+        outs.setdefault(B, []).append(y)
+    assert np.array_equal(outs[512][0].view(np.uint32), outs[512][1].view(np.uint32))
