@@ -82,9 +82,11 @@ def _sampled_rows_check(w, rows):
 
 def test_palm_ffn2d_decode_512_sampled_rows():
     """512 tokens: the down-projection splits K 4 ways and maps one split and
-    half the N-tiles to each XCD; a row in every 64-row M-tile (each row
-    covers every N-tile and split) plus tile edges."""
-    rows = sorted({0, 1, 63, 64, 127, 128, 300, 511} | {64 * t + 17 for t in range(8)})
+    half the N-tiles to each XCD; 128 rows (one in every 4, at every residue
+    mod 16, so every lane row of the 16-row MFMA tiles and every 64-row M-tile;
+    each row covers every N-tile and split) plus tile edges."""
+    rows = sorted({0, 1, 63, 64, 127, 128, 300, 511} | {64 * t + 17 for t in range(8)}
+                  | {4 * i + (i // 4) % 4 for i in range(128)})
     y = _sampled_rows_check(synth.PALM_DEC, rows)
     # deterministic: a second run is bitwise equal
     d = synth.ffn2d_inputs(synth.PALM_DEC)
@@ -94,14 +96,17 @@ def test_palm_ffn2d_decode_512_sampled_rows():
 
 def test_palm_ffn2d_prefill_8192_sampled_rows():
     """8192 tokens: the one-split down-projection gives each XCD 1/8 of the
-    256-row M-tiles with every N-tile; a row in every M-tile."""
-    _sampled_rows_check(synth.PALM_PRE, sorted({0, 4095, 8191} | {256 * t + 101 for t in range(32)}))
+    256-row M-tiles with every N-tile; a row in every M-tile, and 128 rows
+    spread over every 64-row quarter of them at varying offsets."""
+    _sampled_rows_check(synth.PALM_PRE, sorted({0, 4095, 8191} | {256 * t + 101 for t in range(32)}
+                                               | {64 * i + (5 * i) % 64 for i in range(128)}))
 
 
 def test_palm_ffn2d_weight_gathered_sampled_rows():
     """The weight-gathered prefill share (E = F' = 18432, 18432 tokens): the
-    same kernels at a 37.6 TFLOP shape; rows at 256-row tile edges."""
-    _sampled_rows_check(synth.PALM_GATHERED, [0, 255, 256, 18431])
+    same kernels at a 37.6 TFLOP shape; rows at 256-row tile edges and four
+    more inside tiles across the batch."""
+    _sampled_rows_check(synth.PALM_GATHERED, [0, 255, 256, 4711, 9300, 13057, 16421, 18431])
 
 
 @pytest.mark.parametrize("B,tile", [(2100, 128), (4100, 256)])
