@@ -391,6 +391,34 @@ def test_int8_weights_codes_and_layer(case):
             assert np.array_equal(got_s, se.view(np.uint32)), f"{case} shard {r} projection {proj}: scales"
 
 
+def test_w8_batch16_outlier_blocks():
+    """Batch 16 through the per-tile MFMA kernels with int8 weights whose
+    32-blocks each hold one weight of magnitude 2 among weights of deviation
+    0.02: every block's scale follows that outlier, so nearly all other codes
+    fall in -2..2. The MFMA
+    operand is code + 128 with the block's bias taken out by starting the
+    accumulator at -128 times the activations' sum, so these blocks are where
+    the two nearly cancel; the layer must still match the oracle's layer on
+    the dequantised weights, and the packed codes its codec."""
+    w = synth.small_llama(name="w8_outliers_b16", dim=1024, n_heads=8, n_kv_heads=2, head_dim=128,
+                          ffn_hidden=7936, tp=2, batch=16, past=(1, 70), w_dtype=synth.BF16,
+                          kv_dtype=synth.BF16, quant=synth.Q_WEIGHTS, seed=84)
+    d = synth.llama_inputs(w)
+    for k in ("wq", "wk", "wv", "wo", "w1", "w3", "w2"):
+        a = synth.bf16_bits_to_f32(d[k]).copy()
+        a[:, 5::32] = np.where(a[:, 5::32] >= 0, 2.0, -2.0)
+        d[k] = synth.f32_to_bf16_bits(a)
+    L, _, _ = check_layer(w, d)
+    from gpu_harness import to_np
+    for r in range(w.tp):
+        packed = to_np(L.shards[r].packed)
+        for proj, (ce, se) in enumerate(_w8_expected(w, d, r)):
+            co, so, rows, cols = tp.packed_int8_view(L.shards[r].handle, proj)
+            got_c = packed[co:co + rows * cols].view(np.int8).reshape(rows, cols)
+            assert np.array_equal(got_c, ce), f"shard {r} projection {proj}: codes differ"
+            assert np.mean(np.abs(ce.astype(np.int32)) <= 2) > 0.9  # the near-cancelling case
+
+
 def test_determinism_and_batch_rows():
     w = synth.small_llama(name="micro_b16", dim=256, n_heads=8, n_kv_heads=4, head_dim=32,
                           ffn_hidden=512, tp=2, batch=16, past=(1, 200), w_dtype=synth.BF16,
@@ -419,6 +447,20 @@ def test_llama70b_tp8_b16_all_shards_and_merges():
     oracle.use_threads(True)
     try:
         check_layer(synth.L70B)
+    finally:
+        oracle.use_threads(False)
+
+
+@pytest.mark.timeout(600)
+def test_llama70b_tp8_b16_int8_weights_all_shards():
+    """The 70B-shaped layer with int8 weights as it is benchmarked (TP = 8,
+    batch 16): the up-projections through the split-K int8 kernels with the
+    RMSNorm folded in, W_O and W2 through the per-tile int8 kernels, all 8
+    shards, KV appends and both merges against the oracle's layer on the
+    dequantised weights."""
+    oracle.use_threads(True)
+    try:
+        check_layer(synth.L70B_W8)
     finally:
         oracle.use_threads(False)
 
