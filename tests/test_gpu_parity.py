@@ -419,6 +419,45 @@ def test_w8_batch16_outlier_blocks():
             assert np.mean(np.abs(ce.astype(np.int32)) <= 2) > 0.9  # the near-cancelling case
 
 
+def test_three_layer_chain():
+    """Three layers in a row, as a decode step chains them: distinct weights
+    and KV caches per layer, one set of sequence lengths, every shard of
+    every layer with its merges, each layer fed the GPU's merged output of the
+    one before. At batch 3 with head dim 128 every attention stage is the
+    one-launch QKV + attention (each shard with its own hand-off words and
+    epoch). Each layer against the oracle's layer on the same input (the
+    per-row relative L2 of its update out - x), then the GPU's three-layer
+    update against the oracle's own chain from the first input; the error
+    words stay clear."""
+    base = dict(dim=512, n_heads=4, n_kv_heads=4, head_dim=128, ffn_hidden=1024, tp=2, batch=3,
+                past=(5, 150), w_dtype=synth.BF16, kv_dtype=synth.BF16)
+    ws = [synth.small_llama(name=f"chain{l}", seed=120 + l, **base) for l in range(3)]
+    ds = [synth.llama_inputs(w) for w in ws]
+    lens = ds[0]["lens"]
+    for w, d in zip(ws, ds):
+        d["lens"] = lens
+        d["kcache"] = synth.llama_kv_cache(w, lens, "kcache")
+        d["vcache"] = synth.llama_kv_cache(w, lens, "vcache")
+    layers = [Layer(w, d) for w, d in zip(ws, ds)]
+    tol = _tol(ws[0])
+    x0 = ds[0]["x"]
+    x_gpu, x_orc = x0, x0.astype(np.float64)
+    for l, (w, d, L) in enumerate(zip(ws, ds, layers)):
+        say(f"chain layer {l} lens={lens.tolist()}")
+        g = L.run(x_gpu, lens, with_taps=False)
+        o = oracle.llama_layer(w, d, x_gpu, lens, d["kcache"].copy(), d["vcache"].copy())
+        e, ma = _row_errs(g["out"] - x_gpu, o["out"] - x_gpu.astype(np.float64))
+        say(f"chain layer {l}: update rel-L2 {e:.2e} max-abs {ma:.2e}")
+        assert e <= tol, f"layer {l}"
+        x_orc = oracle.llama_layer(w, d, x_orc, lens, d["kcache"].copy(), d["vcache"].copy())["out"]
+        x_gpu = g["out"]
+        for r in range(w.tp):
+            assert L.error_word(r) == 0, f"layer {l} rank {r}"
+    e, ma = _row_errs(x_gpu - x0, x_orc - x0.astype(np.float64))
+    say(f"chain of 3: update rel-L2 {e:.2e} max-abs {ma:.2e}")
+    assert e <= 3 * tol
+
+
 def test_determinism_and_batch_rows():
     w = synth.small_llama(name="micro_b16", dim=256, n_heads=8, n_kv_heads=4, head_dim=32,
                           ffn_hidden=512, tp=2, batch=16, past=(1, 200), w_dtype=synth.BF16,
