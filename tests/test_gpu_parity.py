@@ -547,14 +547,31 @@ def test_bad_length_mfma_attention_skips_row():
         assert e <= 1e-3, f"row {b} rel-L2 {e:.3e}"
 
 
-def test_graph_replay_matches_eager():
+GRAPH_CASES = {
+    # batch 2, int8 wires and inputs: the LDS GEMVs with their int8 epilogues
+    "micro_q8_b2": (dict(dim=256, n_heads=8, n_kv_heads=8, head_dim=32, ffn_hidden=512, batch=2,
+                         past=(30, 70)), synth.Q_PARTIALS | synth.Q_INPUTS),
+    # batch 11 at dim 4096: split-K up-projections with the RMSNorm folded in,
+    # their reduce launches, the per-tile MFMA down-projections with the merge
+    "splitk_b11": (dict(dim=4096, n_heads=8, n_kv_heads=2, head_dim=128, ffn_hidden=7168, batch=11,
+                        past=(1, 40)), synth.Q_NONE),
+    "splitk_b11_w8": (dict(dim=4096, n_heads=8, n_kv_heads=2, head_dim=128, ffn_hidden=7168, batch=11,
+                           past=(1, 40)), synth.Q_WEIGHTS),
+}
+
+
+@pytest.mark.parametrize("case", list(GRAPH_CASES))
+def test_graph_replay_matches_eager(case):
+    """A whole layer step (every shard, both merges) captured once and
+    replayed three times, with the program's own eager work between the
+    replays: every replay bitwise equal to the eager step."""
     import torch
-    w = synth.small_llama(name="micro_graph", dim=256, n_heads=8, n_kv_heads=8, head_dim=32,
-                          ffn_hidden=512, tp=2, batch=2, past=(30, 70), w_dtype=synth.BF16,
-                          kv_dtype=synth.BF16, quant=synth.Q_PARTIALS | synth.Q_INPUTS, seed=80)
+    shape, quant = GRAPH_CASES[case]
+    w = synth.small_llama(name=f"graph_{case}", tp=2, w_dtype=synth.BF16, kv_dtype=synth.BF16,
+                          quant=quant, seed=80, **shape)
     d = synth.llama_inputs(w)
     from gpu_harness import dev_tensor
-    say("graph replay")
+    say(f"graph replay {case}")
     L = Layer(w, d)
     x = dev_tensor(d["x"])
     lens = dev_tensor(d["lens"])
