@@ -150,3 +150,41 @@ def test_palm_ffn2d_split_k_across_calls():
             assert e <= TOL, f"call {call} row {r} rel-L2 {e:.3e}"
         outs.setdefault(B, []).append(y)
     assert np.array_equal(outs[512][0].view(np.uint32), outs[512][1].view(np.uint32))
+
+
+def test_palm_ffn2d_graph_replays_match_eager():
+    """The 512-token block (up-projection, 4-way split-K down-projection and
+    its reduce) captured once and replayed three times with new inputs copied
+    in between and the program's own eager work after each: every replay
+    bitwise equal to an eager step on the same inputs."""
+    import torch
+    w = synth.PALM_DEC
+    d = synth.ffn2d_inputs(w)
+    B, E = d["x"].shape
+    F = d["w_gate"].shape[0]
+    cfg = tp.make_config(kind=tp.TP_FFN_2D, dim=E, ffn_hidden=F, tp_size=1, tp_rank=0,
+                         max_batch=B, w_dtype=tp.TP_BF16)
+    sh = tp.Shard(cfg, caches=False)
+    sh.load({"w1": dev(d["w_gate"]), "w3": dev(d["w_in"]), "w2": dev(d["w_out"])})
+    x = dev(d["x"])
+    y = torch.empty((B, E), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    say("ffn2d graph replays")
+    with torch.cuda.stream(s):
+        sh.step(tp.TP_STAGE_FFN, x, None, B, y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        sh.step(tp.TP_STAGE_FFN, x, None, B, y)
+    for rep, shift in enumerate((0, 101, 333)):
+        x.copy_(dev(np.roll(d["x"], shift, axis=0)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.cpu().numpy().copy()
+        ref = torch.empty_like(y)
+        sh.step(tp.TP_STAGE_FFN, x, None, B, ref)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.view(np.uint32), ref.cpu().numpy().view(np.uint32)), f"replay {rep}"
+        torch.zeros(1000, device="cuda").sum().item()  # eager work between replays
