@@ -153,3 +153,55 @@ def test_fused_merge_of_many_wires(case):
     sh.step_merge(tp.TP_STAGE_FFN, h, None, B, own, others[:9] + [own] + others[9:10], out)
     torch.cuda.synchronize()
     assert np.array_equal(_bits(out), _bits(ref))
+
+
+@pytest.mark.parametrize("case", ["fused_qkv_attn_b3", "micro_q8_b3", "splitk_bf16_b16"])
+def test_merge_step_graph_replays(case):
+    """Rank 0's whole layer step as the benchmark replays it: decode_merge_step
+    for the attention stage (one launch of QKV + attention at batch 3, its
+    W_O merging) and for the FFN stage, the other ranks' wires computed once
+    beforehand; captured once, replayed three times with new inputs copied in
+    between and the program's own eager work after each, every replay bitwise
+    equal to an eager step on the same inputs."""
+    import torch
+    w = CASES[case]
+    B = w.batch
+    d = synth.llama_inputs(w)
+    say(f"decode_merge_step graph replays {case}")
+    L = Layer(w, d)
+    ranks = L.ranks
+    x = dev_tensor(d["x"])
+    lens = dev_tensor(d["lens"])
+    wa, _ = L.stage(tp.TP_STAGE_ATTN, x, lens, B, with_taps=False)
+    h_ref = L.merge(tp.TP_STAGE_ATTN, wa, x, B)
+    wf, _ = L.stage(tp.TP_STAGE_FFN, h_ref, None, B, with_taps=False)
+    sh = L.shards[ranks[0]]
+    own_a, own_f = sh.new_wire(), sh.new_wire()
+    h, out = torch.empty_like(x), torch.empty_like(x)
+
+    def step(h, out):
+        sh.step_merge(tp.TP_STAGE_ATTN, x, lens, B, own_a, [own_a] + [wa[r] for r in ranks[1:]], h)
+        sh.step_merge(tp.TP_STAGE_FFN, h, None, B, own_f, [own_f] + [wf[r] for r in ranks[1:]], out)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(h, out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step(h, out)
+    rng = np.random.default_rng(308)
+    h_e, out_e = torch.empty_like(x), torch.empty_like(x)
+    for rep in range(3):
+        x.copy_(torch.from_numpy(rng.standard_normal(d["x"].shape).astype(np.float32)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_h, got_out = _bits(h).copy(), _bits(out).copy()
+        step(h_e, out_e)
+        torch.cuda.synchronize()
+        assert np.array_equal(got_h, _bits(h_e)), f"replay {rep}: h"
+        assert np.array_equal(got_out, _bits(out_e)), f"replay {rep}: out"
+        torch.zeros(1000, device="cuda").sum().item()  # eager work between replays
+    assert tp.read_error_word(sh.handle) == 0
